@@ -1,0 +1,396 @@
+// api.cpp -- C ABI of the TTT-MLP layer: validation, workspace planning and
+// the launch sequence on the caller's stream.  The semantics of every entry
+// point are documented in include/ttt_mlp.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/ttt_mlp.h"
+#include "layer.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ttt_status_t fail(ttt_status_t code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ttt_status_t fail(ttt_status_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+ttt_status_t ok() {
+  g_err.clear();
+  return TTT_OK;
+}
+
+// ---------------------------------------------------------------- profiling
+const char* const kStageNames[TTT_NUM_STAGES] = {"state_reset", "weight_prep", "pad_fill",
+                                                 "swiglu",      "target",      "prefix_update",
+                                                 "down_proj"};
+enum Stage { kReset = 0, kPrep, kPad, kSwiglu, kTarget, kPrefix, kDown };
+
+struct Profiler {
+  std::mutex mu;
+  bool enabled = false;
+  struct Rec {
+    int stage;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Profiler g_prof;
+
+// Enqueue one launch, bracketed by events when profiling is on.
+template <class F>
+hipError_t staged(int stage, hipStream_t s, F&& launch) {
+  hipEvent_t a = nullptr, b = nullptr;
+  bool prof;
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    prof = g_prof.enabled;
+    if (prof) {
+      a = g_prof.get();
+      b = g_prof.get();
+    }
+  }
+  if (prof && a) (void)hipEventRecord(a, s);
+  const hipError_t err = launch();
+  if (prof && b) (void)hipEventRecord(b, s);
+  if (prof) {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (a && b)
+      g_prof.recs.push_back({stage, a, b});
+    else {
+      if (a) g_prof.pool.push_back(a);
+      if (b) g_prof.pool.push_back(b);
+    }
+  }
+  return err;
+}
+
+// ----------------------------------------------------------------- checking
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(const Range& x, const Range& y) {
+  return x.lo < y.hi && y.lo < x.hi && x.hi > x.lo && y.hi > y.lo;
+}
+
+Range range(const char* name, const void* p, size_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{name, lo, lo + bytes};
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxInt32 = 2147483647;
+
+ttt_status_t make_dims(const ttt_mlp_desc_t* desc, ttt::Dims* dm) {
+  if (!desc) return fail(TTT_ERR_INVALID_ARGUMENT, "desc is NULL");
+  const ttt_mlp_desc_t& q = *desc;
+  if (q.batch < 1) return fail(TTT_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %lld)", (long long)q.batch);
+  if (q.seq_len < 1) return fail(TTT_ERR_INVALID_ARGUMENT, "seq_len must be >= 1 (got %lld)", (long long)q.seq_len);
+  if (q.d_model < 64 || q.d_model % 64)
+    return fail(TTT_ERR_UNSUPPORTED, "d_model must be a positive multiple of 64 (got %lld)", (long long)q.d_model);
+  if (q.d_ff < 64 || q.d_ff % 64)
+    return fail(TTT_ERR_UNSUPPORTED, "d_ff must be a positive multiple of 64 (got %lld)", (long long)q.d_ff);
+  if (q.chunk < 1) return fail(TTT_ERR_INVALID_ARGUMENT, "chunk must be >= 1 (got %d)", q.chunk);
+  if (q.conv_k < 1) return fail(TTT_ERR_INVALID_ARGUMENT, "conv_k must be >= 1 (got %d)", q.conv_k);
+  if (q.conv_k > 8) return fail(TTT_ERR_UNSUPPORTED, "conv_k must be <= 8 (got %d)", q.conv_k);
+  if (!std::isfinite(q.eta)) return fail(TTT_ERR_INVALID_ARGUMENT, "eta must be finite");
+  if (q.dtype != TTT_F32 && q.dtype != TTT_BF16)
+    return fail(TTT_ERR_INVALID_ARGUMENT, "dtype must be TTT_F32 or TTT_BF16 (got %d)", (int)q.dtype);
+  if (q.mode != TTT_MODE_AUTO && q.mode != TTT_MODE_SEQUENTIAL && q.mode != TTT_MODE_CHUNK_PARALLEL)
+    return fail(TTT_ERR_INVALID_ARGUMENT, "unknown mode %d", (int)q.mode);
+  if (q.init_from_w0 != 0 && q.init_from_w0 != 1)
+    return fail(TTT_ERR_INVALID_ARGUMENT, "init_from_w0 must be 0 or 1");
+  ttt::Dims d{};
+  d.B = q.batch;
+  d.T = q.seq_len;
+  d.d = q.d_model;
+  d.f = q.d_ff;
+  d.C = std::min<int64_t>(q.chunk, q.seq_len);  // C >= T is one chunk of T tokens
+  d.N = (d.T + d.C - 1) / d.C;
+  d.Cp = (d.C + 63) / 64 * 64;
+  d.K = q.conv_k;
+  d.eta = q.eta;
+  d.dt = q.dtype == TTT_BF16 ? ttt::Dtype::BF16 : ttt::Dtype::F32;
+  if (d.B > kMaxInt32 / d.T) return fail(TTT_ERR_UNSUPPORTED, "batch * seq_len must be < 2^31");
+  if (d.d * d.f > kMaxInt32) return fail(TTT_ERR_UNSUPPORTED, "d_model * d_ff must be < 2^31");
+  if (d.B * d.N > kMaxInt32 / d.Cp) return fail(TTT_ERR_UNSUPPORTED, "padded token count must be < 2^31");
+  d.P = d.B * d.N * d.Cp;
+  if (d.f > kMaxInt32 / d.P) return fail(TTT_ERR_UNSUPPORTED, "d_ff * padded tokens must be < 2^31");
+  *dm = d;
+  return TTT_OK;
+}
+
+ttt_status_t plan_group(const ttt::Dims& dm, ttt_mode_t mode, size_t ws_bytes, int64_t* group) {
+  const ttt::WorkspacePlan p1 = ttt::plan_workspace(dm, 1);
+  if (ws_bytes < p1.total_bytes)
+    return fail(TTT_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is below the minimum %zu",
+                ws_bytes, p1.total_bytes);
+  int64_t g = 1;
+  if (mode != TTT_MODE_SEQUENTIAL) {
+    const size_t room = (ws_bytes - p1.fixed_bytes) / p1.slot_bytes;
+    g = std::max<int64_t>(1, std::min<int64_t>(dm.N, (int64_t)std::min<size_t>(room, (size_t)dm.N)));
+  }
+  *group = g;
+  return TTT_OK;
+}
+
+ttt_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(TTT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// The whole layer for B sequences whose starting weights are in W_state.
+ttt_status_t run_layer(const ttt::Dims& dm, ttt_mode_t mode, bool reset, const void* H,
+                       const void* X0, const void* Wg, const void* Wu, const void* W0,
+                       const void* taps, const void* Wt, void* O, float* W_state, void* ws,
+                       size_t ws_bytes, hipStream_t s) {
+  int64_t G = 1;
+  ttt_status_t st = plan_group(dm, mode, ws_bytes, &G);
+  if (st) return st;
+  const ttt::WorkspacePlan wp = ttt::plan_workspace(dm, G);
+  char* base = static_cast<char*>(ws);
+  void* Z = base + wp.z_off;
+  void* Zt = base + wp.zt_off;
+  void* Vt = base + wp.vt_off;
+  void* WtT = base + wp.wtt_off;
+  float* tapsT = reinterpret_cast<float*>(base + wp.taps_off);
+  void* slots = base + wp.slots_off;
+
+  hipError_t e;
+  if (reset) {
+    e = staged(kReset, s, [&] { return ttt::launch_state_reset(W_state, W0, dm.dt, dm.B, dm.d, dm.f, s); });
+    if (e != hipSuccess) return hip_fail(e, "state_reset");
+  }
+  e = staged(kPrep, s, [&] {
+    const hipError_t r = ttt::launch_transpose(WtT, Wt, dm.d, dm.dt, s);
+    if (r != hipSuccess) return r;
+    return ttt::launch_taps(tapsT, taps, dm, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "weight_prep");
+  const bool padded = dm.Cp != dm.C || dm.T % dm.C != 0;
+  if (padded) {
+    e = staged(kPad, s, [&] { return ttt::launch_pad_fill(Zt, Vt, dm, s); });
+    if (e != hipSuccess) return hip_fail(e, "pad_fill");
+  }
+  e = staged(kSwiglu, s, [&] { return ttt::launch_swiglu(dm, H, Wg, Wu, Z, Zt, s); });
+  if (e != hipSuccess) return hip_fail(e, "swiglu");
+  e = staged(kTarget, s, [&] { return ttt::launch_target(dm, X0, tapsT, WtT, Vt, s); });
+  if (e != hipSuccess) return hip_fail(e, "target");
+  for (int64_t g0 = 0; g0 < dm.N; g0 += G) {
+    const int64_t gc = std::min<int64_t>(G, dm.N - g0);
+    e = staged(kPrefix, s, [&] { return ttt::launch_prefix_update(dm, Vt, Zt, W_state, slots, g0, gc, s); });
+    if (e != hipSuccess) return hip_fail(e, "prefix_update");
+    e = staged(kDown, s, [&] { return ttt::launch_down_proj(dm, Z, slots, O, g0, gc, s); });
+    if (e != hipSuccess) return hip_fail(e, "down_proj");
+  }
+  return ok();
+}
+
+struct Buffers {
+  const void *H, *X0, *Wg, *Wu, *W0, *taps, *Wt;
+  void* O;
+  float* W;
+  void* ws;
+  size_t ws_bytes;
+};
+
+ttt_status_t check_buffers(const ttt::Dims& dm, const Buffers& b, bool need_w0) {
+  struct P {
+    const char* name;
+    const void* p;
+    bool needed;
+  } ptrs[] = {{"H", b.H, true},       {"X0", b.X0, true},     {"W_gate", b.Wg, true},
+              {"W_up", b.Wu, true},   {"W_down0", b.W0, need_w0}, {"conv_taps", b.taps, true},
+              {"W_target", b.Wt, true}, {"O", b.O, true},     {"W_state", b.W, true},
+              {"ws", b.ws, true}};
+  for (const P& q : ptrs) {
+    if (!q.needed) continue;
+    if (!q.p) return fail(TTT_ERR_INVALID_ARGUMENT, "%s is NULL", q.name);
+    if (!aligned(q.p, 16)) return fail(TTT_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", q.name);
+  }
+  if (!aligned(b.ws, 256)) return fail(TTT_ERR_INVALID_ARGUMENT, "ws is not 256-byte aligned");
+  const size_t es = ttt::dtype_bytes(dm.dt);
+  const size_t act = (size_t)(dm.B * dm.T) * dm.d * es;
+  std::vector<Range> ins = {range("H", b.H, act),
+                            range("X0", b.X0, act),
+                            range("W_gate", b.Wg, (size_t)dm.f * dm.d * es),
+                            range("W_up", b.Wu, (size_t)dm.f * dm.d * es),
+                            range("conv_taps", b.taps, (size_t)dm.d * dm.K * es),
+                            range("W_target", b.Wt, (size_t)dm.d * dm.d * es)};
+  if (need_w0) ins.push_back(range("W_down0", b.W0, (size_t)dm.d * dm.f * es));
+  const Range outs[] = {range("O", b.O, act),
+                        range("W_state", b.W, (size_t)dm.B * dm.d * dm.f * sizeof(float)),
+                        range("ws", b.ws, b.ws_bytes)};
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (overlaps(o, i)) return fail(TTT_ERR_INVALID_ARGUMENT, "%s overlaps input %s", o.name, i.name);
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outs[j]))
+        return fail(TTT_ERR_INVALID_ARGUMENT, "%s overlaps %s", outs[i].name, outs[j].name);
+  return TTT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ttt_mlp_workspace_size(const ttt_mlp_desc_t* desc, int64_t max_group) {
+  ttt::Dims dm;
+  if (make_dims(desc, &dm)) return 0;
+  if (max_group < 0) {
+    fail(TTT_ERR_INVALID_ARGUMENT, "max_group must be >= 0");
+    return 0;
+  }
+  const int64_t g = max_group == 0 ? dm.N : std::min<int64_t>(max_group, dm.N);
+  ok();
+  return ttt::plan_workspace(dm, g).total_bytes;
+}
+
+int64_t ttt_mlp_group_size(const ttt_mlp_desc_t* desc, size_t ws_bytes) {
+  ttt::Dims dm;
+  ttt_status_t st = make_dims(desc, &dm);
+  if (st) return st;
+  int64_t g = 0;
+  st = plan_group(dm, desc->mode, ws_bytes, &g);
+  if (st) return st;
+  ok();
+  return g;
+}
+
+ttt_status_t ttt_mlp_forward(const ttt_mlp_desc_t* desc, const void* H, const void* X0,
+                             const void* W_gate, const void* W_up, const void* W_down0,
+                             const void* conv_taps, const void* W_target, void* O,
+                             float* W_down_final, void* ws, size_t ws_bytes, void* stream) {
+  ttt::Dims dm;
+  ttt_status_t st = make_dims(desc, &dm);
+  if (st) return st;
+  if (dm.B != 1) return fail(TTT_ERR_INVALID_ARGUMENT, "ttt_mlp_forward takes one sequence (batch == 1)");
+  const Buffers b{H, X0, W_gate, W_up, W_down0, conv_taps, W_target, O, W_down_final, ws, ws_bytes};
+  st = check_buffers(dm, b, true);
+  if (st) return st;
+  int64_t g;
+  st = plan_group(dm, desc->mode, ws_bytes, &g);
+  if (st) return st;
+  return run_layer(dm, desc->mode, true, H, X0, W_gate, W_up, W_down0, conv_taps, W_target, O,
+                   W_down_final, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+ttt_status_t ttt_mlp_forward_batched(const ttt_mlp_desc_t* desc, const void* H, const void* X0,
+                                     const void* W_gate, const void* W_up, const void* W_down0,
+                                     const void* conv_taps, const void* W_target, void* O,
+                                     float* W_state, void* ws, size_t ws_bytes, void* stream) {
+  ttt::Dims dm;
+  ttt_status_t st = make_dims(desc, &dm);
+  if (st) return st;
+  const bool init = desc->init_from_w0 == 1;
+  const Buffers b{H, X0, W_gate, W_up, W_down0, conv_taps, W_target, O, W_state, ws, ws_bytes};
+  st = check_buffers(dm, b, init);
+  if (st) return st;
+  int64_t g;
+  st = plan_group(dm, desc->mode, ws_bytes, &g);
+  if (st) return st;
+  return run_layer(dm, desc->mode, init, H, X0, W_gate, W_up, W_down0, conv_taps, W_target, O,
+                   W_state, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+ttt_status_t ttt_fastweight_state_reset(float* W_state, const void* W_down0, ttt_dtype_t w0_dtype,
+                                        int64_t batch, int64_t d_model, int64_t d_ff,
+                                        void* stream) {
+  if (!W_state || !W_down0) return fail(TTT_ERR_INVALID_ARGUMENT, "W_state and W_down0 must be non-NULL");
+  if (!aligned(W_state, 16) || !aligned(W_down0, 16))
+    return fail(TTT_ERR_INVALID_ARGUMENT, "W_state and W_down0 must be 16-byte aligned");
+  if (w0_dtype != TTT_F32 && w0_dtype != TTT_BF16)
+    return fail(TTT_ERR_INVALID_ARGUMENT, "w0_dtype must be TTT_F32 or TTT_BF16");
+  if (batch < 1 || d_model < 1 || d_ff < 1)
+    return fail(TTT_ERR_INVALID_ARGUMENT, "batch, d_model and d_ff must be >= 1");
+  if (d_model > kMaxInt32 / d_ff) return fail(TTT_ERR_UNSUPPORTED, "d_model * d_ff must be < 2^31");
+  const ttt::Dtype dt = w0_dtype == TTT_BF16 ? ttt::Dtype::BF16 : ttt::Dtype::F32;
+  const size_t n = (size_t)d_model * d_ff;
+  if (overlaps(range("W_state", W_state, n * batch * sizeof(float)),
+               range("W_down0", W_down0, n * ttt::dtype_bytes(dt))))
+    return fail(TTT_ERR_INVALID_ARGUMENT, "W_state overlaps W_down0");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = staged(kReset, s, [&] {
+    return ttt::launch_state_reset(W_state, W_down0, dt, batch, d_model, d_ff, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "state_reset");
+  return ok();
+}
+
+const char* ttt_last_error(void) { return g_err.c_str(); }
+
+ttt_status_t ttt_profile_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.enabled = enable != 0;
+  return ok();
+}
+
+int ttt_profile_read(double* ms_total, int64_t* launches, int max_stages) {
+  std::vector<Profiler::Rec> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    recs.swap(g_prof.recs);
+  }
+  double ms[TTT_NUM_STAGES] = {0};
+  int64_t cnt[TTT_NUM_STAGES] = {0};
+  hipError_t first_err = hipSuccess;
+  for (const auto& r : recs) {
+    hipError_t e = hipEventSynchronize(r.b);
+    float t = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+    if (e != hipSuccess && first_err == hipSuccess) first_err = e;
+    ms[r.stage] += t;
+    cnt[r.stage] += 1;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    for (const auto& r : recs) {
+      g_prof.pool.push_back(r.a);
+      g_prof.pool.push_back(r.b);
+    }
+  }
+  if (first_err != hipSuccess) return hip_fail(first_err, "profile_read");
+  for (int i = 0; i < std::min(max_stages, (int)TTT_NUM_STAGES); ++i) {
+    if (ms_total) ms_total[i] = ms[i];
+    if (launches) launches[i] = cnt[i];
+  }
+  ok();
+  return TTT_NUM_STAGES;
+}
+
+const char* ttt_stage_name(int stage) {
+  if (stage < 0 || stage >= TTT_NUM_STAGES) return "";
+  return kStageNames[stage];
+}
+
+}  // extern "C"

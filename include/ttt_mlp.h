@@ -1,0 +1,168 @@
+/*
+ * ttt_mlp.h -- C ABI of the MI355X (gfx950) In-Place TTT fast-weight MLP layer.
+ *
+ * The operation (page "In-Place TTT：给LLM装上'临时记忆插槽'，让它边读边学",
+ * zhichai.net):
+ *   section 3.1  the gated MLP O = SiLU(H W_gate^T) (.) (H W_up^T) W_down^T with
+ *                W_down as the fast ("in-place") weight, all else frozen;
+ *   section 3.2  chunk-wise schedule: each chunk of C tokens is output with the
+ *                current W_down, then W_down takes one update; chunks can be
+ *                run in parallel by per-chunk increments and one prefix sum;
+ *   section 3.3  the LM-aligned target V^ = Conv1D(X0) W_target and the update
+ *                W^(i) = W^(i-1) + eta V^_i^T Z_i.
+ * Per-session fast-weight buffers over shared read-only base weights and their
+ * reset follow the serving notes of the practitioner blog (blog.travelaiplan.net,
+ * section 4 on block-wise updates and multi-request serving, and the TTL/reset
+ * item of its safeguards list).
+ *
+ * Readings fixed by this library where the page is loose:
+ *   - Conv1D is depthwise with K taps, U[t][c] = sum_{k<K} taps[c][k] X0[t+1-k][c],
+ *     X0 zero outside [0, T) of each sequence, not restarted per chunk, no bias;
+ *   - W_target is d x d stored [c_in][j_out] and applied on the right, V^ = U W_target;
+ *   - chunk 0 uses W_down0; the last chunk's update is part of the final weight;
+ *     a tail chunk shorter than C follows the same rules;
+ *   - eta is a plain scalar (no 1/C, no decay).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (HIP, same device as the stream),
+ *     row-major, contiguous, 16-byte aligned; the workspace 256-byte aligned.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *     Calls only enqueue work and return; the caller synchronises.
+ *   - The caller owns every buffer (inputs, outputs, state, workspace).  The
+ *     library allocates no device memory and keeps no device state.  Inputs are
+ *     never written.  Outputs and the workspace must not overlap inputs or each
+ *     other (checked on address ranges).
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error status nothing has been written.  TTT_ERR_HIP means a launch failed
+ *     after validation; outputs are then undefined.  ttt_last_error() returns a
+ *     message for the calling thread's last non-OK status.
+ *   - Nothing throws across the ABI.
+ *
+ * Number formats: dtype TTT_BF16 means activations (H, X0, O) and weights
+ * (W_gate, W_up, W_down0, taps, W_target) are bf16; TTT_F32 means all fp32.
+ * The fast-weight state is always fp32.  Contractions run on MFMA with fp32
+ * accumulation; Z, eta*V^, each chunk's weight and O are rounded (RNE) to the
+ * activation type.
+ */
+#ifndef TTT_MLP_H
+#define TTT_MLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype_t;
+
+typedef enum {
+  TTT_OK = 0,
+  TTT_ERR_INVALID_ARGUMENT = -1,
+  TTT_ERR_UNSUPPORTED = -2,
+  TTT_ERR_WORKSPACE_TOO_SMALL = -3,
+  TTT_ERR_HIP = -4
+} ttt_status_t;
+
+/* How the chunk recurrence is evaluated.  Both give bit-identical results.
+ *   SEQUENTIAL      one chunk at a time: output with the current fp32 state,
+ *                   then read-modify-write the state (section 3.2 schedule);
+ *   CHUNK_PARALLEL  per-chunk increments, one exclusive prefix streamed through
+ *                   the fp32 state, then all chunks' outputs at once (the
+ *                   three-step form of section 3.2), in groups of as many
+ *                   chunks as the workspace holds;
+ *   AUTO            CHUNK_PARALLEL. */
+typedef enum {
+  TTT_MODE_AUTO = 0,
+  TTT_MODE_SEQUENTIAL = 1,
+  TTT_MODE_CHUNK_PARALLEL = 2
+} ttt_mode_t;
+
+/* Shapes and scalars of one call.
+ *   batch    B >= 1 independent sequences (ttt_mlp_forward requires B == 1);
+ *   seq_len  T >= 1 tokens per sequence;
+ *   d_model  d, a multiple of 64;  d_ff  f, a multiple of 64;
+ *            (B*T, d*f and f*B*ceil(T/C)*ceil64(C) must each stay below 2^31);
+ *   chunk    C >= 1 tokens per chunk (the last chunk may be shorter);
+ *   conv_k   K taps, 1 <= K <= 8;
+ *   eta      finite fast-weight learning rate (0 gives the static MLP);
+ *   dtype    TTT_BF16 or TTT_F32 for activations and weights;
+ *   mode     see ttt_mode_t;
+ *   init_from_w0  (batched only) 1: every W_state[b] is first set to W_down0;
+ *                 0: W_state holds each sequence's starting weight on entry. */
+typedef struct {
+  int64_t batch;
+  int64_t seq_len;
+  int64_t d_model;
+  int64_t d_ff;
+  int32_t chunk;
+  int32_t conv_k;
+  float eta;
+  ttt_dtype_t dtype;
+  ttt_mode_t mode;
+  int32_t init_from_w0;
+} ttt_mlp_desc_t;
+
+/* Workspace bytes needed for groups of up to `max_group` chunks (0 = all
+ * ceil(T/C) chunks of a sequence at once).  Returns 0 if the descriptor is
+ * invalid (see ttt_last_error()).  A workspace of ttt_mlp_workspace_size(desc, 1)
+ * bytes is the minimum; chunk-parallel mode uses the largest group that fits. */
+size_t ttt_mlp_workspace_size(const ttt_mlp_desc_t* desc, int64_t max_group);
+
+/* Chunks per group the planner would use for this descriptor and workspace
+ * size (1 in sequential mode), or a negative ttt_status_t. */
+int64_t ttt_mlp_group_size(const ttt_mlp_desc_t* desc, size_t ws_bytes);
+
+/* One sequence (B == 1), starting from W_down0.
+ *   H, X0      [T][d]    hidden states entering the MLP / token embeddings X0
+ *   W_gate     [f][d]    W_up [f][d]     frozen projections
+ *   W_down0    [d][f]    initial fast weight (dtype), read-only
+ *   conv_taps  [d][K]    taps[c][k] multiplies X0[t+1-k][c]
+ *   W_target   [d][d]    [c_in][j_out]
+ *   O          [T][d]    output, dtype
+ *   W_down_final [d][f]  fp32, receives W^(N) (the weight after the last chunk)
+ *   ws, ws_bytes         workspace (>= ttt_mlp_workspace_size(desc, 1)) */
+ttt_status_t ttt_mlp_forward(const ttt_mlp_desc_t* desc, const void* H, const void* X0,
+                             const void* W_gate, const void* W_up, const void* W_down0,
+                             const void* conv_taps, const void* W_target, void* O,
+                             float* W_down_final, void* ws, size_t ws_bytes, void* stream);
+
+/* B independent sequences (sessions), each with its own fp32 fast-weight
+ * buffer over shared read-only weights.
+ *   H, X0 [B][T][d]; O [B][T][d]; W_state [B][d][f] fp32 in/out: holds each
+ *   sequence's W^(0) on entry (or is set from W_down0 when init_from_w0 = 1;
+ *   W_down0 may be NULL otherwise) and W^(N) on exit.  Other arguments as in
+ *   ttt_mlp_forward. */
+ttt_status_t ttt_mlp_forward_batched(const ttt_mlp_desc_t* desc, const void* H, const void* X0,
+                                     const void* W_gate, const void* W_up, const void* W_down0,
+                                     const void* conv_taps, const void* W_target, void* O,
+                                     float* W_state, void* ws, size_t ws_bytes, void* stream);
+
+/* Reset fast-weight buffers: W_state[b] <- fp32(W_down0) for b < batch
+ * (session start / periodic reset).  W_down0 [d][f] of w0_dtype; W_state
+ * [batch][d][f] fp32.  Same validation and error rules as above (d, f >= 1). */
+ttt_status_t ttt_fastweight_state_reset(float* W_state, const void* W_down0,
+                                        ttt_dtype_t w0_dtype, int64_t batch, int64_t d_model,
+                                        int64_t d_ff, void* stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* ttt_last_error(void);
+
+/* ---- Stage timing (measurement support) ----
+ * While enabled, every forward call records a HIP event pair around each
+ * kernel it enqueues, on the caller's stream.  ttt_profile_read() waits for the
+ * recorded events, writes per-stage totals (milliseconds and launch counts) for
+ * up to max_stages stages, clears them, and returns the number of stages
+ * (TTT_NUM_STAGES), or a negative ttt_status_t.  ttt_stage_name() names stage i:
+ * 0 state_reset, 1 weight_prep, 2 pad_fill, 3 swiglu (S1), 4 target (S2),
+ * 5 prefix_update (S4/S5), 6 down_proj (S3). */
+#define TTT_NUM_STAGES 7
+ttt_status_t ttt_profile_enable(int enable);
+int ttt_profile_read(double* ms_total, int64_t* launches, int max_stages);
+const char* ttt_stage_name(int stage);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_MLP_H */

@@ -1,0 +1,207 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point the header declares, plans workspaces, and rejects bad
+arguments with the documented status before touching the device.  Invalid
+calls use fake (never dereferenced) device addresses."""
+import ctypes
+import os
+import re
+import threading
+
+import pytest
+
+from chunk_wise_weight_chunked_amd import ttt_mlp as tm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttt_mlp.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tm.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ttt_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert len(names) >= 9, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(tm.EXPORTS)
+
+
+def desc(**kw):
+    base = dict(batch=1, seq_len=4096, d_model=256, d_ff=512, chunk=512, conv_k=4, eta=1e-3,
+                dtype=tm.TTT_BF16, mode="auto", init_from_w0=1)
+    base.update(kw)
+    return tm.make_desc(**base)
+
+
+def test_workspace_plan():
+    d = desc()
+    w1, wall = tm.ttt_mlp_workspace_size(d, 1), tm.ttt_mlp_workspace_size(d, 0)
+    assert 0 < w1 < wall
+    assert tm.ttt_mlp_workspace_size(d, 8) == wall  # 8 chunks = all of them
+    assert tm.ttt_mlp_workspace_size(d, 100) == wall
+    slot = 256 * 512 * 2
+    assert wall - w1 == 7 * slot
+    assert tm.ttt_mlp_group_size(d, wall) == 8
+    assert tm.ttt_mlp_group_size(d, w1) == 1
+    assert tm.ttt_mlp_group_size(d, w1 + 3 * slot) == 4
+    assert tm.ttt_mlp_group_size(desc(mode="sequential"), wall) == 1
+    with pytest.raises(tm.TTTError) as e:
+        tm.ttt_mlp_group_size(d, w1 - 1)
+    assert e.value.status == tm.TTT_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_workspace_fixed_part_matches_layout():
+    # Z [T][f] + Zt [f][P] + Vt [d][P] + WtT [d][d] + tapsT [8][d] fp32 + 1 slot
+    d = desc(seq_len=1000, chunk=100)  # padded chunks: Cp = 128, P = 10 * 128
+    es = 2
+    parts = [1000 * 512 * es, 512 * 1280 * es, 256 * 1280 * es, 256 * 256 * es, 8 * 256 * 4,
+             256 * 512 * es]
+    expect = sum((p + 255) // 256 * 256 for p in parts)
+    assert tm.ttt_mlp_workspace_size(d, 1) == expect
+
+
+BAD_DESCS = [
+    (dict(batch=0), tm.TTT_ERR_INVALID_ARGUMENT, "batch"),
+    (dict(seq_len=0), tm.TTT_ERR_INVALID_ARGUMENT, "seq_len"),
+    (dict(d_model=96), tm.TTT_ERR_UNSUPPORTED, "d_model"),
+    (dict(d_ff=100), tm.TTT_ERR_UNSUPPORTED, "d_ff"),
+    (dict(chunk=0), tm.TTT_ERR_INVALID_ARGUMENT, "chunk"),
+    (dict(conv_k=0), tm.TTT_ERR_INVALID_ARGUMENT, "conv_k"),
+    (dict(conv_k=9), tm.TTT_ERR_UNSUPPORTED, "conv_k"),
+    (dict(eta=float("nan")), tm.TTT_ERR_INVALID_ARGUMENT, "eta"),
+    (dict(eta=float("inf")), tm.TTT_ERR_INVALID_ARGUMENT, "eta"),
+    (dict(dtype=7), tm.TTT_ERR_INVALID_ARGUMENT, "dtype"),
+    (dict(mode=9), tm.TTT_ERR_INVALID_ARGUMENT, "mode"),
+    (dict(init_from_w0=2), tm.TTT_ERR_INVALID_ARGUMENT, "init_from_w0"),
+    (dict(batch=1 << 20, seq_len=1 << 12), tm.TTT_ERR_UNSUPPORTED, "2^31"),
+]
+
+
+@pytest.mark.parametrize("kw,status,word", BAD_DESCS)
+def test_bad_descriptor(lib, kw, status, word):
+    d = desc(**kw)
+    assert lib.ttt_mlp_workspace_size(ctypes.byref(d), 0) == 0
+    assert word in tm.ttt_last_error()
+    ptrs = fake_ptrs(desc())
+    st = call_forward(lib, d, ptrs)
+    assert st == status, tm.ttt_last_error()
+    assert word in tm.ttt_last_error()
+
+
+BASE = 1 << 40  # fake device addresses, never dereferenced
+
+
+def fake_ptrs(d, ws_bytes=None):
+    """Non-overlapping fake buffers for descriptor d."""
+    es = 2 if d.dtype == tm.TTT_BF16 else 4
+    B, T, dm, f, K = d.batch, d.seq_len, d.d_model, d.d_ff, d.conv_k
+    sizes = dict(H=B * T * dm * es, X0=B * T * dm * es, W_gate=f * dm * es, W_up=f * dm * es,
+                 W_down0=dm * f * es, taps=dm * K * es, W_target=dm * dm * es,
+                 O=B * T * dm * es, W=B * dm * f * 4)
+    ws = ws_bytes if ws_bytes is not None else tm.ttt_mlp_workspace_size(desc(), 0)
+    sizes["ws"] = ws
+    out, addr = {}, BASE
+    for k, n in sizes.items():
+        out[k] = addr
+        addr += (n + 4095) // 4096 * 4096 + 4096
+    out["ws_bytes"] = ws
+    return out
+
+
+def call_forward(lib, d, p, batched=False):
+    fn = lib.ttt_mlp_forward_batched if batched else lib.ttt_mlp_forward
+    return fn(ctypes.byref(d), p["H"], p["X0"], p["W_gate"], p["W_up"], p["W_down0"], p["taps"],
+              p["W_target"], p["O"], p["W"], p["ws"], p["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("name", ["H", "X0", "W_gate", "W_up", "W_down0", "taps", "W_target",
+                                  "O", "W", "ws"])
+def test_null_pointer_rejected(lib, name):
+    d = desc()
+    p = fake_ptrs(d)
+    p[name] = None
+    assert call_forward(lib, d, p) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert "NULL" in tm.ttt_last_error()
+
+
+def test_w_down0_optional_without_init(lib):
+    d = desc(init_from_w0=0, batch=2)
+    p = fake_ptrs(d)
+    p["W_down0"] = None
+    p["H"] = None  # still rejected for the other pointer
+    assert call_forward(lib, d, p, batched=True) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert "H is NULL" in tm.ttt_last_error()
+
+
+@pytest.mark.parametrize("name", ["H", "O", "W", "W_target"])
+def test_misaligned_pointer_rejected(lib, name):
+    d = desc()
+    p = fake_ptrs(d)
+    p[name] += 8
+    assert call_forward(lib, d, p) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert "aligned" in tm.ttt_last_error()
+
+
+def test_workspace_alignment_and_size(lib):
+    d = desc()
+    p = fake_ptrs(d)
+    p["ws"] += 16
+    assert call_forward(lib, d, p) == tm.TTT_ERR_INVALID_ARGUMENT
+    p = fake_ptrs(d, ws_bytes=tm.ttt_mlp_workspace_size(d, 1) - 1)
+    assert call_forward(lib, d, p) == tm.TTT_ERR_WORKSPACE_TOO_SMALL
+
+
+@pytest.mark.parametrize("out,inp", [("O", "H"), ("W", "W_down0"), ("ws", "X0"), ("O", "W"),
+                                     ("ws", "O")])
+def test_overlap_rejected(lib, out, inp):
+    d = desc()
+    p = fake_ptrs(d)
+    p[out] = p[inp] + 4096
+    assert call_forward(lib, d, p) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert "overlaps" in tm.ttt_last_error()
+
+
+def test_forward_requires_single_sequence(lib):
+    d = desc(batch=2)
+    assert call_forward(lib, d, fake_ptrs(d)) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert "batch" in tm.ttt_last_error()
+
+
+def test_state_reset_validation(lib):
+    f = lib.ttt_fastweight_state_reset
+    assert f(None, BASE, tm.TTT_BF16, 1, 64, 64, None) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert f(BASE, BASE + (1 << 30), 5, 1, 64, 64, None) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert f(BASE, BASE + (1 << 30), tm.TTT_BF16, 0, 64, 64, None) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert f(BASE, BASE + 1024, tm.TTT_BF16, 1, 64, 64, None) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert "overlaps" in tm.ttt_last_error()
+    assert f(BASE + 4, BASE + (1 << 30), tm.TTT_F32, 1, 64, 64, None) == tm.TTT_ERR_INVALID_ARGUMENT
+
+
+def test_last_error_is_per_thread(lib):
+    d = desc(batch=0)
+    call_forward(lib, d, fake_ptrs(desc()))
+    seen = {}
+
+    def other():
+        seen["msg"] = tm.ttt_last_error()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""
+    assert "batch" in tm.ttt_last_error()
+
+
+def test_stage_names(lib):
+    names = [tm.ttt_stage_name(i) for i in range(tm.TTT_NUM_STAGES)]
+    assert names == ["state_reset", "weight_prep", "pad_fill", "swiglu", "target",
+                     "prefix_update", "down_proj"]
+    assert tm.ttt_stage_name(99) == ""
