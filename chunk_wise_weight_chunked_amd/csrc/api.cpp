@@ -181,6 +181,7 @@ ttt_status_t run_layer(const ttt::Dims& dm, ttt_mode_t mode, bool reset, const v
   void* Z = base + wp.z_off;
   void* Zt = base + wp.zt_off;
   void* Vt = base + wp.vt_off;
+  void* WgU = base + wp.wgu_off;
   void* WtT = base + wp.wtt_off;
   float* tapsT = reinterpret_cast<float*>(base + wp.taps_off);
   void* slots = base + wp.slots_off;
@@ -191,9 +192,7 @@ ttt_status_t run_layer(const ttt::Dims& dm, ttt_mode_t mode, bool reset, const v
     if (e != hipSuccess) return hip_fail(e, "state_reset");
   }
   e = staged(kPrep, s, [&] {
-    const hipError_t r = ttt::launch_transpose(WtT, Wt, dm.d, dm.dt, s);
-    if (r != hipSuccess) return r;
-    return ttt::launch_taps(tapsT, taps, dm, s);
+    return ttt::launch_weight_prep(dm, Wg, Wu, Wt, taps, WgU, WtT, tapsT, s);
   });
   if (e != hipSuccess) return hip_fail(e, "weight_prep");
   const bool padded = dm.Cp != dm.C || dm.T % dm.C != 0;
@@ -201,7 +200,7 @@ ttt_status_t run_layer(const ttt::Dims& dm, ttt_mode_t mode, bool reset, const v
     e = staged(kPad, s, [&] { return ttt::launch_pad_fill(Zt, Vt, dm, s); });
     if (e != hipSuccess) return hip_fail(e, "pad_fill");
   }
-  e = staged(kSwiglu, s, [&] { return ttt::launch_swiglu(dm, H, Wg, Wu, Z, Zt, s); });
+  e = staged(kSwiglu, s, [&] { return ttt::launch_swiglu(dm, H, WgU, Z, Zt, s); });
   if (e != hipSuccess) return hip_fail(e, "swiglu");
   e = staged(kTarget, s, [&] { return ttt::launch_target(dm, X0, tapsT, WtT, Vt, s); });
   if (e != hipSuccess) return hip_fail(e, "target");

@@ -41,12 +41,12 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN (quiet).
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950; NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
 
 template <typename T> struct Elem;
@@ -76,6 +76,27 @@ __device__ __forceinline__ float chunk_value<uint16_t>(const uint4& c, int i) {
 }
 
 // --------------------------------------------------------------- LDS layout
+// LDS is addressed through address-space-3 pointers so that every access
+// compiles to ds_read / ds_write (a generic pointer would give flat accesses,
+// which also count against the vector-memory counter and serialise the
+// global prefetch with the LDS reads).
+typedef __attribute__((address_space(3))) char lds_char;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// V: a scalar or clang ext_vector type (HIP's vector classes are not
+// address-space aware; convert with the helpers below).
+template <typename V>
+__device__ __forceinline__ V lds_load(const lds_char* p) {
+  return *(const __attribute__((address_space(3))) V*)p;
+}
+template <typename V>
+__device__ __forceinline__ void lds_store(lds_char* p, V v) {
+  *(__attribute__((address_space(3))) V*)p = v;
+}
+__device__ __forceinline__ u32x4_t as_u32x4(const uint4& v) { return u32x4_t{v.x, v.y, v.z, v.w}; }
+__device__ __forceinline__ uint4 as_uint4(const u32x4_t& v) { return make_uint4(v[0], v[1], v[2], v[3]); }
+
 __device__ __forceinline__ uint32_t lds_offset(int row, int chunk) {
   return (uint32_t)row * kRowBytes + (uint32_t)((chunk ^ (row & 7)) << 4);
 }
@@ -133,23 +154,44 @@ struct Mma;
 template <class S>
 struct Mma<uint16_t, S> {
   static constexpr int kSteps = 4;  // 16 K values per step, 64 per k-tile
-  __device__ __forceinline__ static void ktile(Accum<S>& acc, const char* sA, const char* sB,
-                                               const LanePos& p) {
+  struct Frag {
+    bf16x8_t a[S::MB], b[S::NB];
+  };
+  __device__ __forceinline__ static void read(Frag& f, const lds_char* sA, const lds_char* sB,
+                                              const LanePos& p, int s) {
     const int r = p.lane & 31, h = p.lane >> 5;
 #pragma unroll
+    for (int i = 0; i < S::MB; ++i)
+      f.a[i] = lds_load<bf16x8_t>(sA + lds_offset(p.wave_m0 + 32 * i + r, 2 * s + h));
+#pragma unroll
+    for (int j = 0; j < S::NB; ++j)
+      f.b[j] = lds_load<bf16x8_t>(sB + lds_offset(p.wave_n0 + 32 * j + r, 2 * s + h));
+  }
+  // The fragments of step s+1 are read while the MFMAs of step s run.  The
+  // scheduling barriers pin that order (otherwise the compiler sinks each read
+  // down to its first use and the MFMAs wait on LDS latency every time).
+  // mid() runs between the two halves of the steps (the mainloop stages the
+  // next k-tile there).
+  template <class Mid>
+  __device__ __forceinline__ static void ktile(Accum<S>& acc, const lds_char* sA,
+                                               const lds_char* sB, const LanePos& p, Mid&& mid) {
+    Frag f[2];
+    read(f[0], sA, sB, p, 0);
+#pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      bf16x8_t a[S::MB], b[S::NB];
-#pragma unroll
-      for (int i = 0; i < S::MB; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(sA + lds_offset(p.wave_m0 + 32 * i + r, 2 * s + h));
-#pragma unroll
-      for (int j = 0; j < S::NB; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(sB + lds_offset(p.wave_n0 + 32 * j + r, 2 * s + h));
+      if (s + 1 < kSteps) read(f[(s + 1) & 1], sA, sB, p, s + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const Frag& c = f[s & 1];
 #pragma unroll
       for (int i = 0; i < S::MB; ++i)
 #pragma unroll
         for (int j = 0; j < S::NB; ++j)
-          acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.v[i][j], 0, 0, 0);
+          acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.a[i], c.b[j], acc.v[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s == kSteps / 2 - 1) {
+        mid();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 };
@@ -157,8 +199,9 @@ struct Mma<uint16_t, S> {
 template <class S>
 struct Mma<float, S> {
   static constexpr int kSteps = 2;  // 16 K values per step, 32 per k-tile
-  __device__ __forceinline__ static void ktile(Accum<S>& acc, const char* sA, const char* sB,
-                                               const LanePos& p) {
+  template <class Mid>
+  __device__ __forceinline__ static void ktile(Accum<S>& acc, const lds_char* sA,
+                                               const lds_char* sB, const LanePos& p, Mid&& mid) {
     const int r = p.lane & 31, h = p.lane >> 5;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
@@ -167,14 +210,12 @@ struct Mma<float, S> {
       for (int i = 0; i < S::MB; ++i)
 #pragma unroll
         for (int q = 0; q < 2; ++q)
-          a[i][q] = *reinterpret_cast<const floatx4_t*>(
-              sA + lds_offset(p.wave_m0 + 32 * i + r, 4 * s + 2 * h + q));
+          a[i][q] = lds_load<floatx4_t>(sA + lds_offset(p.wave_m0 + 32 * i + r, 4 * s + 2 * h + q));
 #pragma unroll
       for (int j = 0; j < S::NB; ++j)
 #pragma unroll
         for (int q = 0; q < 2; ++q)
-          b[j][q] = *reinterpret_cast<const floatx4_t*>(
-              sB + lds_offset(p.wave_n0 + 32 * j + r, 4 * s + 2 * h + q));
+          b[j][q] = lds_load<floatx4_t>(sB + lds_offset(p.wave_n0 + 32 * j + r, 4 * s + 2 * h + q));
 #pragma unroll
       for (int i = 0; i < S::MB; ++i)
 #pragma unroll
@@ -184,77 +225,142 @@ struct Mma<float, S> {
             acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e >> 2][e & 3],
                                                                b[j][e >> 2][e & 3],
                                                                acc.v[i][j], 0, 0, 0);
+      if (s == kSteps / 2 - 1) mid();
     }
   }
 };
 
 // ------------------------------------------------------------- row loaders
-// A row loader moves one operand's k-tile (ROWS rows x 128 bytes) from global
-// memory to LDS in two phases: load(kt) issues the global loads into
-// registers, store(lds) writes them to the swizzled LDS stage.  Thread t owns
-// chunk (t & 7) of rows (t >> 3) + 32 q, q = 0 .. ROWS/32 - 1.
-template <int ROWS>
-struct RowLoader {
-  static constexpr int kPer = ROWS / 32;
-  const char* ptr[kPer];  // row base (byte address of this thread's chunk at k = 0)
-  uint4 reg[kPer];
+// Global reads use buffer loads: a scalar resource (base, byte range) per
+// operand and k-tile, a per-lane 32-bit offset.  Reads at or beyond the range
+// return zero, which is how rows outside the operand are masked (no branches),
+// and buffer loads are counted by vmcnt only, so the next k-tile's loads stay
+// in flight while the MFMAs consume LDS.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOobOffset = 0x80000000u;  // beyond any range used here
 
-  // row_base(q) returns the byte address of row (t>>3)+32q at K index 0, or
-  // nullptr when that row lies outside the operand (it then loads zeros).
-  template <class F>
-  __device__ __forceinline__ void init(F&& row_base) {
-    const int c = threadIdx.x & 7;
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const char* b = row_base(q);
-      ptr[q] = b ? b + c * 16 : nullptr;
-    }
-  }
-  __device__ __forceinline__ void load(int64_t kt) {
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      if (ptr[q])
-        reg[q] = *reinterpret_cast<const uint4*>(ptr[q] + kt * kRowBytes);
-      else
-        reg[q] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-  __device__ __forceinline__ void store(char* lds) const {
-    const int c = threadIdx.x & 7, r0 = threadIdx.x >> 3;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// s_waitcnt on the vector-memory counter only: vmcnt(N), N a constant.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Loader interface used by the mainloop:
+//   issue(kt, stage)  start the global reads of k-tile kt (into `stage` for
+//                     direct loaders, into registers for staged ones);
+//   commit(stage)     staged loaders write their registers to `stage`;
+//   kStagedLoads      vector-memory instructions one staged issue() makes
+//                     (0 for direct loaders).
+//
+// DirectLoader moves one operand's k-tile (ROWS rows x 128 bytes) with
+// buffer_load ... lds (no registers): wave w fills rows [w ROWS/4, (w+1) ROWS/4)
+// of the stage, 8 rows (1 KB) per instruction, lane l writing 16 bytes at
+// lane * 16 of that KB.  The swizzled layout (row r, chunk c at c ^ (r & 7)) is
+// produced by choosing the source: lane l reads chunk (l & 7) ^ (l >> 3) of
+// row l >> 3 of its group.  Addressing, in bytes and uniform across the
+// workgroup:
+//   row r, k-tile kt  ->  base + kt * kt_stride + r * row_stride + chunk * 16,
+//   valid while the offset from base + kt * kt_stride is below
+//   valid_bytes - kt * kt_shrink (reads beyond return zero).
+// Row-major operands use row_stride = row length, kt_stride = kt_shrink = 128;
+// k-blocked operands ([K/kt][rows][128 B]) use row_stride = 128,
+// kt_stride = rows * 128, kt_shrink = 0.
+template <int ROWS>
+struct DirectLoader {
+  static constexpr int kStagedLoads = 0;
+  static constexpr int kPer = ROWS / 32;  // instructions per wave per k-tile
+  const char* base;
+  int64_t kt_stride, valid_bytes, kt_shrink;
+  uint32_t voff[kPer];
+  uint32_t lds_row0;  // first stage row of this wave
+
+  __device__ __forceinline__ void init(const void* base_, int64_t row_stride, int64_t kt_stride_,
+                                       int64_t valid_bytes_, int64_t kt_shrink_) {
+    base = static_cast<const char*>(base_);
+    kt_stride = kt_stride_;
+    valid_bytes = valid_bytes_;
+    kt_shrink = kt_shrink_;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    lds_row0 = (uint32_t)(wave * (ROWS / 4));
+    const int rr = lane >> 3, c = (lane & 7) ^ rr;
 #pragma unroll
     for (int q = 0; q < kPer; ++q)
-      *reinterpret_cast<uint4*>(lds + lds_offset(r0 + 32 * q, c)) = reg[q];
+      voff[q] = (uint32_t)((lds_row0 + 8 * q + rr) * row_stride + c * 16);
   }
+  __device__ __forceinline__ void issue(int64_t kt, lds_char* stage) {
+    const rsrc_t r = make_rsrc(base + kt * kt_stride, valid_bytes - kt * kt_shrink);
+#pragma unroll
+    for (int q = 0; q < kPer; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(stage + (lds_row0 + 8 * q) * kRowBytes), 16,
+          voff[q], 0, 0, 0);
+  }
+  __device__ __forceinline__ void commit(lds_char*) const {}
 };
 
 // ---------------------------------------------------------------- mainloop
-// Runs k-tiles [0, nk) through a two-stage LDS pipeline: while the MFMAs work
-// on stage kt&1, the global loads of k-tile kt+1 are in flight; one barrier
-// per k-tile separates the LDS writes of the next stage from the reads of the
-// current one.  after_ktile(kt) runs once every wave has finished k-tile kt
-// (it may touch registers and global memory, not LDS).
+// Runs k-tiles [0, nk) through a two-stage LDS pipeline.  Entering k-tile kt
+// (after a barrier), stage kt&1 holds k-tile kt and the other stage is free:
+// direct loaders start k-tile kt+1 into it at once; staged loaders write the
+// registers they fetched one k-tile earlier halfway through kt's MFMAs and
+// then fetch k-tile kt+2.  Before the closing barrier every wave waits for
+// its own direct reads of k-tile kt+1 (the staged fetches, issued later, may
+// stay in flight).  after_ktile(kt) runs once every wave has finished k-tile
+// kt and no direct read is in flight (it may use registers and global memory,
+// not LDS).
 template <typename T, class S, class LA, class LB, class Hook>
-__device__ __forceinline__ void mainloop(Accum<S>& acc, LA& la, LB& lb, int64_t nk, char* smem,
+__device__ __forceinline__ void mainloop(Accum<S>& acc, LA& la, LB& lb, int64_t nk, lds_char* smem,
                                          const LanePos& p, Hook&& after_ktile) {
-  char* stage[2] = {smem, smem + S::kStageBytes};
+  constexpr int kStaged = LA::kStagedLoads + LB::kStagedLoads;
   if (nk <= 0) return;
-  la.load(0);
-  lb.load(0);
-  la.store(stage[0]);
-  lb.store(stage[0] + S::BM * kRowBytes);
+  lds_char* const stage0 = smem;
+  la.issue(0, stage0);
+  lb.issue(0, stage0 + S::BM * kRowBytes);
+  la.commit(stage0);
+  lb.commit(stage0 + S::BM * kRowBytes);
+  if (nk > 1) {
+    if constexpr (LA::kStagedLoads > 0) la.issue(1, nullptr);
+    if constexpr (LB::kStagedLoads > 0) lb.issue(1, nullptr);
+    wait_vmcnt<kStaged>();
+  } else {
+    wait_vmcnt<0>();
+  }
   __syncthreads();
   for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = (int)(kt & 1);
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.load(kt + 1);
-      lb.load(kt + 1);
+    const lds_char* cur = smem + (kt & 1) * S::kStageBytes;
+    lds_char* nxt = smem + ((kt + 1) & 1) * S::kStageBytes;
+    if (kt + 1 < nk) {
+      if constexpr (LA::kStagedLoads == 0) la.issue(kt + 1, nxt);
+      if constexpr (LB::kStagedLoads == 0) lb.issue(kt + 1, nxt + S::BM * kRowBytes);
     }
-    Mma<T, S>::ktile(acc, stage[cur], stage[cur] + S::BM * kRowBytes, p);
-    if (more) {
-      la.store(stage[cur ^ 1]);
-      lb.store(stage[cur ^ 1] + S::BM * kRowBytes);
-    }
+    Mma<T, S>::ktile(acc, cur, cur + S::BM * kRowBytes, p, [&] {
+      if constexpr (kStaged > 0) {
+        if (kt + 1 < nk) {
+          la.commit(nxt);
+          lb.commit(nxt + S::BM * kRowBytes);
+        }
+        if (kt + 2 < nk) {
+          if constexpr (LA::kStagedLoads > 0) la.issue(kt + 2, nullptr);
+          if constexpr (LB::kStagedLoads > 0) lb.issue(kt + 2, nullptr);
+        }
+      }
+    });
+    if (kt + 2 < nk)
+      wait_vmcnt<kStaged>();
+    else
+      wait_vmcnt<0>();
     __syncthreads();
     after_ktile(kt);
   }

@@ -16,17 +16,20 @@
 // chunk); with G = N it is the three-step chunk-parallel form (section 3.2)
 // with the prefix streamed through the accumulators.
 //
-// Operand layouts the kernels agree on (row-major):
-//   H, X0, O   [B*T][d]      activations (T = bf16 bits or fp32)
-//   Z          [B*T][f]      gated activations
-//   Zt         [f][P]        Z transposed, token columns chunk-padded
-//   Vt         [d][P]        eta * V^ transposed, same columns
-//   WtT        [d][d]        W_target transposed ([j_out][c_in])
-//   tapsT      [8][d] fp32   taps transposed, zero for k >= K
-//   W_state    [B][d][f]     fp32 fast weight
-//   slots      [G][B][d][f]  weight used by each chunk of the group
-// Token t of sequence b sits in column (b N + i) Cp + j of Zt/Vt, with
-// i = t / C, j = t % C; columns j >= (chunk length) hold zeros.
+// Layouts the kernels agree on (es = element bytes, TB = 128 / es tokens):
+//   H, X0, O   [B*T][d]            activations (T = bf16 bits or fp32)
+//   Z          [B*T][f]            gated activations, row-major (S3's A operand)
+//   Zt         [P/TB][f][TB]       Z token-major, k-blocked (S4's B operand)
+//   Vt         [P/TB][d][TB]       eta * V^ token-major, k-blocked (S4's A operand)
+//   WgU        [f/32][2][32][d]    W_gate / W_up rows interleaved in blocks of 32
+//   WtT        [d][d]              W_target transposed ([j_out][c_in])
+//   tapsT      [8][d] fp32         taps transposed, zero for k >= K
+//   W_state    [B][d][f] fp32      fast weight
+//   slots      [G][B][d][f]        weight used by each chunk of the group
+// Token t of sequence b has token column p = (b N + i) Cp + j (i = t / C,
+// j = t % C, Cp = C rounded up to 64); columns with j >= chunk length hold
+// zeros.  In the k-blocked layouts one k-tile of a GEMM (TB tokens of R rows)
+// is one contiguous R x 128-byte block.
 #include <math.h>
 
 #include <algorithm>
@@ -56,65 +59,75 @@ __device__ __forceinline__ ChunkMap chunk_map(const Dims& dm) {
   return m;
 }
 
-// LDS staging for the token-major outputs (Zt, Vt): a slice of 64 output
-// columns x 256 tokens is gathered from the accumulators (each lane puts 4
-// consecutive tokens of one column), then every thread copies 8-token runs to
-// dst[col][column of token] with 16-byte stores where the 8 tokens lie in one
-// chunk, element stores otherwise.  Row stride 260 tokens keeps the 4-token
-// writes of 16 lanes on distinct banks.
+// Element index of (row n, token column p) in a k-blocked token-major matrix
+// of R rows.
 template <typename T>
-struct TokStage {
+__device__ __forceinline__ int64_t kblock_index(int64_t n, int64_t p, int64_t R) {
+  constexpr int TB = kRowBytes / (int)sizeof(T);
+  return ((p / TB) * R + n) * TB + (p % TB);
+}
+
+// LDS staging for the epilogues: a slice of 64 output columns x 256 tile rows
+// (tokens), put by lanes 4 rows at a time, read back either as token runs
+// (token-major outputs) or as column runs (row-major outputs).  Row stride of
+// 260 elements keeps the 4-element puts of 16 lanes on distinct banks.
+template <typename T>
+struct Stage {
   static constexpr int kCols = 64;
   static constexpr int kToks = 256;
   static constexpr int kStride = (kToks + 4) * (int)sizeof(T);  // bytes per LDS row
+  static constexpr int TB = kRowBytes / (int)sizeof(T);
+  static constexpr int kBytes = kCols * kStride;
 
-  __device__ __forceinline__ static void put4(char* lds, int col, int tok, const float v[4]) {
-    char* q = lds + col * kStride + tok * (int)sizeof(T);
+  __device__ __forceinline__ static void put4(lds_char* lds, int col, int tok, const float v[4]) {
+    lds_char* q = lds + col * kStride + tok * (int)sizeof(T);
     if constexpr (sizeof(T) == 2) {
-      uint2 w;
-      w.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-      w.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
-      *reinterpret_cast<uint2*>(q) = w;
+      lds_store<u32x2_t>(q, u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
     } else {
-      *reinterpret_cast<float4*>(q) = make_float4(v[0], v[1], v[2], v[3]);
+      lds_store<floatx4_t>(q, floatx4_t{v[0], v[1], v[2], v[3]});
     }
   }
 
-  // Copy columns [0, ncols) of the staged slice; token row0 + t of the tile
-  // goes to dst[(col_base + c) * ld + column(row0 + t)].
-  __device__ __forceinline__ static void flush(const char* lds, T* dst, int64_t ld,
-                                               int64_t col_base, int ncols, int32_t row0,
-                                               int32_t rows_total, const ChunkMap& cm) {
+  // Token-major, k-blocked output of R rows: tile token t of column c goes to
+  // dst[kblock_index(col_base + c, column(row0 + t), R)].  Consecutive lanes
+  // take 8-token runs of one column, then the next column, so a wave writes
+  // contiguous 128-byte block rows.
+  __device__ __forceinline__ static void flush_tokens(const lds_char* lds, T* __restrict__ dst,
+                                                      int64_t R, int64_t col_base, int ncols,
+                                                      int32_t row0, int32_t rows_total,
+                                                      const ChunkMap& cm) {
+    constexpr int GPB = TB / 8;  // 8-token runs per block row
     for (int it = threadIdx.x; it < kCols * (kToks / 8); it += kThreads) {
-      const int c = it >> 5, tok = (it & 31) * 8;
+      const int g = it % GPB, c = (it / GPB) % kCols, tb = it / (GPB * kCols);
+      const int tok = tb * TB + g * 8;
       const int32_t row = row0 + tok;
       if (c >= ncols || row >= rows_total) continue;
-      const char* src = lds + c * kStride + tok * (int)sizeof(T);
-      T* drow = dst + (col_base + c) * ld;
+      const lds_char* src = lds + c * kStride + tok * (int)sizeof(T);
+      const int64_t n = col_base + c;
       const int32_t b = row / cm.T, sq = row - b * cm.T, i = sq / cm.C, j = sq - i * cm.C;
-      const int64_t c0 = ((int64_t)b * cm.N + i) * cm.Cp + j;
+      const int64_t p0 = ((int64_t)b * cm.N + i) * cm.Cp + j;
       const int32_t room = min(cm.C - j, cm.T - sq);
-      if (room >= 8 && (c0 & 7) == 0) {
+      if (room >= 8 && (p0 & 7) == 0) {
+        T* d = dst + kblock_index<T>(n, p0, R);
         if constexpr (sizeof(T) == 2) {
-          const uint2 lo = *reinterpret_cast<const uint2*>(src);
-          const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
-          *reinterpret_cast<uint4*>(drow + c0) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          const u32x2_t lo = lds_load<u32x2_t>(src);
+          const u32x2_t hi = lds_load<u32x2_t>(src + 8);
+          *reinterpret_cast<uint4*>(d) = make_uint4(lo[0], lo[1], hi[0], hi[1]);
         } else {
-          *reinterpret_cast<uint4*>(drow + c0) = *reinterpret_cast<const uint4*>(src);
-          *reinterpret_cast<uint4*>(drow + c0 + 4) = *reinterpret_cast<const uint4*>(src + 16);
+          *reinterpret_cast<uint4*>(d) = as_uint4(lds_load<u32x4_t>(src));
+          *reinterpret_cast<uint4*>(d + 4) = as_uint4(lds_load<u32x4_t>(src + 16));
         }
       } else {
         for (int e = 0; e < 8 && row + e < rows_total; ++e)
-          drow[cm.col(row + e)] = reinterpret_cast<const T*>(src)[e];
+          dst[kblock_index<T>(n, cm.col(row + e), R)] = lds_load<T>(src + e * (int)sizeof(T));
       }
     }
   }
 
-  // Copy the staged slice row-major: token row0 + t, column c goes to
-  // dst[(row0 + t) * ld + col_base + c] for c < ncols (a multiple of 8),
-  // 8 columns (16 bytes for bf16) per store.
-  __device__ __forceinline__ static void flush_rows(const char* lds, T* dst, int64_t ld,
-                                                    int64_t col_base, int ncols, int32_t row0,
+  // Row-major output: tile row t, column c goes to dst[t * ld + col_base + c]
+  // for t < rows_valid, c < ncols (a multiple of 8); 8 columns per store.
+  __device__ __forceinline__ static void flush_rows(const lds_char* lds, T* __restrict__ dst,
+                                                    int64_t ld, int64_t col_base, int ncols,
                                                     int32_t rows_valid) {
     for (int it = threadIdx.x; it < kToks * (kCols / 8); it += kThreads) {
       const int t = it >> 3, c = (it & 7) * 8;
@@ -122,14 +135,11 @@ struct TokStage {
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        v[e] = Elem<T>::to_f32(*reinterpret_cast<const T*>(lds + (c + e) * kStride + t * (int)sizeof(T)));
-      T* d = dst + (int64_t)(row0 + t) * ld + col_base + c;
+        v[e] = Elem<T>::to_f32(lds_load<T>(lds + (c + e) * kStride + t * (int)sizeof(T)));
+      T* d = dst + (int64_t)t * ld + col_base + c;
       if constexpr (sizeof(T) == 2) {
-        uint32_t w[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          w[q] = (uint32_t)f32_to_bf16_bits(v[2 * q]) | ((uint32_t)f32_to_bf16_bits(v[2 * q + 1]) << 16);
-        *reinterpret_cast<uint4*>(d) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(d) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
       } else {
         *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
         *reinterpret_cast<float4*>(d + 4) = make_float4(v[4], v[5], v[6], v[7]);
@@ -143,20 +153,39 @@ __device__ __forceinline__ float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
+// Put the 64 columns [32*j0, 32*j0 + 64) of a wave's accumulators (two block
+// columns j0, j0+1, values transformed by `fn`) into the stage.
+template <typename T, class S, class F>
+__device__ __forceinline__ void stage_two_blocks(lds_char* lds, const Accum<S>& acc, const LanePos& p,
+                                                 int j0, F&& fn) {
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int i = 0; i < S::MB; ++i)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fn(acc.v[i][j0 + jj][4 * rq + e]);
+        Stage<T>::put4(lds, 32 * jj + (p.lane & 31), p.row(i, 4 * rq), v);
+      }
+}
+
 // ===================================================================== S1
-// Z = SiLU(H W_gate^T) (.) (H W_up^T) over all B*T token rows.  The B tile
-// interleaves 32-row blocks of W_gate and W_up (block 2q: gate features
-// f0+32q.., block 2q+1: the same up features), so each wave holds the gate and
-// up sums of the same (token, feature) in the same lane and register.
+// Z = SiLU(H W_gate^T) (.) (H W_up^T) over all B*T token rows.  The B operand
+// is WgU, whose 32-row blocks alternate gate and up rows of the same 32
+// features, so each wave holds the gate and up sums of the same (token,
+// feature) in the same lane and register (block columns 2q and 2q+1).
 template <typename T>
-__global__ __launch_bounds__(kThreads) void swiglu_kernel(Dims dm, const T* __restrict__ H,
-                                                          const T* __restrict__ Wg,
-                                                          const T* __restrict__ Wu,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void swiglu_kernel(Dims dm, const T* __restrict__ H,
+                                                          const T* __restrict__ WgU,
                                                           T* __restrict__ Z, T* __restrict__ Zt) {
   using S = Tile;
-  __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
+  lds_char* smem = (lds_char*)smem_raw;
   const int32_t BT = (int32_t)(dm.B * dm.T);
   const int64_t d = dm.d, f = dm.f;
+  const int64_t ld = d * (int64_t)sizeof(T);
   constexpr int kFeat = S::BN / 2;
   const int tiles_m = (BT + S::BM - 1) / S::BM;
   const int tiles_n = (int)((f + kFeat - 1) / kFeat);
@@ -164,32 +193,23 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(Dims dm, const T* __re
       grouped_tile(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, 8);
   const int32_t row0 = tc.m * S::BM;
   const int64_t feat0 = (int64_t)tc.n * kFeat;
-  const int tr = threadIdx.x >> 3;
 
-  RowLoader<S::BM> la;
-  la.init([&](int q) -> const char* {
-    const int32_t row = row0 + tr + 32 * q;
-    return row < BT ? reinterpret_cast<const char*>(H + (int64_t)row * d) : nullptr;
-  });
-  RowLoader<S::BN> lb;
-  lb.init([&](int q) -> const char* {
-    const int64_t feat = feat0 + 32 * (q >> 1) + tr;
-    if (feat >= f) return nullptr;
-    return reinterpret_cast<const char*>(((q & 1) ? Wu : Wg) + feat * d);
-  });
+  DirectLoader<S::BM> la;
+  la.init(reinterpret_cast<const char*>(H) + row0 * ld, ld, kRowBytes, (BT - row0) * ld,
+          kRowBytes);
+  DirectLoader<S::BN> lb;
+  lb.init(reinterpret_cast<const char*>(WgU) + 2 * feat0 * ld, ld, kRowBytes,
+          (2 * f - 2 * feat0) * ld, kRowBytes);
 
   Accum<S> acc;
   acc.zero();
   const LanePos p = lane_pos<S>();
-  const int64_t nk = d * (int64_t)sizeof(T) / kRowBytes;
-  mainloop<T, S>(acc, la, lb, nk, smem, p, [](int64_t) {});
+  mainloop<T, S>(acc, la, lb, ld / kRowBytes, smem, p, [](int64_t) {});
 
-  // Epilogue: z = silu(gate) * up, staged in LDS in two passes of 64
-  // features (those of wave column 0, then of wave column 1), then copied to
-  // Zt (token-major) and Z (row-major).
+  // z = silu(gate) * up, staged in two passes of 64 features (those of wave
+  // column 0, then of wave column 1), then written to Zt and Z.
   const ChunkMap cm = chunk_map(dm);
   const int wn = (threadIdx.x >> 6) & 1;
-  using Stage = TokStage<T>;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     if (wn == h) {
@@ -203,60 +223,75 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(Dims dm, const T* __re
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               z[e] = silu(acc.v[i][2 * jp][4 * rq + e]) * acc.v[i][2 * jp + 1][4 * rq + e];
-            Stage::put4(smem, 32 * jp + (p.lane & 31), p.row(i, 4 * rq), z);
+            Stage<T>::put4(smem, 32 * jp + (p.lane & 31), p.row(i, 4 * rq), z);
           }
     }
     __syncthreads();
     const int64_t cb = feat0 + 64 * h;
     const int ncols = (int)max<int64_t>(0, min<int64_t>(64, f - cb));
-    Stage::flush(smem, Zt, dm.P, cb, ncols, row0, BT, cm);
-    Stage::flush_rows(smem, Z, f, cb, ncols, row0, min(BT - row0, S::BM));
+    Stage<T>::flush_tokens(smem, Zt, f, cb, ncols, row0, BT, cm);
+    Stage<T>::flush_rows(smem, Z + (int64_t)row0 * f, f, cb, ncols, min(BT - row0, S::BM));
     __syncthreads();
   }
 }
 
 // ===================================================================== S2
 // A operand of the target GEMM: U[t][c] = sum_k taps[c][k] X0[t+1-k][c]
-// (zero outside the token's own sequence), computed in fp32 while staging
-// the k-tile and rounded once to T.  Thread t owns the 16-byte channel chunk
-// (t & 7) of the 8 consecutive rows 8 (t >> 3) .. +7 and keeps the window of
-// X0 rows r0-(KMAX-2) .. r0+8 in registers.  Taps come from the fp32 [8][d]
+// (zero outside the token's own sequence), computed in fp32 while staging the
+// k-tile and rounded once to T.  Thread t owns the 16-byte channel chunk
+// (t & 7) of the 8 consecutive tile rows 8 (t >> 3) .. +7 and keeps the window
+// of X0 rows r0-(KMAX-2) .. r0+8 in registers.  Taps come from the fp32 [8][d]
 // copy (zero for k >= K).
 template <typename T, int KMAX>
 struct ConvLoader {
   static constexpr int kWin = 7 + KMAX;
   static constexpr int EPC = Elem<T>::kPerChunk;
-  const char* x0;      // X0 base + this thread's chunk offset
-  const float* taps;   // tapsT base
-  int64_t row_bytes;   // d * sizeof(T)
+  static constexpr int kTapVecs = EPC / 4;  // 16-byte fp32 tap vectors per tap
+  static constexpr int kStagedLoads = kWin + KMAX * kTapVecs;
+  const char* base;     // X0 row gbase (uniform)
+  int64_t ld;           // d * es
+  int64_t valid_bytes;  // (B*T - gbase) * ld
+  const float* taps;
   int64_t d;
-  int32_t r0, BT, T_seq;
+  int32_t r0, T_seq, BT;
+  uint32_t voff[kWin];
   uint4 win[kWin];
+  uint4 tpv[KMAX][kTapVecs];
 
-  __device__ __forceinline__ void load(int64_t kt) {
+  __device__ __forceinline__ void init(const T* X0, const float* tapsT, const Dims& dm,
+                                       int32_t row0) {
+    BT = (int32_t)(dm.B * dm.T);
+    T_seq = (int32_t)dm.T;
+    d = dm.d;
+    ld = dm.d * (int64_t)sizeof(T);
+    taps = tapsT;
+    const int32_t gbase = max(0, row0 - (KMAX - 2));
+    base = reinterpret_cast<const char*>(X0) + (int64_t)gbase * ld;
+    valid_bytes = (int64_t)(BT - gbase) * ld;
+    r0 = row0 + (threadIdx.x >> 3) * 8;
+    const int c = threadIdx.x & 7;
 #pragma unroll
     for (int w = 0; w < kWin; ++w) {
       const int32_t g = r0 - (KMAX - 2) + w;
-      if (g >= 0 && g < BT)
-        win[w] = *reinterpret_cast<const uint4*>(x0 + (int64_t)g * row_bytes + kt * kRowBytes);
-      else
-        win[w] = make_uint4(0u, 0u, 0u, 0u);
+      voff[w] = g < gbase ? kOobOffset : (uint32_t)((g - gbase) * ld + c * 16);
     }
   }
-  __device__ __forceinline__ void store_kt(char* lds, int64_t kt) const {
-    const int c = threadIdx.x & 7;
-    const int64_t ch0 = kt * (kRowBytes / (int)sizeof(T)) + c * EPC;
-    float tp[KMAX][EPC];
+  // Fetch the X0 window and the taps of this thread's channels for k-tile kt.
+  __device__ __forceinline__ void issue(int64_t kt, lds_char*) {
+    const rsrc_t r = make_rsrc(base + kt * kRowBytes, valid_bytes - kt * kRowBytes);
+#pragma unroll
+    for (int w = 0; w < kWin; ++w) win[w] = buf_load16(r, voff[w]);
+    const int64_t ch0 = kt * (kRowBytes / (int)sizeof(T)) + (threadIdx.x & 7) * EPC;
+    const rsrc_t tr = make_rsrc(taps, 8 * d * (int64_t)sizeof(float));
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
 #pragma unroll
-      for (int e = 0; e < EPC; e += 4) {
-        const float4 t4 = *reinterpret_cast<const float4*>(taps + k * d + ch0 + e);
-        tp[k][e] = t4.x;
-        tp[k][e + 1] = t4.y;
-        tp[k][e + 2] = t4.z;
-        tp[k][e + 3] = t4.w;
-      }
+      for (int v = 0; v < kTapVecs; ++v)
+        tpv[k][v] = buf_load16(tr, (uint32_t)((k * d + ch0 + 4 * v) * 4));
+  }
+  // U for the thread's 8 rows in fp32, rounded to T, into the stage.
+  __device__ __forceinline__ void commit(lds_char* lds) const {
+    const int c = threadIdx.x & 7;
     const int lrow0 = (threadIdx.x >> 3) * 8;
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
@@ -265,111 +300,72 @@ struct ConvLoader {
       float u[EPC];
 #pragma unroll
       for (int e = 0; e < EPC; ++e) u[e] = 0.0f;
-      if (o < BT) {
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-          const int32_t src = s + 1 - k;  // X0 row of this tap, inside the sequence
-          if (src < 0 || src >= T_seq) continue;
+      for (int k = 0; k < KMAX; ++k) {
+        const int32_t src = s + 1 - k;  // X0 row of this tap, inside the sequence
+        const bool ok = o < BT && src >= 0 && src < T_seq;
 #pragma unroll
-          for (int e = 0; e < EPC; ++e)
-            u[e] = fmaf(tp[k][e], chunk_value<T>(win[jj + KMAX - 1 - k], e), u[e]);
+        for (int e = 0; e < EPC; ++e) {
+          const float t = chunk_value<float>(tpv[k][e >> 2], e & 3);
+          u[e] = fmaf(ok ? t : 0.0f, chunk_value<T>(win[jj + KMAX - 1 - k], e), u[e]);
         }
       }
       uint4 out;
       if constexpr (sizeof(T) == 2) {
-        uint32_t w[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          w[q] = (uint32_t)f32_to_bf16_bits(u[2 * q]) |
-                 ((uint32_t)f32_to_bf16_bits(u[2 * q + 1]) << 16);
-        out = make_uint4(w[0], w[1], w[2], w[3]);
+        out = make_uint4(pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]), pack_bf16x2(u[4], u[5]),
+                         pack_bf16x2(u[6], u[7]));
       } else {
         out = make_uint4(__float_as_uint(u[0]), __float_as_uint(u[1]), __float_as_uint(u[2]),
                          __float_as_uint(u[3]));
       }
-      *reinterpret_cast<uint4*>(lds + lds_offset(lrow0 + jj, c)) = out;
+      lds_store<u32x4_t>(lds + lds_offset(lrow0 + jj, c), as_u32x4(out));
     }
   }
 };
 
-// Adapts ConvLoader to the mainloop's load/store interface (the store needs
-// the k-tile index for the taps).
+// eta * V^ = eta * U W_target over all token rows, written token-major to Vt.
 template <typename T, int KMAX>
-struct ConvLoaderRef {
-  ConvLoader<T, KMAX>& l;
-  int64_t pending;
-  __device__ __forceinline__ void load(int64_t kt) {
-    l.load(kt);
-    pending = kt;
-  }
-  __device__ __forceinline__ void store(char* lds) const { l.store_kt(lds, pending); }
-};
-
-// eta * V^ = eta * U W_target over all token rows, written transposed into Vt.
-template <typename T, int KMAX>
-__global__ __launch_bounds__(kThreads) void target_kernel(Dims dm, const T* __restrict__ X0,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void target_kernel(Dims dm, const T* __restrict__ X0,
                                                           const float* __restrict__ tapsT,
                                                           const T* __restrict__ WtT,
                                                           T* __restrict__ Vt) {
   using S = Tile;
-  __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
+  lds_char* smem = (lds_char*)smem_raw;
   const int32_t BT = (int32_t)(dm.B * dm.T);
   const int64_t d = dm.d;
+  const int64_t ld = d * (int64_t)sizeof(T);
   const int tiles_m = (BT + S::BM - 1) / S::BM;
   const int tiles_n = (int)((d + S::BN - 1) / S::BN);
   const TileCoord tc =
       grouped_tile(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, 8);
   const int32_t row0 = tc.m * S::BM;
   const int64_t col0 = (int64_t)tc.n * S::BN;
-  const int tr = threadIdx.x >> 3;
 
-  ConvLoader<T, KMAX> conv;
-  conv.x0 = reinterpret_cast<const char*>(X0) + (threadIdx.x & 7) * 16;
-  conv.taps = tapsT;
-  conv.row_bytes = d * (int64_t)sizeof(T);
-  conv.d = d;
-  conv.r0 = row0 + tr * 8;
-  conv.BT = BT;
-  conv.T_seq = (int32_t)dm.T;
-  ConvLoaderRef<T, KMAX> la{conv, 0};
-  RowLoader<S::BN> lb;
-  lb.init([&](int q) -> const char* {
-    const int64_t j = col0 + tr + 32 * q;
-    return j < d ? reinterpret_cast<const char*>(WtT + j * d) : nullptr;
-  });
+  ConvLoader<T, KMAX> la;
+  la.init(X0, tapsT, dm, row0);
+  DirectLoader<S::BN> lb;
+  lb.init(reinterpret_cast<const char*>(WtT) + col0 * ld, ld, kRowBytes, (d - col0) * ld,
+          kRowBytes);
 
   Accum<S> acc;
   acc.zero();
   const LanePos p = lane_pos<S>();
-  const int64_t nk = d * (int64_t)sizeof(T) / kRowBytes;
-  mainloop<T, S>(acc, la, lb, nk, smem, p, [](int64_t) {});
+  mainloop<T, S>(acc, la, lb, ld / kRowBytes, smem, p, [](int64_t) {});
 
-  // Epilogue: eta * V^ goes to Vt through LDS in four passes of 64 columns
-  // (pass q: wave column q/2, its block columns 2(q%2) and 2(q%2)+1).
+  // eta * acc to Vt through the stage, four passes of 64 columns (pass q: wave
+  // column q/2, its block columns 2(q%2), 2(q%2)+1).
   const ChunkMap cm = chunk_map(dm);
   const float eta = dm.eta;
   const int wn = (threadIdx.x >> 6) & 1;
-  using Stage = TokStage<T>;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    if (wn == (q >> 1)) {
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int j = 2 * (q & 1) + jj;
-#pragma unroll
-        for (int i = 0; i < S::MB; ++i)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            float v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = eta * acc.v[i][j][4 * rq + e];
-            Stage::put4(smem, 32 * jj + (p.lane & 31), p.row(i, 4 * rq), v);
-          }
-      }
-    }
+    if (wn == (q >> 1))
+      stage_two_blocks<T, S>(smem, acc, p, 2 * (q & 1), [&](float x) { return eta * x; });
     __syncthreads();
     const int64_t cb = col0 + 64 * q;
-    Stage::flush(smem, Vt, dm.P, cb, (int)max<int64_t>(0, min<int64_t>(64, d - cb)), row0, BT, cm);
+    Stage<T>::flush_tokens(smem, Vt, d, cb, (int)max<int64_t>(0, min<int64_t>(64, d - cb)), row0,
+                           BT, cm);
     __syncthreads();
   }
 }
@@ -380,78 +376,90 @@ __global__ __launch_bounds__(kThreads) void target_kernel(Dims dm, const T* __re
 //   slot[jj] <- W                        (the weight chunk g0+jj uses)
 //   W        <- W + (eta V^_i)^T Z_i      (MFMA accumulation into the fp32 tile)
 // and finally W_state <- W.  The accumulator is the fp32 state itself, so the
-// result does not depend on how the chunks are grouped.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void prefix_update_kernel(Dims dm, const T* __restrict__ Vt,
-                                                                 const T* __restrict__ Zt,
-                                                                 float* __restrict__ W_state,
-                                                                 T* __restrict__ slots, int64_t g0,
-                                                                 int64_t gc) {
-  using S = Tile;
-  __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
+// result does not depend on how the chunks are grouped.  The tile shape S
+// divides d and f exactly (the host picks it), so every tile is full.
+template <typename T, class S>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefix_update_kernel(
+    Dims dm, const T* __restrict__ Vt, const T* __restrict__ Zt, float* __restrict__ W_state,
+    T* __restrict__ slots, int64_t g0, int64_t gc) {
+  constexpr int TB = kRowBytes / (int)sizeof(T);
+  __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
+  lds_char* smem = (lds_char*)smem_raw;
   const int64_t d = dm.d, f = dm.f;
-  const int tiles_m = (int)((d + S::BM - 1) / S::BM);
-  const int tiles_n = (int)((f + S::BN - 1) / S::BN);
+  const int tiles_m = (int)(d / S::BM);
+  const int tiles_n = (int)(f / S::BN);
   const int per_seq = tiles_m * tiles_n;
-  // XCD-aware: consecutive logical tiles land on the same XCD.
   const int L = xcd_remap(blockIdx.x, per_seq * (int)dm.B);
   const int64_t b = L / per_seq;
   const TileCoord tc = grouped_tile(L - (int)b * per_seq, tiles_m, tiles_n, 4);
   const int64_t m0 = (int64_t)tc.m * S::BM, n0 = (int64_t)tc.n * S::BN;
-  const int tr = threadIdx.x >> 3;
-  const int64_t col_start = (b * dm.N + g0) * dm.Cp;
+  const int64_t kb0 = (b * dm.N + g0) * dm.Cp / TB;  // first k-block of the group
 
-  RowLoader<S::BM> la;
-  la.init([&](int q) -> const char* {
-    const int64_t m = m0 + tr + 32 * q;
-    return m < d ? reinterpret_cast<const char*>(Vt + m * dm.P + col_start) : nullptr;
-  });
-  RowLoader<S::BN> lb;
-  lb.init([&](int q) -> const char* {
-    const int64_t n = n0 + tr + 32 * q;
-    return n < f ? reinterpret_cast<const char*>(Zt + n * dm.P + col_start) : nullptr;
-  });
+  DirectLoader<S::BM> la;
+  la.init(reinterpret_cast<const char*>(Vt) + (kb0 * d + m0) * kRowBytes, kRowBytes,
+          d * kRowBytes, (d - m0) * kRowBytes, 0);
+  DirectLoader<S::BN> lb;
+  lb.init(reinterpret_cast<const char*>(Zt) + (kb0 * f + n0) * kRowBytes, kRowBytes,
+          f * kRowBytes, (f - n0) * kRowBytes, 0);
 
   const LanePos p = lane_pos<S>();
-  // Lane base: row m0 + wave_m0 + 4 (lane / 32), column n0 + wave_n0 + lane % 32.
-  // d and f are multiples of 32, so each 32x32 block is wholly inside or
-  // wholly outside the weight.
-  const int64_t lane_off = (m0 + p.wave_m0 + 4 * (p.lane >> 5)) * f + n0 + p.wave_n0 + (p.lane & 31);
-  bool blk_ok[S::MB][S::NB];
+  // Accumulator element (i, j, 4q + e) of this lane is W[m][n] with
+  //   m = m0 + wave_m0 + 32 i + 8 q + 4 (lane / 32) + e,  n = n0 + wave_n0 + 32 j + lane % 32.
+  // Buffer accesses: per-lane offset for each e (4 registers), the uniform
+  // row part (32 i + 8 q) f as the scalar offset, 32 j as the immediate.
+  uint32_t lane_e[4];
 #pragma unroll
-  for (int i = 0; i < S::MB; ++i)
-#pragma unroll
-    for (int j = 0; j < S::NB; ++j)
-      blk_ok[i][j] = (m0 + p.wave_m0 + 32 * i < d) && (n0 + p.wave_n0 + 32 * j < f);
-  auto elem_off = [&](int i, int j, int r) -> int64_t {
-    return (int64_t)(32 * i + 8 * (r >> 2) + (r & 3)) * f + 32 * j;
-  };
+  for (int e = 0; e < 4; ++e)
+    lane_e[e] = (uint32_t)((p.wave_m0 + 4 * (p.lane >> 5) + e) * f + p.wave_n0 + (p.lane & 31));
+  const int64_t corner = m0 * f + n0;
+  const int64_t span = (d - m0) * f - n0;  // elements addressable from the corner
+  const uint32_t fu = (uint32_t)f;
 
-  float* Wb = W_state + b * d * f + lane_off;
+  const rsrc_t wr = make_rsrc(W_state + b * d * f + corner, span * 4);
   Accum<S> acc;
 #pragma unroll
   for (int i = 0; i < S::MB; ++i)
 #pragma unroll
-    for (int j = 0; j < S::NB; ++j)
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t so = (uint32_t)(32 * i + 8 * q) * fu * 4u;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc.v[i][j][r] = blk_ok[i][j] ? Wb[elem_off(i, j, r)] : 0.0f;
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int j = 0; j < S::NB; ++j)
+          acc.v[i][j][4 * q + e] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(wr, (lane_e[e] + 32 * j) * 4, so, 0));
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
   const int64_t slot_stride = dm.B * d * f;
-  T* slot_b = slots + b * d * f + lane_off;
   auto write_slot = [&](int64_t jj) {
-    T* dst = slot_b + jj * slot_stride;
+    const rsrc_t sr = make_rsrc(slots + jj * slot_stride + b * d * f + corner,
+                                span * (int64_t)sizeof(T));
 #pragma unroll
     for (int i = 0; i < S::MB; ++i)
 #pragma unroll
-      for (int j = 0; j < S::NB; ++j)
-        if (blk_ok[i][j]) {
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t so = (uint32_t)(32 * i + 8 * q) * fu * (uint32_t)sizeof(T);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) Elem<T>::store(dst + elem_off(i, j, r), acc.v[i][j][r]);
-        }
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int j = 0; j < S::NB; ++j) {
+            const uint32_t vo = (lane_e[e] + 32 * j) * (uint32_t)sizeof(T);
+            if constexpr (sizeof(T) == 2)
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc.v[i][j][4 * q + e]), sr,
+                                                    vo, so, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.v[i][j][4 * q + e]), sr,
+                                                    vo, so, 0);
+          }
+        // one row group at a time: keeps the compiler from hoisting every
+        // accumulator read (and conversion) ahead of the stores
+        __builtin_amdgcn_sched_barrier(0);
+      }
   };
 
   write_slot(0);
-  const int64_t kt_per_chunk = dm.Cp * (int64_t)sizeof(T) / kRowBytes;
+  const int64_t kt_per_chunk = dm.Cp / TB;
   const int64_t nk = gc * kt_per_chunk;
   mainloop<T, S>(acc, la, lb, nk, smem, p, [&](int64_t kt) {
     const int64_t done = kt + 1;
@@ -461,23 +469,30 @@ __global__ __launch_bounds__(kThreads) void prefix_update_kernel(Dims dm, const 
 #pragma unroll
   for (int i = 0; i < S::MB; ++i)
 #pragma unroll
-    for (int j = 0; j < S::NB; ++j)
-      if (blk_ok[i][j]) {
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t so = (uint32_t)(32 * i + 8 * q) * fu * 4u;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) Wb[elem_off(i, j, r)] = acc.v[i][j][r];
-      }
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int j = 0; j < S::NB; ++j)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.v[i][j][4 * q + e]), wr,
+                                                (lane_e[e] + 32 * j) * 4, so, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // ===================================================================== S3
 // O_i = Z_i slot_i^T for every chunk of the group and every sequence.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void down_proj_kernel(Dims dm, const T* __restrict__ Z,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void down_proj_kernel(Dims dm, const T* __restrict__ Z,
                                                              const T* __restrict__ slots,
                                                              T* __restrict__ O, int64_t g0,
                                                              int64_t gc) {
   using S = Tile;
-  __shared__ __attribute__((aligned(16))) char smem[S::kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
+  lds_char* smem = (lds_char*)smem_raw;
   const int64_t d = dm.d, f = dm.f, C = dm.C, T_seq = dm.T;
+  const int64_t ld = f * (int64_t)sizeof(T);
   const int tiles_m = (int)((C + S::BM - 1) / S::BM);
   const int tiles_n = (int)((d + S::BN - 1) / S::BN);
   const int per_chunk = tiles_m * tiles_n;
@@ -489,52 +504,32 @@ __global__ __launch_bounds__(kThreads) void down_proj_kernel(Dims dm, const T* _
   const int64_t c_begin = chunk * C;
   const int64_t c_len = min(C, T_seq - c_begin);
   const int64_t m0 = (int64_t)tc.m * S::BM, n0 = (int64_t)tc.n * S::BN;
-  const int64_t tok0 = b * T_seq + c_begin;  // first token row of the chunk
-  const int tr = threadIdx.x >> 3;
+  const int64_t row0 = b * T_seq + c_begin + m0;  // first token row of the tile
   const T* slot = slots + (jj * dm.B + b) * d * f;
 
-  RowLoader<S::BM> la;
-  la.init([&](int q) -> const char* {
-    const int64_t r = m0 + tr + 32 * q;
-    return r < c_len ? reinterpret_cast<const char*>(Z + (tok0 + r) * f) : nullptr;
-  });
-  RowLoader<S::BN> lb;
-  lb.init([&](int q) -> const char* {
-    const int64_t n = n0 + tr + 32 * q;
-    return n < d ? reinterpret_cast<const char*>(slot + n * f) : nullptr;
-  });
+  DirectLoader<S::BM> la;
+  la.init(reinterpret_cast<const char*>(Z) + row0 * ld, ld, kRowBytes, (c_len - m0) * ld,
+          kRowBytes);
+  DirectLoader<S::BN> lb;
+  lb.init(reinterpret_cast<const char*>(slot) + n0 * ld, ld, kRowBytes, (d - n0) * ld, kRowBytes);
 
   Accum<S> acc;
   acc.zero();
   const LanePos p = lane_pos<S>();
-  const int64_t nk = f * (int64_t)sizeof(T) / kRowBytes;
-  mainloop<T, S>(acc, la, lb, nk, smem, p, [](int64_t) {});
+  mainloop<T, S>(acc, la, lb, ld / kRowBytes, smem, p, [](int64_t) {});
 
-  // Epilogue through LDS, four passes of 64 columns (pass q: wave column
-  // q/2, block columns 2(q%2), 2(q%2)+1), written row-major; rows beyond the
-  // chunk are skipped.
+  // O through the stage, four passes of 64 columns, written row-major; rows
+  // beyond the chunk are skipped.
   const int wn = (threadIdx.x >> 6) & 1;
-  using Stage = TokStage<T>;
+  const int32_t rows_valid = (int32_t)min<int64_t>(S::BM, c_len - m0);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    if (wn == (q >> 1)) {
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int i = 0; i < S::MB; ++i)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            float v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = acc.v[i][2 * (q & 1) + jj][4 * rq + e];
-            Stage::put4(smem, 32 * jj + (p.lane & 31), p.row(i, 4 * rq), v);
-          }
-    }
+    if (wn == (q >> 1))
+      stage_two_blocks<T, S>(smem, acc, p, 2 * (q & 1), [](float x) { return x; });
     __syncthreads();
-    const int64_t cb = n0 + 64 * q;
-    const int ncols = (int)max<int64_t>(0, min<int64_t>(64, d - cb));
-    Stage::flush_rows(smem, O + (tok0 + m0) * d, d, cb, ncols, 0,
-                      (int32_t)min<int64_t>(S::BM, c_len - m0));
+    const int64_t cbase = n0 + 64 * q;
+    Stage<T>::flush_rows(smem, O + row0 * d, d, cbase,
+                         (int)max<int64_t>(0, min<int64_t>(64, d - cbase)), rows_valid);
     __syncthreads();
   }
 }
@@ -567,6 +562,20 @@ __global__ void transpose_kernel(T* __restrict__ dst, const T* __restrict__ src,
   }
 }
 
+// WgU[(n/32)*64 + (n%32)] = W_gate[n], WgU[(n/32)*64 + 32 + (n%32)] = W_up[n]
+// (rows of d elements), 16 bytes per thread.
+__global__ void interleave_kernel(uint4* __restrict__ dst, const uint4* __restrict__ wg,
+                                  const uint4* __restrict__ wu, int64_t f, int64_t row_vecs) {
+  const int64_t total = 2 * f * row_vecs;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+    const int64_t r = e / row_vecs, v = e - r * row_vecs;
+    const int64_t blk = r / 64, w = r % 64;
+    const int64_t n = blk * 32 + (w & 31);
+    dst[e] = (w < 32 ? wg : wu)[n * row_vecs + v];
+  }
+}
+
 // tapsT[k][c] = taps[c][k] as fp32 for k < K, 0 for K <= k < 8.
 template <typename T>
 __global__ void taps_kernel(float* __restrict__ tapsT, const T* __restrict__ taps, int64_t d,
@@ -576,8 +585,8 @@ __global__ void taps_kernel(float* __restrict__ tapsT, const T* __restrict__ tap
   for (int k = 0; k < 8; ++k) tapsT[k * d + c] = k < K ? Elem<T>::to_f32(taps[c * K + k]) : 0.0f;
 }
 
-// Zero the padding columns (token index inside the chunk >= chunk length) of
-// Zt ([f][P]) and Vt ([d][P]).
+// Zero the padding token columns (index inside the chunk >= chunk length) of
+// Zt and Vt (k-blocked, f and d rows).
 template <typename T>
 __global__ void pad_fill_kernel(T* __restrict__ zt, T* __restrict__ vt, Dims dm) {
   const int64_t rows = dm.f + dm.d;
@@ -589,8 +598,10 @@ __global__ void pad_fill_kernel(T* __restrict__ zt, T* __restrict__ vt, Dims dm)
     const int64_t i = q % dm.N;
     const int64_t len = min(dm.C, dm.T - i * dm.C);
     if (j < len) continue;
-    T* dst = row < dm.f ? zt + row * dm.P + col : vt + (row - dm.f) * dm.P + col;
-    Elem<T>::store(dst, 0.0f);
+    if (row < dm.f)
+      Elem<T>::store(zt + kblock_index<T>(row, col, dm.f), 0.0f);
+    else
+      Elem<T>::store(vt + kblock_index<T>(row - dm.f, col, dm.d), 0.0f);
   }
 }
 
@@ -607,6 +618,8 @@ WorkspacePlan plan_workspace(const Dims& dm, int64_t group) {
   off = align256(off + (size_t)dm.f * dm.P * es);
   w.vt_off = off;
   off = align256(off + (size_t)dm.d * dm.P * es);
+  w.wgu_off = off;
+  off = align256(off + (size_t)2 * dm.f * dm.d * es);
   w.wtt_off = off;
   off = align256(off + (size_t)dm.d * dm.d * es);
   w.taps_off = off;
@@ -619,67 +632,69 @@ WorkspacePlan plan_workspace(const Dims& dm, int64_t group) {
   return w;
 }
 
+static inline unsigned grid_for(int64_t n, int64_t per_block, int64_t cap) {
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + per_block - 1) / per_block, cap));
+}
+
 hipError_t launch_state_reset(float* W_state, const void* W0, Dtype w0_dt, int64_t B, int64_t d,
                               int64_t f, hipStream_t s) {
   const int64_t n = d * f;
-  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
   if (w0_dt == Dtype::BF16)
-    hipLaunchKernelGGL(state_reset_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, s,
+    hipLaunchKernelGGL(state_reset_kernel<uint16_t>, dim3(grid_for(n, 256, 8192)), dim3(256), 0, s,
                        W_state, static_cast<const uint16_t*>(W0), B, n);
   else
-    hipLaunchKernelGGL(state_reset_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s,
+    hipLaunchKernelGGL(state_reset_kernel<float>, dim3(grid_for(n, 256, 8192)), dim3(256), 0, s,
                        W_state, static_cast<const float*>(W0), B, n);
   return hipGetLastError();
 }
 
-hipError_t launch_transpose(void* dst, const void* src, int64_t n, Dtype dt, hipStream_t s) {
-  const dim3 grid((unsigned)((n + 63) / 64), (unsigned)((n + 63) / 64));
-  if (dt == Dtype::BF16)
-    hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(256), 0, s,
-                       static_cast<uint16_t*>(dst), static_cast<const uint16_t*>(src), n);
-  else
-    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s, static_cast<float*>(dst),
-                       static_cast<const float*>(src), n);
-  return hipGetLastError();
-}
-
-hipError_t launch_taps(float* tapsT, const void* taps, const Dims& dm, hipStream_t s) {
-  const unsigned blocks = (unsigned)((dm.d + 255) / 256);
-  if (dm.dt == Dtype::BF16)
-    hipLaunchKernelGGL(taps_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, tapsT,
+hipError_t launch_weight_prep(const Dims& dm, const void* Wg, const void* Wu, const void* Wt,
+                              const void* taps, void* WgU, void* WtT, float* tapsT,
+                              hipStream_t s) {
+  const int64_t row_vecs = dm.d * (int64_t)dtype_bytes(dm.dt) / 16;
+  hipLaunchKernelGGL(interleave_kernel, dim3(grid_for(2 * dm.f * row_vecs, 256, 16384)), dim3(256),
+                     0, s, static_cast<uint4*>(WgU), static_cast<const uint4*>(Wg),
+                     static_cast<const uint4*>(Wu), dm.f, row_vecs);
+  const dim3 tgrid((unsigned)((dm.d + 63) / 64), (unsigned)((dm.d + 63) / 64));
+  const unsigned tblocks = (unsigned)((dm.d + 255) / 256);
+  if (dm.dt == Dtype::BF16) {
+    hipLaunchKernelGGL(transpose_kernel<uint16_t>, tgrid, dim3(256), 0, s,
+                       static_cast<uint16_t*>(WtT), static_cast<const uint16_t*>(Wt), dm.d);
+    hipLaunchKernelGGL(taps_kernel<uint16_t>, dim3(tblocks), dim3(256), 0, s, tapsT,
                        static_cast<const uint16_t*>(taps), dm.d, dm.K);
-  else
-    hipLaunchKernelGGL(taps_kernel<float>, dim3(blocks), dim3(256), 0, s, tapsT,
+  } else {
+    hipLaunchKernelGGL(transpose_kernel<float>, tgrid, dim3(256), 0, s, static_cast<float*>(WtT),
+                       static_cast<const float*>(Wt), dm.d);
+    hipLaunchKernelGGL(taps_kernel<float>, dim3(tblocks), dim3(256), 0, s, tapsT,
                        static_cast<const float*>(taps), dm.d, dm.K);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_pad_fill(void* zt, void* vt, const Dims& dm, hipStream_t s) {
   const int64_t total = (dm.f + dm.d) * dm.P;
-  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 65536);
   if (dm.dt == Dtype::BF16)
-    hipLaunchKernelGGL(pad_fill_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<uint16_t*>(zt), static_cast<uint16_t*>(vt), dm);
+    hipLaunchKernelGGL(pad_fill_kernel<uint16_t>, dim3(grid_for(total, 256, 65536)), dim3(256), 0,
+                       s, static_cast<uint16_t*>(zt), static_cast<uint16_t*>(vt), dm);
   else
-    hipLaunchKernelGGL(pad_fill_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s,
+    hipLaunchKernelGGL(pad_fill_kernel<float>, dim3(grid_for(total, 256, 65536)), dim3(256), 0, s,
                        static_cast<float*>(zt), static_cast<float*>(vt), dm);
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu(const Dims& dm, const void* H, const void* Wg, const void* Wu, void* Z,
-                         void* Zt, hipStream_t s) {
+hipError_t launch_swiglu(const Dims& dm, const void* H, const void* WgU, void* Z, void* Zt,
+                         hipStream_t s) {
   const int64_t BT = dm.B * dm.T;
-  const int64_t tiles = ((BT + Tile::BM - 1) / Tile::BM) * ((dm.f + Tile::BN / 2 - 1) / (Tile::BN / 2));
+  const int64_t tiles =
+      ((BT + Tile::BM - 1) / Tile::BM) * ((dm.f + Tile::BN / 2 - 1) / (Tile::BN / 2));
   if (dm.dt == Dtype::BF16)
     hipLaunchKernelGGL(swiglu_kernel<uint16_t>, dim3((unsigned)tiles), dim3(kThreads), 0, s, dm,
-                       static_cast<const uint16_t*>(H), static_cast<const uint16_t*>(Wg),
-                       static_cast<const uint16_t*>(Wu), static_cast<uint16_t*>(Z),
-                       static_cast<uint16_t*>(Zt));
+                       static_cast<const uint16_t*>(H), static_cast<const uint16_t*>(WgU),
+                       static_cast<uint16_t*>(Z), static_cast<uint16_t*>(Zt));
   else
     hipLaunchKernelGGL(swiglu_kernel<float>, dim3((unsigned)tiles), dim3(kThreads), 0, s, dm,
-                       static_cast<const float*>(H), static_cast<const float*>(Wg),
-                       static_cast<const float*>(Wu), static_cast<float*>(Z),
-                       static_cast<float*>(Zt));
+                       static_cast<const float*>(H), static_cast<const float*>(WgU),
+                       static_cast<float*>(Z), static_cast<float*>(Zt));
   return hipGetLastError();
 }
 
@@ -708,18 +723,34 @@ hipError_t launch_target(const Dims& dm, const void* X0, const void* tapsT, cons
   return hipGetLastError();
 }
 
+template <typename T, class S>
+static void launch_prefix_update_t(const Dims& dm, const T* Vt, const T* Zt, float* W_state, T* slots,
+                                   int64_t g0, int64_t gc, hipStream_t s) {
+  const int64_t tiles = (dm.d / S::BM) * (dm.f / S::BN) * dm.B;
+  hipLaunchKernelGGL((prefix_update_kernel<T, S>), dim3((unsigned)tiles), dim3(kThreads), 0, s, dm,
+                     Vt, Zt, W_state, slots, g0, gc);
+}
+
+// 256 x 256 tiles when they divide the weight, 64 x 64 otherwise (d and f are
+// multiples of 64).
+template <typename T>
+static void launch_prefix_update_dt(const Dims& dm, const T* Vt, const T* Zt, float* W_state,
+                                    T* slots, int64_t g0, int64_t gc, hipStream_t s) {
+  if (dm.d % 256 == 0 && dm.f % 256 == 0)
+    launch_prefix_update_t<T, TileShape<256, 256>>(dm, Vt, Zt, W_state, slots, g0, gc, s);
+  else
+    launch_prefix_update_t<T, TileShape<64, 64>>(dm, Vt, Zt, W_state, slots, g0, gc, s);
+}
+
 hipError_t launch_prefix_update(const Dims& dm, const void* Vt, const void* Zt, float* W_state,
                                 void* slots, int64_t g0, int64_t gc, hipStream_t s) {
-  const int64_t tiles =
-      ((dm.d + Tile::BM - 1) / Tile::BM) * ((dm.f + Tile::BN - 1) / Tile::BN) * dm.B;
   if (dm.dt == Dtype::BF16)
-    hipLaunchKernelGGL(prefix_update_kernel<uint16_t>, dim3((unsigned)tiles), dim3(kThreads), 0,
-                       s, dm, static_cast<const uint16_t*>(Vt), static_cast<const uint16_t*>(Zt),
-                       W_state, static_cast<uint16_t*>(slots), g0, gc);
+    launch_prefix_update_dt<uint16_t>(dm, static_cast<const uint16_t*>(Vt),
+                                      static_cast<const uint16_t*>(Zt), W_state,
+                                      static_cast<uint16_t*>(slots), g0, gc, s);
   else
-    hipLaunchKernelGGL(prefix_update_kernel<float>, dim3((unsigned)tiles), dim3(kThreads), 0, s,
-                       dm, static_cast<const float*>(Vt), static_cast<const float*>(Zt), W_state,
-                       static_cast<float*>(slots), g0, gc);
+    launch_prefix_update_dt<float>(dm, static_cast<const float*>(Vt), static_cast<const float*>(Zt),
+                                   W_state, static_cast<float*>(slots), g0, gc, s);
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ struct Dims {
 
 // Workspace regions (byte offsets from the workspace base, 256-byte aligned).
 struct WorkspacePlan {
-  size_t z_off, zt_off, vt_off, wtt_off, taps_off, slots_off;
+  size_t z_off, zt_off, vt_off, wgu_off, wtt_off, taps_off, slots_off;
   size_t slot_bytes;   // one chunk slot for all B sequences: B * d * f * es
   size_t fixed_bytes;  // everything except the slots
   int64_t group;       // chunks per group G
@@ -37,11 +37,12 @@ WorkspacePlan plan_workspace(const Dims& dm, int64_t group);
 // Kernel launchers (asynchronous on `s`; return hipGetLastError()).
 hipError_t launch_state_reset(float* W_state, const void* W0, Dtype w0_dt, int64_t B, int64_t d,
                               int64_t f, hipStream_t s);
-hipError_t launch_transpose(void* dst, const void* src, int64_t n, Dtype dt, hipStream_t s);
-hipError_t launch_taps(float* tapsT, const void* taps, const Dims& dm, hipStream_t s);
+// W_gate/W_up interleaved into WgU, W_target transposed into WtT, taps to fp32 tapsT.
+hipError_t launch_weight_prep(const Dims& dm, const void* Wg, const void* Wu, const void* Wt,
+                              const void* taps, void* WgU, void* WtT, float* tapsT, hipStream_t s);
 hipError_t launch_pad_fill(void* zt, void* vt, const Dims& dm, hipStream_t s);
-hipError_t launch_swiglu(const Dims& dm, const void* H, const void* Wg, const void* Wu, void* Z,
-                         void* Zt, hipStream_t s);
+hipError_t launch_swiglu(const Dims& dm, const void* H, const void* WgU, void* Z, void* Zt,
+                         hipStream_t s);
 hipError_t launch_target(const Dims& dm, const void* X0, const void* taps, const void* WtT,
                          void* Vt, hipStream_t s);
 hipError_t launch_prefix_update(const Dims& dm, const void* Vt, const void* Zt, float* W_state,

@@ -59,11 +59,11 @@ def test_workspace_plan():
 
 
 def test_workspace_fixed_part_matches_layout():
-    # Z [T][f] + Zt [f][P] + Vt [d][P] + WtT [d][d] + tapsT [8][d] fp32 + 1 slot
+    # Z [T][f] + Zt [f][P] + Vt [d][P] + WgU [2f][d] + WtT [d][d] + tapsT [8][d] fp32 + 1 slot
     d = desc(seq_len=1000, chunk=100)  # padded chunks: Cp = 128, P = 10 * 128
     es = 2
-    parts = [1000 * 512 * es, 512 * 1280 * es, 256 * 1280 * es, 256 * 256 * es, 8 * 256 * 4,
-             256 * 512 * es]
+    parts = [1000 * 512 * es, 512 * 1280 * es, 256 * 1280 * es, 2 * 512 * 256 * es,
+             256 * 256 * es, 8 * 256 * 4, 256 * 512 * es]
     expect = sum((p + 255) // 256 * 256 for p in parts)
     assert tm.ttt_mlp_workspace_size(d, 1) == expect
 
