@@ -7,8 +7,9 @@
 // operand rows are found (row loaders) and what happens to the accumulator
 // (epilogues).
 //
-// Tile geometry (one workgroup = 4 wave64s in a 2 x 2 grid):
-//   * BM x BN output tile, each wave owns (BM/2) x (BN/2) as 32x32 MFMA blocks;
+// Tile geometry (one workgroup = WAVES_M x WAVES_N wave64s):
+//   * BM x BN output tile, each wave owns (BM/WAVES_M) x (BN/WAVES_N) as 32x32
+//     MFMA blocks;
 //   * one k-tile = 128 bytes of K per operand row (64 bf16 or 32 fp32 values);
 //   * LDS holds two stages of A (BM x 128 B) and B (BN x 128 B); each 128-byte
 //     row is eight 16-byte chunks stored at chunk ^ (row & 7), so both the
@@ -31,7 +32,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;     // 4 waves
 constexpr int kRowBytes = 128;    // bytes of K per operand row per k-tile
 constexpr int kChunks = 8;        // 16-byte chunks per row per k-tile
 constexpr int kTokenAlign = 64;   // chunk padding in the token-major layouts
@@ -97,22 +97,32 @@ __device__ __forceinline__ void lds_store(lds_char* p, V v) {
 __device__ __forceinline__ u32x4_t as_u32x4(const uint4& v) { return u32x4_t{v.x, v.y, v.z, v.w}; }
 __device__ __forceinline__ uint4 as_uint4(const u32x4_t& v) { return make_uint4(v[0], v[1], v[2], v[3]); }
 
+#ifndef TTT_LDS_SWZ_SHIFT
+#define TTT_LDS_SWZ_SHIFT 1
+#endif
+__device__ __forceinline__ int lds_swz(int row) { return (row >> TTT_LDS_SWZ_SHIFT) & 7; }
 __device__ __forceinline__ uint32_t lds_offset(int row, int chunk) {
-  return (uint32_t)row * kRowBytes + (uint32_t)((chunk ^ (row & 7)) << 4);
+  return (uint32_t)row * kRowBytes + (uint32_t)((chunk ^ lds_swz(row)) << 4);
 }
 
 // ------------------------------------------------------------- tile shapes
-template <int BM_, int BN_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct TileShape {
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
-  static constexpr int WM = BM / 2;   // wave sub-tile rows
-  static constexpr int WN = BN / 2;   // wave sub-tile cols
-  static constexpr int MB = WM / 32;  // 32x32 blocks per wave, rows
-  static constexpr int NB = WN / 32;  // 32x32 blocks per wave, cols
+  static constexpr int WAVES_M = WAVES_M_;
+  static constexpr int WAVES_N = WAVES_N_;
+  static constexpr int kWaves = WAVES_M * WAVES_N;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int WM = BM / WAVES_M;  // wave sub-tile rows
+  static constexpr int WN = BN / WAVES_N;  // wave sub-tile cols
+  static constexpr int MB = WM / 32;       // 32x32 blocks per wave, rows
+  static constexpr int NB = WN / 32;       // 32x32 blocks per wave, cols
   static constexpr int kStageBytes = (BM + BN) * kRowBytes;
   static constexpr int kLdsBytes = 2 * kStageBytes;
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must hold 2x2 waves of 32x32 blocks");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "waves hold whole 32x32 blocks");
+  static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0,
+                "each wave loads whole 8-row groups");
 };
 
 template <class S>
@@ -141,8 +151,8 @@ template <class S>
 __device__ __forceinline__ LanePos lane_pos() {
   const int wave = threadIdx.x >> 6;
   LanePos p;
-  p.wave_m0 = (wave >> 1) * S::WM;
-  p.wave_n0 = (wave & 1) * S::WN;
+  p.wave_m0 = (wave / S::WAVES_N) * S::WM;
+  p.wave_n0 = (wave % S::WAVES_N) * S::WN;
   p.lane = threadIdx.x & 63;
   return p;
 }
@@ -264,8 +274,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 //                     (0 for direct loaders).
 //
 // DirectLoader moves one operand's k-tile (ROWS rows x 128 bytes) with
-// buffer_load ... lds (no registers): wave w fills rows [w ROWS/4, (w+1) ROWS/4)
-// of the stage, 8 rows (1 KB) per instruction, lane l writing 16 bytes at
+// buffer_load ... lds (no registers): wave w of WAVES fills rows
+// [w ROWS/WAVES, (w+1) ROWS/WAVES) of the stage, 8 rows (1 KB) per instruction, lane l writing 16 bytes at
 // lane * 16 of that KB.  The swizzled layout (row r, chunk c at c ^ (r & 7)) is
 // produced by choosing the source: lane l reads chunk (l & 7) ^ (l >> 3) of
 // row l >> 3 of its group.  Addressing, in bytes and uniform across the
@@ -276,10 +286,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Row-major operands use row_stride = row length, kt_stride = kt_shrink = 128;
 // k-blocked operands ([K/kt][rows][128 B]) use row_stride = 128,
 // kt_stride = rows * 128, kt_shrink = 0.
-template <int ROWS>
+template <int ROWS, int WAVES>
 struct DirectLoader {
   static constexpr int kStagedLoads = 0;
-  static constexpr int kPer = ROWS / 32;  // instructions per wave per k-tile
+  static constexpr int kRowsPerWave = ROWS / WAVES;
+  static constexpr int kPer = kRowsPerWave / 8;  // instructions per wave per k-tile
   const char* base;
   int64_t kt_stride, valid_bytes, kt_shrink;
   uint32_t voff[kPer];
@@ -293,11 +304,14 @@ struct DirectLoader {
     kt_shrink = kt_shrink_;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-    lds_row0 = (uint32_t)(wave * (ROWS / 4));
-    const int rr = lane >> 3, c = (lane & 7) ^ rr;
+    lds_row0 = (uint32_t)(wave * kRowsPerWave);
+    const int rr = lane >> 3;
 #pragma unroll
-    for (int q = 0; q < kPer; ++q)
-      voff[q] = (uint32_t)((lds_row0 + 8 * q + rr) * row_stride + c * 16);
+    for (int q = 0; q < kPer; ++q) {
+      const int row = (int)lds_row0 + 8 * q + rr;
+      const int c = (lane & 7) ^ lds_swz(row);  // source chunk landing at chunk lane & 7
+      voff[q] = (uint32_t)(row * row_stride + c * 16);
+    }
   }
   __device__ __forceinline__ void issue(int64_t kt, lds_char* stage) {
     const rsrc_t r = make_rsrc(base + kt * kt_stride, valid_bytes - kt * kt_shrink);
@@ -308,6 +322,49 @@ struct DirectLoader {
           voff[q], 0, 0, 0);
   }
   __device__ __forceinline__ void commit(lds_char*) const {}
+};
+
+// RegLoader: the same addressing as DirectLoader, through registers (global ->
+// VGPR with buffer loads in issue(), VGPR -> swizzled LDS in commit()).
+template <int ROWS, int WAVES>
+struct RegLoader {
+  static constexpr int kRowsPerWave = ROWS / WAVES;
+  static constexpr int kPer = kRowsPerWave / 8;
+  static constexpr int kStagedLoads = kPer;
+  const char* base;
+  int64_t kt_stride, valid_bytes, kt_shrink;
+  uint32_t voff[kPer];
+  uint32_t lds_row0;
+  uint4 reg[kPer];
+
+  __device__ __forceinline__ void init(const void* base_, int64_t row_stride, int64_t kt_stride_,
+                                       int64_t valid_bytes_, int64_t kt_shrink_) {
+    base = static_cast<const char*>(base_);
+    kt_stride = kt_stride_;
+    valid_bytes = valid_bytes_;
+    kt_shrink = kt_shrink_;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    lds_row0 = (uint32_t)(wave * kRowsPerWave);
+    const int rr = lane >> 3;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int row = (int)lds_row0 + 8 * q + rr;
+      voff[q] = (uint32_t)(row * row_stride + (lane & 7) * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(int64_t kt, lds_char*) {
+    const rsrc_t r = make_rsrc(base + kt * kt_stride, valid_bytes - kt * kt_shrink);
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) reg[q] = buf_load16(r, voff[q]);
+  }
+  __device__ __forceinline__ void commit(lds_char* stage) const {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q)
+      lds_store<u32x4_t>(stage + lds_offset((int)lds_row0 + 8 * q + (lane >> 3), lane & 7),
+                         as_u32x4(reg[q]));
+  }
 };
 
 // ---------------------------------------------------------------- mainloop

@@ -39,7 +39,24 @@
 
 namespace ttt {
 
-using Tile = TileShape<256, 256>;
+// Workgroup shape of the GEMM kernels: 256 x 256 output tile, WAVES_M x
+// WAVES_N waves (wave tile 128 x 64 with 2 x 4 waves: two waves per SIMD, so
+// one wave's MFMAs cover the other's LDS and barrier waits).
+#ifndef TTT_WAVES_M
+#define TTT_WAVES_M 2
+#endif
+#ifndef TTT_WAVES_N
+#define TTT_WAVES_N 4
+#endif
+#define TTT_GEMM_THREADS (64 * TTT_WAVES_M * TTT_WAVES_N)
+#define TTT_GEMM_WPE (TTT_WAVES_M * TTT_WAVES_N / 4)
+using Tile = TileShape<256, 256, TTT_WAVES_M, TTT_WAVES_N>;
+// The target GEMM keeps one wave per SIMD: its A operand is built in registers
+// (the conv window and taps), which needs the larger register budget.
+using TargetTile = TileShape<256, 256, 2, 2>;
+#define TTT_GEMM_KERNEL                                  \
+  __global__ __launch_bounds__(TTT_GEMM_THREADS)          \
+  __attribute__((amdgpu_waves_per_eu(TTT_GEMM_WPE, TTT_GEMM_WPE)))
 
 // ------------------------------------------------------------ chunk columns
 struct ChunkMap {
@@ -71,7 +88,7 @@ __device__ __forceinline__ int64_t kblock_index(int64_t n, int64_t p, int64_t R)
 // (tokens), put by lanes 4 rows at a time, read back either as token runs
 // (token-major outputs) or as column runs (row-major outputs).  Row stride of
 // 260 elements keeps the 4-element puts of 16 lanes on distinct banks.
-template <typename T>
+template <typename T, int NTHREADS>
 struct Stage {
   static constexpr int kCols = 64;
   static constexpr int kToks = 256;
@@ -97,7 +114,7 @@ struct Stage {
                                                       int32_t row0, int32_t rows_total,
                                                       const ChunkMap& cm) {
     constexpr int GPB = TB / 8;  // 8-token runs per block row
-    for (int it = threadIdx.x; it < kCols * (kToks / 8); it += kThreads) {
+    for (int it = threadIdx.x; it < kCols * (kToks / 8); it += NTHREADS) {
       const int g = it % GPB, c = (it / GPB) % kCols, tb = it / (GPB * kCols);
       const int tok = tb * TB + g * 8;
       const int32_t row = row0 + tok;
@@ -129,7 +146,7 @@ struct Stage {
   __device__ __forceinline__ static void flush_rows(const lds_char* lds, T* __restrict__ dst,
                                                     int64_t ld, int64_t col_base, int ncols,
                                                     int32_t rows_valid) {
-    for (int it = threadIdx.x; it < kToks * (kCols / 8); it += kThreads) {
+    for (int it = threadIdx.x; it < kToks * (kCols / 8); it += NTHREADS) {
       const int t = it >> 3, c = (it & 7) * 8;
       if (t >= rows_valid || c >= ncols) continue;
       float v[8];
@@ -153,22 +170,28 @@ __device__ __forceinline__ float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
-// Put the 64 columns [32*j0, 32*j0 + 64) of a wave's accumulators (two block
-// columns j0, j0+1, values transformed by `fn`) into the stage.
+// Put tile columns [64 q, 64 q + 64) into the stage (values transformed by
+// `fn`); only the waves owning those columns write.
 template <typename T, class S, class F>
-__device__ __forceinline__ void stage_two_blocks(lds_char* lds, const Accum<S>& acc, const LanePos& p,
-                                                 int j0, F&& fn) {
+__device__ __forceinline__ void stage_cols64(lds_char* lds, const Accum<S>& acc, const LanePos& p,
+                                             int q, F&& fn) {
+  static_assert(S::WN % 64 == 0 || 64 % S::WN == 0, "64-column passes");
+  constexpr int kBlk = 64 / 32;  // block columns per pass
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj)
+  for (int j = 0; j < S::NB; ++j) {
+    const int col = p.wave_n0 + 32 * j;  // first tile column of block j
+    if (col < 64 * q || col >= 64 * q + 64) continue;
 #pragma unroll
     for (int i = 0; i < S::MB; ++i)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = fn(acc.v[i][j0 + jj][4 * rq + e]);
-        Stage<T>::put4(lds, 32 * jj + (p.lane & 31), p.row(i, 4 * rq), v);
+        for (int e = 0; e < 4; ++e) v[e] = fn(acc.v[i][j][4 * rq + e]);
+        Stage<T, S::kThreads>::put4(lds, col - 64 * q + (p.lane & 31), p.row(i, 4 * rq), v);
       }
+  }
+  (void)kBlk;
 }
 
 // ===================================================================== S1
@@ -177,10 +200,10 @@ __device__ __forceinline__ void stage_two_blocks(lds_char* lds, const Accum<S>& 
 // features, so each wave holds the gate and up sums of the same (token,
 // feature) in the same lane and register (block columns 2q and 2q+1).
 template <typename T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void swiglu_kernel(Dims dm, const T* __restrict__ H,
-                                                          const T* __restrict__ WgU,
-                                                          T* __restrict__ Z, T* __restrict__ Zt) {
+TTT_GEMM_KERNEL void swiglu_kernel(Dims dm, const T* __restrict__ H, const T* __restrict__ WgU,
+                                   T* __restrict__ Z, T* __restrict__ Zt) {
   using S = Tile;
+  static_assert(S::NB % 2 == 0, "gate/up block pairs");
   __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
   lds_char* smem = (lds_char*)smem_raw;
   const int32_t BT = (int32_t)(dm.B * dm.T);
@@ -194,10 +217,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int32_t row0 = tc.m * S::BM;
   const int64_t feat0 = (int64_t)tc.n * kFeat;
 
-  DirectLoader<S::BM> la;
+  DirectLoader<S::BM, S::kWaves> la;
   la.init(reinterpret_cast<const char*>(H) + row0 * ld, ld, kRowBytes, (BT - row0) * ld,
           kRowBytes);
-  DirectLoader<S::BN> lb;
+  DirectLoader<S::BN, S::kWaves> lb;
   lb.init(reinterpret_cast<const char*>(WgU) + 2 * feat0 * ld, ld, kRowBytes,
           (2 * f - 2 * feat0) * ld, kRowBytes);
 
@@ -206,31 +229,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const LanePos p = lane_pos<S>();
   mainloop<T, S>(acc, la, lb, ld / kRowBytes, smem, p, [](int64_t) {});
 
-  // z = silu(gate) * up, staged in two passes of 64 features (those of wave
-  // column 0, then of wave column 1), then written to Zt and Z.
+  // z = silu(gate) * up, staged in two passes of 64 features (B-tile rows
+  // [128 h, 128 h + 128)), then written to Zt and Z.
   const ChunkMap cm = chunk_map(dm);
-  const int wn = (threadIdx.x >> 6) & 1;
+  using St = Stage<T, S::kThreads>;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    if (wn == h) {
 #pragma unroll
-      for (int jp = 0; jp < S::NB / 2; ++jp)
+    for (int jp = 0; jp < S::NB / 2; ++jp) {
+      const int brow = p.wave_n0 + 64 * jp;  // B-tile row of the gate block of this pair
+      if (brow < 128 * h || brow >= 128 * h + 128) continue;
+      const int fcol = brow / 2 - 64 * h;      // feature column inside the pass
 #pragma unroll
-        for (int i = 0; i < S::MB; ++i)
+      for (int i = 0; i < S::MB; ++i)
 #pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            float z[4];
+        for (int rq = 0; rq < 4; ++rq) {
+          float z[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              z[e] = silu(acc.v[i][2 * jp][4 * rq + e]) * acc.v[i][2 * jp + 1][4 * rq + e];
-            Stage<T>::put4(smem, 32 * jp + (p.lane & 31), p.row(i, 4 * rq), z);
-          }
+          for (int e = 0; e < 4; ++e)
+            z[e] = silu(acc.v[i][2 * jp][4 * rq + e]) * acc.v[i][2 * jp + 1][4 * rq + e];
+          St::put4(smem, fcol + (p.lane & 31), p.row(i, 4 * rq), z);
+        }
     }
     __syncthreads();
     const int64_t cb = feat0 + 64 * h;
     const int ncols = (int)max<int64_t>(0, min<int64_t>(64, f - cb));
-    Stage<T>::flush_tokens(smem, Zt, f, cb, ncols, row0, BT, cm);
-    Stage<T>::flush_rows(smem, Z + (int64_t)row0 * f, f, cb, ncols, min(BT - row0, S::BM));
+    St::flush_tokens(smem, Zt, f, cb, ncols, row0, BT, cm);
+    St::flush_rows(smem, Z + (int64_t)row0 * f, f, cb, ncols, min(BT - row0, S::BM));
     __syncthreads();
   }
 }
@@ -239,12 +264,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 // A operand of the target GEMM: U[t][c] = sum_k taps[c][k] X0[t+1-k][c]
 // (zero outside the token's own sequence), computed in fp32 while staging the
 // k-tile and rounded once to T.  Thread t owns the 16-byte channel chunk
-// (t & 7) of the 8 consecutive tile rows 8 (t >> 3) .. +7 and keeps the window
-// of X0 rows r0-(KMAX-2) .. r0+8 in registers.  Taps come from the fp32 [8][d]
-// copy (zero for k >= K).
-template <typename T, int KMAX>
+// (t & 7) of RPT consecutive tile rows RPT (t >> 3) .. +RPT-1 and keeps the
+// window of X0 rows r0-(KMAX-2) .. r0+RPT in registers.  Taps come from the
+// fp32 [8][d] copy (zero for k >= K).
+template <typename T, int KMAX, int ROWS, int NTHREADS>
 struct ConvLoader {
-  static constexpr int kWin = 7 + KMAX;
+  static constexpr int RPT = ROWS * 8 / NTHREADS;  // rows per thread
+  static constexpr int kWin = RPT - 1 + KMAX;
   static constexpr int EPC = Elem<T>::kPerChunk;
   static constexpr int kTapVecs = EPC / 4;  // 16-byte fp32 tap vectors per tap
   static constexpr int kStagedLoads = kWin + KMAX * kTapVecs;
@@ -268,7 +294,7 @@ struct ConvLoader {
     const int32_t gbase = max(0, row0 - (KMAX - 2));
     base = reinterpret_cast<const char*>(X0) + (int64_t)gbase * ld;
     valid_bytes = (int64_t)(BT - gbase) * ld;
-    r0 = row0 + (threadIdx.x >> 3) * 8;
+    r0 = row0 + (threadIdx.x >> 3) * RPT;
     const int c = threadIdx.x & 7;
 #pragma unroll
     for (int w = 0; w < kWin; ++w) {
@@ -289,12 +315,12 @@ struct ConvLoader {
       for (int v = 0; v < kTapVecs; ++v)
         tpv[k][v] = buf_load16(tr, (uint32_t)((k * d + ch0 + 4 * v) * 4));
   }
-  // U for the thread's 8 rows in fp32, rounded to T, into the stage.
+  // U for the thread's RPT rows in fp32, rounded to T, into the stage.
   __device__ __forceinline__ void commit(lds_char* lds) const {
     const int c = threadIdx.x & 7;
-    const int lrow0 = (threadIdx.x >> 3) * 8;
+    const int lrow0 = (threadIdx.x >> 3) * RPT;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
+    for (int jj = 0; jj < RPT; ++jj) {
       const int32_t o = r0 + jj;
       const int32_t s = o - (o / T_seq) * T_seq;  // position inside its sequence
       float u[EPC];
@@ -325,11 +351,10 @@ struct ConvLoader {
 
 // eta * V^ = eta * U W_target over all token rows, written token-major to Vt.
 template <typename T, int KMAX>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void target_kernel(Dims dm, const T* __restrict__ X0,
-                                                          const float* __restrict__ tapsT,
-                                                          const T* __restrict__ WtT,
-                                                          T* __restrict__ Vt) {
-  using S = Tile;
+__global__ __launch_bounds__(TargetTile::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+target_kernel(Dims dm, const T* __restrict__ X0, const float* __restrict__ tapsT,
+              const T* __restrict__ WtT, T* __restrict__ Vt) {
+  using S = TargetTile;
   __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
   lds_char* smem = (lds_char*)smem_raw;
   const int32_t BT = (int32_t)(dm.B * dm.T);
@@ -342,9 +367,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int32_t row0 = tc.m * S::BM;
   const int64_t col0 = (int64_t)tc.n * S::BN;
 
-  ConvLoader<T, KMAX> la;
+  ConvLoader<T, KMAX, S::BM, S::kThreads> la;
   la.init(X0, tapsT, dm, row0);
-  DirectLoader<S::BN> lb;
+  DirectLoader<S::BN, S::kWaves> lb;
   lb.init(reinterpret_cast<const char*>(WtT) + col0 * ld, ld, kRowBytes, (d - col0) * ld,
           kRowBytes);
 
@@ -353,19 +378,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const LanePos p = lane_pos<S>();
   mainloop<T, S>(acc, la, lb, ld / kRowBytes, smem, p, [](int64_t) {});
 
-  // eta * acc to Vt through the stage, four passes of 64 columns (pass q: wave
-  // column q/2, its block columns 2(q%2), 2(q%2)+1).
+  // eta * acc to Vt through the stage, four passes of 64 columns.
   const ChunkMap cm = chunk_map(dm);
   const float eta = dm.eta;
-  const int wn = (threadIdx.x >> 6) & 1;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    if (wn == (q >> 1))
-      stage_two_blocks<T, S>(smem, acc, p, 2 * (q & 1), [&](float x) { return eta * x; });
+  for (int q = 0; q < S::BN / 64; ++q) {
+    stage_cols64<T, S>(smem, acc, p, q, [&](float x) { return eta * x; });
     __syncthreads();
     const int64_t cb = col0 + 64 * q;
-    Stage<T>::flush_tokens(smem, Vt, d, cb, (int)max<int64_t>(0, min<int64_t>(64, d - cb)), row0,
-                           BT, cm);
+    Stage<T, S::kThreads>::flush_tokens(smem, Vt, d, cb,
+                                        (int)max<int64_t>(0, min<int64_t>(64, d - cb)), row0, BT,
+                                        cm);
     __syncthreads();
   }
 }
@@ -379,7 +402,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 // result does not depend on how the chunks are grouped.  The tile shape S
 // divides d and f exactly (the host picks it), so every tile is full.
 template <typename T, class S>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefix_update_kernel(
+__global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::kWaves / 4, S::kWaves / 4))) void prefix_update_kernel(
     Dims dm, const T* __restrict__ Vt, const T* __restrict__ Zt, float* __restrict__ W_state,
     T* __restrict__ slots, int64_t g0, int64_t gc) {
   constexpr int TB = kRowBytes / (int)sizeof(T);
@@ -395,10 +418,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int64_t m0 = (int64_t)tc.m * S::BM, n0 = (int64_t)tc.n * S::BN;
   const int64_t kb0 = (b * dm.N + g0) * dm.Cp / TB;  // first k-block of the group
 
-  DirectLoader<S::BM> la;
+  DirectLoader<S::BM, S::kWaves> la;
   la.init(reinterpret_cast<const char*>(Vt) + (kb0 * d + m0) * kRowBytes, kRowBytes,
           d * kRowBytes, (d - m0) * kRowBytes, 0);
-  DirectLoader<S::BN> lb;
+  DirectLoader<S::BN, S::kWaves> lb;
   lb.init(reinterpret_cast<const char*>(Zt) + (kb0 * f + n0) * kRowBytes, kRowBytes,
           f * kRowBytes, (f - n0) * kRowBytes, 0);
 
@@ -484,10 +507,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 // ===================================================================== S3
 // O_i = Z_i slot_i^T for every chunk of the group and every sequence.
 template <typename T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void down_proj_kernel(Dims dm, const T* __restrict__ Z,
-                                                             const T* __restrict__ slots,
-                                                             T* __restrict__ O, int64_t g0,
-                                                             int64_t gc) {
+TTT_GEMM_KERNEL void down_proj_kernel(Dims dm, const T* __restrict__ Z,
+                                      const T* __restrict__ slots, T* __restrict__ O, int64_t g0,
+                                      int64_t gc) {
   using S = Tile;
   __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
   lds_char* smem = (lds_char*)smem_raw;
@@ -507,10 +529,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int64_t row0 = b * T_seq + c_begin + m0;  // first token row of the tile
   const T* slot = slots + (jj * dm.B + b) * d * f;
 
-  DirectLoader<S::BM> la;
+  DirectLoader<S::BM, S::kWaves> la;
   la.init(reinterpret_cast<const char*>(Z) + row0 * ld, ld, kRowBytes, (c_len - m0) * ld,
           kRowBytes);
-  DirectLoader<S::BN> lb;
+  DirectLoader<S::BN, S::kWaves> lb;
   lb.init(reinterpret_cast<const char*>(slot) + n0 * ld, ld, kRowBytes, (d - n0) * ld, kRowBytes);
 
   Accum<S> acc;
@@ -520,16 +542,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   // O through the stage, four passes of 64 columns, written row-major; rows
   // beyond the chunk are skipped.
-  const int wn = (threadIdx.x >> 6) & 1;
   const int32_t rows_valid = (int32_t)min<int64_t>(S::BM, c_len - m0);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    if (wn == (q >> 1))
-      stage_two_blocks<T, S>(smem, acc, p, 2 * (q & 1), [](float x) { return x; });
+  for (int q = 0; q < S::BN / 64; ++q) {
+    stage_cols64<T, S>(smem, acc, p, q, [](float x) { return x; });
     __syncthreads();
     const int64_t cbase = n0 + 64 * q;
-    Stage<T>::flush_rows(smem, O + row0 * d, d, cbase,
-                         (int)max<int64_t>(0, min<int64_t>(64, d - cbase)), rows_valid);
+    Stage<T, S::kThreads>::flush_rows(smem, O + row0 * d, d, cbase,
+                                      (int)max<int64_t>(0, min<int64_t>(64, d - cbase)),
+                                      rows_valid);
     __syncthreads();
   }
 }
@@ -688,11 +709,11 @@ hipError_t launch_swiglu(const Dims& dm, const void* H, const void* WgU, void* Z
   const int64_t tiles =
       ((BT + Tile::BM - 1) / Tile::BM) * ((dm.f + Tile::BN / 2 - 1) / (Tile::BN / 2));
   if (dm.dt == Dtype::BF16)
-    hipLaunchKernelGGL(swiglu_kernel<uint16_t>, dim3((unsigned)tiles), dim3(kThreads), 0, s, dm,
+    hipLaunchKernelGGL(swiglu_kernel<uint16_t>, dim3((unsigned)tiles), dim3(Tile::kThreads), 0, s, dm,
                        static_cast<const uint16_t*>(H), static_cast<const uint16_t*>(WgU),
                        static_cast<uint16_t*>(Z), static_cast<uint16_t*>(Zt));
   else
-    hipLaunchKernelGGL(swiglu_kernel<float>, dim3((unsigned)tiles), dim3(kThreads), 0, s, dm,
+    hipLaunchKernelGGL(swiglu_kernel<float>, dim3((unsigned)tiles), dim3(Tile::kThreads), 0, s, dm,
                        static_cast<const float*>(H), static_cast<const float*>(WgU),
                        static_cast<float*>(Z), static_cast<float*>(Zt));
   return hipGetLastError();
@@ -702,12 +723,13 @@ template <typename T>
 static void launch_target_t(const Dims& dm, const T* X0, const float* tapsT, const T* WtT, T* Vt,
                             hipStream_t s) {
   const int64_t BT = dm.B * dm.T;
-  const int64_t tiles = ((BT + Tile::BM - 1) / Tile::BM) * ((dm.d + Tile::BN - 1) / Tile::BN);
+  const int64_t tiles =
+      ((BT + TargetTile::BM - 1) / TargetTile::BM) * ((dm.d + TargetTile::BN - 1) / TargetTile::BN);
   if (dm.K <= 4)
-    hipLaunchKernelGGL((target_kernel<T, 4>), dim3((unsigned)tiles), dim3(kThreads), 0, s, dm, X0,
+    hipLaunchKernelGGL((target_kernel<T, 4>), dim3((unsigned)tiles), dim3(TargetTile::kThreads), 0, s, dm, X0,
                        tapsT, WtT, Vt);
   else
-    hipLaunchKernelGGL((target_kernel<T, 8>), dim3((unsigned)tiles), dim3(kThreads), 0, s, dm, X0,
+    hipLaunchKernelGGL((target_kernel<T, 8>), dim3((unsigned)tiles), dim3(TargetTile::kThreads), 0, s, dm, X0,
                        tapsT, WtT, Vt);
 }
 
@@ -727,7 +749,7 @@ template <typename T, class S>
 static void launch_prefix_update_t(const Dims& dm, const T* Vt, const T* Zt, float* W_state, T* slots,
                                    int64_t g0, int64_t gc, hipStream_t s) {
   const int64_t tiles = (dm.d / S::BM) * (dm.f / S::BN) * dm.B;
-  hipLaunchKernelGGL((prefix_update_kernel<T, S>), dim3((unsigned)tiles), dim3(kThreads), 0, s, dm,
+  hipLaunchKernelGGL((prefix_update_kernel<T, S>), dim3((unsigned)tiles), dim3(S::kThreads), 0, s, dm,
                      Vt, Zt, W_state, slots, g0, gc);
 }
 
@@ -737,9 +759,9 @@ template <typename T>
 static void launch_prefix_update_dt(const Dims& dm, const T* Vt, const T* Zt, float* W_state,
                                     T* slots, int64_t g0, int64_t gc, hipStream_t s) {
   if (dm.d % 256 == 0 && dm.f % 256 == 0)
-    launch_prefix_update_t<T, TileShape<256, 256>>(dm, Vt, Zt, W_state, slots, g0, gc, s);
+    launch_prefix_update_t<T, Tile>(dm, Vt, Zt, W_state, slots, g0, gc, s);
   else
-    launch_prefix_update_t<T, TileShape<64, 64>>(dm, Vt, Zt, W_state, slots, g0, gc, s);
+    launch_prefix_update_t<T, TileShape<64, 64, 2, 2>>(dm, Vt, Zt, W_state, slots, g0, gc, s);
 }
 
 hipError_t launch_prefix_update(const Dims& dm, const void* Vt, const void* Zt, float* W_state,
@@ -759,11 +781,11 @@ hipError_t launch_down_proj(const Dims& dm, const void* Z, const void* slots, vo
   const int64_t tiles = ((dm.C + Tile::BM - 1) / Tile::BM) * ((dm.d + Tile::BN - 1) / Tile::BN) *
                         gc * dm.B;
   if (dm.dt == Dtype::BF16)
-    hipLaunchKernelGGL(down_proj_kernel<uint16_t>, dim3((unsigned)tiles), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(down_proj_kernel<uint16_t>, dim3((unsigned)tiles), dim3(Tile::kThreads), 0, s,
                        dm, static_cast<const uint16_t*>(Z), static_cast<const uint16_t*>(slots),
                        static_cast<uint16_t*>(O), g0, gc);
   else
-    hipLaunchKernelGGL(down_proj_kernel<float>, dim3((unsigned)tiles), dim3(kThreads), 0, s, dm,
+    hipLaunchKernelGGL(down_proj_kernel<float>, dim3((unsigned)tiles), dim3(Tile::kThreads), 0, s, dm,
                        static_cast<const float*>(Z), static_cast<const float*>(slots),
                        static_cast<float*>(O), g0, gc);
   return hipGetLastError();
