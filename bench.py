@@ -50,17 +50,98 @@ def stage_work(w, group: int) -> dict:
     }
 
 
-def traffic_for(kernel: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+def stage_bytes(w, group: int) -> dict:
+    """Algorithmic HBM bytes per launch of each kernel: every operand read once
+    and every result written once (the fp32 state once per group)."""
+    B, T, C, d, f = w.batch, w.seq_len, w.chunk, w.d_model, w.d_ff
+    e = 2 if w.dtype == torch_bf16() else 4
+    tok = B * T
+    chunk_tokens = B * min(group * C, T)
+    chunks = B * min(group, w.n_chunks)
+    return {
+        "state_reset": e * d * f + 4 * B * d * f,
+        "swiglu": e * tok * (d + f) + e * 2 * f * d,
+        "target": e * tok * 2 * d + e * d * d,
+        "prefix_update": e * chunk_tokens * (d + f) + e * chunks * d * f + 8 * B * d * f,
+        "down_proj": e * chunk_tokens * (f + d) + e * chunks * d * f,
+    }
+
+
+def torch_bf16():
+    import torch
+    return torch.bfloat16
+
+
+# layer stage -> the kernel's name as rocprofv3 prints it (prefix match)
+STAGE_KERNELS = {
+    "state_reset": "void ttt::state_reset_kernel",
+    "swiglu": "void ttt::swiglu_kernel",
+    "target": "void ttt::target_kernel",
+    "prefix_update": "void ttt::prefix_update_kernel",
+    "down_proj": "void ttt::down_proj_kernel",
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"layer_{workload}_traffic.json")
+
+
+def traffic_for(stage: str, workload: str):
+    """HBM bytes per launch of a stage's kernel from the committed rocprofv3
+    counter runs, if they were taken on the current kernel sources; else None."""
+    path = traffic_path(workload)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         t = json.load(fh)
     if t.get("source_hash") != kernel_source_hash():
         return None
-    return t.get("bytes_per_launch")
+    k = t.get("kernels", {}).get(stage)
+    return None if k is None else k["bytes_per_launch"]
+
+
+def _counter_medians(csv_path: str) -> dict:
+    """Median counter value per kernel name of a rocprofv3 counter_collection.csv."""
+    import csv
+    import statistics
+    vals = {}
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: statistics.median(v) for k, v in vals.items()}
+
+
+def write_traffic(workload: str, fetch_csv: str, write_csv: str, cfetch_csv: str,
+                  cwrite_csv: str, copy_bytes: int, commands: list) -> dict:
+    """Turn four rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE, in KiB per
+    dispatch, on the layer and on a plain copy of copy_bytes) into bytes per
+    launch of each stage's kernel, each counter scaled by copy_bytes over what
+    it read for the copy."""
+    def scale(csv_path):
+        m = _counter_medians(csv_path)
+        kib = next(v for k, v in m.items() if k.startswith(COPY_KERNEL))
+        return kib, copy_bytes / (kib * 1024.0)
+    cf_kib, f_scale = scale(cfetch_csv)
+    cw_kib, w_scale = scale(cwrite_csv)
+    fetch, write = _counter_medians(fetch_csv), _counter_medians(write_csv)
+    kernels = {}
+    for stage, prefix in STAGE_KERNELS.items():
+        fk = [v for k, v in fetch.items() if k.startswith(prefix)]
+        wk = [v for k, v in write.items() if k.startswith(prefix)]
+        if not fk or not wk:
+            continue
+        fb, wb = fk[0] * 1024.0 * f_scale, wk[0] * 1024.0 * w_scale
+        kernels[stage] = {"fetch_kib": fk[0], "write_kib": wk[0], "fetch_bytes": fb,
+                          "write_bytes": wb, "bytes_per_launch": fb + wb}
+    out = {"workload": workload, "source_hash": kernel_source_hash(),
+           "calibration": {"copy_bytes": copy_bytes, "fetch_kib": cf_kib, "write_kib": cw_kib,
+                           "fetch_scale": f_scale, "write_scale": w_scale},
+           "kernels": kernels, "commands": commands}
+    with open(traffic_path(workload), "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    return out
 
 
 def cpu_baseline(w, inp) -> dict:
@@ -111,7 +192,20 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"),
+                    help="write the traffic record of --workload from four rocprofv3 "
+                         "counter_collection.csv files (layer FETCH_SIZE, layer WRITE_SIZE, "
+                         "copy FETCH_SIZE, copy WRITE_SIZE) and exit; no GPU needed")
+    ap.add_argument("--traffic-copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--traffic-command", action="append", default=[],
+                    help="command that produced the counter files (repeatable)")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        t = write_traffic(args.workload, *args.traffic_from, args.traffic_copy_bytes,
+                          args.traffic_command)
+        print(json.dumps(t["kernels"], indent=1))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -190,7 +284,9 @@ def main() -> int:
     roofline = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": peak,
                 "unit": "TFLOP/s", "frac": ach / peak,
                 "traffic": traffic_for(dom, w.name),
+                "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "flops_per_launch": work[dom],
+                "algorithmic_bytes_per_launch": stage_bytes(w, group)[dom],
                 "ms_per_launch": per_stage[dom]["ms_per_launch"]}
     layer_frac = w.flops() / (ms_step / 1e3) / (peak * 1e12)
 

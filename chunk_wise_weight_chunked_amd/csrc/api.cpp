@@ -145,7 +145,8 @@ ttt_status_t make_dims(const ttt_mlp_desc_t* desc, ttt::Dims* dm) {
   if (d.d * d.f > kMaxInt32) return fail(TTT_ERR_UNSUPPORTED, "d_model * d_ff must be < 2^31");
   if (d.B * d.N > kMaxInt32 / d.Cp) return fail(TTT_ERR_UNSUPPORTED, "padded token count must be < 2^31");
   d.P = d.B * d.N * d.Cp;
-  if (d.f > kMaxInt32 / d.P) return fail(TTT_ERR_UNSUPPORTED, "d_ff * padded tokens must be < 2^31");
+  // fast-weight tiles address 256 rows of f fp32 values with 32-bit byte offsets
+  if (d.f > (int64_t)1 << 20) return fail(TTT_ERR_UNSUPPORTED, "d_ff must be <= 2^20");
   *dm = d;
   return TTT_OK;
 }
