@@ -201,10 +201,11 @@ ttt_status_t run_layer(const ttt::Dims& dm, ttt_mode_t mode, bool reset, const v
     e = staged(kPad, s, [&] { return ttt::launch_pad_fill(Zt, Vt, dm, s); });
     if (e != hipSuccess) return hip_fail(e, "pad_fill");
   }
+  // S2 first: its conv output U lives in the Z region until S1 overwrites it
+  e = staged(kTarget, s, [&] { return ttt::launch_target(dm, X0, tapsT, WtT, Z, Vt, s); });
+  if (e != hipSuccess) return hip_fail(e, "target");
   e = staged(kSwiglu, s, [&] { return ttt::launch_swiglu(dm, H, WgU, Z, Zt, s); });
   if (e != hipSuccess) return hip_fail(e, "swiglu");
-  e = staged(kTarget, s, [&] { return ttt::launch_target(dm, X0, tapsT, WtT, Vt, s); });
-  if (e != hipSuccess) return hip_fail(e, "target");
   for (int64_t g0 = 0; g0 < dm.N; g0 += G) {
     const int64_t gc = std::min<int64_t>(G, dm.N - g0);
     e = staged(kPrefix, s, [&] { return ttt::launch_prefix_update(dm, Vt, Zt, W_state, slots, g0, gc, s); });

@@ -51,9 +51,6 @@ namespace ttt {
 #define TTT_GEMM_THREADS (64 * TTT_WAVES_M * TTT_WAVES_N)
 #define TTT_GEMM_WPE (TTT_WAVES_M * TTT_WAVES_N / 4)
 using Tile = TileShape<256, 256, TTT_WAVES_M, TTT_WAVES_N>;
-// The target GEMM keeps one wave per SIMD: its A operand is built in registers
-// (the conv window and taps), which needs the larger register budget.
-using TargetTile = TileShape<256, 256, 2, 2>;
 #define TTT_GEMM_KERNEL                                  \
   __global__ __launch_bounds__(TTT_GEMM_THREADS)          \
   __attribute__((amdgpu_waves_per_eu(TTT_GEMM_WPE, TTT_GEMM_WPE)))
@@ -261,100 +258,80 @@ TTT_GEMM_KERNEL void swiglu_kernel(Dims dm, const T* __restrict__ H, const T* __
 }
 
 // ===================================================================== S2
-// A operand of the target GEMM: U[t][c] = sum_k taps[c][k] X0[t+1-k][c]
-// (zero outside the token's own sequence), computed in fp32 while staging the
-// k-tile and rounded once to T.  Thread t owns the 16-byte channel chunk
-// (t & 7) of RPT consecutive tile rows RPT (t >> 3) .. +RPT-1 and keeps the
-// window of X0 rows r0-(KMAX-2) .. r0+RPT in registers.  Taps come from the
-// fp32 [8][d] copy (zero for k >= K).
-template <typename T, int KMAX, int ROWS, int NTHREADS>
-struct ConvLoader {
-  static constexpr int RPT = ROWS * 8 / NTHREADS;  // rows per thread
-  static constexpr int kWin = RPT - 1 + KMAX;
-  static constexpr int EPC = Elem<T>::kPerChunk;
-  static constexpr int kTapVecs = EPC / 4;  // 16-byte fp32 tap vectors per tap
-  static constexpr int kStagedLoads = kWin + KMAX * kTapVecs;
-  const char* base;     // X0 row gbase (uniform)
-  int64_t ld;           // d * es
-  int64_t valid_bytes;  // (B*T - gbase) * ld
-  const float* taps;
-  int64_t d;
-  int32_t r0, T_seq, BT;
-  uint32_t voff[kWin];
-  uint4 win[kWin];
-  uint4 tpv[KMAX][kTapVecs];
-
-  __device__ __forceinline__ void init(const T* X0, const float* tapsT, const Dims& dm,
-                                       int32_t row0) {
-    BT = (int32_t)(dm.B * dm.T);
-    T_seq = (int32_t)dm.T;
-    d = dm.d;
-    ld = dm.d * (int64_t)sizeof(T);
-    taps = tapsT;
-    const int32_t gbase = max(0, row0 - (KMAX - 2));
-    base = reinterpret_cast<const char*>(X0) + (int64_t)gbase * ld;
-    valid_bytes = (int64_t)(BT - gbase) * ld;
-    r0 = row0 + (threadIdx.x >> 3) * RPT;
-    const int c = threadIdx.x & 7;
+// U[t][c] = sum_{k<K} taps[c][k] X0[t+1-k][c] (zero outside the token's own
+// sequence), accumulated in fp32 over k = 0..K-1 and rounded once to T.
+// Thread work item: one 16-byte channel chunk of kConvRows consecutive token
+// rows, with the X0 window of those rows (kConvRows + KMAX - 1 rows) in
+// registers; consecutive threads take consecutive chunks of a row group, so
+// every access is a coalesced 16-byte load or store.
+constexpr int kConvRows = 4;
+template <typename T, int KMAX>
+__global__ __launch_bounds__(256) void conv_kernel(Dims dm, const T* __restrict__ X0,
+                                                   const float* __restrict__ tapsT,
+                                                   T* __restrict__ U) {
+  constexpr int EPC = Elem<T>::kPerChunk;
+  constexpr int kWin = kConvRows + KMAX - 1;
+  const int64_t d = dm.d, BT = dm.B * dm.T, T_seq = dm.T;
+  const int K = dm.K;
+  const int64_t chunks = d / EPC;
+  const int64_t total = (BT + kConvRows - 1) / kConvRows * chunks;
+  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < total;
+       it += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t c = it % chunks, r0 = it / chunks * kConvRows;
+    float tp[KMAX][EPC];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const float4* src = reinterpret_cast<const float4*>(tapsT + k * d + c * EPC);
+#pragma unroll
+      for (int v = 0; v < EPC / 4; ++v) {
+        const float4 t = src[v];
+        tp[k][4 * v] = t.x;
+        tp[k][4 * v + 1] = t.y;
+        tp[k][4 * v + 2] = t.z;
+        tp[k][4 * v + 3] = t.w;
+      }
+    }
+    uint4 win[kWin];  // X0 rows r0 - (KMAX - 2) + w
 #pragma unroll
     for (int w = 0; w < kWin; ++w) {
-      const int32_t g = r0 - (KMAX - 2) + w;
-      voff[w] = g < gbase ? kOobOffset : (uint32_t)((g - gbase) * ld + c * 16);
+      const int64_t row = r0 - (KMAX - 2) + w;
+      win[w] = row >= 0 && row < BT
+                   ? *reinterpret_cast<const uint4*>(X0 + row * d + c * EPC)
+                   : make_uint4(0, 0, 0, 0);
     }
-  }
-  // Fetch the X0 window and the taps of this thread's channels for k-tile kt.
-  __device__ __forceinline__ void issue(int64_t kt, lds_char*) {
-    const rsrc_t r = make_rsrc(base + kt * kRowBytes, valid_bytes - kt * kRowBytes);
 #pragma unroll
-    for (int w = 0; w < kWin; ++w) win[w] = buf_load16(r, voff[w]);
-    const int64_t ch0 = kt * (kRowBytes / (int)sizeof(T)) + (threadIdx.x & 7) * EPC;
-    const rsrc_t tr = make_rsrc(taps, 8 * d * (int64_t)sizeof(float));
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-#pragma unroll
-      for (int v = 0; v < kTapVecs; ++v)
-        tpv[k][v] = buf_load16(tr, (uint32_t)((k * d + ch0 + 4 * v) * 4));
-  }
-  // U for the thread's RPT rows in fp32, rounded to T, into the stage.
-  __device__ __forceinline__ void commit(lds_char* lds) const {
-    const int c = threadIdx.x & 7;
-    const int lrow0 = (threadIdx.x >> 3) * RPT;
-#pragma unroll
-    for (int jj = 0; jj < RPT; ++jj) {
-      const int32_t o = r0 + jj;
-      const int32_t s = o - (o / T_seq) * T_seq;  // position inside its sequence
+    for (int jj = 0; jj < kConvRows; ++jj) {
+      const int64_t o = r0 + jj;
+      if (o >= BT) break;
+      const int64_t sq = o % T_seq;  // position inside its sequence
       float u[EPC];
 #pragma unroll
       for (int e = 0; e < EPC; ++e) u[e] = 0.0f;
 #pragma unroll
       for (int k = 0; k < KMAX; ++k) {
-        const int32_t src = s + 1 - k;  // X0 row of this tap, inside the sequence
-        const bool ok = o < BT && src >= 0 && src < T_seq;
+        const int64_t src = sq + 1 - k;  // X0 row of tap k, inside the sequence
+        if (k >= K || src < 0 || src >= T_seq) continue;
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          const float t = chunk_value<float>(tpv[k][e >> 2], e & 3);
-          u[e] = fmaf(ok ? t : 0.0f, chunk_value<T>(win[jj + KMAX - 1 - k], e), u[e]);
-        }
+        for (int e = 0; e < EPC; ++e)
+          u[e] = fmaf(tp[k][e], chunk_value<T>(win[jj + KMAX - 1 - k], e), u[e]);
       }
       uint4 out;
-      if constexpr (sizeof(T) == 2) {
+      if constexpr (sizeof(T) == 2)
         out = make_uint4(pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]), pack_bf16x2(u[4], u[5]),
                          pack_bf16x2(u[6], u[7]));
-      } else {
+      else
         out = make_uint4(__float_as_uint(u[0]), __float_as_uint(u[1]), __float_as_uint(u[2]),
                          __float_as_uint(u[3]));
-      }
-      lds_store<u32x4_t>(lds + lds_offset(lrow0 + jj, c), as_u32x4(out));
+      *reinterpret_cast<uint4*>(U + o * d + c * EPC) = out;
     }
   }
-};
+}
 
 // eta * V^ = eta * U W_target over all token rows, written token-major to Vt.
-template <typename T, int KMAX>
-__global__ __launch_bounds__(TargetTile::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
-target_kernel(Dims dm, const T* __restrict__ X0, const float* __restrict__ tapsT,
-              const T* __restrict__ WtT, T* __restrict__ Vt) {
-  using S = TargetTile;
+template <typename T>
+TTT_GEMM_KERNEL void target_kernel(Dims dm, const T* __restrict__ U, const T* __restrict__ WtT,
+                                   T* __restrict__ Vt) {
+  using S = Tile;
   __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
   lds_char* smem = (lds_char*)smem_raw;
   const int32_t BT = (int32_t)(dm.B * dm.T);
@@ -367,8 +344,9 @@ target_kernel(Dims dm, const T* __restrict__ X0, const float* __restrict__ tapsT
   const int32_t row0 = tc.m * S::BM;
   const int64_t col0 = (int64_t)tc.n * S::BN;
 
-  ConvLoader<T, KMAX, S::BM, S::kThreads> la;
-  la.init(X0, tapsT, dm, row0);
+  DirectLoader<S::BM, S::kWaves> la;
+  la.init(reinterpret_cast<const char*>(U) + row0 * ld, ld, kRowBytes, (BT - row0) * ld,
+          kRowBytes);
   DirectLoader<S::BN, S::kWaves> lb;
   lb.init(reinterpret_cast<const char*>(WtT) + col0 * ld, ld, kRowBytes, (d - col0) * ld,
           kRowBytes);
@@ -633,8 +611,8 @@ WorkspacePlan plan_workspace(const Dims& dm, int64_t group) {
   const size_t es = dtype_bytes(dm.dt);
   WorkspacePlan w;
   size_t off = 0;
-  w.z_off = off;
-  off = align256(off + (size_t)(dm.B * dm.T) * dm.f * es);
+  w.z_off = off;  // Z, and before S1 runs, U of S2
+  off = align256(off + (size_t)(dm.B * dm.T) * std::max(dm.f, dm.d) * es);
   w.zt_off = off;
   off = align256(off + (size_t)dm.f * dm.P * es);
   w.vt_off = off;
@@ -720,28 +698,30 @@ hipError_t launch_swiglu(const Dims& dm, const void* H, const void* WgU, void* Z
 }
 
 template <typename T>
-static void launch_target_t(const Dims& dm, const T* X0, const float* tapsT, const T* WtT, T* Vt,
-                            hipStream_t s) {
+static void launch_target_t(const Dims& dm, const T* X0, const float* tapsT, const T* WtT, T* U,
+                            T* Vt, hipStream_t s) {
   const int64_t BT = dm.B * dm.T;
-  const int64_t tiles =
-      ((BT + TargetTile::BM - 1) / TargetTile::BM) * ((dm.d + TargetTile::BN - 1) / TargetTile::BN);
+  const int64_t items = (BT + kConvRows - 1) / kConvRows * (dm.d / Elem<T>::kPerChunk);
+  const dim3 cgrid(grid_for(items, 256, 65536));
   if (dm.K <= 4)
-    hipLaunchKernelGGL((target_kernel<T, 4>), dim3((unsigned)tiles), dim3(TargetTile::kThreads), 0, s, dm, X0,
-                       tapsT, WtT, Vt);
+    hipLaunchKernelGGL((conv_kernel<T, 4>), cgrid, dim3(256), 0, s, dm, X0, tapsT, U);
   else
-    hipLaunchKernelGGL((target_kernel<T, 8>), dim3((unsigned)tiles), dim3(TargetTile::kThreads), 0, s, dm, X0,
-                       tapsT, WtT, Vt);
+    hipLaunchKernelGGL((conv_kernel<T, 8>), cgrid, dim3(256), 0, s, dm, X0, tapsT, U);
+  const int64_t tiles = ((BT + Tile::BM - 1) / Tile::BM) * ((dm.d + Tile::BN - 1) / Tile::BN);
+  hipLaunchKernelGGL(target_kernel<T>, dim3((unsigned)tiles), dim3(Tile::kThreads), 0, s, dm, U,
+                     WtT, Vt);
 }
 
 hipError_t launch_target(const Dims& dm, const void* X0, const void* tapsT, const void* WtT,
-                         void* Vt, hipStream_t s) {
+                         void* U, void* Vt, hipStream_t s) {
   if (dm.dt == Dtype::BF16)
     launch_target_t<uint16_t>(dm, static_cast<const uint16_t*>(X0),
-                              static_cast<const float*>(tapsT),
-                              static_cast<const uint16_t*>(WtT), static_cast<uint16_t*>(Vt), s);
+                              static_cast<const float*>(tapsT), static_cast<const uint16_t*>(WtT),
+                              static_cast<uint16_t*>(U), static_cast<uint16_t*>(Vt), s);
   else
     launch_target_t<float>(dm, static_cast<const float*>(X0), static_cast<const float*>(tapsT),
-                           static_cast<const float*>(WtT), static_cast<float*>(Vt), s);
+                           static_cast<const float*>(WtT), static_cast<float*>(U),
+                           static_cast<float*>(Vt), s);
   return hipGetLastError();
 }
 

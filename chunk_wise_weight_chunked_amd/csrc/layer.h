@@ -43,8 +43,9 @@ hipError_t launch_weight_prep(const Dims& dm, const void* Wg, const void* Wu, co
 hipError_t launch_pad_fill(void* zt, void* vt, const Dims& dm, hipStream_t s);
 hipError_t launch_swiglu(const Dims& dm, const void* H, const void* WgU, void* Z, void* Zt,
                          hipStream_t s);
+// Conv of X0 into U (scratch of B*T x d elements), then eta * U W_target into Vt.
 hipError_t launch_target(const Dims& dm, const void* X0, const void* taps, const void* WtT,
-                         void* Vt, hipStream_t s);
+                         void* U, void* Vt, hipStream_t s);
 hipError_t launch_prefix_update(const Dims& dm, const void* Vt, const void* Zt, float* W_state,
                                 void* slots, int64_t g0, int64_t gc, hipStream_t s);
 hipError_t launch_down_proj(const Dims& dm, const void* Z, const void* slots, void* O,

@@ -68,6 +68,16 @@ def test_workspace_fixed_part_matches_layout():
     assert tm.ttt_mlp_workspace_size(d, 1) == expect
 
 
+def test_workspace_z_region_holds_conv_output():
+    # the Z region also holds the conv output U [T][d] before S1 runs: max(d, f) columns
+    d = desc(d_model=512, d_ff=256, seq_len=1000, chunk=100)
+    es = 2
+    parts = [1000 * 512 * es, 256 * 1280 * es, 512 * 1280 * es, 2 * 256 * 512 * es,
+             512 * 512 * es, 8 * 512 * 4, 512 * 256 * es]
+    expect = sum((p + 255) // 256 * 256 for p in parts)
+    assert tm.ttt_mlp_workspace_size(d, 1) == expect
+
+
 BAD_DESCS = [
     (dict(batch=0), tm.TTT_ERR_INVALID_ARGUMENT, "batch"),
     (dict(seq_len=0), tm.TTT_ERR_INVALID_ARGUMENT, "seq_len"),

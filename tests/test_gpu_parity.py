@@ -78,6 +78,7 @@ SMALL = [
     (3, 260, 192, 256, 2, 37, torch.float32, 1e-2),     # fp32, odd chunk
     (1, 1, 64, 64, 4, 16, torch.float32, 1e-1),         # a single token
     (2, 513, 320, 384, 5, 256, torch.float32, 1e-2),    # fp32, several tiles
+    (1, 600, 320, 128, 4, 128, torch.bfloat16, 1e-2),   # d > f: conv output wider than Z
 ]
 
 
