@@ -37,17 +37,31 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def _group_tokens(w, group: int) -> list:
+    """Tokens (all sequences) in each group of `group` chunks."""
+    B, T, C, N = w.batch, w.seq_len, w.chunk, w.n_chunks
+    groups = -(-N // group)
+    return [B * (min(T, (g + 1) * group * C) - g * group * C) for g in range(groups)]
+
+
+def _per_launch(scan, apply, toks) -> dict:
+    """Per-launch averages of the group pipeline's three launch kinds, given
+    the work of one group's scan and outputs as functions of its tokens."""
+    n = len(toks)
+    out = {"prefix_update": scan(toks[0]), "down_proj": apply(toks[-1])}
+    if n > 1:
+        out["scan_apply"] = sum(scan(toks[g]) + apply(toks[g - 1]) for g in range(1, n)) / (n - 1)
+    return out
+
+
 def stage_work(w, group: int) -> dict:
-    """Algorithmic flops per launch of each kernel (and the chunks it covers)."""
-    B, T, C, d, f = w.batch, w.seq_len, w.chunk, w.d_model, w.d_ff
+    """Algorithmic flops per launch of each kernel."""
+    B, T, d, f = w.batch, w.seq_len, w.d_model, w.d_ff
     tok = B * T
-    chunk_tokens = B * min(group * C, T)  # tokens one prefix/down launch covers (full groups)
-    return {
-        "swiglu": 4.0 * tok * d * f,
-        "target": 2.0 * tok * d * d,
-        "prefix_update": 2.0 * chunk_tokens * d * f,
-        "down_proj": 2.0 * chunk_tokens * d * f,
-    }
+    out = {"swiglu": 4.0 * tok * d * f, "target": 2.0 * tok * d * d}
+    out.update(_per_launch(lambda t: 2.0 * t * d * f, lambda t: 2.0 * t * d * f,
+                           _group_tokens(w, group)))
+    return out
 
 
 def stage_bytes(w, group: int) -> dict:
@@ -56,15 +70,19 @@ def stage_bytes(w, group: int) -> dict:
     B, T, C, d, f = w.batch, w.seq_len, w.chunk, w.d_model, w.d_ff
     e = 2 if w.dtype == torch_bf16() else 4
     tok = B * T
-    chunk_tokens = B * min(group * C, T)
-    chunks = B * min(group, w.n_chunks)
-    return {
+    out = {
         "state_reset": e * d * f + 4 * B * d * f,
         "swiglu": e * tok * (d + f) + e * 2 * f * d,
         "target": e * tok * 2 * d + e * d * d,
-        "prefix_update": e * chunk_tokens * (d + f) + e * chunks * d * f + 8 * B * d * f,
-        "down_proj": e * chunk_tokens * (f + d) + e * chunks * d * f,
     }
+
+    def slots(t):  # chunks (over all sequences) in a group of t tokens
+        return -(-t // (B * C)) * B
+
+    out.update(_per_launch(lambda t: e * t * (d + f) + e * slots(t) * d * f + 8 * B * d * f,
+                           lambda t: e * t * (f + d) + e * slots(t) * d * f,
+                           _group_tokens(w, group)))
+    return out
 
 
 def torch_bf16():
@@ -73,12 +91,13 @@ def torch_bf16():
 
 
 # layer stage -> the kernel's name as rocprofv3 prints it (prefix match)
+# (the scan-only, fused and output-only launches of the group pipeline are
+# one kernel; its median dispatch is a fused one when there are >= 3 groups)
 STAGE_KERNELS = {
     "state_reset": "void ttt::state_reset_kernel",
     "swiglu": "void ttt::swiglu_kernel",
     "target": "void ttt::target_kernel",
-    "prefix_update": "void ttt::prefix_update_kernel",
-    "down_proj": "void ttt::down_proj_kernel",
+    "scan_apply": "void ttt::scan_apply_kernel",
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 

@@ -36,10 +36,10 @@ ttt_status_t ok() {
 }
 
 // ---------------------------------------------------------------- profiling
-const char* const kStageNames[TTT_NUM_STAGES] = {"state_reset", "weight_prep", "pad_fill",
-                                                 "swiglu",      "target",      "prefix_update",
-                                                 "down_proj"};
-enum Stage { kReset = 0, kPrep, kPad, kSwiglu, kTarget, kPrefix, kDown };
+const char* const kStageNames[TTT_NUM_STAGES] = {
+    "state_reset", "weight_prep", "pad_fill", "swiglu", "target", "prefix_update", "down_proj",
+    "scan_apply"};
+enum Stage { kReset = 0, kPrep, kPad, kSwiglu, kTarget, kPrefix, kDown, kScanApply };
 
 struct Profiler {
   std::mutex mu;
@@ -151,17 +151,29 @@ ttt_status_t make_dims(const ttt_mlp_desc_t* desc, ttt::Dims* dm) {
   return TTT_OK;
 }
 
+// Groups the default (AUTO) plan splits a sequence's chunks into: with
+// several groups every launch runs one group's scan next to the previous
+// group's outputs, and four keep the scan's last partial wave of tiles busy
+// while the state is read and written only four times.
+constexpr int64_t kAutoGroups = 4;
+
+// The largest group the mode allows (before looking at the workspace).
+int64_t mode_group(const ttt::Dims& dm, ttt_mode_t mode) {
+  if (mode == TTT_MODE_SEQUENTIAL) return 1;
+  if (mode == TTT_MODE_CHUNK_PARALLEL) return dm.N;
+  return (dm.N + kAutoGroups - 1) / kAutoGroups;
+}
+
 ttt_status_t plan_group(const ttt::Dims& dm, ttt_mode_t mode, size_t ws_bytes, int64_t* group) {
   const ttt::WorkspacePlan p1 = ttt::plan_workspace(dm, 1);
   if (ws_bytes < p1.total_bytes)
     return fail(TTT_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is below the minimum %zu",
                 ws_bytes, p1.total_bytes);
-  int64_t g = 1;
-  if (mode != TTT_MODE_SEQUENTIAL) {
-    const size_t room = (ws_bytes - p1.fixed_bytes) / p1.slot_bytes;
-    g = std::max<int64_t>(1, std::min<int64_t>(dm.N, (int64_t)std::min<size_t>(room, (size_t)dm.N)));
-  }
-  *group = g;
+  const int64_t room = (int64_t)((ws_bytes - p1.fixed_bytes) / p1.slot_bytes);  // slots
+  int64_t g = mode_group(dm, mode);
+  if (g == dm.N && room < dm.N) g = dm.N - 1;  // one set of N slots does not fit
+  if (g < dm.N) g = std::min<int64_t>(g, room / 2);  // two sets of g
+  *group = std::max<int64_t>(g, 1);
   return TTT_OK;
 }
 
@@ -206,12 +218,22 @@ ttt_status_t run_layer(const ttt::Dims& dm, ttt_mode_t mode, bool reset, const v
   if (e != hipSuccess) return hip_fail(e, "target");
   e = staged(kSwiglu, s, [&] { return ttt::launch_swiglu(dm, H, WgU, Z, Zt, s); });
   if (e != hipSuccess) return hip_fail(e, "swiglu");
-  for (int64_t g0 = 0; g0 < dm.N; g0 += G) {
-    const int64_t gc = std::min<int64_t>(G, dm.N - g0);
-    e = staged(kPrefix, s, [&] { return ttt::launch_prefix_update(dm, Vt, Zt, W_state, slots, g0, gc, s); });
-    if (e != hipSuccess) return hip_fail(e, "prefix_update");
-    e = staged(kDown, s, [&] { return ttt::launch_down_proj(dm, Z, slots, O, g0, gc, s); });
-    if (e != hipSuccess) return hip_fail(e, "down_proj");
+  // Group pipeline: launch g scans group g (slot set g & 1) and computes the
+  // outputs of group g - 1 (the other set, completed by launch g - 1).
+  const int64_t groups = (dm.N + G - 1) / G;
+  const size_t set_bytes = (size_t)G * wp.slot_bytes;
+  for (int64_t g = 0; g <= groups; ++g) {
+    const int64_t g0 = g * G, gc = g < groups ? std::min<int64_t>(G, dm.N - g0) : 0;
+    const int64_t a0 = (g - 1) * G, ac = g > 0 ? std::min<int64_t>(G, dm.N - a0) : 0;
+    char* scan_slots = static_cast<char*>(slots) + (g & 1) * (wp.slot_sets > 1 ? set_bytes : 0);
+    const char* apply_slots =
+        static_cast<char*>(slots) + ((g - 1) & 1) * (wp.slot_sets > 1 ? set_bytes : 0);
+    const int stage = gc > 0 && ac > 0 ? kScanApply : gc > 0 ? kPrefix : kDown;
+    e = staged(stage, s, [&] {
+      return ttt::launch_scan_apply(dm, Vt, Zt, W_state, scan_slots, g0, gc, Z, apply_slots, O, a0,
+                                    ac, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "scan_apply");
   }
   return ok();
 }
@@ -272,7 +294,7 @@ size_t ttt_mlp_workspace_size(const ttt_mlp_desc_t* desc, int64_t max_group) {
     fail(TTT_ERR_INVALID_ARGUMENT, "max_group must be >= 0");
     return 0;
   }
-  const int64_t g = max_group == 0 ? dm.N : std::min<int64_t>(max_group, dm.N);
+  const int64_t g = max_group == 0 ? mode_group(dm, desc->mode) : std::min<int64_t>(max_group, dm.N);
   ok();
   return ttt::plan_workspace(dm, g).total_bytes;
 }

@@ -51,6 +51,7 @@ namespace ttt {
 #define TTT_GEMM_THREADS (64 * TTT_WAVES_M * TTT_WAVES_N)
 #define TTT_GEMM_WPE (TTT_WAVES_M * TTT_WAVES_N / 4)
 using Tile = TileShape<256, 256, TTT_WAVES_M, TTT_WAVES_N>;
+using PrefixTile = Tile;
 #define TTT_GEMM_KERNEL                                  \
   __global__ __launch_bounds__(TTT_GEMM_THREADS)          \
   __attribute__((amdgpu_waves_per_eu(TTT_GEMM_WPE, TTT_GEMM_WPE)))
@@ -379,18 +380,19 @@ TTT_GEMM_KERNEL void target_kernel(Dims dm, const T* __restrict__ U, const T* __
 // and finally W_state <- W.  The accumulator is the fp32 state itself, so the
 // result does not depend on how the chunks are grouped.  The tile shape S
 // divides d and f exactly (the host picks it), so every tile is full.
+// Tile `blk` of `nblk` (workgroups [0, nblk) of the launch are these tiles).
 template <typename T, class S>
-__global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::kWaves / 4, S::kWaves / 4))) void prefix_update_kernel(
-    Dims dm, const T* __restrict__ Vt, const T* __restrict__ Zt, float* __restrict__ W_state,
-    T* __restrict__ slots, int64_t g0, int64_t gc) {
+__device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __restrict__ Vt,
+                                                   const T* __restrict__ Zt,
+                                                   float* __restrict__ W_state,
+                                                   T* __restrict__ slots, int64_t g0, int64_t gc,
+                                                   int blk, int nblk, lds_char* smem) {
   constexpr int TB = kRowBytes / (int)sizeof(T);
-  __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
-  lds_char* smem = (lds_char*)smem_raw;
   const int64_t d = dm.d, f = dm.f;
   const int tiles_m = (int)(d / S::BM);
   const int tiles_n = (int)(f / S::BN);
   const int per_seq = tiles_m * tiles_n;
-  const int L = xcd_remap(blockIdx.x, per_seq * (int)dm.B);
+  const int L = xcd_remap(blk, nblk);
   const int64_t b = L / per_seq;
   const TileCoord tc = grouped_tile(L - (int)b * per_seq, tiles_m, tiles_n, 4);
   const int64_t m0 = (int64_t)tc.m * S::BM, n0 = (int64_t)tc.n * S::BN;
@@ -482,21 +484,31 @@ __global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::
     }
 }
 
+template <typename T, class S>
+__global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::kWaves / 4, S::kWaves / 4))) void prefix_update_kernel(
+    Dims dm, const T* __restrict__ Vt, const T* __restrict__ Zt, float* __restrict__ W_state,
+    T* __restrict__ slots, int64_t g0, int64_t gc) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
+  prefix_update_tile<T, S>(dm, Vt, Zt, W_state, slots, g0, gc, blockIdx.x, gridDim.x,
+                           (lds_char*)smem_raw);
+}
+
 // ===================================================================== S3
 // O_i = Z_i slot_i^T for every chunk of the group and every sequence.
+// Tile `blk` of `nblk` (the launch's workgroups [first, first + nblk), first a
+// multiple of 8 so that the XCD of workgroup first + blk is blk % 8).
 template <typename T>
-TTT_GEMM_KERNEL void down_proj_kernel(Dims dm, const T* __restrict__ Z,
-                                      const T* __restrict__ slots, T* __restrict__ O, int64_t g0,
-                                      int64_t gc) {
+__device__ __forceinline__ void down_proj_tile(const Dims& dm, const T* __restrict__ Z,
+                                               const T* __restrict__ slots, T* __restrict__ O,
+                                               int64_t g0, int64_t gc, int blk, int nblk,
+                                               lds_char* smem) {
   using S = Tile;
-  __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
-  lds_char* smem = (lds_char*)smem_raw;
   const int64_t d = dm.d, f = dm.f, C = dm.C, T_seq = dm.T;
   const int64_t ld = f * (int64_t)sizeof(T);
   const int tiles_m = (int)((C + S::BM - 1) / S::BM);
   const int tiles_n = (int)((d + S::BN - 1) / S::BN);
   const int per_chunk = tiles_m * tiles_n;
-  const int L = xcd_remap(blockIdx.x, per_chunk * (int)(gc * dm.B));
+  const int L = xcd_remap(blk, nblk);
   const int64_t cb = L / per_chunk;  // = b * gc + jj
   const int64_t b = cb / gc, jj = cb - b * gc;
   const int64_t chunk = g0 + jj;
@@ -531,6 +543,40 @@ TTT_GEMM_KERNEL void down_proj_kernel(Dims dm, const T* __restrict__ Z,
                                       rows_valid);
     __syncthreads();
   }
+}
+
+template <typename T>
+TTT_GEMM_KERNEL void down_proj_kernel(Dims dm, const T* __restrict__ Z,
+                                      const T* __restrict__ slots, T* __restrict__ O, int64_t g0,
+                                      int64_t gc) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[Tile::kLdsBytes];
+  down_proj_tile<T>(dm, Z, slots, O, g0, gc, blockIdx.x, gridDim.x, (lds_char*)smem_raw);
+}
+
+// ============================================================== S4 + S3
+// One launch of the group pipeline: workgroups [0, scan_blocks) run the scan
+// tiles of chunks g0.. (dispatched first: they are the long ones), workgroups
+// [scan_blocks, scan_pad) exit at once (scan_pad rounds up to a multiple of
+// 8), the rest compute the outputs of chunks a0.. of the previous group,
+// whose slots the previous launch completed.
+template <typename T>
+TTT_GEMM_KERNEL void scan_apply_kernel(Dims dm, const T* __restrict__ Vt, const T* __restrict__ Zt,
+                                       float* __restrict__ W_state, T* __restrict__ scan_slots,
+                                       int64_t g0, int64_t gc, int scan_blocks, int scan_pad,
+                                       const T* __restrict__ Z, const T* __restrict__ apply_slots,
+                                       T* __restrict__ O, int64_t a0, int64_t ac) {
+  static_assert(Tile::kThreads == PrefixTile::kThreads && Tile::kLdsBytes == PrefixTile::kLdsBytes,
+                "both parts share the launch shape");
+  __shared__ __attribute__((aligned(16))) char smem_raw[Tile::kLdsBytes];
+  const int b = blockIdx.x;
+  if (b < scan_pad) {
+    if (b < scan_blocks)
+      prefix_update_tile<T, PrefixTile>(dm, Vt, Zt, W_state, scan_slots, g0, gc, b, scan_blocks,
+                                        (lds_char*)smem_raw);
+    return;
+  }
+  down_proj_tile<T>(dm, Z, apply_slots, O, a0, ac, b - scan_pad, (int)gridDim.x - scan_pad,
+                    (lds_char*)smem_raw);
 }
 
 // ============================================================ small kernels
@@ -627,7 +673,8 @@ WorkspacePlan plan_workspace(const Dims& dm, int64_t group) {
   w.fixed_bytes = off;
   w.slot_bytes = align256((size_t)dm.B * dm.d * dm.f * es);
   w.group = group;
-  w.total_bytes = off + (size_t)group * w.slot_bytes;
+  w.slot_sets = group < dm.N ? 2 : 1;
+  w.total_bytes = off + (size_t)(w.slot_sets * group) * w.slot_bytes;
   return w;
 }
 
@@ -725,49 +772,50 @@ hipError_t launch_target(const Dims& dm, const void* X0, const void* tapsT, cons
   return hipGetLastError();
 }
 
-template <typename T, class S>
-static void launch_prefix_update_t(const Dims& dm, const T* Vt, const T* Zt, float* W_state, T* slots,
-                                   int64_t g0, int64_t gc, hipStream_t s) {
-  const int64_t tiles = (dm.d / S::BM) * (dm.f / S::BN) * dm.B;
-  hipLaunchKernelGGL((prefix_update_kernel<T, S>), dim3((unsigned)tiles), dim3(S::kThreads), 0, s, dm,
-                     Vt, Zt, W_state, slots, g0, gc);
-}
-
-// 256 x 256 tiles when they divide the weight, 64 x 64 otherwise (d and f are
-// multiples of 64).
 template <typename T>
-static void launch_prefix_update_dt(const Dims& dm, const T* Vt, const T* Zt, float* W_state,
-                                    T* slots, int64_t g0, int64_t gc, hipStream_t s) {
-  if (dm.d % 256 == 0 && dm.f % 256 == 0)
-    launch_prefix_update_t<T, Tile>(dm, Vt, Zt, W_state, slots, g0, gc, s);
-  else
-    launch_prefix_update_t<T, TileShape<64, 64, 2, 2>>(dm, Vt, Zt, W_state, slots, g0, gc, s);
+static void launch_scan_apply_t(const Dims& dm, const T* Vt, const T* Zt, float* W_state,
+                                T* scan_slots, int64_t g0, int64_t gc, const T* Z,
+                                const T* apply_slots, T* O, int64_t a0, int64_t ac, hipStream_t s) {
+  const int64_t down_tiles = ac > 0 ? ((dm.C + Tile::BM - 1) / Tile::BM) *
+                                          ((dm.d + Tile::BN - 1) / Tile::BN) * ac * dm.B
+                                    : 0;
+  if (dm.d % PrefixTile::BM == 0 && dm.f % PrefixTile::BN == 0) {
+    const int64_t scan = gc > 0 ? (dm.d / PrefixTile::BM) * (dm.f / PrefixTile::BN) * dm.B : 0;
+    const int64_t pad = (scan + 7) / 8 * 8;
+    if (pad + down_tiles == 0) return;
+    hipLaunchKernelGGL(scan_apply_kernel<T>, dim3((unsigned)(pad + down_tiles)),
+                       dim3(Tile::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, g0, gc,
+                       (int)scan, (int)pad, Z, apply_slots, O, a0, ac);
+    return;
+  }
+  // 64 x 64 scan tiles when 256 does not divide the weight (d and f are
+  // multiples of 64): two launches in the same order.
+  using Small = TileShape<64, 64, 2, 2>;
+  if (gc > 0)
+    hipLaunchKernelGGL((prefix_update_kernel<T, Small>),
+                       dim3((unsigned)((dm.d / Small::BM) * (dm.f / Small::BN) * dm.B)),
+                       dim3(Small::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, g0, gc);
+  if (down_tiles > 0)
+    hipLaunchKernelGGL(down_proj_kernel<T>, dim3((unsigned)down_tiles), dim3(Tile::kThreads), 0, s,
+                       dm, Z, apply_slots, O, a0, ac);
 }
 
-hipError_t launch_prefix_update(const Dims& dm, const void* Vt, const void* Zt, float* W_state,
-                                void* slots, int64_t g0, int64_t gc, hipStream_t s) {
+hipError_t launch_scan_apply(const Dims& dm, const void* Vt, const void* Zt, float* W_state,
+                             void* scan_slots, int64_t g0, int64_t gc, const void* Z,
+                             const void* apply_slots, void* O, int64_t a0, int64_t ac,
+                             hipStream_t s) {
   if (dm.dt == Dtype::BF16)
-    launch_prefix_update_dt<uint16_t>(dm, static_cast<const uint16_t*>(Vt),
-                                      static_cast<const uint16_t*>(Zt), W_state,
-                                      static_cast<uint16_t*>(slots), g0, gc, s);
+    launch_scan_apply_t<uint16_t>(dm, static_cast<const uint16_t*>(Vt),
+                                  static_cast<const uint16_t*>(Zt), W_state,
+                                  static_cast<uint16_t*>(scan_slots), g0, gc,
+                                  static_cast<const uint16_t*>(Z),
+                                  static_cast<const uint16_t*>(apply_slots),
+                                  static_cast<uint16_t*>(O), a0, ac, s);
   else
-    launch_prefix_update_dt<float>(dm, static_cast<const float*>(Vt), static_cast<const float*>(Zt),
-                                   W_state, static_cast<float*>(slots), g0, gc, s);
-  return hipGetLastError();
-}
-
-hipError_t launch_down_proj(const Dims& dm, const void* Z, const void* slots, void* O, int64_t g0,
-                            int64_t gc, hipStream_t s) {
-  const int64_t tiles = ((dm.C + Tile::BM - 1) / Tile::BM) * ((dm.d + Tile::BN - 1) / Tile::BN) *
-                        gc * dm.B;
-  if (dm.dt == Dtype::BF16)
-    hipLaunchKernelGGL(down_proj_kernel<uint16_t>, dim3((unsigned)tiles), dim3(Tile::kThreads), 0, s,
-                       dm, static_cast<const uint16_t*>(Z), static_cast<const uint16_t*>(slots),
-                       static_cast<uint16_t*>(O), g0, gc);
-  else
-    hipLaunchKernelGGL(down_proj_kernel<float>, dim3((unsigned)tiles), dim3(Tile::kThreads), 0, s, dm,
-                       static_cast<const float*>(Z), static_cast<const float*>(slots),
-                       static_cast<float*>(O), g0, gc);
+    launch_scan_apply_t<float>(dm, static_cast<const float*>(Vt), static_cast<const float*>(Zt),
+                               W_state, static_cast<float*>(scan_slots), g0, gc,
+                               static_cast<const float*>(Z), static_cast<const float*>(apply_slots),
+                               static_cast<float*>(O), a0, ac, s);
   return hipGetLastError();
 }
 

@@ -24,12 +24,16 @@ struct Dims {
 };
 
 // Workspace regions (byte offsets from the workspace base, 256-byte aligned).
+// The slots are one set of G per group, two sets when there are several
+// groups: the scan of group g+1 writes one set while the outputs of group g
+// read the other.
 struct WorkspacePlan {
   size_t z_off, zt_off, vt_off, wgu_off, wtt_off, taps_off, slots_off;
   size_t slot_bytes;   // one chunk slot for all B sequences: B * d * f * es
   size_t fixed_bytes;  // everything except the slots
   int64_t group;       // chunks per group G
-  size_t total_bytes;  // fixed_bytes + group * slot_bytes
+  int64_t slot_sets;   // 1 if G covers all chunks, else 2
+  size_t total_bytes;  // fixed_bytes + slot_sets * group * slot_bytes
 };
 
 WorkspacePlan plan_workspace(const Dims& dm, int64_t group);
@@ -46,9 +50,14 @@ hipError_t launch_swiglu(const Dims& dm, const void* H, const void* WgU, void* Z
 // Conv of X0 into U (scratch of B*T x d elements), then eta * U W_target into Vt.
 hipError_t launch_target(const Dims& dm, const void* X0, const void* taps, const void* WtT,
                          void* U, void* Vt, hipStream_t s);
-hipError_t launch_prefix_update(const Dims& dm, const void* Vt, const void* Zt, float* W_state,
-                                void* slots, int64_t g0, int64_t gc, hipStream_t s);
-hipError_t launch_down_proj(const Dims& dm, const void* Z, const void* slots, void* O,
-                            int64_t g0, int64_t gc, hipStream_t s);
+// One step of the group pipeline: the scan (S4) of chunks [g0, g0 + gc) into
+// scan_slots, and the outputs (S3) of chunks [a0, a0 + ac) from apply_slots;
+// gc == 0 or ac == 0 leaves that part out.  Both parts run in one launch
+// where the tile shapes allow, so the outputs fill the CUs the scan's last
+// partial wave of tiles leaves idle.
+hipError_t launch_scan_apply(const Dims& dm, const void* Vt, const void* Zt, float* W_state,
+                             void* scan_slots, int64_t g0, int64_t gc, const void* Z,
+                             const void* apply_slots, void* O, int64_t a0, int64_t ac,
+                             hipStream_t s);
 
 }  // namespace ttt

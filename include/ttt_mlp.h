@@ -64,14 +64,18 @@ typedef enum {
   TTT_ERR_HIP = -4
 } ttt_status_t;
 
-/* How the chunk recurrence is evaluated.  Both give bit-identical results.
- *   SEQUENTIAL      one chunk at a time: output with the current fp32 state,
- *                   then read-modify-write the state (section 3.2 schedule);
- *   CHUNK_PARALLEL  per-chunk increments, one exclusive prefix streamed through
- *                   the fp32 state, then all chunks' outputs at once (the
- *                   three-step form of section 3.2), in groups of as many
- *                   chunks as the workspace holds;
- *   AUTO            CHUNK_PARALLEL. */
+/* How the chunk recurrence is evaluated.  All give bit-identical results.
+ * The chunks of a sequence go in groups of G: a scan over the group streams
+ * the exclusive prefix of the per-chunk increments through the fp32 state and
+ * writes the weight each chunk uses into a slot; the group's outputs are then
+ * computed from its slots, in the same launch as the next group's scan.
+ *   SEQUENTIAL      G = 1: output with the current state, then one
+ *                   read-modify-write of the state per chunk (section 3.2
+ *                   schedule);
+ *   CHUNK_PARALLEL  G as large as the workspace holds, up to all chunks (the
+ *                   three-step form of section 3.2);
+ *   AUTO            chunk-parallel in four groups (fewer if the workspace is
+ *                   smaller), so that scans and outputs share launches. */
 typedef enum {
   TTT_MODE_AUTO = 0,
   TTT_MODE_SEQUENTIAL = 1,
@@ -81,8 +85,8 @@ typedef enum {
 /* Shapes and scalars of one call.
  *   batch    B >= 1 independent sequences (ttt_mlp_forward requires B == 1);
  *   seq_len  T >= 1 tokens per sequence;
- *   d_model  d, a multiple of 64;  d_ff  f, a multiple of 64;
- *            (B*T, d*f and f*B*ceil(T/C)*ceil64(C) must each stay below 2^31);
+ *   d_model  d, a multiple of 64;  d_ff  f, a multiple of 64, at most 2^20;
+ *            (B*T, d*f and B*ceil(T/C)*ceil64(C) must each stay below 2^31);
  *   chunk    C >= 1 tokens per chunk (the last chunk may be shorter);
  *   conv_k   K taps, 1 <= K <= 8;
  *   eta      finite fast-weight learning rate (0 gives the static MLP);
@@ -103,10 +107,13 @@ typedef struct {
   int32_t init_from_w0;
 } ttt_mlp_desc_t;
 
-/* Workspace bytes needed for groups of up to `max_group` chunks (0 = all
- * ceil(T/C) chunks of a sequence at once).  Returns 0 if the descriptor is
- * invalid (see ttt_last_error()).  A workspace of ttt_mlp_workspace_size(desc, 1)
- * bytes is the minimum; chunk-parallel mode uses the largest group that fits. */
+/* Workspace bytes needed for groups of up to `max_group` chunks (0 = the
+ * mode's own group: 1 sequential, all ceil(T/C) chunks chunk-parallel, a
+ * quarter of them (rounded up) auto).  The workspace holds the activations in
+ * the layouts the kernels read, the prepared weights, and one weight slot
+ * (B * d * f elements) per chunk of a group, twice over when there is more
+ * than one group.  Returns 0 if the descriptor is invalid (see
+ * ttt_last_error()).  ttt_mlp_workspace_size(desc, 1) bytes is the minimum. */
 size_t ttt_mlp_workspace_size(const ttt_mlp_desc_t* desc, int64_t max_group);
 
 /* Chunks per group the planner would use for this descriptor and workspace
@@ -155,8 +162,10 @@ const char* ttt_last_error(void);
  * up to max_stages stages, clears them, and returns the number of stages
  * (TTT_NUM_STAGES), or a negative ttt_status_t.  ttt_stage_name() names stage i:
  * 0 state_reset, 1 weight_prep, 2 pad_fill, 3 swiglu (S1), 4 target (S2),
- * 5 prefix_update (S4/S5), 6 down_proj (S3). */
-#define TTT_NUM_STAGES 7
+ * 5 prefix_update (the first group's scan, S4/S5), 6 down_proj (the last
+ * group's outputs, S3), 7 scan_apply (a group's scan next to the previous
+ * group's outputs). */
+#define TTT_NUM_STAGES 8
 ttt_status_t ttt_profile_enable(int enable);
 int ttt_profile_read(double* ms_total, int64_t* launches, int max_stages);
 const char* ttt_stage_name(int stage);

@@ -42,28 +42,45 @@ def desc(**kw):
 
 
 def test_workspace_plan():
+    # T = 4096, C = 512: N = 8 chunks.  One slot set if a group covers every
+    # chunk, else two (the scan of group g+1 runs next to the outputs of g).
     d = desc()
-    w1, wall = tm.ttt_mlp_workspace_size(d, 1), tm.ttt_mlp_workspace_size(d, 0)
-    assert 0 < w1 < wall
-    assert tm.ttt_mlp_workspace_size(d, 8) == wall  # 8 chunks = all of them
-    assert tm.ttt_mlp_workspace_size(d, 100) == wall
     slot = 256 * 512 * 2
-    assert wall - w1 == 7 * slot
-    assert tm.ttt_mlp_group_size(d, wall) == 8
+    w1 = tm.ttt_mlp_workspace_size(d, 1)           # groups of 1: 2 sets of 1
+    fixed = w1 - 2 * slot
+    assert tm.ttt_mlp_workspace_size(d, 0) == fixed + 2 * 2 * slot   # auto: 4 groups of 2
+    w_all = tm.ttt_mlp_workspace_size(d, 8)
+    assert w_all == fixed + 8 * slot               # one group, one set
+    assert tm.ttt_mlp_workspace_size(d, 100) == w_all
+    assert tm.ttt_mlp_workspace_size(d, 3) == fixed + 2 * 3 * slot
+    cp, seq = desc(mode="chunk_parallel"), desc(mode="sequential")
+    assert tm.ttt_mlp_workspace_size(cp, 0) == w_all
+    assert tm.ttt_mlp_workspace_size(seq, 0) == w1
+    # auto takes a quarter of the chunks at most
+    assert tm.ttt_mlp_group_size(d, w_all) == 2
     assert tm.ttt_mlp_group_size(d, w1) == 1
-    assert tm.ttt_mlp_group_size(d, w1 + 3 * slot) == 4
-    assert tm.ttt_mlp_group_size(desc(mode="sequential"), wall) == 1
+    assert tm.ttt_mlp_group_size(d, w1 + slot) == 1   # 3 slots: still 2 sets of 1
+    # chunk-parallel takes as much as fits
+    assert tm.ttt_mlp_group_size(cp, w_all) == 8
+    assert tm.ttt_mlp_group_size(cp, w_all - 1) == 3  # 7 slots: 2 sets of 3
+    assert tm.ttt_mlp_group_size(cp, w1) == 1
+    assert tm.ttt_mlp_group_size(seq, w_all) == 1
     with pytest.raises(tm.TTTError) as e:
         tm.ttt_mlp_group_size(d, w1 - 1)
     assert e.value.status == tm.TTT_ERR_WORKSPACE_TOO_SMALL
+    # a single chunk needs one slot
+    one = desc(seq_len=300)
+    assert tm.ttt_mlp_workspace_size(one, 1) == tm.ttt_mlp_workspace_size(one, 0)
+    assert tm.ttt_mlp_group_size(one, tm.ttt_mlp_workspace_size(one, 0)) == 1
 
 
 def test_workspace_fixed_part_matches_layout():
-    # Z [T][f] + Zt [f][P] + Vt [d][P] + WgU [2f][d] + WtT [d][d] + tapsT [8][d] fp32 + 1 slot
+    # Z [T][f] + Zt [f][P] + Vt [d][P] + WgU [2f][d] + WtT [d][d] + tapsT [8][d] fp32
+    # + 2 slot sets of 1
     d = desc(seq_len=1000, chunk=100)  # padded chunks: Cp = 128, P = 10 * 128
     es = 2
     parts = [1000 * 512 * es, 512 * 1280 * es, 256 * 1280 * es, 2 * 512 * 256 * es,
-             256 * 256 * es, 8 * 256 * 4, 256 * 512 * es]
+             256 * 256 * es, 8 * 256 * 4, 2 * 256 * 512 * es]
     expect = sum((p + 255) // 256 * 256 for p in parts)
     assert tm.ttt_mlp_workspace_size(d, 1) == expect
 
@@ -73,7 +90,7 @@ def test_workspace_z_region_holds_conv_output():
     d = desc(d_model=512, d_ff=256, seq_len=1000, chunk=100)
     es = 2
     parts = [1000 * 512 * es, 256 * 1280 * es, 512 * 1280 * es, 2 * 256 * 512 * es,
-             512 * 512 * es, 8 * 512 * 4, 512 * 256 * es]
+             512 * 512 * es, 8 * 512 * 4, 2 * 512 * 256 * es]
     expect = sum((p + 255) // 256 * 256 for p in parts)
     assert tm.ttt_mlp_workspace_size(d, 1) == expect
 
@@ -213,5 +230,7 @@ def test_last_error_is_per_thread(lib):
 def test_stage_names(lib):
     names = [tm.ttt_stage_name(i) for i in range(tm.TTT_NUM_STAGES)]
     assert names == ["state_reset", "weight_prep", "pad_fill", "swiglu", "target",
-                     "prefix_update", "down_proj"]
+                     "prefix_update", "down_proj", "scan_apply"]
+    header = open(os.path.join(ROOT, "include", "ttt_mlp.h")).read()
+    assert f"#define TTT_NUM_STAGES {tm.TTT_NUM_STAGES}" in header
     assert tm.ttt_stage_name(99) == ""
