@@ -82,13 +82,13 @@ __device__ __forceinline__ int64_t kblock_index(int64_t n, int64_t p, int64_t R)
   return ((p / TB) * R + n) * TB + (p % TB);
 }
 
-// LDS staging for the epilogues: a slice of 64 output columns x 256 tile rows
+// LDS staging for the epilogues: a slice of COLS output columns x 256 tile rows
 // (tokens), put by lanes 4 rows at a time, read back either as token runs
 // (token-major outputs) or as column runs (row-major outputs).  Row stride of
 // 260 elements keeps the 4-element puts of 16 lanes on distinct banks.
-template <typename T, int NTHREADS>
+template <typename T, int NTHREADS, int COLS = 64>
 struct Stage {
-  static constexpr int kCols = 64;
+  static constexpr int kCols = COLS;
   static constexpr int kToks = 256;
   static constexpr int kStride = (kToks + 4) * (int)sizeof(T);  // bytes per LDS row
   static constexpr int TB = kRowBytes / (int)sizeof(T);
@@ -144,8 +144,9 @@ struct Stage {
   __device__ __forceinline__ static void flush_rows(const lds_char* lds, T* __restrict__ dst,
                                                     int64_t ld, int64_t col_base, int ncols,
                                                     int32_t rows_valid) {
-    for (int it = threadIdx.x; it < kToks * (kCols / 8); it += NTHREADS) {
-      const int t = it >> 3, c = (it & 7) * 8;
+    constexpr int kRuns = kCols / 8;  // 8-column runs per row
+    for (int it = threadIdx.x; it < kToks * kRuns; it += NTHREADS) {
+      const int t = it / kRuns, c = (it % kRuns) * 8;
       if (t >= rows_valid || c >= ncols) continue;
       float v[8];
 #pragma unroll
@@ -227,17 +228,20 @@ TTT_GEMM_KERNEL void swiglu_kernel(Dims dm, const T* __restrict__ H, const T* __
   const LanePos p = lane_pos<S>();
   mainloop<T, S>(acc, la, lb, ld / kRowBytes, smem, p, [](int64_t) {});
 
-  // z = silu(gate) * up, staged in two passes of 64 features (B-tile rows
-  // [128 h, 128 h + 128)), then written to Zt and Z.
+  // z = silu(gate) * up, staged through LDS and written to Zt and Z: all 128
+  // features in one pass for bf16 (every wave computes at once), two passes
+  // of 64 for fp32 (the staging would not fit the LDS otherwise).
   const ChunkMap cm = chunk_map(dm);
-  using St = Stage<T, S::kThreads>;
+  constexpr int kPass = sizeof(T) == 2 ? kFeat : 64;  // features per pass
+  using St = Stage<T, S::kThreads, kPass>;
+  static_assert(St::kBytes <= S::kLdsBytes, "staging fits the pipeline's LDS");
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < kFeat / kPass; ++h) {
 #pragma unroll
     for (int jp = 0; jp < S::NB / 2; ++jp) {
       const int brow = p.wave_n0 + 64 * jp;  // B-tile row of the gate block of this pair
-      if (brow < 128 * h || brow >= 128 * h + 128) continue;
-      const int fcol = brow / 2 - 64 * h;      // feature column inside the pass
+      if (brow < 2 * kPass * h || brow >= 2 * kPass * (h + 1)) continue;
+      const int fcol = brow / 2 - kPass * h;   // feature column inside the pass
 #pragma unroll
       for (int i = 0; i < S::MB; ++i)
 #pragma unroll
@@ -250,8 +254,8 @@ TTT_GEMM_KERNEL void swiglu_kernel(Dims dm, const T* __restrict__ H, const T* __
         }
     }
     __syncthreads();
-    const int64_t cb = feat0 + 64 * h;
-    const int ncols = (int)max<int64_t>(0, min<int64_t>(64, f - cb));
+    const int64_t cb = feat0 + kPass * h;
+    const int ncols = (int)max<int64_t>(0, min<int64_t>(kPass, f - cb));
     St::flush_tokens(smem, Zt, f, cb, ncols, row0, BT, cm);
     St::flush_rows(smem, Z + (int64_t)row0 * f, f, cb, ncols, min(BT - row0, S::BM));
     __syncthreads();
