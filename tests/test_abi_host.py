@@ -234,3 +234,14 @@ def test_stage_names(lib):
     header = open(os.path.join(ROOT, "include", "ttt_mlp.h")).read()
     assert f"#define TTT_NUM_STAGES {tm.TTT_NUM_STAGES}" in header
     assert tm.ttt_stage_name(99) == ""
+
+
+def test_library_has_no_unresolved_internal_symbols():
+    """Every kernel's host stub and every internal function is defined in the
+    built library (an unresolved one would only fail when loaded on the GPU)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", tm.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    missing = [l.split()[-1] for l in out.splitlines() if "3ttt" in l]
+    assert not missing, missing
+
