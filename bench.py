@@ -163,7 +163,7 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, cfetch_csv: str
     return out
 
 
-def cpu_baseline(w, inp) -> dict:
+def cpu_baseline(w, inp, target: str = "conv_proj") -> dict:
     """The oracle as it stands, sequential form, on the first chunk(s) of
     sequence 0 (a causal prefix of the same workload)."""
     import oracle
@@ -181,7 +181,7 @@ def cpu_baseline(w, inp) -> dict:
           for k in ("H", "X0", "W_gate", "W_up", "W_down0", "taps", "W_target")}
     t0 = time.perf_counter()
     oracle.forward(ni["H"], ni["X0"], ni["W_gate"], ni["W_up"], ni["W_down0"], ni["taps"],
-                   ni["W_target"], w.eta, w.chunk, form="sequential")
+                   ni["W_target"], w.eta, w.chunk, form="sequential", target=target)
     dt = time.perf_counter() - t0
     return {"value": m / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"sequential fp64 oracle on the first {chunks} chunk(s) ({m} tokens) of "
@@ -207,6 +207,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3_4b_128k")
     ap.add_argument("--mode", default="auto", choices=["auto", "sequential", "chunk_parallel"])
+    ap.add_argument("--target", default="conv_proj", choices=["conv_proj", "proj", "conv", "embed"],
+                    help="fast-weight target (the variants of the ablation table)")
     ap.add_argument("--max-group", type=int, default=0, help="chunks per group (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
@@ -249,7 +251,8 @@ def main() -> int:
     inp = synth.workload_inputs(w)
     dev = {k: v.cuda() for k, v in inp.items()}
     B, T, d, f, K = w.batch, w.seq_len, w.d_model, w.d_ff, w.conv_k
-    desc = tm.make_desc(B, T, d, f, w.chunk, K, w.eta, w.dtype, args.mode, init_from_w0=1)
+    desc = tm.make_desc(B, T, d, f, w.chunk, K, w.eta, w.dtype, args.mode, init_from_w0=1,
+                        target=args.target)
     ws = tm.alloc_workspace(desc, args.max_group)
     group = tm.ttt_mlp_group_size(desc, ws.numel())
     O = torch.empty_like(dev["H"])
@@ -285,6 +288,9 @@ def main() -> int:
     log(f"[bench] {ms_step:.3f} ms/step, {value / 1e6:.3f} M tokens/s")
 
     work = stage_work(w, group)
+    proj = args.target in ("conv_proj", "proj")
+    if not proj:
+        work.pop("target")  # no projection GEMM: the stage only moves rows
     per_stage = {}
     for name, (ms, n) in stages.items():
         if n == 0:
@@ -307,12 +313,13 @@ def main() -> int:
                 "flops_per_launch": work[dom],
                 "algorithmic_bytes_per_launch": stage_bytes(w, group)[dom],
                 "ms_per_launch": per_stage[dom]["ms_per_launch"]}
-    layer_frac = w.flops() / (ms_step / 1e3) / (peak * 1e12)
+    layer_flops = w.flops() - (0 if proj else 2.0 * w.tokens * d * d)
+    layer_frac = layer_flops / (ms_step / 1e3) / (peak * 1e12)
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle) ...")
-        cpu = cpu_baseline(w, inp)
+        cpu = cpu_baseline(w, inp, args.target)
         log(f"[bench] oracle: {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
 
     out = {
@@ -330,7 +337,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "seq_len": T, "chunk": w.chunk,
                    "d_model": d, "d_ff": f, "conv_k": K, "eta": w.eta, "mode": args.mode,
-                   "group": group, "state": "fp32"},
+                   "group": group, "state": "fp32", "target": args.target},
         "layer_mfma_frac": layer_frac,
         "roofline": roofline,
         "stages": per_stage,

@@ -130,6 +130,8 @@ ttt_status_t make_dims(const ttt_mlp_desc_t* desc, ttt::Dims* dm) {
     return fail(TTT_ERR_INVALID_ARGUMENT, "unknown mode %d", (int)q.mode);
   if (q.init_from_w0 != 0 && q.init_from_w0 != 1)
     return fail(TTT_ERR_INVALID_ARGUMENT, "init_from_w0 must be 0 or 1");
+  if (q.target < TTT_TARGET_CONV_PROJ || q.target > TTT_TARGET_EMBED)
+    return fail(TTT_ERR_INVALID_ARGUMENT, "unknown target %d", (int)q.target);
   ttt::Dims d{};
   d.B = q.batch;
   d.T = q.seq_len;
@@ -141,6 +143,8 @@ ttt_status_t make_dims(const ttt_mlp_desc_t* desc, ttt::Dims* dm) {
   d.K = q.conv_k;
   d.eta = q.eta;
   d.dt = q.dtype == TTT_BF16 ? ttt::Dtype::BF16 : ttt::Dtype::F32;
+  d.conv = q.target == TTT_TARGET_CONV_PROJ || q.target == TTT_TARGET_CONV;
+  d.proj = q.target == TTT_TARGET_CONV_PROJ || q.target == TTT_TARGET_PROJ;
   if (d.B > kMaxInt32 / d.T) return fail(TTT_ERR_UNSUPPORTED, "batch * seq_len must be < 2^31");
   if (d.d * d.f > kMaxInt32) return fail(TTT_ERR_UNSUPPORTED, "d_model * d_ff must be < 2^31");
   if (d.B * d.N > kMaxInt32 / d.Cp) return fail(TTT_ERR_UNSUPPORTED, "padded token count must be < 2^31");
@@ -252,8 +256,8 @@ ttt_status_t check_buffers(const ttt::Dims& dm, const Buffers& b, bool need_w0) 
     const void* p;
     bool needed;
   } ptrs[] = {{"H", b.H, true},       {"X0", b.X0, true},     {"W_gate", b.Wg, true},
-              {"W_up", b.Wu, true},   {"W_down0", b.W0, need_w0}, {"conv_taps", b.taps, true},
-              {"W_target", b.Wt, true}, {"O", b.O, true},     {"W_state", b.W, true},
+              {"W_up", b.Wu, true},   {"W_down0", b.W0, need_w0}, {"conv_taps", b.taps, dm.conv},
+              {"W_target", b.Wt, dm.proj}, {"O", b.O, true},     {"W_state", b.W, true},
               {"ws", b.ws, true}};
   for (const P& q : ptrs) {
     if (!q.needed) continue;
@@ -266,9 +270,9 @@ ttt_status_t check_buffers(const ttt::Dims& dm, const Buffers& b, bool need_w0) 
   std::vector<Range> ins = {range("H", b.H, act),
                             range("X0", b.X0, act),
                             range("W_gate", b.Wg, (size_t)dm.f * dm.d * es),
-                            range("W_up", b.Wu, (size_t)dm.f * dm.d * es),
-                            range("conv_taps", b.taps, (size_t)dm.d * dm.K * es),
-                            range("W_target", b.Wt, (size_t)dm.d * dm.d * es)};
+                            range("W_up", b.Wu, (size_t)dm.f * dm.d * es)};
+  if (dm.conv) ins.push_back(range("conv_taps", b.taps, (size_t)dm.d * dm.K * es));
+  if (dm.proj) ins.push_back(range("W_target", b.Wt, (size_t)dm.d * dm.d * es));
   if (need_w0) ins.push_back(range("W_down0", b.W0, (size_t)dm.d * dm.f * es));
   const Range outs[] = {range("O", b.O, act),
                         range("W_state", b.W, (size_t)dm.B * dm.d * dm.f * sizeof(float)),

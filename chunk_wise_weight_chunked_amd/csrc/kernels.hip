@@ -380,6 +380,35 @@ TTT_GEMM_KERNEL void target_kernel(Dims dm, const T* __restrict__ U, const T* __
   }
 }
 
+// eta * R (R [B*T][d] row-major: X0 or U) into Vt, for the targets without a
+// projection.  A workgroup stages 256 token rows x 64 channels through LDS and
+// leaves through the token-major flush.
+template <typename T>
+__global__ __launch_bounds__(256) void rows_to_vt_kernel(Dims dm, const T* __restrict__ R,
+                                                         T* __restrict__ Vt) {
+  using St = Stage<T, 256, 64>;
+  __shared__ __attribute__((aligned(16))) char smem_raw[St::kBytes];
+  lds_char* smem = (lds_char*)smem_raw;
+  constexpr int EPC = Elem<T>::kPerChunk;
+  const int32_t BT = (int32_t)(dm.B * dm.T);
+  const int32_t row0 = (int32_t)blockIdx.x * St::kToks;
+  const int64_t c0 = (int64_t)blockIdx.y * St::kCols;
+  const int ncols = (int)min<int64_t>(St::kCols, dm.d - c0);
+  for (int it = threadIdx.x; it < St::kToks * (St::kCols / EPC); it += 256) {
+    const int t = it / (St::kCols / EPC), c = (it % (St::kCols / EPC)) * EPC;
+    if (row0 + t >= BT || c >= ncols) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(R + (int64_t)(row0 + t) * dm.d + c0 + c);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      T x;
+      Elem<T>::store(&x, dm.eta * chunk_value<T>(v, e));
+      lds_store<T>(smem + (c + e) * St::kStride + t * (int)sizeof(T), x);
+    }
+  }
+  __syncthreads();
+  St::flush_tokens(smem, Vt, dm.d, c0, ncols, row0, BT, chunk_map(dm));
+}
+
 // ===================================================================== S4
 // For each sequence b and fast-weight tile (m0.., n0..), over the chunks
 // g0 .. g0+gc-1 in order:
@@ -712,15 +741,19 @@ hipError_t launch_weight_prep(const Dims& dm, const void* Wg, const void* Wu, co
   const dim3 tgrid((unsigned)((dm.d + 63) / 64), (unsigned)((dm.d + 63) / 64));
   const unsigned tblocks = (unsigned)((dm.d + 255) / 256);
   if (dm.dt == Dtype::BF16) {
-    hipLaunchKernelGGL(transpose_kernel<uint16_t>, tgrid, dim3(256), 0, s,
-                       static_cast<uint16_t*>(WtT), static_cast<const uint16_t*>(Wt), dm.d);
-    hipLaunchKernelGGL(taps_kernel<uint16_t>, dim3(tblocks), dim3(256), 0, s, tapsT,
-                       static_cast<const uint16_t*>(taps), dm.d, dm.K);
+    if (dm.proj)
+      hipLaunchKernelGGL(transpose_kernel<uint16_t>, tgrid, dim3(256), 0, s,
+                         static_cast<uint16_t*>(WtT), static_cast<const uint16_t*>(Wt), dm.d);
+    if (dm.conv)
+      hipLaunchKernelGGL(taps_kernel<uint16_t>, dim3(tblocks), dim3(256), 0, s, tapsT,
+                         static_cast<const uint16_t*>(taps), dm.d, dm.K);
   } else {
-    hipLaunchKernelGGL(transpose_kernel<float>, tgrid, dim3(256), 0, s, static_cast<float*>(WtT),
-                       static_cast<const float*>(Wt), dm.d);
-    hipLaunchKernelGGL(taps_kernel<float>, dim3(tblocks), dim3(256), 0, s, tapsT,
-                       static_cast<const float*>(taps), dm.d, dm.K);
+    if (dm.proj)
+      hipLaunchKernelGGL(transpose_kernel<float>, tgrid, dim3(256), 0, s, static_cast<float*>(WtT),
+                         static_cast<const float*>(Wt), dm.d);
+    if (dm.conv)
+      hipLaunchKernelGGL(taps_kernel<float>, dim3(tblocks), dim3(256), 0, s, tapsT,
+                         static_cast<const float*>(taps), dm.d, dm.K);
   }
   return hipGetLastError();
 }
@@ -756,15 +789,24 @@ template <typename T>
 static void launch_target_t(const Dims& dm, const T* X0, const float* tapsT, const T* WtT, T* U,
                             T* Vt, hipStream_t s) {
   const int64_t BT = dm.B * dm.T;
-  const int64_t items = (BT + kConvRows - 1) / kConvRows * (dm.d / Elem<T>::kPerChunk);
-  const dim3 cgrid(grid_for(items, 256, 65536));
-  if (dm.K <= 4)
-    hipLaunchKernelGGL((conv_kernel<T, 4>), cgrid, dim3(256), 0, s, dm, X0, tapsT, U);
-  else
-    hipLaunchKernelGGL((conv_kernel<T, 8>), cgrid, dim3(256), 0, s, dm, X0, tapsT, U);
-  const int64_t tiles = ((BT + Tile::BM - 1) / Tile::BM) * ((dm.d + Tile::BN - 1) / Tile::BN);
-  hipLaunchKernelGGL(target_kernel<T>, dim3((unsigned)tiles), dim3(Tile::kThreads), 0, s, dm, U,
-                     WtT, Vt);
+  const T* rows = X0;  // the rows the projection (or the copy into Vt) reads
+  if (dm.conv) {
+    const int64_t items = (BT + kConvRows - 1) / kConvRows * (dm.d / Elem<T>::kPerChunk);
+    const dim3 cgrid(grid_for(items, 256, 65536));
+    if (dm.K <= 4)
+      hipLaunchKernelGGL((conv_kernel<T, 4>), cgrid, dim3(256), 0, s, dm, X0, tapsT, U);
+    else
+      hipLaunchKernelGGL((conv_kernel<T, 8>), cgrid, dim3(256), 0, s, dm, X0, tapsT, U);
+    rows = U;
+  }
+  if (dm.proj) {
+    const int64_t tiles = ((BT + Tile::BM - 1) / Tile::BM) * ((dm.d + Tile::BN - 1) / Tile::BN);
+    hipLaunchKernelGGL(target_kernel<T>, dim3((unsigned)tiles), dim3(Tile::kThreads), 0, s, dm,
+                       rows, WtT, Vt);
+  } else {
+    hipLaunchKernelGGL(rows_to_vt_kernel<T>, dim3((unsigned)((BT + 255) / 256), (unsigned)((dm.d + 63) / 64)),
+                       dim3(256), 0, s, dm, rows, Vt);
+  }
 }
 
 hipError_t launch_target(const Dims& dm, const void* X0, const void* tapsT, const void* WtT,

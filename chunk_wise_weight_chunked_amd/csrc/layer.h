@@ -21,6 +21,7 @@ struct Dims {
   int32_t K;
   float eta;
   Dtype dt;
+  bool conv, proj;  // the target's conv and projection (both: the method)
 };
 
 // Workspace regions (byte offsets from the workspace base, 256-byte aligned).
@@ -47,7 +48,9 @@ hipError_t launch_weight_prep(const Dims& dm, const void* Wg, const void* Wu, co
 hipError_t launch_pad_fill(void* zt, void* vt, const Dims& dm, hipStream_t s);
 hipError_t launch_swiglu(const Dims& dm, const void* H, const void* WgU, void* Z, void* Zt,
                          hipStream_t s);
-// Conv of X0 into U (scratch of B*T x d elements), then eta * U W_target into Vt.
+// eta * V^ into Vt: the conv of X0 into U (scratch of B*T x d elements) if
+// dm.conv, then the projection by W_target if dm.proj (each part left out is
+// the identity).
 hipError_t launch_target(const Dims& dm, const void* X0, const void* taps, const void* WtT,
                          void* U, void* Vt, hipStream_t s);
 // One step of the group pipeline: the scan (S4) of chunks [g0, g0 + gc) into

@@ -26,10 +26,13 @@ TTT_ERR_UNSUPPORTED = -2
 TTT_ERR_WORKSPACE_TOO_SMALL = -3
 TTT_ERR_HIP = -4
 TTT_MODE_AUTO, TTT_MODE_SEQUENTIAL, TTT_MODE_CHUNK_PARALLEL = 0, 1, 2
+TTT_TARGET_CONV_PROJ, TTT_TARGET_PROJ, TTT_TARGET_CONV, TTT_TARGET_EMBED = 0, 1, 2, 3
 TTT_NUM_STAGES = 8
 
 _MODES = {"auto": TTT_MODE_AUTO, "sequential": TTT_MODE_SEQUENTIAL,
           "chunk_parallel": TTT_MODE_CHUNK_PARALLEL}
+_TARGETS = {"conv_proj": TTT_TARGET_CONV_PROJ, "proj": TTT_TARGET_PROJ,
+            "conv": TTT_TARGET_CONV, "embed": TTT_TARGET_EMBED}
 
 
 class TTTError(RuntimeError):
@@ -50,6 +53,7 @@ class ttt_mlp_desc_t(ctypes.Structure):
         ("dtype", ctypes.c_int),
         ("mode", ctypes.c_int),
         ("init_from_w0", ctypes.c_int32),
+        ("target", ctypes.c_int),
     ]
 
 
@@ -117,13 +121,16 @@ def _check(status: int):
 
 
 def make_desc(batch, seq_len, d_model, d_ff, chunk, conv_k, eta, dtype, mode="auto",
-              init_from_w0=1) -> ttt_mlp_desc_t:
+              init_from_w0=1, target="conv_proj") -> ttt_mlp_desc_t:
     if isinstance(dtype, torch.dtype):
         dtype = {torch.float32: TTT_F32, torch.bfloat16: TTT_BF16}[dtype]
     if isinstance(mode, str):
         mode = _MODES[mode]
+    if isinstance(target, str):
+        target = _TARGETS[target]
     return ttt_mlp_desc_t(int(batch), int(seq_len), int(d_model), int(d_ff), int(chunk),
-                          int(conv_k), float(eta), int(dtype), int(mode), int(init_from_w0))
+                          int(conv_k), float(eta), int(dtype), int(mode), int(init_from_w0),
+                          int(target))
 
 
 def _ptr(t) -> int | None:
@@ -213,13 +220,21 @@ def alloc_workspace(desc: ttt_mlp_desc_t, max_group: int = 0, device="cuda") -> 
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def _conv_k(conv_taps, conv_k):
+    if conv_taps is not None:
+        return conv_taps.shape[1]
+    return 1 if conv_k is None else conv_k
+
+
 def forward(H, X0, W_gate, W_up, W_down0, conv_taps, W_target, eta, chunk, mode="auto",
-            max_group=0, ws=None, stream=None):
+            max_group=0, ws=None, stream=None, target="conv_proj", conv_k=None):
     """One sequence: H, X0 [T][d] (or [1][T][d]) device tensors.  Returns
-    (O like H, W_down_final [d][f] fp32)."""
+    (O like H, W_down_final [d][f] fp32).  conv_taps / W_target may be None
+    when `target` leaves the conv / projection out."""
     T, d = H.shape[-2], H.shape[-1]
     f = W_gate.shape[0]
-    desc = make_desc(1, T, d, f, chunk, conv_taps.shape[1], eta, H.dtype, mode)
+    desc = make_desc(1, T, d, f, chunk, _conv_k(conv_taps, conv_k), eta, H.dtype, mode,
+                     target=target)
     if ws is None:
         ws = alloc_workspace(desc, max_group, H.device)
     O = torch.empty_like(H)
@@ -230,7 +245,8 @@ def forward(H, X0, W_gate, W_up, W_down0, conv_taps, W_target, eta, chunk, mode=
 
 
 def forward_batched(H, X0, W_gate, W_up, W_down0, conv_taps, W_target, eta, chunk, W_state=None,
-                    mode="auto", max_group=0, ws=None, stream=None):
+                    mode="auto", max_group=0, ws=None, stream=None, target="conv_proj",
+                    conv_k=None):
     """B sequences: H, X0 [B][T][d].  If W_state ([B][d][f] fp32) is None it is
     allocated and initialised from W_down0; otherwise it is used (and updated)
     in place as each sequence's starting weight.  Returns (O, W_state)."""
@@ -239,8 +255,8 @@ def forward_batched(H, X0, W_gate, W_up, W_down0, conv_taps, W_target, eta, chun
     init = W_state is None
     if init:
         W_state = torch.empty((B, d, f), dtype=torch.float32, device=H.device)
-    desc = make_desc(B, T, d, f, chunk, conv_taps.shape[1], eta, H.dtype, mode,
-                     init_from_w0=1 if init else 0)
+    desc = make_desc(B, T, d, f, chunk, _conv_k(conv_taps, conv_k), eta, H.dtype, mode,
+                     init_from_w0=1 if init else 0, target=target)
     if ws is None:
         ws = alloc_workspace(desc, max_group, H.device)
     O = torch.empty_like(H)

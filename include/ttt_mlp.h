@@ -82,6 +82,22 @@ typedef enum {
   TTT_MODE_CHUNK_PARALLEL = 2
 } ttt_mode_t;
 
+/* Which target the fast weight is trained toward (section 3.3's
+ * V^ = Conv1D(X0) W_target, and the variants of the page's ablation table in
+ * section 6, read as replacing the left-out part by the identity):
+ *   CONV_PROJ  V^ = Conv1D(X0) W_target (the method)
+ *   PROJ       V^ = X0 W_target         ("w/o Conv": the token's own embedding)
+ *   CONV       V^ = Conv1D(X0)          ("w/o Proj")
+ *   EMBED      V^ = X0                  ("w/o Conv, Proj")
+ * conv_taps may be NULL when the mode has no conv, W_target when it has no
+ * projection. */
+typedef enum {
+  TTT_TARGET_CONV_PROJ = 0,
+  TTT_TARGET_PROJ = 1,
+  TTT_TARGET_CONV = 2,
+  TTT_TARGET_EMBED = 3
+} ttt_target_t;
+
 /* Shapes and scalars of one call.
  *   batch    B >= 1 independent sequences (ttt_mlp_forward requires B == 1);
  *   seq_len  T >= 1 tokens per sequence;
@@ -93,7 +109,8 @@ typedef enum {
  *   dtype    TTT_BF16 or TTT_F32 for activations and weights;
  *   mode     see ttt_mode_t;
  *   init_from_w0  (batched only) 1: every W_state[b] is first set to W_down0;
- *                 0: W_state holds each sequence's starting weight on entry. */
+ *                 0: W_state holds each sequence's starting weight on entry;
+ *   target   see ttt_target_t (0 for the method itself). */
 typedef struct {
   int64_t batch;
   int64_t seq_len;
@@ -105,6 +122,7 @@ typedef struct {
   ttt_dtype_t dtype;
   ttt_mode_t mode;
   int32_t init_from_w0;
+  ttt_target_t target;
 } ttt_mlp_desc_t;
 
 /* Workspace bytes needed for groups of up to `max_group` chunks (0 = the

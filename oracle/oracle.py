@@ -118,13 +118,38 @@ def gated_activations(H, W_gate, W_up) -> np.ndarray:
     return Z
 
 
-def lm_target(X0, taps, W_target) -> np.ndarray:
-    """V^ = Conv1D(X0) W_target for X0 of shape [B][T][d] (or [T][d])."""
+# The target variants of the In-Place TTT page's ablation table (section 6):
+# "w/o Conv" and "w/o Proj" leave out the conv or the projection of the
+# section 3.3 target V^ = Conv1D(X0) W_target.  Read literally, a part left
+# out is the identity: without the conv V^[t] = X0[t] W_target (the token's
+# own embedding: the conv's tap k = 1 alone, X0[t+1-1]); without the
+# projection V^ = Conv1D(X0) (W_target = I).  The oracle evaluates a variant
+# as the method itself on those identity parts, which in fp64 is exact
+# (multiplications by 1 and additions of 0).
+TARGETS = ("conv_proj", "proj", "conv", "embed")
+
+
+def target_parts(target: str, taps, W_target, d: int):
+    """(taps, W_target) that give `target` through the section 3.3 formula."""
+    if target not in TARGETS:
+        raise ValueError(f"unknown target {target!r}")
+    if target in ("proj", "embed"):       # no conv: U[t] = X0[t]
+        taps = np.zeros((d, 2), dtype=np.float32)
+        taps[:, 1] = 1.0
+    if target in ("conv", "embed"):       # no projection
+        W_target = np.eye(d, dtype=np.float32)
+    return taps, W_target
+
+
+def lm_target(X0, taps, W_target, target: str = "conv_proj") -> np.ndarray:
+    """V^ = Conv1D(X0) W_target (or a variant, see TARGETS) for X0 of shape
+    [B][T][d] (or [T][d])."""
     X0 = _f32(X0)
     squeeze = X0.ndim == 2
     if squeeze:
         X0 = X0[None]
     B, T, d = X0.shape
+    taps, W_target = target_parts(target, taps, W_target, d)
     taps, Wt = _f32(taps), _f32(W_target)
     K = taps.shape[1]
     assert taps.shape == (d, K) and Wt.shape == (d, d)
@@ -145,12 +170,14 @@ _FORMS = {
 
 
 def forward(H, X0, W_gate, W_up, W_down0, taps, W_target, eta: float, chunk: int,
-            form: str = "sequential"):
+            form: str = "sequential", target: str = "conv_proj"):
     """Run the layer; returns (O [B][T][d] float64, W_final [B][d][f] float64).
 
     H and X0 may be [T][d] (one sequence; outputs are then squeezed) or
     [B][T][d].  W_down0 may be [d][f] (shared starting weight) or [B][d][f]
-    (one starting state per sequence).
+    (one starting state per sequence).  `target` selects a variant of the
+    fast weight's target (TARGETS); taps / W_target are ignored (may be None)
+    when it leaves the conv / the projection out.
     """
     H, X0 = _f32(H), _f32(X0)
     squeeze = H.ndim == 2
@@ -158,6 +185,7 @@ def forward(H, X0, W_gate, W_up, W_down0, taps, W_target, eta: float, chunk: int
         H, X0 = H[None], X0[None]
     B, T, d = H.shape
     assert X0.shape == (B, T, d)
+    taps, W_target = target_parts(target, taps, W_target, d)
     Wg, Wu, taps, Wt = _f32(W_gate), _f32(W_up), _f32(taps), _f32(W_target)
     f = Wg.shape[0]
     K = taps.shape[1]
@@ -182,11 +210,13 @@ def forward(H, X0, W_gate, W_up, W_down0, taps, W_target, eta: float, chunk: int
     return O, W
 
 
-def final_weight_grid(H, X0, W_gate, W_up, W_down0, taps, W_target, eta: float, ms, ns):
+def final_weight_grid(H, X0, W_gate, W_up, W_down0, taps, W_target, eta: float, ms, ns,
+                      target: str = "conv_proj"):
     """Entries W_final[m][n] for m in ms, n in ns of ONE sequence, by the closed
     form W0 + eta * sum_t V^[t][m] Z[t][n] (independent of the chunk size)."""
     H, X0 = _f32(H), _f32(X0)
     T, d = H.shape
+    taps, W_target = target_parts(target, taps, W_target, d)
     Wg, Wu, W0, taps, Wt = (_f32(W_gate), _f32(W_up), _f32(W_down0), _f32(taps),
                             _f32(W_target))
     f = Wg.shape[0]

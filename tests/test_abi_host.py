@@ -108,6 +108,7 @@ BAD_DESCS = [
     (dict(dtype=7), tm.TTT_ERR_INVALID_ARGUMENT, "dtype"),
     (dict(mode=9), tm.TTT_ERR_INVALID_ARGUMENT, "mode"),
     (dict(init_from_w0=2), tm.TTT_ERR_INVALID_ARGUMENT, "init_from_w0"),
+    (dict(target=4), tm.TTT_ERR_INVALID_ARGUMENT, "target"),
     (dict(batch=1 << 20, seq_len=1 << 12), tm.TTT_ERR_UNSUPPORTED, "2^31"),
 ]
 
@@ -166,6 +167,23 @@ def test_w_down0_optional_without_init(lib):
     p["H"] = None  # still rejected for the other pointer
     assert call_forward(lib, d, p, batched=True) == tm.TTT_ERR_INVALID_ARGUMENT
     assert "H is NULL" in tm.ttt_last_error()
+
+
+@pytest.mark.parametrize("target,unused", [("proj", "taps"), ("conv", "W_target"),
+                                           ("embed", "taps"), ("embed", "W_target")])
+def test_unused_target_inputs_may_be_null(lib, target, unused):
+    """A target variant without the conv / projection accepts NULL taps /
+    W_target: the pointer checks pass and the call fails later, on a workspace
+    below the minimum."""
+    d = desc(target=target)
+    p = fake_ptrs(d, ws_bytes=tm.ttt_mlp_workspace_size(d, 1) - 256)
+    p[unused] = None
+    assert call_forward(lib, d, p) == tm.TTT_ERR_WORKSPACE_TOO_SMALL, tm.ttt_last_error()
+    d = desc()  # the method itself needs both
+    p = fake_ptrs(d)
+    p[unused] = None
+    assert call_forward(lib, d, p) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert "NULL" in tm.ttt_last_error() and "H " not in tm.ttt_last_error()
 
 
 @pytest.mark.parametrize("name", ["H", "O", "W", "W_target"])

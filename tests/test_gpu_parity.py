@@ -187,6 +187,39 @@ def test_nan_input_propagates_without_fault():
     assert np.isnan(O[0, 128:]).any()         # later chunks see the updated weight
 
 
+# --------------------------------------------------- ablation targets (section 6)
+TARGET_CASES = [
+    # B, T, d, f, K, C, dtype
+    (2, 333, 128, 192, 3, 100, torch.bfloat16),
+    (1, 300, 192, 256, 4, 64, torch.float32),
+]
+
+
+@pytest.mark.parametrize("target", ["proj", "conv", "embed"])
+@pytest.mark.parametrize("case", TARGET_CASES, ids=lambda c: f"T{c[1]}d{c[2]}{str(c[6])[6:]}")
+def test_target_variants(case, target):
+    """The ablation targets against the oracle; the inputs a variant leaves out
+    are passed as NULL."""
+    B, T, d, f, K, C, dtype = case
+    print(f"[parity] target={target} B,T,d,f,K,C={B},{T},{d},{f},{K},{C} {dtype}", flush=True)
+    inp = synth.make_inputs(B, T, d, f, K, dtype, seed=77)
+    dev = to_device(inp)
+    taps = None if target in ("proj", "embed") else dev["taps"]
+    Wt = None if target in ("conv", "embed") else dev["W_target"]
+    eta = 2e-2
+    O, W = tm.forward_batched(dev["H"], dev["X0"], dev["W_gate"], dev["W_up"], dev["W_down0"],
+                              taps, Wt, eta, C, target=target, conv_k=K)
+    torch.cuda.synchronize()
+    ni = numpy_inputs(inp)
+    Oo, Wo = oracle.forward(ni["H"], ni["X0"], ni["W_gate"], ni["W_up"], ni["W_down0"],
+                            ni["taps"], ni["W_target"], eta, C, target=target)
+    W0 = ni["W_down0"].astype(np.float64)
+    Og, Wg = O.float().cpu().numpy(), W.cpu().numpy()
+    e_o, e_dw = rel(Og, Oo), rel(Wg - W0, Wo - W0)
+    print(f"  rel O {e_o:.3e}  dW {e_dw:.3e}", flush=True)
+    assert e_o <= tol_for(dtype) and e_dw <= tol_for(dtype), (e_o, e_dw)
+
+
 # --------------------------------------------------------------- full-size workloads
 FULL = ["qwen3_4b_32k", "qwen3_4b_128k", "multi_session_16x8k", "small_4x128k"]
 PREFIX_CHUNKS = {"qwen3_4b_32k": 2, "qwen3_4b_128k": 1, "multi_session_16x8k": 1,

@@ -294,3 +294,46 @@ def test_rejects_inexact_inputs():
     inp["H"] = inp["H"].astype(np.float64) + 1e-12
     with pytest.raises(ValueError):
         run(inp, 0.1, 2)
+
+
+# ------------------------------------------ ablation targets (section 6 table)
+def test_target_variants_are_their_definitions():
+    """Without the conv V^ = X0 W_target; without the projection V^ = Conv1D(X0);
+    without both V^ = X0 (exactly); the conv checked against numpy.correlate."""
+    T, d, K = 11, 5, 3
+    rng = np.random.default_rng(31)
+    X0 = rng.standard_normal((T, d)).astype(np.float32)
+    taps = rng.standard_normal((d, K)).astype(np.float32)
+    Wt = rng.standard_normal((d, d)).astype(np.float32)
+    assert np.array_equal(oracle.lm_target(X0, None, None, target="embed"), X0.astype(np.float64))
+    np.testing.assert_allclose(oracle.lm_target(X0, None, Wt, target="proj"),
+                               X0.astype(np.float64) @ Wt.astype(np.float64),
+                               rtol=1e-13, atol=1e-13)
+    U = np.zeros((T, d))
+    for c in range(d):
+        x = np.concatenate([np.zeros(K - 2), X0[:, c].astype(np.float64), np.zeros(1)])
+        U[:, c] = np.correlate(x, taps[c, ::-1].astype(np.float64), mode="valid")[:T]
+    np.testing.assert_allclose(oracle.lm_target(X0, taps, None, target="conv"), U,
+                               rtol=1e-13, atol=1e-13)
+    with pytest.raises(ValueError):
+        oracle.lm_target(X0, taps, Wt, target="nope")
+
+
+@pytest.mark.parametrize("target", ["proj", "conv", "embed"])
+def test_target_variant_layer_closed_form_and_forms_agree(target):
+    """Every variant still follows the update rule: W_final = W0 + eta V^^T Z, and
+    the three evaluation forms agree."""
+    inp = rand_inputs(1, 37, 8, 12, 3, seed=33)
+    eta, C = 0.05, 8
+    outs = [oracle.forward(inp["H"], inp["X0"], inp["W_gate"], inp["W_up"], inp["W_down0"],
+                           inp["taps"], inp["W_target"], eta, C, form=form, target=target)
+            for form in ("sequential", "chunk_parallel", "dual")]
+    for O, W in outs[1:]:
+        assert rel(O, outs[0][0]) < 1e-12 and rel(W, outs[0][1]) < 1e-12
+    X0 = inp["X0"][0].astype(np.float64)
+    V = {"proj": X0 @ inp["W_target"].astype(np.float64),
+         "embed": X0,
+         "conv": oracle.lm_target(inp["X0"][0], inp["taps"], None, target="conv")}[target]
+    Z = oracle.gated_activations(inp["H"][0], inp["W_gate"], inp["W_up"])
+    ref = inp["W_down0"].astype(np.float64) + eta * V.T @ Z
+    assert rel(outs[0][1][0], ref) < 1e-13
