@@ -5,7 +5,9 @@
 
 One step = one call of the whole layer (S1 SwiGLU, S2 conv + target, the
 chunk-wise fast-weight recurrence S3/S4) over one batch of synthetic inputs
-that are already resident in HBM.  Prints ONE JSON line on stdout:
+that are already resident in HBM.  With --segment L a step instead streams the
+same sequences through the streaming entry point in calls of L tokens
+(--segment-calls n: only the first n calls, e.g. a decode rate with L = 1).  Prints ONE JSON line on stdout:
 tokens/s over the timed steps, the roofline position of the dominant kernel
 (timed with HIP events inside the library, on the stream it runs on), and the
 fp64 CPU oracle timed on a bounded sample on the host cores.
@@ -13,6 +15,7 @@ fp64 CPU oracle timed on a bounded sample on the host cores.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -200,6 +203,71 @@ def calib_copy(nbytes: int, reps: int) -> None:
     log(f"copied {nbytes} bytes x {reps}")
 
 
+def stream_bench(args, w, dev, inp) -> int:
+    """Tokens/s of the streaming entry point: each step feeds the B sequences
+    from position 0 in calls of L tokens (the last call closes the streams
+    when the whole sequence is fed)."""
+    import torch
+    from chunk_wise_weight_chunked_amd import ttt_mlp as tm
+
+    B, T, d, f, K = w.batch, w.seq_len, w.d_model, w.d_ff, w.conv_k
+    L = args.segment
+    calls = [(p, min(L, T - p)) for p in range(0, T, L)]
+    if args.segment_calls:
+        calls = calls[:args.segment_calls]
+    closing = calls[-1][0] + calls[-1][1] == T
+    descs = {n: tm.make_desc(B, n, d, f, w.chunk, K, w.eta, w.dtype, args.mode, init_from_w0=1,
+                             target=args.target) for n in {n for _, n in calls}}
+    ws = torch.empty(tm.ttt_mlp_stream_workspace_size(descs[calls[0][1]], args.max_group),
+                     dtype=torch.uint8, device="cuda")
+    carry = torch.empty(tm.ttt_mlp_carry_size(descs[calls[0][1]]), dtype=torch.uint8,
+                        device="cuda")
+    segs = [(dev["H"][:, p:p + n].contiguous(), dev["X0"][:, p:p + n].contiguous())
+            for p, n in calls]
+    O = torch.empty((B, L, d), dtype=dev["H"].dtype, device="cuda")
+    W = torch.empty((B, d, f), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for i, ((p, n), (h, x0)) in enumerate(zip(calls, segs)):
+            last = 1 if closing and i == len(calls) - 1 else 0
+            tm.ttt_mlp_forward_stream(descs[n], p, last, h, x0, dev["W_gate"], dev["W_up"],
+                                      dev["W_down0"], dev["taps"], dev["W_target"], O, W, carry,
+                                      ws, stream=stream)
+
+    log(f"[bench] streaming {len(calls)} calls of {L} tokens, warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    tokens = B * sum(n for _, n in calls)
+    value = tokens / (ms_step / 1e3)
+    log(f"[bench] {ms_step:.3f} ms/step, {value / 1e6:.4f} M tokens/s, "
+        f"{ms_step * 1e3 / len(calls):.1f} us per call")
+    out = {
+        "metric": "TTT-MLP layer tokens/sec, streamed in segments",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "seq_len": T, "chunk": w.chunk,
+                   "d_model": d, "d_ff": f, "conv_k": K, "eta": w.eta, "mode": args.mode,
+                   "target": args.target, "segment": L, "calls": len(calls),
+                   "closing": closing},
+        "us_per_call": ms_step * 1e3 / len(calls),
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,6 +278,11 @@ def main() -> int:
     ap.add_argument("--target", default="conv_proj", choices=["conv_proj", "proj", "conv", "embed"],
                     help="fast-weight target (the variants of the ablation table)")
     ap.add_argument("--max-group", type=int, default=0, help="chunks per group (0 = all)")
+    ap.add_argument("--chunk", type=int, default=0, help="chunk size C (0 = the workload's)")
+    ap.add_argument("--segment", type=int, default=0, metavar="L",
+                    help="stream the sequences in calls of L tokens (0 = one call)")
+    ap.add_argument("--segment-calls", type=int, default=0, metavar="N",
+                    help="with --segment: time only the first N calls of each step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
@@ -243,6 +316,10 @@ def main() -> int:
     from chunk_wise_weight_chunked_amd import ttt_mlp as tm
 
     w = synth.WORKLOADS[args.workload]
+    default_config = (args.chunk in (0, w.chunk) and args.mode == "auto"
+                      and args.target == "conv_proj" and args.max_group == 0)
+    if args.chunk:
+        w = dataclasses.replace(w, chunk=args.chunk)
     if not torch.cuda.is_available():
         log("no GPU available")
         return 1
@@ -253,6 +330,8 @@ def main() -> int:
     B, T, d, f, K = w.batch, w.seq_len, w.d_model, w.d_ff, w.conv_k
     desc = tm.make_desc(B, T, d, f, w.chunk, K, w.eta, w.dtype, args.mode, init_from_w0=1,
                         target=args.target)
+    if args.segment:
+        return stream_bench(args, w, dev, inp)
     ws = tm.alloc_workspace(desc, args.max_group)
     group = tm.ttt_mlp_group_size(desc, ws.numel())
     O = torch.empty_like(dev["H"])
@@ -308,7 +387,7 @@ def main() -> int:
     ach = per_stage[dom]["tflops"]
     roofline = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": peak,
                 "unit": "TFLOP/s", "frac": ach / peak,
-                "traffic": traffic_for(dom, w.name),
+                "traffic": traffic_for(dom, w.name) if default_config else None,
                 "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "flops_per_launch": work[dom],
                 "algorithmic_bytes_per_launch": stage_bytes(w, group)[dom],

@@ -289,6 +289,57 @@ ttt_status_t check_buffers(const ttt::Dims& dm, const Buffers& b, bool need_w0) 
 
 }  // namespace
 
+// ---------------------------------------------------------------- streaming
+namespace {
+
+// Pending tokens a session carries into a call at stream position pos: the
+// tokens of the chunk holding token pos - 1 (its update waits for the next
+// token's X0, the look-ahead of the last target).
+int64_t pending_tokens(int64_t pos, int64_t C) { return pos == 0 ? 0 : pos - (pos - 1) / C * C; }
+
+size_t carry_bytes(const ttt::Dims& dm, int64_t C) {
+  return (size_t)dm.B * (size_t)(2 * C + ttt::kHaloRows) * dm.d * ttt::dtype_bytes(dm.dt);
+}
+
+// A streaming call's workspace: the layer's workspace for the virtual
+// sequences (sized for the longest, L + C rows), then Hv and X0v
+// [B][L + C][d], then the carry being built.
+struct StreamPlan {
+  size_t layer_bytes, hv_off, x0v_off, tmp_off, total;
+};
+
+ttt_status_t plan_stream(const ttt_mlp_desc_t* desc, int64_t max_group, size_t ws_bytes,
+                         StreamPlan* sp) {
+  ttt_mlp_desc_t q = *desc;
+  q.seq_len = desc->seq_len + desc->chunk;
+  ttt::Dims dmax;
+  ttt_status_t st = make_dims(&q, &dmax);
+  if (st) return st;
+  const size_t es = ttt::dtype_bytes(dmax.dt);
+  auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t rows = a256((size_t)(dmax.B * dmax.T) * dmax.d * es);
+  // bytes after the layer's part (which is a multiple of 256)
+  const size_t extra = 2 * rows + carry_bytes(dmax, desc->chunk);
+  if (ws_bytes == 0) {  // size for groups of up to max_group chunks
+    const int64_t g =
+        max_group == 0 ? mode_group(dmax, desc->mode) : std::min<int64_t>(max_group, dmax.N);
+    sp->layer_bytes = ttt::plan_workspace(dmax, g).total_bytes;
+  } else {  // what a given workspace leaves for the layer
+    const size_t minimum = ttt::plan_workspace(dmax, 1).total_bytes + extra;
+    if (ws_bytes < minimum)
+      return fail(TTT_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is below the minimum %zu",
+                  ws_bytes, minimum);
+    sp->layer_bytes = (ws_bytes - extra) / 256 * 256;
+  }
+  sp->hv_off = sp->layer_bytes;
+  sp->x0v_off = sp->hv_off + rows;
+  sp->tmp_off = sp->x0v_off + rows;
+  sp->total = sp->tmp_off + carry_bytes(dmax, desc->chunk);
+  return TTT_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t ttt_mlp_workspace_size(const ttt_mlp_desc_t* desc, int64_t max_group) {
@@ -348,6 +399,98 @@ ttt_status_t ttt_mlp_forward_batched(const ttt_mlp_desc_t* desc, const void* H, 
   if (st) return st;
   return run_layer(dm, desc->mode, init, H, X0, W_gate, W_up, W_down0, conv_taps, W_target, O,
                    W_state, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t ttt_mlp_carry_size(const ttt_mlp_desc_t* desc) {
+  ttt::Dims dm;
+  if (make_dims(desc, &dm)) return 0;
+  ok();
+  return carry_bytes(dm, desc->chunk);
+}
+
+size_t ttt_mlp_stream_workspace_size(const ttt_mlp_desc_t* desc, int64_t max_group) {
+  ttt::Dims dm;
+  if (make_dims(desc, &dm)) return 0;
+  if (max_group < 0) {
+    fail(TTT_ERR_INVALID_ARGUMENT, "max_group must be >= 0");
+    return 0;
+  }
+  StreamPlan sp;
+  if (plan_stream(desc, max_group, 0, &sp)) return 0;
+  ok();
+  return sp.total;
+}
+
+ttt_status_t ttt_mlp_forward_stream(const ttt_mlp_desc_t* desc, int64_t pos, int32_t last,
+                                    const void* H, const void* X0, const void* W_gate,
+                                    const void* W_up, const void* W_down0, const void* conv_taps,
+                                    const void* W_target, void* O, float* W_state, void* carry,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  ttt::Dims du;  // the call's own L tokens (user buffers)
+  ttt_status_t st = make_dims(desc, &du);
+  if (st) return st;
+  if (pos < 0) return fail(TTT_ERR_INVALID_ARGUMENT, "pos must be >= 0 (got %lld)", (long long)pos);
+  if (last != 0 && last != 1) return fail(TTT_ERR_INVALID_ARGUMENT, "last must be 0 or 1");
+  const bool need_carry = pos > 0 || last == 0;
+  if (need_carry && !carry) return fail(TTT_ERR_INVALID_ARGUMENT, "carry is NULL");
+  if (need_carry && !aligned(carry, 16))
+    return fail(TTT_ERR_INVALID_ARGUMENT, "carry is not 16-byte aligned");
+  const bool init = desc->init_from_w0 == 1 && pos == 0;
+  const Buffers b{H, X0, W_gate, W_up, W_down0, conv_taps, W_target, O, W_state, ws, ws_bytes};
+  st = check_buffers(du, b, init);
+  if (st) return st;
+  if (need_carry) {
+    const Range c = range("carry", carry, carry_bytes(du, desc->chunk));
+    const Range others[] = {range("H", H, (size_t)(du.B * du.T) * du.d * ttt::dtype_bytes(du.dt)),
+                            range("X0", X0, (size_t)(du.B * du.T) * du.d * ttt::dtype_bytes(du.dt)),
+                            range("O", O, (size_t)(du.B * du.T) * du.d * ttt::dtype_bytes(du.dt)),
+                            range("W_state", W_state, (size_t)du.B * du.d * du.f * sizeof(float)),
+                            range("ws", ws, ws_bytes)};
+    for (const Range& o : others)
+      if (overlaps(c, o)) return fail(TTT_ERR_INVALID_ARGUMENT, "carry overlaps %s", o.name);
+  }
+  StreamPlan sp;
+  st = plan_stream(desc, 0, ws_bytes, &sp);
+  if (st) return st;
+
+  const int64_t C = desc->chunk, L = du.T;
+  const int64_t n_pend = pending_tokens(pos, C);
+  ttt_mlp_desc_t vq = *desc;
+  vq.seq_len = n_pend + L;
+  ttt::Dims dv;
+  st = make_dims(&vq, &dv);
+  if (st) return st;
+  const size_t carry_seq = (size_t)(2 * C + ttt::kHaloRows) * dv.d;  // elements per session
+  char* base = static_cast<char*>(ws);
+  char* cb = static_cast<char*>(carry);
+  if (pos > 0) {
+    dv.halo = cb + (size_t)C * dv.d * ttt::dtype_bytes(dv.dt);
+    dv.halo_stride = (int64_t)carry_seq;
+  }
+  dv.skip_last = last == 0;
+  dv.out_skip = n_pend;
+  dv.out_T = L;
+  int64_t G;
+  st = plan_group(dv, desc->mode, sp.layer_bytes, &G);
+  if (st) return st;
+
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* Hv = base + sp.hv_off;
+  void* X0v = base + sp.x0v_off;
+  hipError_t e = ttt::launch_stream_build(dv, H, X0, carry, Hv, X0v, L, n_pend, C, s);
+  if (e != hipSuccess) return hip_fail(e, "stream_build");
+  st = run_layer(dv, desc->mode, init, Hv, X0v, W_gate, W_up, W_down0, conv_taps, W_target, O,
+                 W_state, ws, sp.layer_bytes, s);
+  if (st) return st;
+  if (last == 0) {
+    const int64_t c_new = (dv.T - 1) / C * C;
+    void* tmp = base + sp.tmp_off;
+    e = ttt::launch_stream_save(dv, Hv, X0v, pos > 0 ? carry : nullptr, tmp, c_new, C, s);
+    if (e != hipSuccess) return hip_fail(e, "stream_save");
+    e = hipMemcpyAsync(carry, tmp, carry_bytes(dv, C), hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "carry copy");
+  }
+  return ok();
 }
 
 ttt_status_t ttt_fastweight_state_reset(float* W_state, const void* W_down0, ttt_dtype_t w0_dtype,

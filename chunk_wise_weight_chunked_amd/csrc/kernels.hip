@@ -142,20 +142,22 @@ struct Stage {
     }
   }
 
-  // Row-major output: tile row t, column c goes to dst[t * ld + col_base + c]
-  // for t < rows_valid, c < ncols (a multiple of 8); 8 columns per store.
+  // Row-major output: tile row t, column c goes to
+  // dst[(dst_row0 + t) * ld + col_base + c] for rows_lo <= t < rows_valid,
+  // c < ncols (a multiple of 8); 8 columns per store.
   __device__ __forceinline__ static void flush_rows(const lds_char* lds, T* __restrict__ dst,
-                                                    int64_t ld, int64_t col_base, int ncols,
+                                                    int64_t dst_row0, int64_t ld,
+                                                    int64_t col_base, int ncols, int32_t rows_lo,
                                                     int32_t rows_valid) {
     constexpr int kRuns = kCols / 8;  // 8-column runs per row
     for (int it = threadIdx.x; it < kToks * kRuns; it += NTHREADS) {
       const int t = it / kRuns, c = (it % kRuns) * 8;
-      if (t >= rows_valid || c >= ncols) continue;
+      if (t < rows_lo || t >= rows_valid || c >= ncols) continue;
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         v[e] = Elem<T>::to_f32(lds_load<T>(lds + (c + e) * kStride + t * (int)sizeof(T)));
-      T* d = dst + (int64_t)t * ld + col_base + c;
+      T* d = dst + (dst_row0 + t) * ld + col_base + c;
       if constexpr (sizeof(T) == 2) {
         __builtin_nontemporal_store(u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                                             pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])},
@@ -261,7 +263,7 @@ TTT_GEMM_KERNEL void swiglu_kernel(Dims dm, const T* __restrict__ H, const T* __
     const int64_t cb = feat0 + kPass * h;
     const int ncols = (int)max<int64_t>(0, min<int64_t>(kPass, f - cb));
     St::flush_tokens(smem, Zt, f, cb, ncols, row0, BT, cm);
-    St::flush_rows(smem, Z + (int64_t)row0 * f, f, cb, ncols, min(BT - row0, S::BM));
+    St::flush_rows(smem, Z, row0, f, cb, ncols, 0, min(BT - row0, S::BM));
     __syncthreads();
   }
 }
@@ -319,7 +321,16 @@ __global__ __launch_bounds__(256) void conv_kernel(Dims dm, const T* __restrict_
 #pragma unroll
       for (int k = 0; k < KMAX; ++k) {
         const int64_t src = sq + 1 - k;  // X0 row of tap k, inside the sequence
-        if (k >= K || src < 0 || src >= T_seq) continue;
+        if (k >= K || src >= T_seq) continue;
+        if (src < 0) {  // before the sequence: zero, or the streaming halo
+          if (dm.halo == nullptr || src < -kHaloRows) continue;
+          const uint4 hv = *reinterpret_cast<const uint4*>(
+              static_cast<const T*>(dm.halo) + (o / T_seq) * dm.halo_stride +
+              (kHaloRows + src) * d + c * EPC);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) u[e] = fmaf(tp[k][e], chunk_value<T>(hv, e), u[e]);
+          continue;
+        }
 #pragma unroll
         for (int e = 0; e < EPC; ++e)
           u[e] = fmaf(tp[k][e], chunk_value<T>(win[jj + KMAX - 1 - k], e), u[e]);
@@ -500,11 +511,16 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
 
   write_slot(0);
   const int64_t kt_per_chunk = dm.Cp / TB;
-  const int64_t nk = gc * kt_per_chunk;
+  // a streaming call leaves the sequence's last chunk out of the state (its
+  // last token's target needs the next call's first token); its slot is
+  // still written
+  const bool skip = dm.skip_last && g0 + gc == dm.N;
+  const int64_t nk = (skip ? gc - 1 : gc) * kt_per_chunk;
   mainloop<T, S>(acc, la, lb, nk, smem, p, [&](int64_t kt) {
     const int64_t done = kt + 1;
     if (done % kt_per_chunk == 0 && done < nk) write_slot(done / kt_per_chunk);
   });
+  if (skip && gc > 1) write_slot(gc - 1);
 
 #pragma unroll
   for (int i = 0; i < S::MB; ++i)
@@ -568,16 +584,20 @@ __device__ __forceinline__ void down_proj_tile(const Dims& dm, const T* __restri
   mainloop<T, S>(acc, la, lb, ld / kRowBytes, smem, p, [](int64_t) {});
 
   // O through the stage, four passes of 64 columns, written row-major; rows
-  // beyond the chunk are skipped.
+  // beyond the chunk are skipped, and so are the first out_skip rows of each
+  // session (tokens a previous streaming call has already output).
   const int32_t rows_valid = (int32_t)min<int64_t>(S::BM, c_len - m0);
+  const int64_t srow = c_begin + m0;  // session row of tile row 0
+  const int32_t rows_lo = (int32_t)max<int64_t>(0, min<int64_t>(S::BM, dm.out_skip - srow));
+  const int64_t out_T = dm.out_T > 0 ? dm.out_T : T_seq;
 #pragma unroll
   for (int q = 0; q < S::BN / 64; ++q) {
     stage_cols64<T, S>(smem, acc, p, q, [](float x) { return x; });
     __syncthreads();
     const int64_t cbase = n0 + 64 * q;
-    Stage<T, S::kThreads>::flush_rows(smem, O + row0 * d, d, cbase,
+    Stage<T, S::kThreads>::flush_rows(smem, O, b * out_T + srow - dm.out_skip, d, cbase,
                                       (int)max<int64_t>(0, min<int64_t>(64, d - cbase)),
-                                      rows_valid);
+                                      rows_lo, rows_valid);
     __syncthreads();
   }
 }
@@ -684,6 +704,71 @@ __global__ void pad_fill_kernel(T* __restrict__ zt, T* __restrict__ vt, Dims dm)
       Elem<T>::store(zt + kblock_index<T>(row, col, dm.f), 0.0f);
     else
       Elem<T>::store(vt + kblock_index<T>(row - dm.f, col, dm.d), 0.0f);
+  }
+}
+
+// ========================================================= streaming calls
+// A streaming call runs the layer on a virtual sequence per session: the
+// carried rows of the pending chunk (n_pend tokens that an earlier call has
+// seen but whose chunk update is still open) followed by the call's L new
+// tokens.  Carry of a session (element offsets, e = element type):
+//   H rows   [C][d]            at 0
+//   X0 rows  [kHaloRows + C][d] at C * d: the kHaloRows rows before the
+//            pending chunk, then its rows
+// All copies move 16-byte chunks of rows.
+template <typename T>
+__global__ void stream_build_kernel(const T* __restrict__ H, const T* __restrict__ X0,
+                                    const T* __restrict__ carry, T* __restrict__ Hv,
+                                    T* __restrict__ X0v, int64_t B, int64_t L, int64_t n_pend,
+                                    int64_t C, int64_t d) {
+  constexpr int EPC = Elem<T>::kPerChunk;
+  const int64_t Tv = n_pend + L, cpr = d / EPC, per_seq = Tv * cpr;
+  const int64_t carry_seq = (C + kHaloRows + C) * d;
+  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < 2 * B * per_seq;
+       it += (int64_t)gridDim.x * blockDim.x) {
+    const bool x = it >= B * per_seq;  // second half: X0
+    const int64_t j = x ? it - B * per_seq : it;
+    const int64_t b = j / per_seq, r = j % per_seq / cpr, c = j % cpr * EPC;
+    const T* src;
+    if (r < n_pend)
+      src = carry + b * carry_seq + (x ? (C + kHaloRows + r) * d : r * d) + c;
+    else
+      src = (x ? X0 : H) + (b * L + r - n_pend) * d + c;
+    T* dst = (x ? X0v : Hv) + (b * Tv + r) * d + c;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  }
+}
+
+// The carry after a call, into `out` (a separate buffer: the halo of the new
+// pending chunk may come from the old carry).  Pending chunk = virtual rows
+// [c_new, Tv); its halo = virtual rows [c_new - kHaloRows, c_new), read from
+// X0v, or before the virtual start from the old carry's halo (zeros at the
+// stream's start: `old` is null there).
+template <typename T>
+__global__ void stream_save_kernel(const T* __restrict__ Hv, const T* __restrict__ X0v,
+                                   const T* __restrict__ old, T* __restrict__ out, int64_t B,
+                                   int64_t Tv, int64_t c_new, int64_t C, int64_t d) {
+  constexpr int EPC = Elem<T>::kPerChunk;
+  const int64_t cpr = d / EPC, n_new = Tv - c_new;
+  const int64_t rows = n_new + kHaloRows + n_new;  // H rows, then halo + X0 rows
+  const int64_t carry_seq = (C + kHaloRows + C) * d;
+  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < B * rows * cpr;
+       it += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = it / (rows * cpr), r = it % (rows * cpr) / cpr, c = it % cpr * EPC;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    T* dst;
+    if (r < n_new) {  // H row c_new + r
+      v = *reinterpret_cast<const uint4*>(Hv + (b * Tv + c_new + r) * d + c);
+      dst = out + b * carry_seq + r * d + c;
+    } else {  // X0 row j of the halo + pending block = virtual row c_new - kHaloRows + j
+      const int64_t j = r - n_new, vr = c_new - kHaloRows + j;
+      if (vr >= 0)
+        v = *reinterpret_cast<const uint4*>(X0v + (b * Tv + vr) * d + c);
+      else if (old != nullptr)
+        v = *reinterpret_cast<const uint4*>(old + b * carry_seq + (C + kHaloRows + vr) * d + c);
+      dst = out + b * carry_seq + (C + j) * d + c;
+    }
+    *reinterpret_cast<uint4*>(dst) = v;
   }
 }
 
@@ -866,6 +951,42 @@ hipError_t launch_scan_apply(const Dims& dm, const void* Vt, const void* Zt, flo
                                W_state, static_cast<float*>(scan_slots), g0, gc,
                                static_cast<const float*>(Z), static_cast<const float*>(apply_slots),
                                static_cast<float*>(O), a0, ac, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_build(const Dims& dv, const void* H, const void* X0, const void* carry,
+                               void* Hv, void* X0v, int64_t L, int64_t n_pend, int64_t C,
+                               hipStream_t s) {
+  const int64_t n = 2 * dv.B * dv.T * (dv.d / (16 / (int64_t)dtype_bytes(dv.dt)));
+  const dim3 g(grid_for(n, 256, 65536));
+  if (dv.dt == Dtype::BF16)
+    hipLaunchKernelGGL(stream_build_kernel<uint16_t>, g, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(H), static_cast<const uint16_t*>(X0),
+                       static_cast<const uint16_t*>(carry), static_cast<uint16_t*>(Hv),
+                       static_cast<uint16_t*>(X0v), dv.B, L, n_pend, C, dv.d);
+  else
+    hipLaunchKernelGGL(stream_build_kernel<float>, g, dim3(256), 0, s,
+                       static_cast<const float*>(H), static_cast<const float*>(X0),
+                       static_cast<const float*>(carry), static_cast<float*>(Hv),
+                       static_cast<float*>(X0v), dv.B, L, n_pend, C, dv.d);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_save(const Dims& dv, const void* Hv, const void* X0v, const void* old,
+                              void* out, int64_t c_new, int64_t C, hipStream_t s) {
+  const int64_t rows = 2 * (dv.T - c_new) + kHaloRows;
+  const int64_t n = dv.B * rows * (dv.d / (16 / (int64_t)dtype_bytes(dv.dt)));
+  const dim3 g(grid_for(n, 256, 65536));
+  if (dv.dt == Dtype::BF16)
+    hipLaunchKernelGGL(stream_save_kernel<uint16_t>, g, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(Hv), static_cast<const uint16_t*>(X0v),
+                       static_cast<const uint16_t*>(old), static_cast<uint16_t*>(out), dv.B,
+                       dv.T, c_new, C, dv.d);
+  else
+    hipLaunchKernelGGL(stream_save_kernel<float>, g, dim3(256), 0, s,
+                       static_cast<const float*>(Hv), static_cast<const float*>(X0v),
+                       static_cast<const float*>(old), static_cast<float*>(out), dv.B, dv.T,
+                       c_new, C, dv.d);
   return hipGetLastError();
 }
 

@@ -16,12 +16,22 @@ inline size_t dtype_bytes(Dtype t) { return t == Dtype::F32 ? 4 : 2; }
 //   Cp = C rounded up to 64 tokens: the chunk stride of the token-major
 //        layouts Zt and Vt, whose extra columns hold zeros;
 //   P  = B * N * Cp columns of Zt and Vt.
+// X0 rows a streaming call keeps before each session's first row (the conv
+// reaches back K - 2 <= 6 tokens).
+constexpr int kHaloRows = 6;
+
 struct Dims {
   int64_t B, T, d, f, C, N, Cp, P;
   int32_t K;
   float eta;
   Dtype dt;
   bool conv, proj;  // the target's conv and projection (both: the method)
+  // Streaming continuation (defaults give the one-shot layer):
+  const void* halo = nullptr;  // [B][halo_stride]: kHaloRows X0 rows before each session's row 0
+  int64_t halo_stride = 0;     // elements between sessions in `halo`
+  bool skip_last = false;      // leave the last chunk's update out of the state
+  int64_t out_skip = 0;        // rows [0, out_skip) of each session are not output ...
+  int64_t out_T = 0;           // ... and output row t goes to O row b * out_T + t - out_skip
 };
 
 // Workspace regions (byte offsets from the workspace base, 256-byte aligned).
@@ -62,5 +72,14 @@ hipError_t launch_scan_apply(const Dims& dm, const void* Vt, const void* Zt, flo
                              void* scan_slots, int64_t g0, int64_t gc, const void* Z,
                              const void* apply_slots, void* O, int64_t a0, int64_t ac,
                              hipStream_t s);
+
+// Streaming calls: the virtual sequences (carried pending rows + the call's L
+// new rows) into Hv / X0v, and the carry after the call (pending chunk from
+// virtual row c_new on, with its halo) into `out`.
+hipError_t launch_stream_build(const Dims& dv, const void* H, const void* X0, const void* carry,
+                               void* Hv, void* X0v, int64_t L, int64_t n_pend, int64_t C,
+                               hipStream_t s);
+hipError_t launch_stream_save(const Dims& dv, const void* Hv, const void* X0v, const void* old,
+                              void* out, int64_t c_new, int64_t C, hipStream_t s);
 
 }  // namespace ttt

@@ -61,6 +61,7 @@ EXPORTS = (
     "ttt_mlp_workspace_size", "ttt_mlp_group_size", "ttt_mlp_forward",
     "ttt_mlp_forward_batched", "ttt_fastweight_state_reset", "ttt_last_error",
     "ttt_profile_enable", "ttt_profile_read", "ttt_stage_name",
+    "ttt_mlp_carry_size", "ttt_mlp_stream_workspace_size", "ttt_mlp_forward_stream",
 )
 
 _lib = None
@@ -96,6 +97,12 @@ def load(path: str | None = None):
     lib.ttt_mlp_forward.restype = ctypes.c_int
     lib.ttt_mlp_forward_batched.argtypes = [dp] + [vp] * 9 + [vp, sz, vp]
     lib.ttt_mlp_forward_batched.restype = ctypes.c_int
+    lib.ttt_mlp_carry_size.argtypes = [dp]
+    lib.ttt_mlp_carry_size.restype = sz
+    lib.ttt_mlp_stream_workspace_size.argtypes = [dp, i64]
+    lib.ttt_mlp_stream_workspace_size.restype = sz
+    lib.ttt_mlp_forward_stream.argtypes = [dp, i64, ctypes.c_int32] + [vp] * 11 + [sz, vp]
+    lib.ttt_mlp_forward_stream.restype = ctypes.c_int
     lib.ttt_fastweight_state_reset.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp]
     lib.ttt_fastweight_state_reset.restype = ctypes.c_int
     lib.ttt_last_error.restype = ctypes.c_char_p
@@ -187,6 +194,30 @@ def ttt_mlp_forward_batched(desc, H, X0, W_gate, W_up, W_down0, conv_taps, W_tar
         _stream(stream)))
 
 
+def ttt_mlp_carry_size(desc: ttt_mlp_desc_t) -> int:
+    n = load().ttt_mlp_carry_size(ctypes.byref(desc))
+    if n == 0:
+        raise TTTError(TTT_ERR_INVALID_ARGUMENT, ttt_last_error())
+    return int(n)
+
+
+def ttt_mlp_stream_workspace_size(desc: ttt_mlp_desc_t, max_group: int = 0) -> int:
+    n = load().ttt_mlp_stream_workspace_size(ctypes.byref(desc), int(max_group))
+    if n == 0:
+        raise TTTError(TTT_ERR_INVALID_ARGUMENT, ttt_last_error())
+    return int(n)
+
+
+def ttt_mlp_forward_stream(desc, pos, last, H, X0, W_gate, W_up, W_down0, conv_taps, W_target,
+                           O, W_state, carry, ws, ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(load().ttt_mlp_forward_stream(
+        ctypes.byref(desc), int(pos), int(last), _ptr(H), _ptr(X0), _ptr(W_gate), _ptr(W_up),
+        _ptr(W_down0), _ptr(conv_taps), _ptr(W_target), _ptr(O), _ptr(W_state), _ptr(carry),
+        _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
 def ttt_fastweight_state_reset(W_state, W_down0, w0_dtype, batch, d_model, d_ff,
                                stream=None) -> None:
     if isinstance(w0_dtype, torch.dtype):
@@ -263,3 +294,44 @@ def forward_batched(H, X0, W_gate, W_up, W_down0, conv_taps, W_target, eta, chun
     ttt_mlp_forward_batched(desc, H, X0, W_gate, W_up, W_down0 if init else None, conv_taps,
                             W_target, O, W_state, ws, stream=stream)
     return O, W_state
+
+
+class Stream:
+    """B sessions fed over consecutive calls (ttt_mlp_forward_stream): owns the
+    fp32 states and the carry.  step(H, X0) takes the next [B][L][d] tokens and
+    returns their O; the call with last=True closes the streams, after which
+    `state` holds the final weights."""
+
+    def __init__(self, W_gate, W_up, W_down0, conv_taps, W_target, eta, chunk, batch,
+                 mode="auto", target="conv_proj", conv_k=None, device="cuda"):
+        self.w = (W_gate, W_up, W_down0, conv_taps, W_target)
+        self.eta, self.chunk, self.batch = float(eta), int(chunk), int(batch)
+        self.mode, self.target = mode, target
+        self.conv_k = _conv_k(conv_taps, conv_k)
+        d, f = W_gate.shape[1], W_gate.shape[0]
+        self.dtype = W_gate.dtype
+        self.state = torch.empty((self.batch, d, f), dtype=torch.float32, device=device)
+        desc = self._desc(1)
+        self.carry = torch.empty(ttt_mlp_carry_size(desc), dtype=torch.uint8, device=device)
+        self.pos = 0
+        self.closed = False
+
+    def _desc(self, L):
+        d, f = self.w[0].shape[1], self.w[0].shape[0]
+        return make_desc(self.batch, L, d, f, self.chunk, self.conv_k, self.eta, self.dtype,
+                         self.mode, init_from_w0=1, target=self.target)
+
+    def step(self, H, X0, last=False, stream=None):
+        if self.closed:
+            raise RuntimeError("stream already closed")
+        B, L, d = H.shape
+        desc = self._desc(L)
+        ws = torch.empty(ttt_mlp_stream_workspace_size(desc), dtype=torch.uint8, device=H.device)
+        O = torch.empty_like(H)
+        Wg, Wu, W0, taps, Wt = self.w
+        ttt_mlp_forward_stream(desc, self.pos, 1 if last else 0, H, X0, Wg, Wu, W0, taps, Wt, O,
+                               self.state, self.carry, ws, stream=stream)
+        self.pos += L
+        self.closed = bool(last)
+        return O
+

@@ -170,6 +170,46 @@ ttt_status_t ttt_fastweight_state_reset(float* W_state, const void* W_down0,
                                         ttt_dtype_t w0_dtype, int64_t batch, int64_t d_model,
                                         int64_t d_ff, void* stream);
 
+/* ---- Streaming continuation (serving) ----
+ * Feeds each of B sessions its tokens over consecutive calls, the way a
+ * server reads a long context piece by piece (the page's future-work item on
+ * streaming inference, section 9; per-session fast-weight buffers from the
+ * practitioner blog's serving notes, section 4).  Outputs and the final
+ * weight equal those of one ttt_mlp_forward_batched call over the
+ * concatenated tokens, bit for bit.
+ *
+ * The desc describes one call: seq_len = L >= 1 new tokens per session (the
+ * same L for all B sessions), chunk = the sessions' chunk size C.  A call at
+ * stream position pos (tokens each session has already fed) outputs the L
+ * tokens' O rows.  A chunk's update needs the target of its last token, which
+ * reads the next token's X0, so the chunk holding a call's last token stays
+ * pending: its H and X0 rows (and the few X0 rows before it that the conv
+ * reaches back to) go into the caller-owned carry, and the next call
+ * re-enters them before its own tokens.  W_state therefore holds the weight
+ * after every chunk before the pending one; a call with last = 1 closes the
+ * streams (the final chunk is applied with the zero padding of the sequence's
+ * end) and leaves the final weight.
+ *   pos       tokens the sessions have fed before this call (0: the start;
+ *             init_from_w0 = 1 then sets W_state from W_down0, otherwise
+ *             init_from_w0 is ignored)
+ *   last      1 for the closing call, else 0
+ *   carry     ttt_mlp_carry_size(desc) bytes of device memory, 16-byte
+ *             aligned, owned by the caller and kept between calls; read when
+ *             pos > 0, written when last = 0 (may be NULL if pos = 0 and
+ *             last = 1); its contents are opaque
+ *   ws        ttt_mlp_stream_workspace_size(desc, 0) bytes (the minimum is
+ *             ttt_mlp_stream_workspace_size(desc, 1))
+ * Each call costs the layer over the pending rows (at most C) plus the new
+ * ones; calls of one token at a time are supported (decoding) but repeat up
+ * to C rows each. */
+size_t ttt_mlp_carry_size(const ttt_mlp_desc_t* desc);
+size_t ttt_mlp_stream_workspace_size(const ttt_mlp_desc_t* desc, int64_t max_group);
+ttt_status_t ttt_mlp_forward_stream(const ttt_mlp_desc_t* desc, int64_t pos, int32_t last,
+                                    const void* H, const void* X0, const void* W_gate,
+                                    const void* W_up, const void* W_down0, const void* conv_taps,
+                                    const void* W_target, void* O, float* W_state, void* carry,
+                                    void* ws, size_t ws_bytes, void* stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char* ttt_last_error(void);
 

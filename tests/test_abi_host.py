@@ -263,3 +263,66 @@ def test_library_has_no_unresolved_internal_symbols():
     missing = [l.split()[-1] for l in out.splitlines() if "3ttt" in l]
     assert not missing, missing
 
+
+
+def stream_ptrs(d, ws_bytes):
+    p = fake_ptrs(d, ws_bytes=ws_bytes)
+    p["carry"] = p["ws"] + (ws_bytes + 4095) // 4096 * 4096 + 4096
+    return p
+
+
+def call_stream(lib, d, p, pos, last):
+    return lib.ttt_mlp_forward_stream(
+        ctypes.byref(d), pos, last, p["H"], p["X0"], p["W_gate"], p["W_up"], p["W_down0"],
+        p["taps"], p["W_target"], p["O"], p["W"], p["carry"], p["ws"], p["ws_bytes"], None)
+
+
+def test_stream_sizes():
+    # carry per session: C rows of H, then K - 1 + C rows of X0 (the conv halo
+    # holds up to 6 rows, K <= 7)
+    for dt, es in ((tm.TTT_BF16, 2), (tm.TTT_F32, 4)):
+        d = desc(batch=3, seq_len=100, chunk=64, dtype=dt)
+        assert tm.ttt_mlp_carry_size(d) == 3 * (2 * 64 + 6) * 256 * es
+    d = desc(batch=2, seq_len=300, chunk=128)
+    w1 = tm.ttt_mlp_stream_workspace_size(d, 1)
+    # the layer runs on sequences of up to L + C tokens
+    longest = desc(batch=2, seq_len=300 + 128, chunk=128)
+    rows = (2 * 428 * 256 * 2 + 255) // 256 * 256
+    assert w1 == tm.ttt_mlp_workspace_size(longest, 1) + 2 * rows + tm.ttt_mlp_carry_size(d)
+    assert tm.ttt_mlp_stream_workspace_size(d, 2) > w1
+    assert tm.ttt_mlp_stream_workspace_size(d, 0) >= w1
+    with pytest.raises(tm.TTTError, match="max_group"):
+        tm.ttt_mlp_stream_workspace_size(d, -1)
+    with pytest.raises(tm.TTTError, match="batch"):
+        tm.ttt_mlp_carry_size(desc(batch=0))
+
+
+def test_stream_validation(lib):
+    d = desc(batch=2, seq_len=300, chunk=128)
+    w1 = tm.ttt_mlp_stream_workspace_size(d, 1)
+    p = stream_ptrs(d, w1 - 256)
+    # the argument checks come first; a good call then stops at the workspace
+    assert call_stream(lib, d, p, 128, 0) == tm.TTT_ERR_WORKSPACE_TOO_SMALL
+    assert "minimum %d" % w1 in tm.ttt_last_error()
+    assert call_stream(lib, d, p, -1, 0) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert "pos" in tm.ttt_last_error()
+    assert call_stream(lib, d, p, 0, 2) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert "last" in tm.ttt_last_error()
+    q = dict(p, carry=None)
+    for pos, last in ((0, 0), (5, 1), (5, 0)):
+        assert call_stream(lib, d, q, pos, last) == tm.TTT_ERR_INVALID_ARGUMENT
+        assert "carry is NULL" in tm.ttt_last_error()
+    # a single closing call from the start needs no carry
+    assert call_stream(lib, d, q, 0, 1) == tm.TTT_ERR_WORKSPACE_TOO_SMALL
+    assert call_stream(lib, d, dict(p, carry=p["carry"] + 8), 5, 0) == \
+        tm.TTT_ERR_INVALID_ARGUMENT
+    assert "aligned" in tm.ttt_last_error()
+    for other in ("H", "X0", "O", "W", "ws"):
+        assert call_stream(lib, d, dict(p, carry=p[other] + 4096), 5, 0) == \
+            tm.TTT_ERR_INVALID_ARGUMENT
+        assert "carry overlaps" in tm.ttt_last_error()
+    # W_down0 is read only on the first call of a stream
+    d0 = desc(batch=2, seq_len=300, chunk=128)
+    assert call_stream(lib, d0, dict(p, W_down0=None), 0, 0) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert call_stream(lib, d0, dict(p, W_down0=None), 256, 0) == \
+        tm.TTT_ERR_WORKSPACE_TOO_SMALL

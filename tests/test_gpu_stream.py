@@ -1,0 +1,106 @@
+"""Streaming continuation on the GPU: sessions fed over consecutive calls give
+the outputs and final weights of one call over the whole sequence, bit for
+bit, and the oracle's to tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunk_wise_weight_chunked_amd import synth
+from chunk_wise_weight_chunked_amd import ttt_mlp as tm
+
+from _common import numpy_inputs, rel, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tm.load()
+
+
+CASES = [
+    # B, T, d, f, K, C, dtype, call lengths, target
+    (2, 700, 128, 192, 4, 128, torch.bfloat16, [700], "conv_proj"),
+    (2, 700, 128, 192, 4, 128, torch.bfloat16, [128, 572], "conv_proj"),
+    (2, 700, 128, 192, 4, 128, torch.bfloat16, [100, 300, 300], "conv_proj"),
+    (1, 300, 128, 256, 8, 4, torch.bfloat16, [3, 1, 50, 246], "conv_proj"),   # C < halo
+    (1, 64, 64, 128, 4, 16, torch.bfloat16, [1] * 64, "conv_proj"),           # decoding
+    (1, 200, 64, 64, 3, 1, torch.bfloat16, [7, 13, 180], "conv_proj"),        # C = 1
+    (2, 513, 192, 256, 5, 100, torch.float32, [200, 313], "conv_proj"),
+    (1, 300, 128, 192, 4, 64, torch.bfloat16, [50, 250], "conv"),
+    (1, 300, 128, 192, 4, 64, torch.bfloat16, [50, 250], "proj"),
+]
+
+
+def _id(c):
+    return f"B{c[0]}T{c[1]}C{c[5]}{str(c[6])[6:]}-{len(c[7])}calls-{c[8]}"
+
+
+@pytest.mark.parametrize("case", CASES, ids=_id)
+def test_stream_equals_one_call(case):
+    B, T, d, f, K, C, dtype, calls, target = case
+    assert sum(calls) == T
+    print(f"[stream] {_id(case)}", flush=True)
+    inp = synth.make_inputs(B, T, d, f, K, dtype, seed=91)
+    dev = to_device(inp)
+    eta = 2e-2
+    O1, W1 = tm.forward_batched(dev["H"], dev["X0"], dev["W_gate"], dev["W_up"], dev["W_down0"],
+                                dev["taps"], dev["W_target"], eta, C, target=target)
+    st = tm.Stream(dev["W_gate"], dev["W_up"], dev["W_down0"], dev["taps"], dev["W_target"], eta,
+                   C, B, target=target)
+    outs, p = [], 0
+    for i, L in enumerate(calls):
+        outs.append(st.step(dev["H"][:, p:p + L].contiguous(), dev["X0"][:, p:p + L].contiguous(),
+                            last=i == len(calls) - 1))
+        p += L
+    torch.cuda.synchronize()
+    Os = torch.cat(outs, dim=1)
+    assert torch.equal(Os, O1), (Os.float() - O1.float()).abs().max().item()
+    assert torch.equal(st.state, W1), (st.state - W1).abs().max().item()
+
+
+def test_stream_state_between_calls_matches_oracle():
+    """After a call that ends inside a chunk, the state is the weight after the
+    chunks before the pending one: the next call's outputs, made with it,
+    match the oracle on the whole sequence."""
+    B, T, d, f, K, C, dtype = 1, 400, 128, 192, 4, 64, torch.bfloat16
+    inp = synth.make_inputs(B, T, d, f, K, dtype, seed=92)
+    dev = to_device(inp)
+    eta = 2e-2
+    st = tm.Stream(dev["W_gate"], dev["W_up"], dev["W_down0"], dev["taps"], dev["W_target"], eta,
+                   C, B)
+    O_a = st.step(dev["H"][:, :150].contiguous(), dev["X0"][:, :150].contiguous())
+    O_b = st.step(dev["H"][:, 150:].contiguous(), dev["X0"][:, 150:].contiguous(), last=True)
+    torch.cuda.synchronize()
+    ni = numpy_inputs(inp)
+    Oo, Wo = oracle.forward(ni["H"], ni["X0"], ni["W_gate"], ni["W_up"], ni["W_down0"],
+                            ni["taps"], ni["W_target"], eta, C)
+    O = torch.cat([O_a, O_b], dim=1).float().cpu().numpy()
+    W0 = ni["W_down0"].astype(np.float64)
+    e_o, e_dw = rel(O, Oo), rel(st.state.cpu().numpy() - W0, Wo - W0)
+    print(f"  rel O {e_o:.3e}  dW {e_dw:.3e}", flush=True)
+    assert e_o <= 2e-2 and e_dw <= 2e-2
+
+
+def test_stream_rejects_bad_arguments():
+    B, T, d, f, K, C = 1, 64, 64, 128, 4, 16
+    inp = synth.make_inputs(B, T, d, f, K, torch.bfloat16, seed=93)
+    dev = to_device(inp)
+    desc = tm.make_desc(B, T, d, f, C, K, 1e-2, torch.bfloat16)
+    ws = torch.empty(tm.ttt_mlp_stream_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    carry = torch.zeros(tm.ttt_mlp_carry_size(desc), dtype=torch.uint8, device="cuda")
+    W = torch.empty((B, d, f), dtype=torch.float32, device="cuda")
+    O = torch.empty_like(dev["H"])
+    args = (dev["H"], dev["X0"], dev["W_gate"], dev["W_up"], dev["W_down0"], dev["taps"],
+            dev["W_target"], O, W)
+    for pos, last, c, word in ((-1, 0, carry, "pos"), (0, 2, carry, "last"),
+                               (16, 0, None, "carry")):
+        with pytest.raises(tm.TTTError) as e:
+            tm.ttt_mlp_forward_stream(desc, pos, last, *args, c, ws)
+        assert word in str(e.value)
+    with pytest.raises(tm.TTTError) as e:
+        tm.ttt_mlp_forward_stream(desc, 0, 0, *args, carry, ws, ws_bytes=1024)
+    assert e.value.status == tm.TTT_ERR_WORKSPACE_TOO_SMALL
