@@ -203,6 +203,23 @@ def calib_copy(nbytes: int, reps: int) -> None:
     log(f"copied {nbytes} bytes x {reps}")
 
 
+def decode_roofline(w, L: int, us_per_call: float):
+    """HBM roofline of decode-shaped streaming (bf16, L <= 16 rows per session,
+    B*L <= 64): a decode call reads W_gate and W_up once for all sessions and
+    each session's bf16 copy of its current weight once (2*f*d*2 + B*d*f*2
+    bytes; the rows themselves are negligible).  The time per call includes
+    the calls at chunk boundaries, which run the full layer."""
+    import torch
+    if w.dtype != torch.bfloat16 or L > 16 or w.batch * L > 64:
+        return None
+    d, f = w.d_model, w.d_ff
+    nbytes = 2.0 * f * d * 2 + w.batch * d * f * 2.0
+    gbs = nbytes / (us_per_call * 1e-6) / 1e9
+    return {"kernel": "decode_swiglu + decode_down", "bound": "hbm", "achieved": gbs,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "traffic": None, "algorithmic_bytes_per_call": nbytes}
+
+
 def stream_bench(args, w, dev, inp) -> int:
     """Tokens/s of the streaming entry point: each step feeds the B sequences
     from position 0 in calls of L tokens (the last call closes the streams
@@ -261,7 +278,7 @@ def stream_bench(args, w, dev, inp) -> int:
                    "target": args.target, "segment": L, "calls": len(calls),
                    "closing": closing},
         "us_per_call": ms_step * 1e3 / len(calls),
-        "roofline": None,
+        "roofline": decode_roofline(w, L, ms_step * 1e3 / len(calls)),
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(BUILD, "libttt_mlp.so")
-SOURCES = ["kernels.hip", "api.cpp"]
+SOURCES = ["kernels.hip", "decode.hip", "api.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

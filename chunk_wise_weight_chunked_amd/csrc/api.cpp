@@ -297,8 +297,28 @@ namespace {
 // token's X0, the look-ahead of the last target).
 int64_t pending_tokens(int64_t pos, int64_t C) { return pos == 0 ? 0 : pos - (pos - 1) / C * C; }
 
-size_t carry_bytes(const ttt::Dims& dm, int64_t C) {
+// The carry of a stream: per session C rows of H, then kHaloRows + C rows of
+// X0 (the halo before the pending chunk, then the chunk); for bf16 then, at a
+// 256-byte boundary, the sessions' current weights in bf16 [B][d][f] (read by
+// the decode kernels until the next update).
+size_t carry_rows_bytes(const ttt::Dims& dm, int64_t C) {
   return (size_t)dm.B * (size_t)(2 * C + ttt::kHaloRows) * dm.d * ttt::dtype_bytes(dm.dt);
+}
+size_t carry_wcur_offset(const ttt::Dims& dm, int64_t C) {
+  return (carry_rows_bytes(dm, C) + 255) & ~(size_t)255;
+}
+size_t carry_bytes(const ttt::Dims& dm, int64_t C) {
+  if (dm.dt != ttt::Dtype::BF16) return carry_rows_bytes(dm, C);
+  return carry_wcur_offset(dm, C) + (size_t)dm.B * dm.d * dm.f * 2;
+}
+
+// Calls the decode kernels serve: bf16, not closing the stream, at most 16
+// new rows per session and 64 in all, and no update due (the new rows stay in
+// the pending chunk, which is not complete before the call).
+constexpr int64_t kDecodeMaxRows = 16, kDecodeMaxTotal = 64;
+bool decode_call(const ttt::Dims& du, int64_t C, int64_t n_pend, int32_t last) {
+  return du.dt == ttt::Dtype::BF16 && last == 0 && du.T <= kDecodeMaxRows &&
+         du.B * du.T <= kDecodeMaxTotal && n_pend + du.T <= C;
 }
 
 // A streaming call's workspace: the layer's workspace for the virtual
@@ -319,7 +339,7 @@ ttt_status_t plan_stream(const ttt_mlp_desc_t* desc, int64_t max_group, size_t w
   auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t rows = a256((size_t)(dmax.B * dmax.T) * dmax.d * es);
   // bytes after the layer's part (which is a multiple of 256)
-  const size_t extra = 2 * rows + carry_bytes(dmax, desc->chunk);
+  const size_t extra = 2 * rows + carry_rows_bytes(dmax, desc->chunk);
   if (ws_bytes == 0) {  // size for groups of up to max_group chunks
     const int64_t g =
         max_group == 0 ? mode_group(dmax, desc->mode) : std::min<int64_t>(max_group, dmax.N);
@@ -334,7 +354,7 @@ ttt_status_t plan_stream(const ttt_mlp_desc_t* desc, int64_t max_group, size_t w
   sp->hv_off = sp->layer_bytes;
   sp->x0v_off = sp->hv_off + rows;
   sp->tmp_off = sp->x0v_off + rows;
-  sp->total = sp->tmp_off + carry_bytes(dmax, desc->chunk);
+  sp->total = sp->tmp_off + carry_rows_bytes(dmax, desc->chunk);
   return TTT_OK;
 }
 
@@ -455,6 +475,27 @@ ttt_status_t ttt_mlp_forward_stream(const ttt_mlp_desc_t* desc, int64_t pos, int
 
   const int64_t C = desc->chunk, L = du.T;
   const int64_t n_pend = pending_tokens(pos, C);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* cb = static_cast<char*>(carry);
+  const size_t es = ttt::dtype_bytes(du.dt);
+  if (decode_call(du, C, n_pend, last)) {
+    // The outputs of the new rows with the current weight; the rows join the
+    // pending chunk, whose update a later call makes.
+    void* wcur = cb + carry_wcur_offset(du, C);
+    hipError_t e = hipSuccess;
+    if (pos == 0) {
+      if (init) e = ttt::launch_state_reset(W_state, W_down0, du.dt, du.B, du.d, du.f, s);
+      if (e == hipSuccess) e = ttt::launch_state_to_bf16(W_state, wcur, du.B * du.d * du.f, s);
+      if (e != hipSuccess) return hip_fail(e, "decode state");
+    }
+    void* Zd = ws;  // [B·L][f]
+    e = ttt::launch_decode_swiglu(H, du.B * L, W_gate, W_up, Zd, du.d, du.f, X0, carry, du.B, L,
+                                  n_pend, C, pos == 0, s);
+    if (e == hipSuccess) e = ttt::launch_decode_down(Zd, wcur, O, du.B, L, du.d, du.f, s);
+    if (e != hipSuccess) return hip_fail(e, "decode");
+    return ok();
+  }
+
   ttt_mlp_desc_t vq = *desc;
   vq.seq_len = n_pend + L;
   ttt::Dims dv;
@@ -462,7 +503,6 @@ ttt_status_t ttt_mlp_forward_stream(const ttt_mlp_desc_t* desc, int64_t pos, int
   if (st) return st;
   const size_t carry_seq = (size_t)(2 * C + ttt::kHaloRows) * dv.d;  // elements per session
   char* base = static_cast<char*>(ws);
-  char* cb = static_cast<char*>(carry);
   if (pos > 0) {
     dv.halo = cb + (size_t)C * dv.d * ttt::dtype_bytes(dv.dt);
     dv.halo_stride = (int64_t)carry_seq;
@@ -474,7 +514,6 @@ ttt_status_t ttt_mlp_forward_stream(const ttt_mlp_desc_t* desc, int64_t pos, int
   st = plan_group(dv, desc->mode, sp.layer_bytes, &G);
   if (st) return st;
 
-  const hipStream_t s = static_cast<hipStream_t>(stream);
   void* Hv = base + sp.hv_off;
   void* X0v = base + sp.x0v_off;
   hipError_t e = ttt::launch_stream_build(dv, H, X0, carry, Hv, X0v, L, n_pend, C, s);
@@ -487,8 +526,12 @@ ttt_status_t ttt_mlp_forward_stream(const ttt_mlp_desc_t* desc, int64_t pos, int
     void* tmp = base + sp.tmp_off;
     e = ttt::launch_stream_save(dv, Hv, X0v, pos > 0 ? carry : nullptr, tmp, c_new, C, s);
     if (e != hipSuccess) return hip_fail(e, "stream_save");
-    e = hipMemcpyAsync(carry, tmp, carry_bytes(dv, C), hipMemcpyDeviceToDevice, s);
+    e = hipMemcpyAsync(carry, tmp, carry_rows_bytes(dv, C), hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "carry copy");
+    if (dv.dt == ttt::Dtype::BF16) {
+      e = ttt::launch_state_to_bf16(W_state, cb + carry_wcur_offset(dv, C), dv.B * dv.d * dv.f, s);
+      if (e != hipSuccess) return hip_fail(e, "carry weight");
+    }
   }
   return ok();
 }

@@ -174,9 +174,10 @@ ttt_status_t ttt_fastweight_state_reset(float* W_state, const void* W_down0,
  * Feeds each of B sessions its tokens over consecutive calls, the way a
  * server reads a long context piece by piece (the page's future-work item on
  * streaming inference, section 9; per-session fast-weight buffers from the
- * practitioner blog's serving notes, section 4).  Outputs and the final
- * weight equal those of one ttt_mlp_forward_batched call over the
- * concatenated tokens, bit for bit.
+ * practitioner blog's serving notes, section 4).  The final weight equals
+ * that of one ttt_mlp_forward_batched call over the concatenated tokens bit
+ * for bit, and so do the outputs, except those of decode calls (below), which
+ * agree to rounding.
  *
  * The desc describes one call: seq_len = L >= 1 new tokens per session (the
  * same L for all B sessions), chunk = the sessions' chunk size C.  A call at
@@ -196,12 +197,19 @@ ttt_status_t ttt_fastweight_state_reset(float* W_state, const void* W_down0,
  *   carry     ttt_mlp_carry_size(desc) bytes of device memory, 16-byte
  *             aligned, owned by the caller and kept between calls; read when
  *             pos > 0, written when last = 0 (may be NULL if pos = 0 and
- *             last = 1); its contents are opaque
+ *             last = 1); its contents are opaque.  For bf16 it also holds a
+ *             bf16 copy of every session's current weight (B*d_model*d_ff*2
+ *             bytes), so W_state must not be changed between the calls of a
+ *             stream.
  *   ws        ttt_mlp_stream_workspace_size(desc, 0) bytes (the minimum is
  *             ttt_mlp_stream_workspace_size(desc, 1))
- * Each call costs the layer over the pending rows (at most C) plus the new
- * ones; calls of one token at a time are supported (decoding) but repeat up
- * to C rows each. */
+ * A call costs the layer over the pending rows (at most C) plus the new ones,
+ * except a decode call: bf16, last = 0, L <= 16 and B*L <= 64, with the new
+ * rows staying inside the pending chunk (pos = 0 and L <= C, or fewer than C
+ * tokens pending and pending + L <= C).  A decode call computes only the new
+ * rows' outputs with the current weight (reading W_gate, W_up and the weight
+ * copy once) and appends the rows to the carry; the pending chunk's update
+ * comes with the first call that goes past it. */
 size_t ttt_mlp_carry_size(const ttt_mlp_desc_t* desc);
 size_t ttt_mlp_stream_workspace_size(const ttt_mlp_desc_t* desc, int64_t max_group);
 ttt_status_t ttt_mlp_forward_stream(const ttt_mlp_desc_t* desc, int64_t pos, int32_t last,

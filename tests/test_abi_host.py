@@ -278,17 +278,21 @@ def call_stream(lib, d, p, pos, last):
 
 
 def test_stream_sizes():
-    # carry per session: C rows of H, then K - 1 + C rows of X0 (the conv halo
-    # holds up to 6 rows, K <= 7)
-    for dt, es in ((tm.TTT_BF16, 2), (tm.TTT_F32, 4)):
-        d = desc(batch=3, seq_len=100, chunk=64, dtype=dt)
-        assert tm.ttt_mlp_carry_size(d) == 3 * (2 * 64 + 6) * 256 * es
+    # carry per session: C rows of H, then 6 + C rows of X0 (the conv halo
+    # holds up to K - 2 <= 6 rows); for bf16 then the bf16 copies of the
+    # sessions' current weights at a 256-byte boundary
+    rows = 3 * (2 * 64 + 6) * 256
+    assert tm.ttt_mlp_carry_size(desc(batch=3, seq_len=100, chunk=64, dtype=tm.TTT_F32)) == \
+        rows * 4
+    assert tm.ttt_mlp_carry_size(desc(batch=3, seq_len=100, chunk=64)) == \
+        (rows * 2 + 255) // 256 * 256 + 3 * 256 * 512 * 2
     d = desc(batch=2, seq_len=300, chunk=128)
     w1 = tm.ttt_mlp_stream_workspace_size(d, 1)
     # the layer runs on sequences of up to L + C tokens
     longest = desc(batch=2, seq_len=300 + 128, chunk=128)
     rows = (2 * 428 * 256 * 2 + 255) // 256 * 256
-    assert w1 == tm.ttt_mlp_workspace_size(longest, 1) + 2 * rows + tm.ttt_mlp_carry_size(d)
+    carry_rows = 2 * (2 * 128 + 6) * 256 * 2  # the new carry's rows, built before the copy
+    assert w1 == tm.ttt_mlp_workspace_size(longest, 1) + 2 * rows + carry_rows
     assert tm.ttt_mlp_stream_workspace_size(d, 2) > w1
     assert tm.ttt_mlp_stream_workspace_size(d, 0) >= w1
     with pytest.raises(tm.TTTError, match="max_group"):

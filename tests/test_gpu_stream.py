@@ -1,6 +1,7 @@
 """Streaming continuation on the GPU: sessions fed over consecutive calls give
-the outputs and final weights of one call over the whole sequence, bit for
-bit, and the oracle's to tolerance."""
+the final weights of one call over the whole sequence bit for bit, and its
+outputs bit for bit except for the rows of decode calls (a few rows that do
+not complete a chunk: computed by the decode kernels, equal to rounding)."""
 import numpy as np
 import pytest
 import torch
@@ -21,6 +22,15 @@ def _gpu():
     tm.load()
 
 
+def decode_call(B, L, pos, C, last, dtype):
+    """Which calls the library serves with its decode kernels: bf16, not the
+    closing call, at most 16 new rows per session and 64 in all, and the new
+    rows stay inside the pending chunk."""
+    n_pend = 0 if pos == 0 else pos - (pos - 1) // C * C
+    return (dtype == torch.bfloat16 and not last and L <= 16 and B * L <= 64
+            and n_pend + L <= C)
+
+
 CASES = [
     # B, T, d, f, K, C, dtype, call lengths, target
     (2, 700, 128, 192, 4, 128, torch.bfloat16, [700], "conv_proj"),
@@ -32,6 +42,11 @@ CASES = [
     (2, 513, 192, 256, 5, 100, torch.float32, [200, 313], "conv_proj"),
     (1, 300, 128, 192, 4, 64, torch.bfloat16, [50, 250], "conv"),
     (1, 300, 128, 192, 4, 64, torch.bfloat16, [50, 250], "proj"),
+    # decode calls: one group of 16 tokens (B*L = 64), two groups (21), mixed
+    (4, 200, 128, 256, 4, 64, torch.bfloat16, [16, 16, 16, 15, 1, 1, 135], "conv_proj"),
+    (3, 150, 192, 320, 4, 32, torch.bfloat16, [7, 7, 7, 11, 1, 16, 101], "conv_proj"),
+    (2, 90, 256, 512, 8, 16, torch.bfloat16, [1] * 40 + [50], "conv"),
+    (1, 120, 128, 192, 4, 128, torch.bfloat16, [16] * 7 + [8], "embed"),
 ]
 
 
@@ -52,14 +67,25 @@ def test_stream_equals_one_call(case):
     st = tm.Stream(dev["W_gate"], dev["W_up"], dev["W_down0"], dev["taps"], dev["W_target"], eta,
                    C, B, target=target)
     outs, p = [], 0
+    dec = torch.zeros(T, dtype=torch.bool)
     for i, L in enumerate(calls):
+        last = i == len(calls) - 1
+        dec[p:p + L] = decode_call(B, L, p, C, last, dtype)
         outs.append(st.step(dev["H"][:, p:p + L].contiguous(), dev["X0"][:, p:p + L].contiguous(),
-                            last=i == len(calls) - 1))
+                            last=last))
         p += L
     torch.cuda.synchronize()
     Os = torch.cat(outs, dim=1)
-    assert torch.equal(Os, O1), (Os.float() - O1.float()).abs().max().item()
     assert torch.equal(st.state, W1), (st.state - W1).abs().max().item()
+    rows = ~dec.cuda()
+    assert torch.equal(Os[:, rows], O1[:, rows]), \
+        (Os[:, rows].float() - O1[:, rows].float()).abs().max().item()
+    if dec.any():
+        a = Os[:, dec.cuda()].double().cpu().numpy()
+        b = O1[:, dec.cuda()].double().cpu().numpy()
+        e = rel(a, b)
+        print(f"  {int(dec.sum())} decode rows: rel to one call {e:.3e}", flush=True)
+        assert e <= 1e-2
 
 
 def test_stream_state_between_calls_matches_oracle():
@@ -81,6 +107,30 @@ def test_stream_state_between_calls_matches_oracle():
     O = torch.cat([O_a, O_b], dim=1).float().cpu().numpy()
     W0 = ni["W_down0"].astype(np.float64)
     e_o, e_dw = rel(O, Oo), rel(st.state.cpu().numpy() - W0, Wo - W0)
+    print(f"  rel O {e_o:.3e}  dW {e_dw:.3e}", flush=True)
+    assert e_o <= 2e-2 and e_dw <= 2e-2
+
+
+def test_decode_at_model_size_matches_oracle():
+    """Token-by-token decoding at the Qwen3-4B MLP shape (d = 2560, f = 9728)
+    for two sessions over 40 tokens with C = 16: the decode kernels' outputs
+    and the updates made at the chunk boundaries against the oracle."""
+    B, T, d, f, K, C, dtype = 2, 40, 2560, 9728, 4, 16, torch.bfloat16
+    inp = synth.make_inputs(B, T, d, f, K, dtype, seed=94)
+    dev = to_device(inp)
+    eta = 1e-3
+    st = tm.Stream(dev["W_gate"], dev["W_up"], dev["W_down0"], dev["taps"], dev["W_target"], eta,
+                   C, B)
+    outs = [st.step(dev["H"][:, t:t + 1].contiguous(), dev["X0"][:, t:t + 1].contiguous(),
+                    last=t == T - 1) for t in range(T)]
+    torch.cuda.synchronize()
+    O = torch.cat(outs, dim=1).double().cpu().numpy()
+    ni = numpy_inputs(inp)
+    Oo, Wo = oracle.forward(ni["H"], ni["X0"], ni["W_gate"], ni["W_up"], ni["W_down0"],
+                            ni["taps"], ni["W_target"], eta, C)
+    W0 = ni["W_down0"].astype(np.float64)
+    e_o = rel(O, Oo)
+    e_dw = rel(st.state.cpu().numpy() - W0[None], Wo - W0[None])
     print(f"  rel O {e_o:.3e}  dW {e_dw:.3e}", flush=True)
     assert e_o <= 2e-2 and e_dw <= 2e-2
 
