@@ -166,7 +166,7 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, cfetch_csv: str
     return out
 
 
-def cpu_baseline(w, inp, target: str = "conv_proj") -> dict:
+def cpu_baseline(w, inp, target: str = "conv_proj", align: str = "next") -> dict:
     """The oracle as it stands, sequential form, on the first chunk(s) of
     sequence 0 (a causal prefix of the same workload)."""
     import oracle
@@ -184,7 +184,8 @@ def cpu_baseline(w, inp, target: str = "conv_proj") -> dict:
           for k in ("H", "X0", "W_gate", "W_up", "W_down0", "taps", "W_target")}
     t0 = time.perf_counter()
     oracle.forward(ni["H"], ni["X0"], ni["W_gate"], ni["W_up"], ni["W_down0"], ni["taps"],
-                   ni["W_target"], w.eta, w.chunk, form="sequential", target=target)
+                   ni["W_target"], w.eta, w.chunk, form="sequential", target=target,
+                   align=align)
     dt = time.perf_counter() - t0
     return {"value": m / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"sequential fp64 oracle on the first {chunks} chunk(s) ({m} tokens) of "
@@ -234,7 +235,8 @@ def stream_bench(args, w, dev, inp) -> int:
         calls = calls[:args.segment_calls]
     closing = calls[-1][0] + calls[-1][1] == T
     descs = {n: tm.make_desc(B, n, d, f, w.chunk, K, w.eta, w.dtype, args.mode, init_from_w0=1,
-                             target=args.target) for n in {n for _, n in calls}}
+                             target=args.target, align=args.align)
+             for n in {n for _, n in calls}}
     ws = torch.empty(tm.ttt_mlp_stream_workspace_size(descs[calls[0][1]], args.max_group),
                      dtype=torch.uint8, device="cuda")
     carry = torch.empty(tm.ttt_mlp_carry_size(descs[calls[0][1]]), dtype=torch.uint8,
@@ -275,7 +277,8 @@ def stream_bench(args, w, dev, inp) -> int:
         "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "seq_len": T, "chunk": w.chunk,
                    "d_model": d, "d_ff": f, "conv_k": K, "eta": w.eta, "mode": args.mode,
-                   "target": args.target, "segment": L, "calls": len(calls),
+                   "target": args.target, "align": args.align, "segment": L,
+                   "calls": len(calls),
                    "closing": closing},
         "us_per_call": ms_step * 1e3 / len(calls),
         "roofline": decode_roofline(w, L, ms_step * 1e3 / len(calls)),
@@ -294,6 +297,9 @@ def main() -> int:
     ap.add_argument("--mode", default="auto", choices=["auto", "sequential", "chunk_parallel"])
     ap.add_argument("--target", default="conv_proj", choices=["conv_proj", "proj", "conv", "embed"],
                     help="fast-weight target (the variants of the ablation table)")
+    ap.add_argument("--align", default="next", choices=["next", "self"],
+                    help="conv window ends at the next token (the method) or at the token "
+                         "itself (the reconstruction alignment)")
     ap.add_argument("--max-group", type=int, default=0, help="chunks per group (0 = all)")
     ap.add_argument("--chunk", type=int, default=0, help="chunk size C (0 = the workload's)")
     ap.add_argument("--segment", type=int, default=0, metavar="L",
@@ -334,7 +340,8 @@ def main() -> int:
 
     w = synth.WORKLOADS[args.workload]
     default_config = (args.chunk in (0, w.chunk) and args.mode == "auto"
-                      and args.target == "conv_proj" and args.max_group == 0)
+                      and args.target == "conv_proj" and args.align == "next"
+                      and args.max_group == 0)
     if args.chunk:
         w = dataclasses.replace(w, chunk=args.chunk)
     if not torch.cuda.is_available():
@@ -346,7 +353,7 @@ def main() -> int:
     dev = {k: v.cuda() for k, v in inp.items()}
     B, T, d, f, K = w.batch, w.seq_len, w.d_model, w.d_ff, w.conv_k
     desc = tm.make_desc(B, T, d, f, w.chunk, K, w.eta, w.dtype, args.mode, init_from_w0=1,
-                        target=args.target)
+                        target=args.target, align=args.align)
     if args.segment:
         return stream_bench(args, w, dev, inp)
     ws = tm.alloc_workspace(desc, args.max_group)
@@ -415,7 +422,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle) ...")
-        cpu = cpu_baseline(w, inp, args.target)
+        cpu = cpu_baseline(w, inp, args.target, args.align)
         log(f"[bench] oracle: {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
 
     out = {
@@ -433,7 +440,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "seq_len": T, "chunk": w.chunk,
                    "d_model": d, "d_ff": f, "conv_k": K, "eta": w.eta, "mode": args.mode,
-                   "group": group, "state": "fp32", "target": args.target},
+                   "group": group, "state": "fp32", "target": args.target,
+                   "align": args.align},
         "layer_mfma_frac": layer_frac,
         "roofline": roofline,
         "stages": per_stage,

@@ -132,6 +132,8 @@ ttt_status_t make_dims(const ttt_mlp_desc_t* desc, ttt::Dims* dm) {
     return fail(TTT_ERR_INVALID_ARGUMENT, "init_from_w0 must be 0 or 1");
   if (q.target < TTT_TARGET_CONV_PROJ || q.target > TTT_TARGET_EMBED)
     return fail(TTT_ERR_INVALID_ARGUMENT, "unknown target %d", (int)q.target);
+  if (q.align != TTT_ALIGN_NEXT && q.align != TTT_ALIGN_SELF)
+    return fail(TTT_ERR_INVALID_ARGUMENT, "unknown align %d", (int)q.align);
   ttt::Dims d{};
   d.B = q.batch;
   d.T = q.seq_len;
@@ -145,6 +147,7 @@ ttt_status_t make_dims(const ttt_mlp_desc_t* desc, ttt::Dims* dm) {
   d.dt = q.dtype == TTT_BF16 ? ttt::Dtype::BF16 : ttt::Dtype::F32;
   d.conv = q.target == TTT_TARGET_CONV_PROJ || q.target == TTT_TARGET_CONV;
   d.proj = q.target == TTT_TARGET_CONV_PROJ || q.target == TTT_TARGET_PROJ;
+  d.shift = q.align == TTT_ALIGN_SELF ? 0 : 1;
   if (d.B > kMaxInt32 / d.T) return fail(TTT_ERR_UNSUPPORTED, "batch * seq_len must be < 2^31");
   if (d.d * d.f > kMaxInt32) return fail(TTT_ERR_UNSUPPORTED, "d_model * d_ff must be < 2^31");
   if (d.B * d.N > kMaxInt32 / d.Cp) return fail(TTT_ERR_UNSUPPORTED, "padded token count must be < 2^31");

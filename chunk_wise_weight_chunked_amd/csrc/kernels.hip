@@ -302,10 +302,10 @@ __global__ __launch_bounds__(256) void conv_kernel(Dims dm, const T* __restrict_
         tp[k][4 * v + 3] = t.w;
       }
     }
-    uint4 win[kWin];  // X0 rows r0 - (KMAX - 2) + w
+    uint4 win[kWin];  // X0 rows r0 + shift - (KMAX - 1) + w
 #pragma unroll
     for (int w = 0; w < kWin; ++w) {
-      const int64_t row = r0 - (KMAX - 2) + w;
+      const int64_t row = r0 + dm.shift - (KMAX - 1) + w;
       win[w] = row >= 0 && row < BT
                    ? *reinterpret_cast<const uint4*>(X0 + row * d + c * EPC)
                    : make_uint4(0, 0, 0, 0);
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(256) void conv_kernel(Dims dm, const T* __restrict_
       for (int e = 0; e < EPC; ++e) u[e] = 0.0f;
 #pragma unroll
       for (int k = 0; k < KMAX; ++k) {
-        const int64_t src = sq + 1 - k;  // X0 row of tap k, inside the sequence
+        const int64_t src = sq + dm.shift - k;  // X0 row of tap k, inside the sequence
         if (k >= K || src >= T_seq) continue;
         if (src < 0) {  // before the sequence: zero, or the streaming halo
           if (dm.halo == nullptr || src < -kHaloRows) continue;

@@ -17,8 +17,8 @@ inline size_t dtype_bytes(Dtype t) { return t == Dtype::F32 ? 4 : 2; }
 //        layouts Zt and Vt, whose extra columns hold zeros;
 //   P  = B * N * Cp columns of Zt and Vt.
 // X0 rows a streaming call keeps before each session's first row (the conv
-// reaches back K - 2 <= 6 tokens).
-constexpr int kHaloRows = 6;
+// reaches back K - 2 <= 6 tokens, K - 1 <= 7 with the reconstruction alignment).
+constexpr int kHaloRows = 7;
 
 struct Dims {
   int64_t B, T, d, f, C, N, Cp, P;
@@ -26,6 +26,7 @@ struct Dims {
   float eta;
   Dtype dt;
   bool conv, proj;  // the target's conv and projection (both: the method)
+  int32_t shift = 1;  // conv tap k reads X0 row t + shift - k (1: next-token alignment)
   // Streaming continuation (defaults give the one-shot layer):
   const void* halo = nullptr;  // [B][halo_stride]: kHaloRows X0 rows before each session's row 0
   int64_t halo_stride = 0;     // elements between sessions in `halo`

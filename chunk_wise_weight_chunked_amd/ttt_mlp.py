@@ -33,6 +33,8 @@ _MODES = {"auto": TTT_MODE_AUTO, "sequential": TTT_MODE_SEQUENTIAL,
           "chunk_parallel": TTT_MODE_CHUNK_PARALLEL}
 _TARGETS = {"conv_proj": TTT_TARGET_CONV_PROJ, "proj": TTT_TARGET_PROJ,
             "conv": TTT_TARGET_CONV, "embed": TTT_TARGET_EMBED}
+TTT_ALIGN_NEXT, TTT_ALIGN_SELF = 0, 1
+_ALIGNS = {"next": TTT_ALIGN_NEXT, "self": TTT_ALIGN_SELF}
 
 
 class TTTError(RuntimeError):
@@ -54,6 +56,7 @@ class ttt_mlp_desc_t(ctypes.Structure):
         ("mode", ctypes.c_int),
         ("init_from_w0", ctypes.c_int32),
         ("target", ctypes.c_int),
+        ("align", ctypes.c_int),
     ]
 
 
@@ -128,16 +131,18 @@ def _check(status: int):
 
 
 def make_desc(batch, seq_len, d_model, d_ff, chunk, conv_k, eta, dtype, mode="auto",
-              init_from_w0=1, target="conv_proj") -> ttt_mlp_desc_t:
+              init_from_w0=1, target="conv_proj", align="next") -> ttt_mlp_desc_t:
     if isinstance(dtype, torch.dtype):
         dtype = {torch.float32: TTT_F32, torch.bfloat16: TTT_BF16}[dtype]
     if isinstance(mode, str):
         mode = _MODES[mode]
     if isinstance(target, str):
         target = _TARGETS[target]
+    if isinstance(align, str):
+        align = _ALIGNS[align]
     return ttt_mlp_desc_t(int(batch), int(seq_len), int(d_model), int(d_ff), int(chunk),
                           int(conv_k), float(eta), int(dtype), int(mode), int(init_from_w0),
-                          int(target))
+                          int(target), int(align))
 
 
 def _ptr(t) -> int | None:
@@ -258,14 +263,14 @@ def _conv_k(conv_taps, conv_k):
 
 
 def forward(H, X0, W_gate, W_up, W_down0, conv_taps, W_target, eta, chunk, mode="auto",
-            max_group=0, ws=None, stream=None, target="conv_proj", conv_k=None):
+            max_group=0, ws=None, stream=None, target="conv_proj", conv_k=None, align="next"):
     """One sequence: H, X0 [T][d] (or [1][T][d]) device tensors.  Returns
     (O like H, W_down_final [d][f] fp32).  conv_taps / W_target may be None
     when `target` leaves the conv / projection out."""
     T, d = H.shape[-2], H.shape[-1]
     f = W_gate.shape[0]
     desc = make_desc(1, T, d, f, chunk, _conv_k(conv_taps, conv_k), eta, H.dtype, mode,
-                     target=target)
+                     target=target, align=align)
     if ws is None:
         ws = alloc_workspace(desc, max_group, H.device)
     O = torch.empty_like(H)
@@ -277,7 +282,7 @@ def forward(H, X0, W_gate, W_up, W_down0, conv_taps, W_target, eta, chunk, mode=
 
 def forward_batched(H, X0, W_gate, W_up, W_down0, conv_taps, W_target, eta, chunk, W_state=None,
                     mode="auto", max_group=0, ws=None, stream=None, target="conv_proj",
-                    conv_k=None):
+                    conv_k=None, align="next"):
     """B sequences: H, X0 [B][T][d].  If W_state ([B][d][f] fp32) is None it is
     allocated and initialised from W_down0; otherwise it is used (and updated)
     in place as each sequence's starting weight.  Returns (O, W_state)."""
@@ -287,7 +292,7 @@ def forward_batched(H, X0, W_gate, W_up, W_down0, conv_taps, W_target, eta, chun
     if init:
         W_state = torch.empty((B, d, f), dtype=torch.float32, device=H.device)
     desc = make_desc(B, T, d, f, chunk, _conv_k(conv_taps, conv_k), eta, H.dtype, mode,
-                     init_from_w0=1 if init else 0, target=target)
+                     init_from_w0=1 if init else 0, target=target, align=align)
     if ws is None:
         ws = alloc_workspace(desc, max_group, H.device)
     O = torch.empty_like(H)
@@ -303,10 +308,10 @@ class Stream:
     `state` holds the final weights."""
 
     def __init__(self, W_gate, W_up, W_down0, conv_taps, W_target, eta, chunk, batch,
-                 mode="auto", target="conv_proj", conv_k=None, device="cuda"):
+                 mode="auto", target="conv_proj", conv_k=None, device="cuda", align="next"):
         self.w = (W_gate, W_up, W_down0, conv_taps, W_target)
         self.eta, self.chunk, self.batch = float(eta), int(chunk), int(batch)
-        self.mode, self.target = mode, target
+        self.mode, self.target, self.align = mode, target, align
         self.conv_k = _conv_k(conv_taps, conv_k)
         d, f = W_gate.shape[1], W_gate.shape[0]
         self.dtype = W_gate.dtype
@@ -319,7 +324,7 @@ class Stream:
     def _desc(self, L):
         d, f = self.w[0].shape[1], self.w[0].shape[0]
         return make_desc(self.batch, L, d, f, self.chunk, self.conv_k, self.eta, self.dtype,
-                         self.mode, init_from_w0=1, target=self.target)
+                         self.mode, init_from_w0=1, target=self.target, align=self.align)
 
     def step(self, H, X0, last=False, stream=None):
         if self.closed:

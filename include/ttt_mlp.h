@@ -98,6 +98,18 @@ typedef enum {
   TTT_TARGET_EMBED = 3
 } ttt_target_t;
 
+/* Which token the conv's window ends at (the comparison of the LM-aligned and
+ * the reconstruction target in section 4's table):
+ *   NEXT  U[t][c] = sum_k taps[c][k] * X0[t+1-k][c]  (the method: tap 0 reads
+ *         the next token, the target is aligned with next-token prediction)
+ *   SELF  U[t][c] = sum_k taps[c][k] * X0[t-k][c]    (the same window shifted
+ *         by one: the reconstruction alignment, tap 0 reads the token itself)
+ * Only the targets with a conv depend on it. */
+typedef enum {
+  TTT_ALIGN_NEXT = 0,
+  TTT_ALIGN_SELF = 1
+} ttt_align_t;
+
 /* Shapes and scalars of one call.
  *   batch    B >= 1 independent sequences (ttt_mlp_forward requires B == 1);
  *   seq_len  T >= 1 tokens per sequence;
@@ -110,7 +122,8 @@ typedef enum {
  *   mode     see ttt_mode_t;
  *   init_from_w0  (batched only) 1: every W_state[b] is first set to W_down0;
  *                 0: W_state holds each sequence's starting weight on entry;
- *   target   see ttt_target_t (0 for the method itself). */
+ *   target   see ttt_target_t (0 for the method itself);
+ *   align    see ttt_align_t (0 for the method itself). */
 typedef struct {
   int64_t batch;
   int64_t seq_len;
@@ -123,6 +136,7 @@ typedef struct {
   ttt_mode_t mode;
   int32_t init_from_w0;
   ttt_target_t target;
+  ttt_align_t align;
 } ttt_mlp_desc_t;
 
 /* Workspace bytes needed for groups of up to `max_group` chunks (0 = the

@@ -2,8 +2,8 @@
 
 Imported only by tests, the smoke check and the benchmark's CPU-baseline leg.
 """
-from .oracle import (TARGETS, build, final_weight_grid, forward, gated_activations, lm_target,
+from .oracle import (ALIGNS, TARGETS, build, final_weight_grid, forward, gated_activations, lm_target,
                      num_threads, set_num_threads)
 
-__all__ = ["TARGETS", "build", "final_weight_grid", "forward", "gated_activations", "lm_target",
+__all__ = ["ALIGNS", "TARGETS", "build", "final_weight_grid", "forward", "gated_activations", "lm_target",
            "num_threads", "set_num_threads"]

@@ -127,21 +127,31 @@ def gated_activations(H, W_gate, W_up) -> np.ndarray:
 # as the method itself on those identity parts, which in fp64 is exact
 # (multiplications by 1 and additions of 0).
 TARGETS = ("conv_proj", "proj", "conv", "embed")
+ALIGNS = ("next", "self")
 
 
-def target_parts(target: str, taps, W_target, d: int):
-    """(taps, W_target) that give `target` through the section 3.3 formula."""
+def target_parts(target: str, taps, W_target, d: int, align: str = "next"):
+    """(taps, W_target) that give `target` through the section 3.3 formula.
+    align "self" (the reconstruction alignment of section 4's table) ends the
+    conv's window at the token itself, U[t] = sum_k taps[k] X0[t-k]: the same
+    sum as the section 3.3 conv over the taps with a zero tap put in front
+    (tap k + 1 of the look-ahead form reads X0[t+1-(k+1)] = X0[t-k])."""
     if target not in TARGETS:
         raise ValueError(f"unknown target {target!r}")
+    if align not in ALIGNS:
+        raise ValueError(f"unknown align {align!r}")
     if target in ("proj", "embed"):       # no conv: U[t] = X0[t]
         taps = np.zeros((d, 2), dtype=np.float32)
         taps[:, 1] = 1.0
+    elif align == "self":
+        taps = _f32(taps)
+        taps = np.concatenate([np.zeros((d, 1), dtype=np.float32), taps], axis=1)
     if target in ("conv", "embed"):       # no projection
         W_target = np.eye(d, dtype=np.float32)
     return taps, W_target
 
 
-def lm_target(X0, taps, W_target, target: str = "conv_proj") -> np.ndarray:
+def lm_target(X0, taps, W_target, target: str = "conv_proj", align: str = "next") -> np.ndarray:
     """V^ = Conv1D(X0) W_target (or a variant, see TARGETS) for X0 of shape
     [B][T][d] (or [T][d])."""
     X0 = _f32(X0)
@@ -149,7 +159,7 @@ def lm_target(X0, taps, W_target, target: str = "conv_proj") -> np.ndarray:
     if squeeze:
         X0 = X0[None]
     B, T, d = X0.shape
-    taps, W_target = target_parts(target, taps, W_target, d)
+    taps, W_target = target_parts(target, taps, W_target, d, align)
     taps, Wt = _f32(taps), _f32(W_target)
     K = taps.shape[1]
     assert taps.shape == (d, K) and Wt.shape == (d, d)
@@ -170,7 +180,7 @@ _FORMS = {
 
 
 def forward(H, X0, W_gate, W_up, W_down0, taps, W_target, eta: float, chunk: int,
-            form: str = "sequential", target: str = "conv_proj"):
+            form: str = "sequential", target: str = "conv_proj", align: str = "next"):
     """Run the layer; returns (O [B][T][d] float64, W_final [B][d][f] float64).
 
     H and X0 may be [T][d] (one sequence; outputs are then squeezed) or
@@ -185,7 +195,7 @@ def forward(H, X0, W_gate, W_up, W_down0, taps, W_target, eta: float, chunk: int
         H, X0 = H[None], X0[None]
     B, T, d = H.shape
     assert X0.shape == (B, T, d)
-    taps, W_target = target_parts(target, taps, W_target, d)
+    taps, W_target = target_parts(target, taps, W_target, d, align)
     Wg, Wu, taps, Wt = _f32(W_gate), _f32(W_up), _f32(taps), _f32(W_target)
     f = Wg.shape[0]
     K = taps.shape[1]
@@ -211,12 +221,12 @@ def forward(H, X0, W_gate, W_up, W_down0, taps, W_target, eta: float, chunk: int
 
 
 def final_weight_grid(H, X0, W_gate, W_up, W_down0, taps, W_target, eta: float, ms, ns,
-                      target: str = "conv_proj"):
+                      target: str = "conv_proj", align: str = "next"):
     """Entries W_final[m][n] for m in ms, n in ns of ONE sequence, by the closed
     form W0 + eta * sum_t V^[t][m] Z[t][n] (independent of the chunk size)."""
     H, X0 = _f32(H), _f32(X0)
     T, d = H.shape
-    taps, W_target = target_parts(target, taps, W_target, d)
+    taps, W_target = target_parts(target, taps, W_target, d, align)
     Wg, Wu, W0, taps, Wt = (_f32(W_gate), _f32(W_up), _f32(W_down0), _f32(taps),
                             _f32(W_target))
     f = Wg.shape[0]

@@ -109,6 +109,7 @@ BAD_DESCS = [
     (dict(mode=9), tm.TTT_ERR_INVALID_ARGUMENT, "mode"),
     (dict(init_from_w0=2), tm.TTT_ERR_INVALID_ARGUMENT, "init_from_w0"),
     (dict(target=4), tm.TTT_ERR_INVALID_ARGUMENT, "target"),
+    (dict(align=2), tm.TTT_ERR_INVALID_ARGUMENT, "align"),
     (dict(batch=1 << 20, seq_len=1 << 12), tm.TTT_ERR_UNSUPPORTED, "2^31"),
 ]
 
@@ -278,10 +279,10 @@ def call_stream(lib, d, p, pos, last):
 
 
 def test_stream_sizes():
-    # carry per session: C rows of H, then 6 + C rows of X0 (the conv halo
-    # holds up to K - 2 <= 6 rows); for bf16 then the bf16 copies of the
+    # carry per session: C rows of H, then 7 + C rows of X0 (the conv halo
+    # holds up to K - 1 <= 7 rows); for bf16 then the bf16 copies of the
     # sessions' current weights at a 256-byte boundary
-    rows = 3 * (2 * 64 + 6) * 256
+    rows = 3 * (2 * 64 + 7) * 256
     assert tm.ttt_mlp_carry_size(desc(batch=3, seq_len=100, chunk=64, dtype=tm.TTT_F32)) == \
         rows * 4
     assert tm.ttt_mlp_carry_size(desc(batch=3, seq_len=100, chunk=64)) == \
@@ -291,7 +292,7 @@ def test_stream_sizes():
     # the layer runs on sequences of up to L + C tokens
     longest = desc(batch=2, seq_len=300 + 128, chunk=128)
     rows = (2 * 428 * 256 * 2 + 255) // 256 * 256
-    carry_rows = 2 * (2 * 128 + 6) * 256 * 2  # the new carry's rows, built before the copy
+    carry_rows = 2 * (2 * 128 + 7) * 256 * 2  # the new carry's rows, built before the copy
     assert w1 == tm.ttt_mlp_workspace_size(longest, 1) + 2 * rows + carry_rows
     assert tm.ttt_mlp_stream_workspace_size(d, 2) > w1
     assert tm.ttt_mlp_stream_workspace_size(d, 0) >= w1

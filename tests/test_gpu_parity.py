@@ -220,6 +220,45 @@ def test_target_variants(case, target):
     assert e_o <= tol_for(dtype) and e_dw <= tol_for(dtype), (e_o, e_dw)
 
 
+ALIGN_CASES = [
+    # B, T, d, f, K, C, dtype, target
+    (2, 333, 128, 192, 8, 100, torch.bfloat16, "conv_proj"),   # window reaches back 7 rows
+    (1, 300, 192, 256, 4, 64, torch.float32, "conv_proj"),
+    (1, 257, 128, 192, 1, 32, torch.bfloat16, "conv"),         # K = 1: V^ = taps * X0
+    (2, 200, 64, 128, 5, 7, torch.float32, "conv"),
+]
+
+
+@pytest.mark.parametrize("case", ALIGN_CASES,
+                         ids=lambda c: f"T{c[1]}K{c[4]}{str(c[6])[6:]}-{c[7]}")
+def test_reconstruction_alignment(case):
+    """The conv window ending at the token itself (the reconstruction target of
+    section 4's table) against the oracle."""
+    B, T, d, f, K, C, dtype, target = case
+    print(f"[parity] align=self target={target} B,T,d,f,K,C={B},{T},{d},{f},{K},{C} {dtype}",
+          flush=True)
+    inp = synth.make_inputs(B, T, d, f, K, dtype, seed=78)
+    dev = to_device(inp)
+    Wt = None if target == "conv" else dev["W_target"]
+    eta = 2e-2
+    O, W = tm.forward_batched(dev["H"], dev["X0"], dev["W_gate"], dev["W_up"], dev["W_down0"],
+                              dev["taps"], Wt, eta, C, target=target, align="self")
+    O_next, _ = tm.forward_batched(dev["H"], dev["X0"], dev["W_gate"], dev["W_up"],
+                                   dev["W_down0"], dev["taps"], Wt, eta, C, target=target)
+    torch.cuda.synchronize()
+    ni = numpy_inputs(inp)
+    Oo, Wo = oracle.forward(ni["H"], ni["X0"], ni["W_gate"], ni["W_up"], ni["W_down0"],
+                            ni["taps"], ni["W_target"], eta, C, target=target, align="self")
+    W0 = ni["W_down0"].astype(np.float64)
+    Og, Wg = O.float().cpu().numpy(), W.cpu().numpy()
+    e_o, e_dw = rel(Og, Oo), rel(Wg - W0, Wo - W0)
+    print(f"  rel O {e_o:.3e}  dW {e_dw:.3e}", flush=True)
+    assert e_o <= tol_for(dtype) and e_dw <= tol_for(dtype), (e_o, e_dw)
+    # chunk 0 uses W0 in both alignments; later chunks see different updates
+    assert torch.equal(O[:, :C], O_next[:, :C])
+    assert not torch.equal(O[:, C:], O_next[:, C:])
+
+
 # --------------------------------------------------------------- full-size workloads
 FULL = ["qwen3_4b_32k", "qwen3_4b_128k", "multi_session_16x8k", "small_4x128k"]
 PREFIX_CHUNKS = {"qwen3_4b_32k": 2, "qwen3_4b_128k": 1, "multi_session_16x8k": 1,

@@ -47,25 +47,31 @@ CASES = [
     (3, 150, 192, 320, 4, 32, torch.bfloat16, [7, 7, 7, 11, 1, 16, 101], "conv_proj"),
     (2, 90, 256, 512, 8, 16, torch.bfloat16, [1] * 40 + [50], "conv"),
     (1, 120, 128, 192, 4, 128, torch.bfloat16, [16] * 7 + [8], "embed"),
+    # reconstruction alignment: the halo holds K - 1 = 7 rows
+    (2, 300, 128, 192, 8, 4, torch.bfloat16, [3, 1, 50, 246], "conv_proj@self"),
+    (1, 200, 128, 192, 8, 64, torch.float32, [70, 1, 129], "conv@self"),
+    (2, 100, 128, 256, 8, 32, torch.bfloat16, [1] * 40 + [60], "conv_proj@self"),
 ]
 
 
 def _id(c):
-    return f"B{c[0]}T{c[1]}C{c[5]}{str(c[6])[6:]}-{len(c[7])}calls-{c[8]}"
+    return f"B{c[0]}T{c[1]}C{c[5]}{str(c[6])[6:]}-{len(c[7])}calls-{c[8].replace('@', '-')}"
 
 
 @pytest.mark.parametrize("case", CASES, ids=_id)
 def test_stream_equals_one_call(case):
     B, T, d, f, K, C, dtype, calls, target = case
+    target, _, align = target.partition("@")
+    align = align or "next"
     assert sum(calls) == T
     print(f"[stream] {_id(case)}", flush=True)
     inp = synth.make_inputs(B, T, d, f, K, dtype, seed=91)
     dev = to_device(inp)
     eta = 2e-2
     O1, W1 = tm.forward_batched(dev["H"], dev["X0"], dev["W_gate"], dev["W_up"], dev["W_down0"],
-                                dev["taps"], dev["W_target"], eta, C, target=target)
+                                dev["taps"], dev["W_target"], eta, C, target=target, align=align)
     st = tm.Stream(dev["W_gate"], dev["W_up"], dev["W_down0"], dev["taps"], dev["W_target"], eta,
-                   C, B, target=target)
+                   C, B, target=target, align=align)
     outs, p = [], 0
     dec = torch.zeros(T, dtype=torch.bool)
     for i, L in enumerate(calls):

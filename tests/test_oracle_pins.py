@@ -319,6 +319,62 @@ def test_target_variants_are_their_definitions():
         oracle.lm_target(X0, taps, Wt, target="nope")
 
 
+def test_reconstruction_alignment_is_the_window_shifted_by_one():
+    """The reconstruction alignment (section 4's table: V_t from the token's own
+    embedding) ends the conv's window at t: a one-hot tap 0 gives V^ = X0
+    exactly, the general conv is sum_k taps[k] X0[t-k] (explicit loops), and
+    every row is the next-token alignment's previous row."""
+    T, d, K = 9, 4, 3
+    rng = np.random.default_rng(35)
+    X0 = rng.standard_normal((T, d)).astype(np.float32)
+    taps = rng.standard_normal((d, K)).astype(np.float32)
+    Wt = rng.standard_normal((d, d)).astype(np.float32)
+    one_hot = np.zeros((d, K), dtype=np.float32)
+    one_hot[:, 0] = 1.0
+    assert np.array_equal(oracle.lm_target(X0, one_hot, None, target="conv", align="self"),
+                          X0.astype(np.float64))
+    U = np.zeros((T, d))
+    for t in range(T):
+        for c in range(d):
+            for k in range(K):
+                if t - k >= 0:
+                    U[t, c] += float(taps[c, k]) * float(X0[t - k, c])
+    V_self = oracle.lm_target(X0, taps, Wt, align="self")
+    np.testing.assert_allclose(V_self, U @ Wt.astype(np.float64), rtol=1e-12, atol=1e-12)
+    V_next = oracle.lm_target(X0, taps, Wt)
+    np.testing.assert_allclose(V_self[1:], V_next[:-1], rtol=1e-13, atol=1e-13)
+    # the variants without a conv do not depend on the alignment
+    for target in ("proj", "embed"):
+        assert np.array_equal(oracle.lm_target(X0, taps, Wt, target=target, align="self"),
+                              oracle.lm_target(X0, taps, Wt, target=target))
+    with pytest.raises(ValueError):
+        oracle.lm_target(X0, taps, Wt, align="prev")
+
+
+def test_reconstruction_alignment_layer_closed_form():
+    """With the reconstruction alignment the update rule is unchanged:
+    W_final = W0 + eta V^^T Z with V^ from the shifted window; forms agree."""
+    inp = rand_inputs(1, 29, 8, 12, 4, seed=36)
+    eta, C = 0.05, 6
+    outs = [oracle.forward(inp["H"], inp["X0"], inp["W_gate"], inp["W_up"], inp["W_down0"],
+                           inp["taps"], inp["W_target"], eta, C, form=form, align="self")
+            for form in ("sequential", "chunk_parallel", "dual")]
+    for O, W in outs[1:]:
+        assert rel(O, outs[0][0]) < 1e-12 and rel(W, outs[0][1]) < 1e-12
+    X0 = inp["X0"][0].astype(np.float64)
+    taps = inp["taps"].astype(np.float64)
+    U = np.zeros_like(X0)
+    for k in range(taps.shape[1]):
+        U[k:] += taps[:, k] * X0[:X0.shape[0] - k]
+    V = U @ inp["W_target"].astype(np.float64)
+    Z = oracle.gated_activations(inp["H"][0], inp["W_gate"], inp["W_up"])
+    ref = inp["W_down0"].astype(np.float64) + eta * V.T @ Z
+    assert rel(outs[0][1][0], ref) < 1e-13
+    # chunk 0's outputs use W0 in either alignment
+    O0 = Z[:C] @ inp["W_down0"].astype(np.float64).T
+    assert rel(outs[0][0][0][:C], O0) < 1e-13
+
+
 @pytest.mark.parametrize("target", ["proj", "conv", "embed"])
 def test_target_variant_layer_closed_form_and_forms_agree(target):
     """Every variant still follows the update rule: W_final = W0 + eta V^^T Z, and
