@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(BUILD, "libttt_mlp.so")
-SOURCES = ["kernels.hip", "decode.hip", "api.cpp"]
+SOURCES = ["kernels.hip", "decode.hip", "backward.hip", "api.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -31,6 +31,10 @@ HIPCC_FLAGS = [
 ]
 
 
+# rocBLAS serves the plain GEMMs of the backward pass
+LINK_FLAGS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -42,7 +46,8 @@ def build(verbose: bool = False) -> str:
     """Compile every source for gfx950 and link the shared library."""
     os.makedirs(BUILD, exist_ok=True)
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp,
+           *LINK_FLAGS]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,0 +1,304 @@
+// Kernels of the layer's backward pass that are not plain GEMMs.
+//
+// The backward follows the chain rule through the forward the In-Place TTT
+// page defines (section 3.1 gated MLP, section 3.3 target and update,
+// section 3.2 chunk order).  Its chunk-structured part, the sums
+// S_j = dW_final + sum_{m > j} dO_mᵀ Z_m, is the forward's streamed prefix
+// run over the chunks in reverse order; the kernels here lay the operands out
+// for that (chunk-reversed, k-blocked token-major), and do the elementwise and
+// reduction steps: the SwiGLU derivative, the conv's transpose and its taps'
+// gradient, and the learning rate's gradient.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "gemm_core.h"
+#include "layer.h"
+
+namespace ttt {
+namespace {
+
+template <typename T>
+__device__ __forceinline__ float ld_f32(const T* p);
+template <>
+__device__ __forceinline__ float ld_f32<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float ld_f32<uint16_t>(const uint16_t* p) {
+  return bf16_bits_to_f32(*p);
+}
+
+unsigned grid_cap(int64_t n, int64_t per_block, int64_t cap) {
+  const int64_t g = (n + per_block - 1) / per_block;
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(g, cap));
+}
+
+// Copies a k-blocked token-major matrix ([P/64][R][64 tokens] in bytes: each
+// chunk of each sequence is a contiguous run of Cp * R * es bytes) with the
+// chunks of every sequence in reverse order.  16-byte items.
+__global__ void reverse_chunks_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                      int64_t B, int64_t N, int64_t chunk_items) {
+  const int64_t n = B * N * chunk_items, stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < n; it += stride) {
+    const int64_t blk = it / chunk_items, off = it - blk * chunk_items;
+    const int64_t b = blk / N, i = blk - b * N;
+    dst[(b * N + (N - 1 - i)) * chunk_items + off] = src[it];
+  }
+}
+
+// dst = the rows of src ([B][T][R] row-major) in the k-blocked token-major
+// layout [P/TB][R][TB] (TB = 128 bytes of tokens: 64 bf16, 32 fp32) with the
+// chunks of every sequence in reverse order and zeros in the padding columns.
+// One TB-token x 64-row tile per workgroup, through LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void to_kblocked_reversed_kernel(const T* __restrict__ src,
+                                                                   T* __restrict__ dst, Dims dm,
+                                                                   int64_t R) {
+  constexpr int TB = kRowBytes / (int)sizeof(T);
+  __shared__ float tile[TB][65];
+  const int64_t q = blockIdx.x;                 // TB-token block of the reversed layout
+  const int64_t r0 = (int64_t)blockIdx.y * 64;  // first row of the tile
+  const int64_t tiles_per_chunk = dm.Cp / TB;
+  const int64_t chunk_rev = q / tiles_per_chunk, jb = q - chunk_rev * tiles_per_chunk;
+  const int64_t b = chunk_rev / dm.N, i = dm.N - 1 - (chunk_rev - b * dm.N);
+  const int64_t len = std::min<int64_t>(dm.C, dm.T - i * dm.C);  // tokens of chunk i
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int e = ty; e < TB; e += 4) {  // token e of the block, row r0 + tx
+    const int64_t j = jb * TB + e;
+    float v = 0.f;
+    if (j < len && r0 + tx < R) v = ld_f32<T>(src + (b * dm.T + i * dm.C + j) * R + r0 + tx);
+    tile[e][tx] = v;
+  }
+  __syncthreads();
+  if (tx >= TB) return;
+  for (int rr = ty; rr < 64; rr += 4) {  // row r0 + rr, token tx
+    if (r0 + rr < R) Elem<T>::store(dst + (q * R + r0 + rr) * TB + tx, tile[tx][rr]);
+  }
+}
+
+// SwiGLU derivative.  With Z = SiLU(A_g) * A_u and s = sigmoid(A_g):
+//   dA_g = dZ * A_u * s * (1 + A_g (1 - s)),  dA_u = dZ * A_g * s.
+// Row t of the output holds [dA_g[t][0..f) | dA_u[t][0..f)] (the A operand
+// of dH = [dA_g | dA_u] [W_gate; W_up]).
+template <typename T>
+__global__ void swiglu_backward_kernel(const float* __restrict__ dZ, const float* __restrict__ Ag,
+                                       const float* __restrict__ Au, T* __restrict__ dA,
+                                       int64_t rows, int64_t f) {
+  const int64_t n4 = rows * f / 4, stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < n4; it += stride) {
+    const float4 z = reinterpret_cast<const float4*>(dZ)[it];
+    const float4 g = reinterpret_cast<const float4*>(Ag)[it];
+    const float4 u = reinterpret_cast<const float4*>(Au)[it];
+    const int64_t t = it * 4 / f, c = it * 4 - t * f;
+    const float zz[4] = {z.x, z.y, z.z, z.w}, gg[4] = {g.x, g.y, g.z, g.w},
+                uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float s = 1.0f / (1.0f + __expf(-gg[e]));
+      Elem<T>::store(dA + t * 2 * f + c + e, zz[e] * uu[e] * s * (1.0f + gg[e] * (1.0f - s)));
+      Elem<T>::store(dA + t * 2 * f + f + c + e, zz[e] * gg[e] * s);
+    }
+  }
+}
+
+// The target's backward.  dU[t][c] = scale * src[t][c] (src: the gradient of
+// U, or of V^ = U when there is no projection).  With the conv
+// (U[t][c] = sum_k taps[c][k] X0[t + shift - k][c]):
+//   dX0[s][c] = sum_k taps[c][k] dU[s - shift + k][c]   (t inside the sequence)
+//   part[r][k][c] = sum over the rows of range r of dU[t][c] X0[t + shift - k][c]
+// without it dX0 = dU.  Thread = one feature c, looping over the rows of its
+// token range (blockIdx.y); partial tap sums are reduced in a second pass.
+template <typename T, typename S>
+__global__ __launch_bounds__(256) void target_backward_kernel(
+    const S* __restrict__ src, float scale, const T* __restrict__ X0,
+    const float* __restrict__ tapsT, T* __restrict__ dX0, float* __restrict__ part, Dims dm,
+    int64_t rows_per_range) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= dm.d) return;
+  const int64_t d = dm.d, BT = dm.B * dm.T, T_seq = dm.T;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_range;
+  const int64_t r1 = std::min<int64_t>(BT, r0 + rows_per_range);
+  const int K = dm.conv ? dm.K : 0;
+  float tp[8], acc[8];
+  for (int k = 0; k < 8; ++k) {
+    tp[k] = k < K ? tapsT[k * d + c] : 0.f;
+    acc[k] = 0.f;
+  }
+  for (int64_t t = r0; t < r1; ++t) {
+    const int64_t b = t / T_seq, s = t - b * T_seq;
+    if (!dm.conv) {
+      Elem<T>::store(dX0 + t * d + c, scale * ld_f32<S>(src + t * d + c));
+      continue;
+    }
+    const float du = scale * ld_f32<S>(src + t * d + c);
+    float dx = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int64_t xs = s + dm.shift - k;  // X0 row tap k of output row s reads
+      if (xs >= 0 && xs < T_seq) acc[k] = fmaf(du, ld_f32<T>(X0 + (b * T_seq + xs) * d + c), acc[k]);
+      const int64_t us = s - dm.shift + k;  // output row whose tap k reads X0 row s
+      if (us >= 0 && us < T_seq) dx = fmaf(tp[k], scale * ld_f32<S>(src + (b * T_seq + us) * d + c), dx);
+    }
+    Elem<T>::store(dX0 + t * d + c, dx);
+  }
+  if (dm.conv)
+    for (int k = 0; k < K; ++k) part[((int64_t)blockIdx.y * 8 + k) * d + c] = acc[k];
+}
+
+// dtaps[c][k] = sum over ranges r (in order) of part[r][k][c].
+__global__ void taps_reduce_kernel(const float* __restrict__ part, float* __restrict__ dtaps,
+                                   int64_t ranges, int64_t d, int K) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= d * K) return;
+  const int64_t c = i / K, k = i - c * K;
+  float s = 0.f;
+  for (int64_t r = 0; r < ranges; ++r) s += part[(r * 8 + k) * d + c];
+  dtaps[c * K + k] = s;
+}
+
+// Partial sums of sum_i a[i] * b[i] (a: T values, b: fp32), one per
+// workgroup; then one workgroup adds the partials in order.
+template <typename T>
+__global__ __launch_bounds__(256) void dot_partial_kernel(const T* __restrict__ a,
+                                                          const float* __restrict__ b, int64_t n,
+                                                          float* __restrict__ part) {
+  __shared__ float red[256];
+  float s = 0.f;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    s = fmaf(ld_f32<T>(a + i), b[i], s);
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restrict__ part, int n,
+                                                           float scale, float* __restrict__ out) {
+  __shared__ float red[256];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < n; i += 256) s += part[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = scale * red[0];
+}
+
+// out[i] = round(in[i]) in the activation type.
+template <typename T>
+__global__ void from_f32_kernel(const float* __restrict__ in, T* __restrict__ out, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    Elem<T>::store(out + i, in[i]);
+}
+
+// out[i] = v.
+__global__ void fill_f32_kernel(float* __restrict__ out, int64_t n, float v) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) out[i] = v;
+}
+
+}  // namespace
+
+hipError_t launch_reverse_chunks(const void* src, void* dst, const Dims& dm, int64_t R,
+                                 hipStream_t s) {
+  const int64_t chunk_items = dm.Cp * R * (int64_t)dtype_bytes(dm.dt) / 16;
+  hipLaunchKernelGGL(reverse_chunks_kernel, dim3(grid_cap(dm.B * dm.N * chunk_items, 256, 65536)),
+                     dim3(256), 0, s, static_cast<const uint4*>(src), static_cast<uint4*>(dst),
+                     dm.B, dm.N, chunk_items);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_kblocked_reversed(const void* src, void* dst, const Dims& dm, int64_t R,
+                                       hipStream_t s) {
+  const int64_t tb = kRowBytes / (int64_t)dtype_bytes(dm.dt);
+  const dim3 grid((unsigned)(dm.P / tb), (unsigned)((R + 63) / 64));
+  if (dm.dt == Dtype::BF16)
+    hipLaunchKernelGGL(to_kblocked_reversed_kernel<uint16_t>, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), dm, R);
+  else
+    hipLaunchKernelGGL(to_kblocked_reversed_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float*>(src), static_cast<float*>(dst), dm, R);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_backward(const float* dZ, const float* Ag, const float* Au, void* dA,
+                                  const Dims& dm, hipStream_t s) {
+  const int64_t rows = dm.B * dm.T, n4 = rows * dm.f / 4;
+  const dim3 g(grid_cap(n4, 256, 65536));
+  if (dm.dt == Dtype::BF16)
+    hipLaunchKernelGGL(swiglu_backward_kernel<uint16_t>, g, dim3(256), 0, s, dZ, Ag, Au,
+                       static_cast<uint16_t*>(dA), rows, dm.f);
+  else
+    hipLaunchKernelGGL(swiglu_backward_kernel<float>, g, dim3(256), 0, s, dZ, Ag, Au,
+                       static_cast<float*>(dA), rows, dm.f);
+  return hipGetLastError();
+}
+
+int64_t target_backward_ranges(const Dims& dm) {
+  return (dm.B * dm.T + kTargetBackwardRows - 1) / kTargetBackwardRows;
+}
+
+hipError_t launch_target_backward(const void* src, bool src_f32, float scale, const void* X0,
+                                  const float* tapsT, void* dX0, float* part, float* dtaps,
+                                  const Dims& dm, hipStream_t s) {
+  const int64_t ranges = target_backward_ranges(dm);
+  const dim3 grid((unsigned)((dm.d + 255) / 256), (unsigned)ranges);
+  if (dm.dt == Dtype::BF16) {
+    const auto x0 = static_cast<const uint16_t*>(X0);
+    const auto dx = static_cast<uint16_t*>(dX0);
+    if (src_f32)
+      hipLaunchKernelGGL((target_backward_kernel<uint16_t, float>), grid, dim3(256), 0, s,
+                         static_cast<const float*>(src), scale, x0, tapsT, dx, part, dm,
+                         (int64_t)kTargetBackwardRows);
+    else
+      hipLaunchKernelGGL((target_backward_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, s,
+                         static_cast<const uint16_t*>(src), scale, x0, tapsT, dx, part, dm,
+                         (int64_t)kTargetBackwardRows);
+  } else {
+    hipLaunchKernelGGL((target_backward_kernel<float, float>), grid, dim3(256), 0, s,
+                       static_cast<const float*>(src), scale, static_cast<const float*>(X0), tapsT,
+                       static_cast<float*>(dX0), part, dm, (int64_t)kTargetBackwardRows);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !dm.conv) return e;
+  hipLaunchKernelGGL(taps_reduce_kernel, dim3((unsigned)((dm.d * dm.K + 255) / 256)), dim3(256),
+                     0, s, part, dtaps, ranges, dm.d, dm.K);
+  return hipGetLastError();
+}
+
+hipError_t launch_dot(const void* a, const float* b, int64_t n, Dtype dt, float scale, float* part,
+                      float* out, hipStream_t s) {
+  if (dt == Dtype::BF16)
+    hipLaunchKernelGGL(dot_partial_kernel<uint16_t>, dim3(kDotPartials), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(a), b, n, part);
+  else
+    hipLaunchKernelGGL(dot_partial_kernel<float>, dim3(kDotPartials), dim3(256), 0, s,
+                       static_cast<const float*>(a), b, n, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sum_partials_kernel, dim3(1), dim3(256), 0, s, part, kDotPartials, scale, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_from_f32(const float* in, void* out, int64_t n, Dtype dt, hipStream_t s) {
+  const dim3 g(grid_cap(n, 256, 65536));
+  if (dt == Dtype::BF16)
+    hipLaunchKernelGGL(from_f32_kernel<uint16_t>, g, dim3(256), 0, s, in,
+                       static_cast<uint16_t*>(out), n);
+  else
+    hipLaunchKernelGGL(from_f32_kernel<float>, g, dim3(256), 0, s, in, static_cast<float*>(out), n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* out, int64_t n, float v, hipStream_t s) {
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_cap(n, 256, 16384)), dim3(256), 0, s, out, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace ttt

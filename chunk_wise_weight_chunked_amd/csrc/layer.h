@@ -95,4 +95,29 @@ hipError_t launch_decode_down(const void* Z, const void* Wc, void* O, int64_t B,
                               int64_t d, int64_t f, hipStream_t s);
 hipError_t launch_state_to_bf16(const float* W, void* out, int64_t n, hipStream_t s);
 
+// Backward-pass kernels (backward.hip).
+constexpr int kTargetBackwardRows = 256;  // token rows per partial sum of the taps' gradient
+constexpr int kDotPartials = 1024;        // partial sums of the learning rate's gradient
+// dst = src (k-blocked token-major, R rows) with each sequence's chunks reversed.
+hipError_t launch_reverse_chunks(const void* src, void* dst, const Dims& dm, int64_t R,
+                                 hipStream_t s);
+// dst = rows of src [B][T][R] in the k-blocked token-major layout, chunks reversed.
+hipError_t launch_to_kblocked_reversed(const void* src, void* dst, const Dims& dm, int64_t R,
+                                       hipStream_t s);
+// dA [B*T][2f] = [dA_g | dA_u] from dZ, A_g, A_u (fp32 [B*T][f]).
+hipError_t launch_swiglu_backward(const float* dZ, const float* Ag, const float* Au, void* dA,
+                                  const Dims& dm, hipStream_t s);
+// dX0 and dtaps from dU = scale * src (fp32 or the activation type); `part`
+// holds target_backward_ranges(dm) * 8 * d floats.
+int64_t target_backward_ranges(const Dims& dm);
+hipError_t launch_target_backward(const void* src, bool src_f32, float scale, const void* X0,
+                                  const float* tapsT, void* dX0, float* part, float* dtaps,
+                                  const Dims& dm, hipStream_t s);
+// *out = scale * sum_i a[i] b[i] (a: activation type, b: fp32); `part` holds
+// kDotPartials floats.
+hipError_t launch_dot(const void* a, const float* b, int64_t n, Dtype dt, float scale, float* part,
+                      float* out, hipStream_t s);
+hipError_t launch_from_f32(const float* in, void* out, int64_t n, Dtype dt, hipStream_t s);
+hipError_t launch_fill_f32(float* out, int64_t n, float v, hipStream_t s);
+
 }  // namespace ttt

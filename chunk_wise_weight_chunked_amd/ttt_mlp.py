@@ -65,6 +65,7 @@ EXPORTS = (
     "ttt_mlp_forward_batched", "ttt_fastweight_state_reset", "ttt_last_error",
     "ttt_profile_enable", "ttt_profile_read", "ttt_stage_name",
     "ttt_mlp_carry_size", "ttt_mlp_stream_workspace_size", "ttt_mlp_forward_stream",
+    "ttt_mlp_backward_workspace_size", "ttt_mlp_backward_batched",
 )
 
 _lib = None
@@ -106,6 +107,10 @@ def load(path: str | None = None):
     lib.ttt_mlp_stream_workspace_size.restype = sz
     lib.ttt_mlp_forward_stream.argtypes = [dp, i64, ctypes.c_int32] + [vp] * 11 + [sz, vp]
     lib.ttt_mlp_forward_stream.restype = ctypes.c_int
+    lib.ttt_mlp_backward_workspace_size.argtypes = [dp]
+    lib.ttt_mlp_backward_workspace_size.restype = sz
+    lib.ttt_mlp_backward_batched.argtypes = [dp] + [vp] * 18 + [vp, sz, vp]
+    lib.ttt_mlp_backward_batched.restype = ctypes.c_int
     lib.ttt_fastweight_state_reset.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp]
     lib.ttt_fastweight_state_reset.restype = ctypes.c_int
     lib.ttt_last_error.restype = ctypes.c_char_p
@@ -299,6 +304,59 @@ def forward_batched(H, X0, W_gate, W_up, W_down0, conv_taps, W_target, eta, chun
     ttt_mlp_forward_batched(desc, H, X0, W_gate, W_up, W_down0 if init else None, conv_taps,
                             W_target, O, W_state, ws, stream=stream)
     return O, W_state
+
+
+def ttt_mlp_backward_workspace_size(desc: ttt_mlp_desc_t) -> int:
+    n = load().ttt_mlp_backward_workspace_size(ctypes.byref(desc))
+    if n == 0:
+        raise TTTError(TTT_ERR_INVALID_ARGUMENT, ttt_last_error())
+    return n
+
+
+def ttt_mlp_backward_batched(desc, H, X0, W_gate, W_up, W_down0, W_start, conv_taps, W_target,
+                             dO, dW_final, dH, dX0, dW_gate, dW_up, dW_start, dtaps, dW_target,
+                             d_eta, ws, ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(load().ttt_mlp_backward_batched(
+        ctypes.byref(desc), *[_ptr(t) for t in (H, X0, W_gate, W_up, W_down0, W_start, conv_taps,
+                                                 W_target, dO, dW_final, dH, dX0, dW_gate, dW_up,
+                                                 dW_start, dtaps, dW_target, d_eta, ws)],
+        int(ws_bytes), _stream(stream)))
+
+
+def backward_batched(H, X0, W_gate, W_up, W_down0, conv_taps, W_target, eta, chunk, dO,
+                     dW_final=None, W_start=None, target="conv_proj", align="next", conv_k=None,
+                     ws=None, stream=None) -> dict:
+    """Gradients of <dO, O> + <dW_final, W_final> for the layer run on H, X0
+    [B][T][d] from W_down0 (or from W_start [B][d][f] fp32 per sequence).
+    Returns a dict of device tensors: H, X0 (activation dtype); W_gate, W_up,
+    W_start ([B][d][f]), taps, W_target (fp32; None where the target has no
+    conv / projection) and eta (a 1-element fp32 tensor)."""
+    B, T, d = H.shape
+    f = W_gate.shape[0]
+    K = _conv_k(conv_taps, conv_k)
+    init = W_start is None
+    desc = make_desc(B, T, d, f, chunk, K, eta, H.dtype, init_from_w0=1 if init else 0,
+                     target=target, align=align)
+    if ws is None:
+        ws = torch.empty(ttt_mlp_backward_workspace_size(desc), dtype=torch.uint8,
+                         device=H.device)
+    dev, f32 = H.device, torch.float32
+    conv = target in ("conv_proj", "conv")
+    proj = target in ("conv_proj", "proj")
+    g = {"H": torch.empty_like(H), "X0": torch.empty_like(X0),
+         "W_gate": torch.empty((f, d), dtype=f32, device=dev),
+         "W_up": torch.empty((f, d), dtype=f32, device=dev),
+         "W_start": torch.empty((B, d, f), dtype=f32, device=dev),
+         "taps": torch.empty((d, K), dtype=f32, device=dev) if conv else None,
+         "W_target": torch.empty((d, d), dtype=f32, device=dev) if proj else None,
+         "eta": torch.empty(1, dtype=f32, device=dev)}
+    ttt_mlp_backward_batched(desc, H, X0, W_gate, W_up, W_down0 if init else None, W_start,
+                             conv_taps, W_target, dO, dW_final, g["H"], g["X0"], g["W_gate"],
+                             g["W_up"], g["W_start"], g["taps"], g["W_target"], g["eta"], ws,
+                             stream=stream)
+    return g
 
 
 class Stream:

@@ -232,6 +232,41 @@ ttt_status_t ttt_mlp_forward_stream(const ttt_mlp_desc_t* desc, int64_t pos, int
                                     const void* W_target, void* O, float* W_state, void* carry,
                                     void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Backward pass ----
+ * Gradients of a loss L through the layer, given dO = dL/dO and (optionally)
+ * dW_final = dL/dW_state after the call, for B sequences laid out as in
+ * ttt_mlp_forward_batched.  The backward is the chain rule through the
+ * forward the page defines (section 3.1 gated MLP, section 3.3 target and
+ * update rule, section 3.2 chunk order): with S_j = dW_final +
+ * sum_{m > j} dO_mᵀ Z_m,
+ *   dZ_j = dO_j W^(j-1) + eta V^_j S_j,   dV^_j = eta Z_j S_jᵀ,
+ *   dW_start = S_{-1},                    deta = sum_j <S_j, V^_jᵀ Z_j>,
+ * then through SwiGLU, the projection and the conv.  The forward is
+ * recomputed inside the call; S_j comes from the forward's streamed prefix
+ * run over the chunks in reverse.
+ *   W_down0 / W_start  the starting weight: W_down0 [d][f] (activation dtype)
+ *             when init_from_w0 = 1, else W_start [B][d][f] fp32 per sequence
+ *             (the other may be NULL)
+ *   dO        [B][T][d] activation dtype;  dW_final [B][d][f] fp32 or NULL (0)
+ * Outputs (overwritten):
+ *   dH, dX0   [B][T][d] activation dtype
+ *   dW_gate, dW_up [f][d], dtaps [d][K], dW_target [d][d]: fp32, summed over
+ *             the batch (dtaps / dW_target may be NULL when the target has no
+ *             conv / projection)
+ *   dW_start  [B][d][f] fp32, the gradient of each sequence's starting weight
+ *             (with init_from_w0 = 1 the gradient of W_down0 is their sum)
+ *   d_eta     one fp32 value in device memory
+ *   ws        ttt_mlp_backward_workspace_size(desc) bytes, 256-byte aligned
+ * desc.mode is ignored.  The plain GEMMs run in rocBLAS (one handle per host
+ * thread, created on first use, working in a slice of ws). */
+size_t ttt_mlp_backward_workspace_size(const ttt_mlp_desc_t* desc);
+ttt_status_t ttt_mlp_backward_batched(
+    const ttt_mlp_desc_t* desc, const void* H, const void* X0, const void* W_gate,
+    const void* W_up, const void* W_down0, const float* W_start, const void* conv_taps,
+    const void* W_target, const void* dO, const float* dW_final, void* dH, void* dX0,
+    float* dW_gate, float* dW_up, float* dW_start, float* dtaps, float* dW_target, float* d_eta,
+    void* ws, size_t ws_bytes, void* stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char* ttt_last_error(void);
 

@@ -68,7 +68,10 @@ def backward(H, X0, W_gate, W_up, W_down0, taps, W_target, eta: float, chunk: in
     state per sequence).  Returns float64 arrays: H, X0 [B][T][d]; W_gate,
     W_up [f][d]; W_state0 [B][d][f] (per sequence) and W_down0 [d][f] (their
     sum); taps [d][K] (None without the conv); W_target [d][d] (None without
-    the projection); eta (a float)."""
+    the projection); eta (a float); eta_scale = ||V^||_F ||G||_F with
+    G_j = Z_j S_jᵀ (eta's gradient is the inner product <V^, G>: the bound of
+    its rounding error scales with these norms, not with the result, whose
+    terms largely cancel)."""
     if target not in TARGETS or align not in ALIGNS:
         raise ValueError(f"unknown target/align {target!r}/{align!r}")
     conv = target in ("conv_proj", "conv")
@@ -92,6 +95,7 @@ def backward(H, X0, W_gate, W_up, W_down0, taps, W_target, eta: float, chunk: in
          "W_up": np.zeros((f, d)), "W_state0": np.zeros((B, d, f)),
          "taps": np.zeros_like(tp) if conv else None,
          "W_target": np.zeros((d, d)) if proj else None, "eta": 0.0}
+    v2 = g2 = 0.0
     for b in range(B):
         # forward, keeping what the backward reads
         Ag, Au = H[b] @ Wg.T, H[b] @ Wu.T
@@ -116,6 +120,8 @@ def backward(H, X0, W_gate, W_up, W_down0, taps, W_target, eta: float, chunk: in
             g["eta"] += float(np.sum(S * (V[r].T @ Z[r])))
             S = S + dO[b][r].T @ Z[r]
         g["W_state0"][b] = S
+        v2 += float(np.sum(V * V))
+        g2 += float(np.sum(G * G))
         dV = eta * G
         # SwiGLU: dZ/dA_g = A_u * SiLU'(A_g), dZ/dA_u = SiLU(A_g)
         dAg = dZ * Au * sig * (1.0 + Ag * (1.0 - sig))
@@ -135,4 +141,5 @@ def backward(H, X0, W_gate, W_up, W_down0, taps, W_target, eta: float, chunk: in
         else:
             g["X0"][b] = dU
     g["W_down0"] = g["W_state0"].sum(axis=0)
+    g["eta_scale"] = float(np.sqrt(v2) * np.sqrt(g2))
     return g

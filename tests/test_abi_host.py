@@ -331,3 +331,61 @@ def test_stream_validation(lib):
     assert call_stream(lib, d0, dict(p, W_down0=None), 0, 0) == tm.TTT_ERR_INVALID_ARGUMENT
     assert call_stream(lib, d0, dict(p, W_down0=None), 256, 0) == \
         tm.TTT_ERR_WORKSPACE_TOO_SMALL
+
+
+def backward_ptrs(d, ws_bytes):
+    es = 2 if d.dtype == tm.TTT_BF16 else 4
+    B, T, dm, f, K = d.batch, d.seq_len, d.d_model, d.d_ff, d.conv_k
+    act, st = B * T * dm * es, B * dm * f * 4
+    sizes = dict(H=act, X0=act, W_gate=f * dm * es, W_up=f * dm * es, W_down0=dm * f * es,
+                 W_start=st, taps=dm * K * es, W_target=dm * dm * es, dO=act, dW_final=st,
+                 dH=act, dX0=act, dW_gate=f * dm * 4, dW_up=f * dm * 4, dW_start=st,
+                 dtaps=dm * K * 4, dW_target=dm * dm * 4, d_eta=4, ws=ws_bytes)
+    out, addr = {}, BASE
+    for k, n in sizes.items():
+        out[k] = addr
+        addr += (n + 4095) // 4096 * 4096 + 4096
+    out["ws_bytes"] = ws_bytes
+    return out
+
+
+BACKWARD_ARGS = ("H", "X0", "W_gate", "W_up", "W_down0", "W_start", "taps", "W_target", "dO",
+                 "dW_final", "dH", "dX0", "dW_gate", "dW_up", "dW_start", "dtaps", "dW_target",
+                 "d_eta", "ws")
+
+
+def call_backward(lib, d, p):
+    return lib.ttt_mlp_backward_batched(ctypes.byref(d), *[p[k] for k in BACKWARD_ARGS],
+                                        p["ws_bytes"], None)
+
+
+def test_backward_workspace_and_validation(lib):
+    d = desc(batch=2, seq_len=300, chunk=128)
+    need = tm.ttt_mlp_backward_workspace_size(d)
+    # at least the forward's workspace with one group of all chunks, plus the
+    # backward's own regions (two fp32 [B*T][f] pre-activations among them)
+    assert need > tm.ttt_mlp_workspace_size(d, 3) + 2 * 2 * 300 * 512 * 4
+    p = backward_ptrs(d, need - 256)
+    assert call_backward(lib, d, p) == tm.TTT_ERR_WORKSPACE_TOO_SMALL, tm.ttt_last_error()
+    # optional inputs: W_start with init_from_w0 = 1, dW_final always
+    assert call_backward(lib, d, dict(p, W_start=None, dW_final=None)) == \
+        tm.TTT_ERR_WORKSPACE_TOO_SMALL
+    for name in ("H", "X0", "W_gate", "W_up", "W_down0", "taps", "W_target", "dO", "dH", "dX0",
+                 "dW_gate", "dW_up", "dW_start", "dtaps", "dW_target", "d_eta", "ws"):
+        assert call_backward(lib, d, dict(p, **{name: None})) == tm.TTT_ERR_INVALID_ARGUMENT
+        assert f"{name} is NULL" in tm.ttt_last_error()
+    d0 = desc(batch=2, seq_len=300, chunk=128, init_from_w0=0)
+    assert call_backward(lib, d0, dict(p, W_start=None)) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert call_backward(lib, d0, dict(p, W_down0=None)) == tm.TTT_ERR_WORKSPACE_TOO_SMALL
+    # a target without the conv / projection takes NULL taps, dtaps / W_target, dW_target
+    de = desc(batch=2, seq_len=300, chunk=128, target="embed")
+    pe = backward_ptrs(de, tm.ttt_mlp_backward_workspace_size(de) - 256)
+    assert call_backward(lib, de, dict(pe, taps=None, dtaps=None, W_target=None,
+                                       dW_target=None)) == tm.TTT_ERR_WORKSPACE_TOO_SMALL
+    assert call_backward(lib, d, dict(p, dH=p["H"] + 4096)) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert "overlaps" in tm.ttt_last_error()
+    assert call_backward(lib, d, dict(p, dW_gate=p["dW_up"])) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert call_backward(lib, d, dict(p, ws=p["dO"])) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert call_backward(lib, d, dict(p, dH=p["dH"] + 8)) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert "aligned" in tm.ttt_last_error()
+    assert call_backward(lib, d, dict(p, d_eta=p["d_eta"] + 2)) == tm.TTT_ERR_INVALID_ARGUMENT
