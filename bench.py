@@ -221,6 +221,76 @@ def decode_roofline(w, L: int, us_per_call: float):
             "traffic": None, "algorithmic_bytes_per_call": nbytes}
 
 
+def backward_bench(args, w, dev) -> int:
+    """Tokens/s of the backward pass (ttt_mlp_backward_batched: the forward
+    recomputed, the reverse scan, the GEMMs of every gradient) for a seeded
+    dO and dW_final on the workload."""
+    import torch
+    from chunk_wise_weight_chunked_amd import ttt_mlp as tm
+
+    B, T, d, f, K = w.batch, w.seq_len, w.d_model, w.d_ff, w.conv_k
+    conv = args.target in ("conv_proj", "conv")
+    proj = args.target in ("conv_proj", "proj")
+    desc = tm.make_desc(B, T, d, f, w.chunk, K, w.eta, w.dtype, init_from_w0=1,
+                        target=args.target, align=args.align)
+    ws = torch.empty(tm.ttt_mlp_backward_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(12)
+    dO = torch.randn((B, T, d), generator=gen, device="cuda").to(w.dtype)
+    dWN = 0.01 * torch.randn((B, d, f), generator=gen, device="cuda")
+    f32 = torch.float32
+    outs = [torch.empty_like(dev["H"]), torch.empty_like(dev["H"]),
+            torch.empty((f, d), dtype=f32, device="cuda"),
+            torch.empty((f, d), dtype=f32, device="cuda"),
+            torch.empty((B, d, f), dtype=f32, device="cuda"),
+            torch.empty((d, K), dtype=f32, device="cuda") if conv else None,
+            torch.empty((d, d), dtype=f32, device="cuda") if proj else None,
+            torch.empty(1, dtype=f32, device="cuda")]
+    stream = torch.cuda.current_stream()
+
+    def step():
+        tm.ttt_mlp_backward_batched(desc, dev["H"], dev["X0"], dev["W_gate"], dev["W_up"],
+                                    dev["W_down0"], None, dev["taps"] if conv else None,
+                                    dev["W_target"] if proj else None, dO, dWN, *outs, ws,
+                                    stream=stream)
+
+    log(f"[bench] backward: workspace {ws.numel() / 2**30:.1f} GiB, warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    value = w.tokens / (ms_step / 1e3)
+    dtype = "bf16" if w.dtype == torch.bfloat16 else "f32"
+    # contractions executed per token: the gate and up pre-activations (4df),
+    # the forward's scan and the reverse scan (2 x 2df), dZ (4df), G (2df),
+    # dH (4df), dW_gate and dW_up (4df); with the projection eta V^ (Vt), V^,
+    # dU and dW_target (4 x 2d^2)
+    flops = w.tokens * (22.0 * d * f + (8.0 * d * d if proj else 0.0))
+    frac = flops / (ms_step / 1e3) / (PEAK_TFLOPS[dtype] * 1e12)
+    log(f"[bench] backward {ms_step:.3f} ms/step, {value / 1e6:.3f} M tokens/s, "
+        f"{frac:.1%} of the {dtype} MFMA peak")
+    out = {
+        "metric": "TTT-MLP layer backward tokens/sec",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "seq_len": T, "chunk": w.chunk,
+                   "d_model": d, "d_ff": f, "conv_k": K, "eta": w.eta, "target": args.target,
+                   "align": args.align, "pass": "backward"},
+        "executed_flops_per_step": flops,
+        "layer_mfma_frac": frac,
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def stream_bench(args, w, dev, inp) -> int:
     """Tokens/s of the streaming entry point: each step feeds the B sequences
     from position 0 in calls of L tokens (the last call closes the streams
@@ -304,6 +374,8 @@ def main() -> int:
     ap.add_argument("--chunk", type=int, default=0, help="chunk size C (0 = the workload's)")
     ap.add_argument("--segment", type=int, default=0, metavar="L",
                     help="stream the sequences in calls of L tokens (0 = one call)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (gradients of all inputs) instead")
     ap.add_argument("--segment-calls", type=int, default=0, metavar="N",
                     help="with --segment: time only the first N calls of each step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -356,6 +428,8 @@ def main() -> int:
                         target=args.target, align=args.align)
     if args.segment:
         return stream_bench(args, w, dev, inp)
+    if args.backward:
+        return backward_bench(args, w, dev)
     ws = tm.alloc_workspace(desc, args.max_group)
     group = tm.ttt_mlp_group_size(desc, ws.numel())
     O = torch.empty_like(dev["H"])

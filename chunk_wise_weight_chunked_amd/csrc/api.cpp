@@ -784,30 +784,18 @@ ttt_status_t ttt_mlp_backward_batched(
   float* tpart = reinterpret_cast<float*>(base + bp.tpart);
   float* dpart = reinterpret_cast<float*>(base + bp.dpart);
 
-  // 1. The forward again: starting state, Z / Zt, U and eta V^ (Vt), and the
-  //    weight every chunk uses (one group of all chunks: slot j = W^(j-1)).
+  // 1. The forward again: the starting state, U and eta V^ (Vt).
   hipError_t e = init ? ttt::launch_state_reset(Wst, W_down0, dm.dt, dm.B, dm.d, dm.f, s)
                       : hipMemcpyAsync(Wst, W_start, state, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess) e = ttt::launch_weight_prep(dm, W_gate, W_up, W_target, conv_taps, WgU, WtT, tapsT, s);
   if (e == hipSuccess && (dm.Cp != dm.C || dm.T % dm.C != 0)) e = ttt::launch_pad_fill(Zt, Vt, dm, s);
   if (e == hipSuccess) e = ttt::launch_target(dm, X0, tapsT, WtT, dm.conv ? U : Z, Vt, s);
-  if (e == hipSuccess) e = ttt::launch_swiglu(dm, H, WgU, Z, Zt, s);
-  if (e == hipSuccess)
-    e = ttt::launch_scan_apply(dm, Vt, Zt, Wst, Wslots, 0, dm.N, nullptr, nullptr, nullptr, 0, 0, s);
-  // 2. S_j: the same scan over dOᵀ and Z with the chunks reversed, from
-  //    dW_final; its final state is the gradient of the starting weight.
-  if (e == hipSuccess) e = ttt::launch_to_kblocked_reversed(dO, dOtr, dm, dm.d, s);
-  if (e == hipSuccess) e = ttt::launch_reverse_chunks(Zt, Ztr, dm, dm.f, s);
-  if (e == hipSuccess)
-    e = dW_final ? hipMemcpyAsync(dW_start, dW_final, state, hipMemcpyDeviceToDevice, s)
-                 : ttt::launch_fill_f32(dW_start, (int64_t)(state / 4), 0.0f, s);
-  if (e == hipSuccess)
-    e = ttt::launch_scan_apply(dm, dOtr, Ztr, dW_start, Sslots, 0, dm.N, nullptr, nullptr, nullptr, 0, 0, s);
   if (e == hipSuccess) e = hipMemcpyAsync(Wgu, W_gate, f * d * es, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(Wgu + f * d * es, W_up, f * d * es, hipMemcpyDeviceToDevice, s);
   if (e != hipSuccess) return hip_fail(e, "backward");
 
-  // 3. The plain GEMMs (rocBLAS, fp32 accumulation).
+  // 2. The plain GEMMs run in rocBLAS (fp32 accumulation): first the fp32
+  //    pre-activations A_g = H W_gateᵀ, A_u = H W_upᵀ and V^ = U W_target.
   if (rocblas_set_stream(h, s) != rocblas_status_success ||
       rocblas_set_workspace(h, base + bp.blas, kBlasWorkspace) != rocblas_status_success)
     return fail(TTT_ERR_HIP, "rocblas set-up failed");
@@ -816,25 +804,53 @@ ttt_status_t ttt_mlp_backward_batched(
   Gemm gemm{h, ab, ab};
   const int64_t B = dm.B, T = dm.T, C = dm.C, N = dm.N, sl = (int64_t)(B * d * f);
   const int64_t Di = (int64_t)d, Fi = (int64_t)f, BTi = (int64_t)BT;
-  // pre-activations A_g = H W_gateᵀ, A_u = H W_upᵀ
   gemm(false, true, BTi, Fi, Di, 1.f, H, Di, 0, W_gate, Di, 0, 0.f, Ag, Fi, 0, 1, f32);
   gemm(false, true, BTi, Fi, Di, 1.f, H, Di, 0, W_up, Di, 0, 0.f, Au, Fi, 0, 1, f32);
-  if (dm.proj)  // V^ = U W_target
+  if (dm.proj)
     gemm(false, false, BTi, Di, Di, 1.f, U, Di, 0, W_target, Di, 0, 0.f, V, Di, 0, 1, ab);
-  // per chunk j (all sequences at once): dZ_j = dO_j W^(j-1) + eta V^_j S_j,
-  // G_j = Z_j S_jᵀ; S_j is slot N - 1 - j of the reversed scan
+  if (gemm.st != rocblas_status_success) return fail(TTT_ERR_HIP, "rocblas gemm failed (%d)", (int)gemm.st);
+
+  // 3. Z from them, in row-major and in the scans' k-blocked layout (chunks in
+  //    order and reversed); dOᵀ k-blocked with the chunks reversed.  Then, in
+  //    one launch, the forward's scan (slot j = W^(j-1)) and the same scan
+  //    over dOᵀ and Z in reverse chunk order from dW_final (slot j = S_j; its
+  //    final state is the gradient of the starting weight).
+  e = ttt::launch_swiglu_rows(Ag, Au, Z, dm, s);
+  if (e == hipSuccess) e = ttt::launch_to_kblocked(Z, Zt, dm, dm.f, false, s);
+  if (e == hipSuccess) e = ttt::launch_to_kblocked(Z, Ztr, dm, dm.f, true, s);
+  if (e == hipSuccess) e = ttt::launch_to_kblocked(dO, dOtr, dm, dm.d, true, s);
+  if (e == hipSuccess)
+    e = dW_final ? hipMemcpyAsync(dW_start, dW_final, state, hipMemcpyDeviceToDevice, s)
+                 : ttt::launch_fill_f32(dW_start, (int64_t)(state / 4), 0.0f, s);
+  ttt::Dims dr = dm;
+  dr.reverse_slots = true;  // S_j lands in slot j
+  if (e == hipSuccess)
+    e = ttt::launch_dual_scan(dm, Vt, Zt, Wst, Wslots, dr, dOtr, Ztr, dW_start, Sslots, s);
+  if (e != hipSuccess) return hip_fail(e, "backward");
+
+  // per chunk j: dZ_j = dO_j W^(j-1) + eta V^_j S_j and G_j = Z_j S_jᵀ, with
+  // W^(j-1) and S_j in slot j.  The full chunks of a sequence are one batch
+  // (rows C apart, slots B*d*f apart); a ragged last chunk is one batch over
+  // the sequences.
   const char* Zc = static_cast<const char*>(Z);
-  for (int64_t j = 0; j < N; ++j) {
-    const int64_t Cj = std::min<int64_t>(C, T - j * C), r = j * C;
-    const char* Wj = Wslots + (size_t)(j * sl) * es;
-    const char* Sj = Sslots + (size_t)((N - 1 - j) * sl) * es;
-    gemm(false, false, Cj, Fi, Di, 1.f, static_cast<const char*>(dO) + r * d * es, Di, T * Di, Wj,
-         Fi, Di * Fi, 0.f, dZ + r * f, Fi, T * Fi, B, f32);
-    gemm(false, false, Cj, Fi, Di, dm.eta, static_cast<const char*>(V) + r * d * es, Di, T * Di,
-         Sj, Fi, Di * Fi, 1.f, dZ + r * f, Fi, T * Fi, B, f32);
-    gemm(false, true, Cj, Di, Fi, 1.f, Zc + r * f * es, Fi, T * Fi, Sj, Fi, Di * Fi, 0.f,
-         Gf + r * d, Di, T * Di, B, f32);
-  }
+  const char* dOc = static_cast<const char*>(dO);
+  const char* Vc = static_cast<const char*>(V);
+  auto chunk_gemms = [&](int64_t j, int64_t rows, int64_t b0, int64_t count, int64_t row_stride,
+                         int64_t slot_stride) {
+    const int64_t r = b0 * T + j * C;  // first row
+    const char* Wj = Wslots + (size_t)(j * sl + b0 * Di * Fi) * es;
+    const char* Sj = Sslots + (size_t)(j * sl + b0 * Di * Fi) * es;
+    gemm(false, false, rows, Fi, Di, 1.f, dOc + r * d * es, Di, row_stride * Di, Wj, Fi,
+         slot_stride, 0.f, dZ + r * f, Fi, row_stride * Fi, count, f32);
+    gemm(false, false, rows, Fi, Di, dm.eta, Vc + r * d * es, Di, row_stride * Di, Sj, Fi,
+         slot_stride, 1.f, dZ + r * f, Fi, row_stride * Fi, count, f32);
+    gemm(false, true, rows, Di, Fi, 1.f, Zc + r * f * es, Fi, row_stride * Fi, Sj, Fi,
+         slot_stride, 0.f, Gf + r * d, Di, row_stride * Di, count, f32);
+  };
+  const int64_t full = T / C;
+  if (full > 0)
+    for (int64_t b = 0; b < B; ++b) chunk_gemms(0, C, b, full, C, sl);
+  if (full < N) chunk_gemms(full, T - full * C, 0, B, T, Di * Fi);
   if (gemm.st != rocblas_status_success) return fail(TTT_ERR_HIP, "rocblas gemm failed (%d)", (int)gemm.st);
   // 4. eta's gradient sum_t <V^[t], G[t]>; the SwiGLU derivative; dH and the
   //    gated MLP's weight gradients

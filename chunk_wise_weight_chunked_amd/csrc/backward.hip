@@ -33,34 +33,22 @@ unsigned grid_cap(int64_t n, int64_t per_block, int64_t cap) {
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>(g, cap));
 }
 
-// Copies a k-blocked token-major matrix ([P/64][R][64 tokens] in bytes: each
-// chunk of each sequence is a contiguous run of Cp * R * es bytes) with the
-// chunks of every sequence in reverse order.  16-byte items.
-__global__ void reverse_chunks_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
-                                      int64_t B, int64_t N, int64_t chunk_items) {
-  const int64_t n = B * N * chunk_items, stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < n; it += stride) {
-    const int64_t blk = it / chunk_items, off = it - blk * chunk_items;
-    const int64_t b = blk / N, i = blk - b * N;
-    dst[(b * N + (N - 1 - i)) * chunk_items + off] = src[it];
-  }
-}
-
 // dst = the rows of src ([B][T][R] row-major) in the k-blocked token-major
-// layout [P/TB][R][TB] (TB = 128 bytes of tokens: 64 bf16, 32 fp32) with the
-// chunks of every sequence in reverse order and zeros in the padding columns.
-// One TB-token x 64-row tile per workgroup, through LDS.
+// layout [P/TB][R][TB] (TB = 128 bytes of tokens: 64 bf16, 32 fp32), with the
+// chunks of every sequence in reverse order if `reverse`, and zeros in the
+// padding columns.  One TB-token x 64-row tile per workgroup, through LDS.
 template <typename T>
-__global__ __launch_bounds__(256) void to_kblocked_reversed_kernel(const T* __restrict__ src,
-                                                                   T* __restrict__ dst, Dims dm,
-                                                                   int64_t R) {
+__global__ __launch_bounds__(256) void to_kblocked_kernel(const T* __restrict__ src,
+                                                          T* __restrict__ dst, Dims dm, int64_t R,
+                                                          int32_t reverse) {
   constexpr int TB = kRowBytes / (int)sizeof(T);
   __shared__ float tile[TB][65];
   const int64_t q = blockIdx.x;                 // TB-token block of the reversed layout
   const int64_t r0 = (int64_t)blockIdx.y * 64;  // first row of the tile
   const int64_t tiles_per_chunk = dm.Cp / TB;
   const int64_t chunk_rev = q / tiles_per_chunk, jb = q - chunk_rev * tiles_per_chunk;
-  const int64_t b = chunk_rev / dm.N, i = dm.N - 1 - (chunk_rev - b * dm.N);
+  const int64_t b = chunk_rev / dm.N, i_dst = chunk_rev - b * dm.N;
+  const int64_t i = reverse ? dm.N - 1 - i_dst : i_dst;
   const int64_t len = std::min<int64_t>(dm.C, dm.T - i * dm.C);  // tokens of chunk i
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   for (int e = ty; e < TB; e += 4) {  // token e of the block, row r0 + tx
@@ -80,6 +68,22 @@ __global__ __launch_bounds__(256) void to_kblocked_reversed_kernel(const T* __re
 //   dA_g = dZ * A_u * s * (1 + A_g (1 - s)),  dA_u = dZ * A_g * s.
 // Row t of the output holds [dA_g[t][0..f) | dA_u[t][0..f)] (the A operand
 // of dH = [dA_g | dA_u] [W_gate; W_up]).
+// Z = SiLU(A_g) * A_u from the fp32 pre-activations, in the activation type
+// (the same SiLU as the forward's epilogue).  4 values per item.
+template <typename T>
+__global__ void swiglu_rows_kernel(const float* __restrict__ Ag, const float* __restrict__ Au,
+                                   T* __restrict__ Z, int64_t n4) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < n4; it += stride) {
+    const float4 g = reinterpret_cast<const float4*>(Ag)[it];
+    const float4 u = reinterpret_cast<const float4*>(Au)[it];
+    const float gg[4] = {g.x, g.y, g.z, g.w}, uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      Elem<T>::store(Z + it * 4 + e, gg[e] * __builtin_amdgcn_rcpf(1.0f + __expf(-gg[e])) * uu[e]);
+  }
+}
+
 template <typename T>
 __global__ void swiglu_backward_kernel(const float* __restrict__ dZ, const float* __restrict__ Ag,
                                        const float* __restrict__ Au, T* __restrict__ dA,
@@ -205,25 +209,31 @@ __global__ void fill_f32_kernel(float* __restrict__ out, int64_t n, float v) {
 
 }  // namespace
 
-hipError_t launch_reverse_chunks(const void* src, void* dst, const Dims& dm, int64_t R,
-                                 hipStream_t s) {
-  const int64_t chunk_items = dm.Cp * R * (int64_t)dtype_bytes(dm.dt) / 16;
-  hipLaunchKernelGGL(reverse_chunks_kernel, dim3(grid_cap(dm.B * dm.N * chunk_items, 256, 65536)),
-                     dim3(256), 0, s, static_cast<const uint4*>(src), static_cast<uint4*>(dst),
-                     dm.B, dm.N, chunk_items);
-  return hipGetLastError();
-}
-
-hipError_t launch_to_kblocked_reversed(const void* src, void* dst, const Dims& dm, int64_t R,
-                                       hipStream_t s) {
+hipError_t launch_to_kblocked(const void* src, void* dst, const Dims& dm, int64_t R, bool reverse,
+                              hipStream_t s) {
   const int64_t tb = kRowBytes / (int64_t)dtype_bytes(dm.dt);
   const dim3 grid((unsigned)(dm.P / tb), (unsigned)((R + 63) / 64));
   if (dm.dt == Dtype::BF16)
-    hipLaunchKernelGGL(to_kblocked_reversed_kernel<uint16_t>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), dm, R);
+    hipLaunchKernelGGL(to_kblocked_kernel<uint16_t>, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), dm, R,
+                       reverse ? 1 : 0);
   else
-    hipLaunchKernelGGL(to_kblocked_reversed_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(src), static_cast<float*>(dst), dm, R);
+    hipLaunchKernelGGL(to_kblocked_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float*>(src), static_cast<float*>(dst), dm, R,
+                       reverse ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_rows(const float* Ag, const float* Au, void* Z, const Dims& dm,
+                              hipStream_t s) {
+  const int64_t n4 = dm.B * dm.T * dm.f / 4;
+  const dim3 g(grid_cap(n4, 256, 65536));
+  if (dm.dt == Dtype::BF16)
+    hipLaunchKernelGGL(swiglu_rows_kernel<uint16_t>, g, dim3(256), 0, s, Ag, Au,
+                       static_cast<uint16_t*>(Z), n4);
+  else
+    hipLaunchKernelGGL(swiglu_rows_kernel<float>, g, dim3(256), 0, s, Ag, Au,
+                       static_cast<float*>(Z), n4);
   return hipGetLastError();
 }
 

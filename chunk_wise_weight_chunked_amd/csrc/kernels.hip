@@ -484,7 +484,8 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
 
   const int64_t slot_stride = dm.B * d * f;
   auto write_slot = [&](int64_t jj) {
-    const rsrc_t sr = make_rsrc(slots + jj * slot_stride + b * d * f + corner,
+    const int64_t js = dm.reverse_slots ? gc - 1 - jj : jj;
+    const rsrc_t sr = make_rsrc(slots + js * slot_stride + b * d * f + corner,
                                 span * (int64_t)sizeof(T));
 #pragma unroll
     for (int i = 0; i < S::MB; ++i)
@@ -634,6 +635,27 @@ TTT_GEMM_KERNEL void scan_apply_kernel(Dims dm, const T* __restrict__ Vt, const 
   }
   down_proj_tile<T>(dm, Z, apply_slots, O, a0, ac, b - scan_pad, (int)gridDim.x - scan_pad,
                     (lds_char*)smem_raw);
+}
+
+// Two independent scans of all N chunks (the backward's forward weights and
+// its chunk-reversed gradient sums) in one launch: one group of all chunks
+// gives ~1.5 waves of tiles per scan, two together fill the chip better.
+template <typename T>
+TTT_GEMM_KERNEL void dual_scan_kernel(Dims d1, const T* __restrict__ Vt1, const T* __restrict__ Zt1,
+                                      float* __restrict__ W1, T* __restrict__ slots1, Dims d2,
+                                      const T* __restrict__ Vt2, const T* __restrict__ Zt2,
+                                      float* __restrict__ W2, T* __restrict__ slots2, int blocks,
+                                      int pad) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[Tile::kLdsBytes];
+  const int b = blockIdx.x;
+  if (b < pad) {
+    if (b < blocks)
+      prefix_update_tile<T, PrefixTile>(d1, Vt1, Zt1, W1, slots1, 0, d1.N, b, blocks,
+                                        (lds_char*)smem_raw);
+  } else if (b - pad < blocks) {
+    prefix_update_tile<T, PrefixTile>(d2, Vt2, Zt2, W2, slots2, 0, d2.N, b - pad, blocks,
+                                      (lds_char*)smem_raw);
+  }
 }
 
 // ============================================================ small kernels
@@ -951,6 +973,32 @@ hipError_t launch_scan_apply(const Dims& dm, const void* Vt, const void* Zt, flo
                                W_state, static_cast<float*>(scan_slots), g0, gc,
                                static_cast<const float*>(Z), static_cast<const float*>(apply_slots),
                                static_cast<float*>(O), a0, ac, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_dual_scan(const Dims& d1, const void* Vt1, const void* Zt1, float* W1,
+                            void* slots1, const Dims& d2, const void* Vt2, const void* Zt2,
+                            float* W2, void* slots2, hipStream_t s) {
+  if (d1.d % PrefixTile::BM != 0 || d1.f % PrefixTile::BN != 0) {
+    hipError_t e = launch_scan_apply(d1, Vt1, Zt1, W1, slots1, 0, d1.N, nullptr, nullptr, nullptr,
+                                     0, 0, s);
+    if (e != hipSuccess) return e;
+    return launch_scan_apply(d2, Vt2, Zt2, W2, slots2, 0, d2.N, nullptr, nullptr, nullptr, 0, 0, s);
+  }
+  const int blocks = (int)((d1.d / PrefixTile::BM) * (d1.f / PrefixTile::BN) * d1.B);
+  const int pad = (blocks + 7) / 8 * 8;  // the second scan starts on XCD 0
+  if (d1.dt == Dtype::BF16)
+    hipLaunchKernelGGL(dual_scan_kernel<uint16_t>, dim3((unsigned)(pad + blocks)),
+                       dim3(Tile::kThreads), 0, s, d1, static_cast<const uint16_t*>(Vt1),
+                       static_cast<const uint16_t*>(Zt1), W1, static_cast<uint16_t*>(slots1), d2,
+                       static_cast<const uint16_t*>(Vt2), static_cast<const uint16_t*>(Zt2), W2,
+                       static_cast<uint16_t*>(slots2), blocks, pad);
+  else
+    hipLaunchKernelGGL(dual_scan_kernel<float>, dim3((unsigned)(pad + blocks)),
+                       dim3(Tile::kThreads), 0, s, d1, static_cast<const float*>(Vt1),
+                       static_cast<const float*>(Zt1), W1, static_cast<float*>(slots1), d2,
+                       static_cast<const float*>(Vt2), static_cast<const float*>(Zt2), W2,
+                       static_cast<float*>(slots2), blocks, pad);
   return hipGetLastError();
 }
 

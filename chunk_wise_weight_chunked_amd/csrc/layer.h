@@ -31,6 +31,7 @@ struct Dims {
   const void* halo = nullptr;  // [B][halo_stride]: kHaloRows X0 rows before each session's row 0
   int64_t halo_stride = 0;     // elements between sessions in `halo`
   bool skip_last = false;      // leave the last chunk's update out of the state
+  bool reverse_slots = false;  // the scan writes chunk jj's slot at gc - 1 - jj
   int64_t out_skip = 0;        // rows [0, out_skip) of each session are not output ...
   int64_t out_T = 0;           // ... and output row t goes to O row b * out_T + t - out_skip
 };
@@ -98,12 +99,17 @@ hipError_t launch_state_to_bf16(const float* W, void* out, int64_t n, hipStream_
 // Backward-pass kernels (backward.hip).
 constexpr int kTargetBackwardRows = 256;  // token rows per partial sum of the taps' gradient
 constexpr int kDotPartials = 1024;        // partial sums of the learning rate's gradient
-// dst = src (k-blocked token-major, R rows) with each sequence's chunks reversed.
-hipError_t launch_reverse_chunks(const void* src, void* dst, const Dims& dm, int64_t R,
-                                 hipStream_t s);
-// dst = rows of src [B][T][R] in the k-blocked token-major layout, chunks reversed.
-hipError_t launch_to_kblocked_reversed(const void* src, void* dst, const Dims& dm, int64_t R,
-                                       hipStream_t s);
+// dst = rows of src [B][T][R] in the k-blocked token-major layout (chunks
+// reversed if `reverse`), zeros in the padding columns.
+hipError_t launch_to_kblocked(const void* src, void* dst, const Dims& dm, int64_t R, bool reverse,
+                              hipStream_t s);
+// Z [B*T][f] = SiLU(A_g) * A_u (activation type) from fp32 pre-activations.
+hipError_t launch_swiglu_rows(const float* Ag, const float* Au, void* Z, const Dims& dm,
+                              hipStream_t s);
+// The scans of two independent problems (same shapes) in one launch.
+hipError_t launch_dual_scan(const Dims& d1, const void* Vt1, const void* Zt1, float* W1,
+                            void* slots1, const Dims& d2, const void* Vt2, const void* Zt2,
+                            float* W2, void* slots2, hipStream_t s);
 // dA [B*T][2f] = [dA_g | dA_u] from dZ, A_g, A_u (fp32 [B*T][f]).
 hipError_t launch_swiglu_backward(const float* dZ, const float* Ag, const float* Au, void* dA,
                                   const Dims& dm, hipStream_t s);
