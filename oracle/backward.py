@@ -143,3 +143,54 @@ def backward(H, X0, W_gate, W_up, W_down0, taps, W_target, eta: float, chunk: in
     g["W_down0"] = g["W_state0"].sum(axis=0)
     g["eta_scale"] = float(np.sqrt(v2) * np.sqrt(g2))
     return g
+
+
+def sampled_weight_grads(H, X0, W_gate, W_up, W_down0, taps, W_target, eta: float, chunk: int,
+                         dO, features, dW_final=None, target: str = "conv_proj",
+                         align: str = "next") -> dict:
+    """Rows `features` of dW_gate and dW_up and columns `features` of each
+    sequence's dW_start, at a cost of O(T d) per feature (plus V^ once), for
+    checking full-size runs.  Column f' of every W^(j) and S_j only involves
+    column f' of Z:  W^(j)[:, f'] = W0[:, f'] + eta sum_{m <= j} V^_mᵀ Z_m[:, f'],
+    S_j[:, f'] = dW_final[:, f'] + sum_{m > j} dO_mᵀ Z_m[:, f'], so
+    dZ[t][f'] = dO[t] . W^(j-1)[:, f'] + eta V^[t] . S_j[:, f'] needs no other
+    feature; then dA_g, dA_u for that feature and their products with H.
+    Returns W_gate, W_up [len(features)][d] and W_start [B][d][len(features)]."""
+    conv = target in ("conv_proj", "conv")
+    proj = target in ("conv_proj", "proj")
+    shift = 1 if align == "next" else 0
+    H, X0, dO = _f64(H), _f64(X0), _f64(dO)
+    if H.ndim == 2:
+        H, X0, dO = H[None], X0[None], dO[None]
+    B, T, d = H.shape
+    Wg, Wu, W0 = _f64(W_gate), _f64(W_up), _f64(W_down0)
+    f = Wg.shape[0]
+    if W0.ndim == 2:
+        W0 = np.broadcast_to(W0, (B, d, f))
+    F = np.asarray(features, dtype=np.int64)
+    dWN = np.zeros((B, d, f)) if dW_final is None else np.broadcast_to(_f64(dW_final), (B, d, f))
+    C = int(chunk)
+    N = -(-T // C)
+    out = {"W_gate": np.zeros((len(F), d)), "W_up": np.zeros((len(F), d)),
+           "W_start": np.zeros((B, d, len(F)))}
+    for b in range(B):
+        U = _conv(X0[b], _f64(taps), shift) if conv else X0[b]
+        V = U @ _f64(W_target) if proj else U
+        Ag, Au = H[b] @ Wg[F].T, H[b] @ Wu[F].T          # [T][|F|]
+        sig = 1.0 / (1.0 + np.exp(-Ag))
+        Z = Ag * sig * Au
+        # per chunk: V^_jᵀ Z_j[:, F] and dO_jᵀ Z_j[:, F]  ([d][|F|] each)
+        inc_w = np.stack([V[j * C:(j + 1) * C].T @ Z[j * C:(j + 1) * C] for j in range(N)])
+        inc_s = np.stack([dO[b][j * C:(j + 1) * C].T @ Z[j * C:(j + 1) * C] for j in range(N)])
+        W_used = W0[b][:, F] + eta * (np.cumsum(inc_w, axis=0) - inc_w)          # W^(j-1)
+        S = dWN[b][:, F] + (inc_s.sum(axis=0) - np.cumsum(inc_s, axis=0))       # S_j
+        dZ = np.zeros_like(Z)
+        for j in range(N):
+            r = slice(j * C, min(T, (j + 1) * C))
+            dZ[r] = dO[b][r] @ W_used[j] + eta * V[r] @ S[j]
+        dAg = dZ * Au * sig * (1.0 + Ag * (1.0 - sig))
+        dAu = dZ * Ag * sig
+        out["W_gate"] += dAg.T @ H[b]
+        out["W_up"] += dAu.T @ H[b]
+        out["W_start"][b] = dWN[b][:, F] + inc_s.sum(axis=0)
+    return out

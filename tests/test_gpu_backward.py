@@ -129,3 +129,37 @@ def test_backward_rejects_bad_arguments():
     with pytest.raises(tm.TTTError) as e:
         tm.ttt_mlp_backward_batched(desc, *bad, ws)
     assert "dO is NULL" in str(e.value)
+
+
+@pytest.mark.parametrize("name", ["qwen3_4b_128k", "multi_session_16x8k"])
+def test_backward_full_size_sampled(name):
+    """The backward at a full workload size, as `bench.py --backward` runs it:
+    rows of dW_gate / dW_up and columns of dW_start for a few features against
+    the oracle's per-feature form (which needs only those features of Z)."""
+    from oracle.backward import sampled_weight_grads
+    w = synth.WORKLOADS[name]
+    print(f"[backward full] {name}: drawing inputs", flush=True)
+    inp = synth.workload_inputs(w)
+    gen = torch.Generator().manual_seed(60)
+    B, T, d, f = w.batch, w.seq_len, w.d_model, w.d_ff
+    dO = torch.randn((B, T, d), generator=gen).to(w.dtype)
+    dWN = 0.01 * torch.randn((B, d, f), generator=gen)
+    dev = to_device(inp)
+    g = tm.backward_batched(dev["H"], dev["X0"], dev["W_gate"], dev["W_up"], dev["W_down0"],
+                            dev["taps"], dev["W_target"], w.eta, w.chunk, dO.cuda(),
+                            dW_final=dWN.cuda())
+    torch.cuda.synchronize()
+    F = [0, 4097, f - 1]
+    got = {"W_gate": g["W_gate"][F].cpu().numpy(), "W_up": g["W_up"][F].cpu().numpy(),
+           "W_start": g["W_start"][:, :, F].cpu().numpy()}
+    del g, dev
+    torch.cuda.empty_cache()
+    print(f"[backward full] {name}: oracle on features {F}", flush=True)
+    ni = numpy_inputs(inp)
+    ref = sampled_weight_grads(ni["H"], ni["X0"], ni["W_gate"], ni["W_up"], ni["W_down0"],
+                               ni["taps"], ni["W_target"], w.eta, w.chunk,
+                               dO.float().numpy(), F, dWN.numpy())
+    errs = {k: rel(got[k], ref[k]) for k in got}
+    print("  " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= tol_for(w.dtype), (k, v)

@@ -135,3 +135,23 @@ def test_backward_with_eta_zero():
     Z = oracle.gated_activations(inp["H"][0], inp["W_gate"], inp["W_up"])
     ref = dWN[0].astype(np.float64) + dO[0].astype(np.float64).T @ Z
     np.testing.assert_allclose(g["W_down0"], ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("target,align", [("conv_proj", "next"), ("conv", "self"),
+                                          ("embed", "next")])
+def test_sampled_weight_grads_match_the_full_backward(target, align):
+    """The per-feature form used on full-size runs gives the full backward's
+    rows of dW_gate / dW_up and columns of dW_start."""
+    from oracle.backward import sampled_weight_grads
+    B, T, d, f, K, C = 2, 29, 8, 12, 3, 6
+    inp, dO, dWN = rand_case(B, T, d, f, K, seed=404)
+    eta = 0.1
+    g = backward(inp["H"], inp["X0"], inp["W_gate"], inp["W_up"], inp["W_down0"], inp["taps"],
+                 inp["W_target"], eta, C, dO, dWN, target=target, align=align)
+    F = [0, 5, 11]
+    s = sampled_weight_grads(inp["H"], inp["X0"], inp["W_gate"], inp["W_up"], inp["W_down0"],
+                             inp["taps"], inp["W_target"], eta, C, dO, F, dWN, target=target,
+                             align=align)
+    np.testing.assert_allclose(s["W_gate"], g["W_gate"][F], rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(s["W_up"], g["W_up"][F], rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(s["W_start"], g["W_state0"][:, :, F], rtol=1e-11, atol=1e-11)
