@@ -868,8 +868,8 @@ ttt_status_t ttt_mlp_backward_batched(
     gemm(true, false, Di, Di, BTi, dm.eta, U, Di, 0, G, Di, 0, 0.f, dW_target, Di, 0, 1, f32);
   }
   if (gemm.st != rocblas_status_success) return fail(TTT_ERR_HIP, "rocblas gemm failed (%d)", (int)gemm.st);
-  e = dm.proj ? ttt::launch_target_backward(dU, true, 1.0f, X0, tapsT, dX0, tpart, dtaps, dm, s)
-              : ttt::launch_target_backward(Gf, true, dm.eta, X0, tapsT, dX0, tpart, dtaps, dm, s);
+  e = dm.proj ? ttt::launch_target_backward(dU, 1.0f, X0, tapsT, dX0, tpart, dtaps, dm, s)
+              : ttt::launch_target_backward(Gf, dm.eta, X0, tapsT, dX0, tpart, dtaps, dm, s);
   if (e != hipSuccess) return hip_fail(e, "backward");
   return ok();
 }

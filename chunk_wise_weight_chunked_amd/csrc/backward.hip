@@ -105,47 +105,85 @@ __global__ void swiglu_backward_kernel(const float* __restrict__ dZ, const float
   }
 }
 
-// The target's backward.  dU[t][c] = scale * src[t][c] (src: the gradient of
-// U, or of V^ = U when there is no projection).  With the conv
+// Four consecutive values of the activation type, as floats.
+template <typename T>
+__device__ __forceinline__ float4 ld4(const T* p);
+template <>
+__device__ __forceinline__ float4 ld4<float>(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+template <>
+__device__ __forceinline__ float4 ld4<uint16_t>(const uint16_t* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return make_float4(bf16_bits_to_f32(v.x & 0xffffu), bf16_bits_to_f32(v.x >> 16),
+                     bf16_bits_to_f32(v.y & 0xffffu), bf16_bits_to_f32(v.y >> 16));
+}
+template <typename T>
+__device__ __forceinline__ void st4(T* p, float4 v);
+template <>
+__device__ __forceinline__ void st4<float>(float* p, float4 v) {
+  *reinterpret_cast<float4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void st4<uint16_t>(uint16_t* p, float4 v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+}
+__device__ __forceinline__ float4 fma4(float a, float4 x, float4 y) {
+  return make_float4(fmaf(a, x.x, y.x), fmaf(a, x.y, y.y), fmaf(a, x.z, y.z), fmaf(a, x.w, y.w));
+}
+__device__ __forceinline__ float4 fma4v(float4 a, float4 x, float4 y) {
+  return make_float4(fmaf(a.x, x.x, y.x), fmaf(a.y, x.y, y.y), fmaf(a.z, x.z, y.z),
+                     fmaf(a.w, x.w, y.w));
+}
+
+// The target's backward.  dU[t][c] = scale * src[t][c] (src: fp32, the
+// gradient of U, or of V^ = U when there is no projection).  With the conv
 // (U[t][c] = sum_k taps[c][k] X0[t + shift - k][c]):
-//   dX0[s][c] = sum_k taps[c][k] dU[s - shift + k][c]   (t inside the sequence)
+//   dX0[s][c] = sum_k taps[c][k] dU[s - shift + k][c]   (rows of the same sequence)
 //   part[r][k][c] = sum over the rows of range r of dU[t][c] X0[t + shift - k][c]
-// without it dX0 = dU.  Thread = one feature c, looping over the rows of its
-// token range (blockIdx.y); partial tap sums are reduced in a second pass.
-template <typename T, typename S>
+// without it dX0 = dU.  Thread = four consecutive features, looping over the
+// rows of its token range (blockIdx.y); partial tap sums are reduced in a
+// second pass.
+template <typename T>
 __global__ __launch_bounds__(256) void target_backward_kernel(
-    const S* __restrict__ src, float scale, const T* __restrict__ X0,
+    const float* __restrict__ src, float scale, const T* __restrict__ X0,
     const float* __restrict__ tapsT, T* __restrict__ dX0, float* __restrict__ part, Dims dm,
     int64_t rows_per_range) {
-  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t c = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (c >= dm.d) return;
   const int64_t d = dm.d, BT = dm.B * dm.T, T_seq = dm.T;
   const int64_t r0 = (int64_t)blockIdx.y * rows_per_range;
   const int64_t r1 = std::min<int64_t>(BT, r0 + rows_per_range);
   const int K = dm.conv ? dm.K : 0;
-  float tp[8], acc[8];
+  float4 tp[8], acc[8];
   for (int k = 0; k < 8; ++k) {
-    tp[k] = k < K ? tapsT[k * d + c] : 0.f;
-    acc[k] = 0.f;
+    tp[k] = k < K ? *reinterpret_cast<const float4*>(tapsT + k * d + c)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   for (int64_t t = r0; t < r1; ++t) {
     const int64_t b = t / T_seq, s = t - b * T_seq;
+    const float4 du0 = *reinterpret_cast<const float4*>(src + t * d + c);
     if (!dm.conv) {
-      Elem<T>::store(dX0 + t * d + c, scale * ld_f32<S>(src + t * d + c));
+      st4<T>(dX0 + t * d + c, make_float4(scale * du0.x, scale * du0.y, scale * du0.z,
+                                          scale * du0.w));
       continue;
     }
-    const float du = scale * ld_f32<S>(src + t * d + c);
-    float dx = 0.f;
+    float4 dx = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int k = 0; k < K; ++k) {
       const int64_t xs = s + dm.shift - k;  // X0 row tap k of output row s reads
-      if (xs >= 0 && xs < T_seq) acc[k] = fmaf(du, ld_f32<T>(X0 + (b * T_seq + xs) * d + c), acc[k]);
+      if (xs >= 0 && xs < T_seq) acc[k] = fma4(scale, fma4v(du0, ld4<T>(X0 + (b * T_seq + xs) * d + c),
+                                                            make_float4(0.f, 0.f, 0.f, 0.f)),
+                                               acc[k]);
       const int64_t us = s - dm.shift + k;  // output row whose tap k reads X0 row s
-      if (us >= 0 && us < T_seq) dx = fmaf(tp[k], scale * ld_f32<S>(src + (b * T_seq + us) * d + c), dx);
+      if (us >= 0 && us < T_seq)
+        dx = fma4v(tp[k], *reinterpret_cast<const float4*>(src + (b * T_seq + us) * d + c), dx);
     }
-    Elem<T>::store(dX0 + t * d + c, dx);
+    st4<T>(dX0 + t * d + c, make_float4(scale * dx.x, scale * dx.y, scale * dx.z, scale * dx.w));
   }
   if (dm.conv)
-    for (int k = 0; k < K; ++k) part[((int64_t)blockIdx.y * 8 + k) * d + c] = acc[k];
+    for (int k = 0; k < K; ++k)
+      *reinterpret_cast<float4*>(part + ((int64_t)blockIdx.y * 8 + k) * d + c) = acc[k];
 }
 
 // dtaps[c][k] = sum over ranges r (in order) of part[r][k][c].
@@ -254,27 +292,19 @@ int64_t target_backward_ranges(const Dims& dm) {
   return (dm.B * dm.T + kTargetBackwardRows - 1) / kTargetBackwardRows;
 }
 
-hipError_t launch_target_backward(const void* src, bool src_f32, float scale, const void* X0,
+hipError_t launch_target_backward(const float* src, float scale, const void* X0,
                                   const float* tapsT, void* dX0, float* part, float* dtaps,
                                   const Dims& dm, hipStream_t s) {
   const int64_t ranges = target_backward_ranges(dm);
-  const dim3 grid((unsigned)((dm.d + 255) / 256), (unsigned)ranges);
-  if (dm.dt == Dtype::BF16) {
-    const auto x0 = static_cast<const uint16_t*>(X0);
-    const auto dx = static_cast<uint16_t*>(dX0);
-    if (src_f32)
-      hipLaunchKernelGGL((target_backward_kernel<uint16_t, float>), grid, dim3(256), 0, s,
-                         static_cast<const float*>(src), scale, x0, tapsT, dx, part, dm,
-                         (int64_t)kTargetBackwardRows);
-    else
-      hipLaunchKernelGGL((target_backward_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, s,
-                         static_cast<const uint16_t*>(src), scale, x0, tapsT, dx, part, dm,
-                         (int64_t)kTargetBackwardRows);
-  } else {
-    hipLaunchKernelGGL((target_backward_kernel<float, float>), grid, dim3(256), 0, s,
-                       static_cast<const float*>(src), scale, static_cast<const float*>(X0), tapsT,
-                       static_cast<float*>(dX0), part, dm, (int64_t)kTargetBackwardRows);
-  }
+  const dim3 grid((unsigned)((dm.d / 4 + 255) / 256), (unsigned)ranges);
+  if (dm.dt == Dtype::BF16)
+    hipLaunchKernelGGL(target_backward_kernel<uint16_t>, grid, dim3(256), 0, s, src, scale,
+                       static_cast<const uint16_t*>(X0), tapsT, static_cast<uint16_t*>(dX0), part,
+                       dm, (int64_t)kTargetBackwardRows);
+  else
+    hipLaunchKernelGGL(target_backward_kernel<float>, grid, dim3(256), 0, s, src, scale,
+                       static_cast<const float*>(X0), tapsT, static_cast<float*>(dX0), part, dm,
+                       (int64_t)kTargetBackwardRows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !dm.conv) return e;
   hipLaunchKernelGGL(taps_reduce_kernel, dim3((unsigned)((dm.d * dm.K + 255) / 256)), dim3(256),

@@ -113,10 +113,10 @@ hipError_t launch_dual_scan(const Dims& d1, const void* Vt1, const void* Zt1, fl
 // dA [B*T][2f] = [dA_g | dA_u] from dZ, A_g, A_u (fp32 [B*T][f]).
 hipError_t launch_swiglu_backward(const float* dZ, const float* Ag, const float* Au, void* dA,
                                   const Dims& dm, hipStream_t s);
-// dX0 and dtaps from dU = scale * src (fp32 or the activation type); `part`
-// holds target_backward_ranges(dm) * 8 * d floats.
+// dX0 and dtaps from dU = scale * src (fp32 [B*T][d]); `part` holds
+// target_backward_ranges(dm) * 8 * d floats.
 int64_t target_backward_ranges(const Dims& dm);
-hipError_t launch_target_backward(const void* src, bool src_f32, float scale, const void* X0,
+hipError_t launch_target_backward(const float* src, float scale, const void* X0,
                                   const float* tapsT, void* dX0, float* part, float* dtaps,
                                   const Dims& dm, hipStream_t s);
 // *out = scale * sum_i a[i] b[i] (a: activation type, b: fp32); `part` holds
