@@ -315,13 +315,16 @@ size_t carry_bytes(const ttt::Dims& dm, int64_t C) {
   return carry_wcur_offset(dm, C) + (size_t)dm.B * dm.d * dm.f * 2;
 }
 
-// Calls the decode kernels serve: bf16, not closing the stream, at most 16
-// new rows per session and 64 in all, and no update due (the new rows stay in
-// the pending chunk, which is not complete before the call).
+// Sessions the decode kernels serve: in a bf16 call of at most 16 new rows
+// per session and 64 in all, a session that does not close its stream and
+// whose new rows stay in its pending chunk (no update due: the chunk is not
+// complete before the call).
 constexpr int64_t kDecodeMaxRows = 16, kDecodeMaxTotal = 64;
-bool decode_call(const ttt::Dims& du, int64_t C, int64_t n_pend, int32_t last) {
-  return du.dt == ttt::Dtype::BF16 && last == 0 && du.T <= kDecodeMaxRows &&
-         du.B * du.T <= kDecodeMaxTotal && n_pend + du.T <= C;
+bool decode_shape(const ttt::Dims& du) {
+  return du.dt == ttt::Dtype::BF16 && du.T <= kDecodeMaxRows && du.B * du.T <= kDecodeMaxTotal;
+}
+bool decode_session(int64_t L, int64_t C, int64_t n_pend, int32_t last) {
+  return last == 0 && n_pend + L <= C;
 }
 
 // A streaming call's workspace: the layer's workspace for the virtual
@@ -444,70 +447,46 @@ size_t ttt_mlp_stream_workspace_size(const ttt_mlp_desc_t* desc, int64_t max_gro
   return sp.total;
 }
 
-ttt_status_t ttt_mlp_forward_stream(const ttt_mlp_desc_t* desc, int64_t pos, int32_t last,
-                                    const void* H, const void* X0, const void* W_gate,
-                                    const void* W_up, const void* W_down0, const void* conv_taps,
-                                    const void* W_target, void* O, float* W_state, void* carry,
-                                    void* ws, size_t ws_bytes, void* stream) {
-  ttt::Dims du;  // the call's own L tokens (user buffers)
-  ttt_status_t st = make_dims(desc, &du);
-  if (st) return st;
-  if (pos < 0) return fail(TTT_ERR_INVALID_ARGUMENT, "pos must be >= 0 (got %lld)", (long long)pos);
-  if (last != 0 && last != 1) return fail(TTT_ERR_INVALID_ARGUMENT, "last must be 0 or 1");
-  const bool need_carry = pos > 0 || last == 0;
-  if (need_carry && !carry) return fail(TTT_ERR_INVALID_ARGUMENT, "carry is NULL");
-  if (need_carry && !aligned(carry, 16))
-    return fail(TTT_ERR_INVALID_ARGUMENT, "carry is not 16-byte aligned");
-  const bool init = desc->init_from_w0 == 1 && pos == 0;
-  const Buffers b{H, X0, W_gate, W_up, W_down0, conv_taps, W_target, O, W_state, ws, ws_bytes};
-  st = check_buffers(du, b, init);
-  if (st) return st;
-  if (need_carry) {
-    const Range c = range("carry", carry, carry_bytes(du, desc->chunk));
-    const Range others[] = {range("H", H, (size_t)(du.B * du.T) * du.d * ttt::dtype_bytes(du.dt)),
-                            range("X0", X0, (size_t)(du.B * du.T) * du.d * ttt::dtype_bytes(du.dt)),
-                            range("O", O, (size_t)(du.B * du.T) * du.d * ttt::dtype_bytes(du.dt)),
-                            range("W_state", W_state, (size_t)du.B * du.d * du.f * sizeof(float)),
-                            range("ws", ws, ws_bytes)};
-    for (const Range& o : others)
-      if (overlaps(c, o)) return fail(TTT_ERR_INVALID_ARGUMENT, "carry overlaps %s", o.name);
-  }
-  StreamPlan sp;
-  st = plan_stream(desc, 0, ws_bytes, &sp);
-  if (st) return st;
+}  // extern "C"
 
-  const int64_t C = desc->chunk, L = du.T;
-  const int64_t n_pend = pending_tokens(pos, C);
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  char* cb = static_cast<char*>(carry);
+namespace {
+
+// Sessions [b0, b0 + nb) of a stream call, all at position `pos`, through the
+// full path: the layer over their pending rows and the new ones.  Pointers are
+// those of the whole call; the sessions' rows, states and carries are found by
+// offset (each session's carry rows are contiguous, and so are the bf16
+// weight copies).
+ttt_status_t stream_full(const ttt_mlp_desc_t* desc, int64_t b0, int64_t nb, int64_t pos,
+                         int32_t last, const void* H, const void* X0, const void* W_gate,
+                         const void* W_up, const void* W_down0, const void* conv_taps,
+                         const void* W_target, void* O, float* W_state, void* carry, void* ws,
+                         size_t ws_bytes, hipStream_t s) {
+  ttt::Dims du;
+  make_dims(desc, &du);  // validated by the caller
+  const int64_t C = desc->chunk, L = du.T, d = du.d, f = du.f;
   const size_t es = ttt::dtype_bytes(du.dt);
-  if (decode_call(du, C, n_pend, last)) {
-    // The outputs of the new rows with the current weight; the rows join the
-    // pending chunk, whose update a later call makes.
-    void* wcur = cb + carry_wcur_offset(du, C);
-    hipError_t e = hipSuccess;
-    if (pos == 0) {
-      if (init) e = ttt::launch_state_reset(W_state, W_down0, du.dt, du.B, du.d, du.f, s);
-      if (e == hipSuccess) e = ttt::launch_state_to_bf16(W_state, wcur, du.B * du.d * du.f, s);
-      if (e != hipSuccess) return hip_fail(e, "decode state");
-    }
-    void* Zd = ws;  // [B·L][f]
-    e = ttt::launch_decode_swiglu(H, du.B * L, W_gate, W_up, Zd, du.d, du.f, X0, carry, du.B, L,
-                                  n_pend, C, pos == 0, s);
-    if (e == hipSuccess) e = ttt::launch_decode_down(Zd, wcur, O, du.B, L, du.d, du.f, s);
-    if (e != hipSuccess) return hip_fail(e, "decode");
-    return ok();
-  }
+  const size_t carry_seq = (size_t)(2 * C + ttt::kHaloRows) * d;  // elements per session
+  char* cb = static_cast<char*>(carry);
+  char* rows = cb + (size_t)b0 * carry_seq * es;
+  char* wcur = cb + carry_wcur_offset(du, C) + (size_t)b0 * d * f * 2;
+  H = static_cast<const char*>(H) + (size_t)(b0 * L * d) * es;
+  X0 = static_cast<const char*>(X0) + (size_t)(b0 * L * d) * es;
+  O = static_cast<char*>(O) + (size_t)(b0 * L * d) * es;
+  W_state += b0 * d * f;
 
-  ttt_mlp_desc_t vq = *desc;
-  vq.seq_len = n_pend + L;
-  ttt::Dims dv;
-  st = make_dims(&vq, &dv);
+  ttt_mlp_desc_t q = *desc;
+  q.batch = nb;
+  StreamPlan sp;
+  ttt_status_t st = plan_stream(&q, 0, ws_bytes, &sp);
   if (st) return st;
-  const size_t carry_seq = (size_t)(2 * C + ttt::kHaloRows) * dv.d;  // elements per session
+  const int64_t n_pend = pending_tokens(pos, C);
+  q.seq_len = n_pend + L;
+  ttt::Dims dv;
+  st = make_dims(&q, &dv);
+  if (st) return st;
   char* base = static_cast<char*>(ws);
   if (pos > 0) {
-    dv.halo = cb + (size_t)C * dv.d * ttt::dtype_bytes(dv.dt);
+    dv.halo = rows + (size_t)C * d * es;
     dv.halo_stride = (int64_t)carry_seq;
   }
   dv.skip_last = last == 0;
@@ -519,24 +498,144 @@ ttt_status_t ttt_mlp_forward_stream(const ttt_mlp_desc_t* desc, int64_t pos, int
 
   void* Hv = base + sp.hv_off;
   void* X0v = base + sp.x0v_off;
-  hipError_t e = ttt::launch_stream_build(dv, H, X0, carry, Hv, X0v, L, n_pend, C, s);
+  hipError_t e = ttt::launch_stream_build(dv, H, X0, rows, Hv, X0v, L, n_pend, C, s);
   if (e != hipSuccess) return hip_fail(e, "stream_build");
+  const bool init = desc->init_from_w0 == 1 && pos == 0;
   st = run_layer(dv, desc->mode, init, Hv, X0v, W_gate, W_up, W_down0, conv_taps, W_target, O,
                  W_state, ws, sp.layer_bytes, s);
   if (st) return st;
   if (last == 0) {
     const int64_t c_new = (dv.T - 1) / C * C;
     void* tmp = base + sp.tmp_off;
-    e = ttt::launch_stream_save(dv, Hv, X0v, pos > 0 ? carry : nullptr, tmp, c_new, C, s);
+    e = ttt::launch_stream_save(dv, Hv, X0v, pos > 0 ? rows : nullptr, tmp, c_new, C, s);
     if (e != hipSuccess) return hip_fail(e, "stream_save");
-    e = hipMemcpyAsync(carry, tmp, carry_rows_bytes(dv, C), hipMemcpyDeviceToDevice, s);
+    e = hipMemcpyAsync(rows, tmp, carry_rows_bytes(dv, C), hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "carry copy");
     if (dv.dt == ttt::Dtype::BF16) {
-      e = ttt::launch_state_to_bf16(W_state, cb + carry_wcur_offset(dv, C), dv.B * dv.d * dv.f, s);
+      e = ttt::launch_state_to_bf16(W_state, wcur, nb * d * f, s);
       if (e != hipSuccess) return hip_fail(e, "carry weight");
     }
   }
+  return TTT_OK;
+}
+
+// A stream call with per-session positions and closing flags.
+ttt_status_t stream_call(const ttt_mlp_desc_t* desc, const int64_t* pos, const int32_t* last,
+                         const void* H, const void* X0, const void* W_gate, const void* W_up,
+                         const void* W_down0, const void* conv_taps, const void* W_target,
+                         void* O, float* W_state, void* carry, void* ws, size_t ws_bytes,
+                         void* stream) {
+  ttt::Dims du;  // the call's own L tokens (user buffers)
+  ttt_status_t st = make_dims(desc, &du);
+  if (st) return st;
+  if (!pos || !last) return fail(TTT_ERR_INVALID_ARGUMENT, "pos and last must be non-NULL");
+  const int64_t B = du.B;
+  bool need_carry = false, need_w0 = false;
+  for (int64_t b = 0; b < B; ++b) {
+    if (pos[b] < 0)
+      return fail(TTT_ERR_INVALID_ARGUMENT, "pos must be >= 0 (got %lld for session %lld)",
+                  (long long)pos[b], (long long)b);
+    if (last[b] != 0 && last[b] != 1)
+      return fail(TTT_ERR_INVALID_ARGUMENT, "last must be 0 or 1 (session %lld)", (long long)b);
+    need_carry |= pos[b] > 0 || last[b] == 0;
+    need_w0 |= desc->init_from_w0 == 1 && pos[b] == 0;
+  }
+  if (need_carry && !carry) return fail(TTT_ERR_INVALID_ARGUMENT, "carry is NULL");
+  if (need_carry && !aligned(carry, 16))
+    return fail(TTT_ERR_INVALID_ARGUMENT, "carry is not 16-byte aligned");
+  const Buffers bufs{H, X0, W_gate, W_up, W_down0, conv_taps, W_target, O, W_state, ws, ws_bytes};
+  st = check_buffers(du, bufs, need_w0);
+  if (st) return st;
+  if (need_carry) {
+    const size_t act = (size_t)(du.B * du.T) * du.d * ttt::dtype_bytes(du.dt);
+    const Range c = range("carry", carry, carry_bytes(du, desc->chunk));
+    const Range others[] = {range("H", H, act), range("X0", X0, act), range("O", O, act),
+                            range("W_state", W_state, (size_t)du.B * du.d * du.f * sizeof(float)),
+                            range("ws", ws, ws_bytes)};
+    for (const Range& o : others)
+      if (overlaps(c, o)) return fail(TTT_ERR_INVALID_ARGUMENT, "carry overlaps %s", o.name);
+  }
+  StreamPlan sp;
+  st = plan_stream(desc, 0, ws_bytes, &sp);  // the whole batch: the largest sub-call fits
+  if (st) return st;
+
+  const int64_t C = desc->chunk, L = du.T, d = du.d, f = du.f;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* cb = static_cast<char*>(carry);
+  std::vector<int64_t> n_pend(B);
+  std::vector<char> dec(B, 0);
+  uint64_t mask = 0, zero_halo = 0;
+  const bool shape = decode_shape(du);
+  for (int64_t b = 0; b < B; ++b) {
+    n_pend[b] = pending_tokens(pos[b], C);
+    dec[b] = shape && decode_session(L, C, n_pend[b], last[b]);
+    if (dec[b]) {
+      mask |= uint64_t{1} << b;
+      if (pos[b] == 0) zero_halo |= uint64_t{1} << b;
+    }
+  }
+  if (mask) {
+    // The decode sessions: their new rows' outputs with the current weight;
+    // the rows join their pending chunks, whose updates later calls make.
+    char* wcur = cb + carry_wcur_offset(du, C);
+    hipError_t e = hipSuccess;
+    for (int64_t b = 0; b < B && e == hipSuccess; ++b) {
+      if (!dec[b] || pos[b] != 0) continue;
+      if (desc->init_from_w0 == 1)
+        e = ttt::launch_state_reset(W_state + b * d * f, W_down0, du.dt, 1, d, f, s);
+      if (e == hipSuccess)
+        e = ttt::launch_state_to_bf16(W_state + b * d * f, wcur + (size_t)b * d * f * 2, d * f, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "decode state");
+    void* Zd = ws;  // [B·L][f]
+    e = ttt::launch_decode_swiglu(H, B * L, W_gate, W_up, Zd, d, f, X0, carry, B, L,
+                                  n_pend.data(), C, mask, zero_halo, s);
+    if (e == hipSuccess) e = ttt::launch_decode_down(Zd, wcur, O, B, L, d, f, mask, s);
+    if (e != hipSuccess) return hip_fail(e, "decode");
+  }
+  // The other sessions through the full path, one call per run of
+  // consecutive sessions at the same position and with the same flag.
+  for (int64_t b0 = 0; b0 < B;) {
+    if (dec[b0]) {
+      ++b0;
+      continue;
+    }
+    int64_t b1 = b0 + 1;
+    while (b1 < B && !dec[b1] && pos[b1] == pos[b0] && last[b1] == last[b0]) ++b1;
+    st = stream_full(desc, b0, b1 - b0, pos[b0], last[b0], H, X0, W_gate, W_up, W_down0,
+                     conv_taps, W_target, O, W_state, carry, ws, ws_bytes, s);
+    if (st) return st;
+    b0 = b1;
+  }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+ttt_status_t ttt_mlp_forward_stream(const ttt_mlp_desc_t* desc, int64_t pos, int32_t last,
+                                    const void* H, const void* X0, const void* W_gate,
+                                    const void* W_up, const void* W_down0, const void* conv_taps,
+                                    const void* W_target, void* O, float* W_state, void* carry,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  ttt::Dims du;
+  ttt_status_t st = make_dims(desc, &du);
+  if (st) return st;
+  const std::vector<int64_t> p(du.B, pos);
+  const std::vector<int32_t> l(du.B, last);
+  return stream_call(desc, p.data(), l.data(), H, X0, W_gate, W_up, W_down0, conv_taps, W_target,
+                     O, W_state, carry, ws, ws_bytes, stream);
+}
+
+ttt_status_t ttt_mlp_forward_stream_ragged(const ttt_mlp_desc_t* desc, const int64_t* pos,
+                                           const int32_t* last, const void* H, const void* X0,
+                                           const void* W_gate, const void* W_up,
+                                           const void* W_down0, const void* conv_taps,
+                                           const void* W_target, void* O, float* W_state,
+                                           void* carry, void* ws, size_t ws_bytes, void* stream) {
+  return stream_call(desc, pos, last, H, X0, W_gate, W_up, W_down0, conv_taps, W_target, O,
+                     W_state, carry, ws, ws_bytes, stream);
 }
 
 ttt_status_t ttt_fastweight_state_reset(float* W_state, const void* W_down0, ttt_dtype_t w0_dtype,

@@ -47,28 +47,30 @@ __device__ __forceinline__ float dec_silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
-// The new rows of every session join the pending chunk in the carry: H rows
-// at n_pend.., X0 rows after the halo; at the start of a stream the halo (the
-// rows before the sequence) is set to zero.  16-byte items, vpr per row.
+// The new rows of the sessions in `mask` join their pending chunks in the
+// carry: H rows at n_pend[b].., X0 rows after the halo; a session at the start
+// of its stream (bit b of zero_halo) gets a zero halo (the rows before its
+// sequence).  16-byte items, vpr per row.
 struct CarryAppend {
   const uint4* H;
   const uint4* X0;
   uint4* carry;
-  int64_t B, L, n_pend, C, vpr;
-  int32_t zero_halo;
-  __device__ __forceinline__ int64_t items() const {
-    return B * (2 * L + (zero_halo ? kHaloRows : 0)) * vpr;
-  }
+  int64_t B, L, C, vpr;
+  uint64_t mask, zero_halo;
+  int32_t n_pend[kDecodeMaxSessions];
+  __device__ __forceinline__ int64_t items() const { return B * (2 * L + kHaloRows) * vpr; }
   __device__ void run(int64_t first, int64_t stride) const {
-    const int64_t rows = 2 * L + (zero_halo ? kHaloRows : 0), carry_seq = (2 * C + kHaloRows) * vpr;
+    const int64_t rows = 2 * L + kHaloRows, carry_seq = (2 * C + kHaloRows) * vpr;
     for (int64_t it = first; it < items(); it += stride) {
       const int64_t b = it / (rows * vpr), rr = it % (rows * vpr) / vpr, c = it % vpr;
+      if (!((mask >> b) & 1)) continue;
+      const int64_t np = n_pend[b];
       uint4* seq = carry + b * carry_seq;
       if (rr < L)
-        seq[(n_pend + rr) * vpr + c] = H[(b * L + rr) * vpr + c];
+        seq[(np + rr) * vpr + c] = H[(b * L + rr) * vpr + c];
       else if (rr < 2 * L)
-        seq[(C + kHaloRows + n_pend + rr - L) * vpr + c] = X0[(b * L + rr - L) * vpr + c];
-      else
+        seq[(C + kHaloRows + np + rr - L) * vpr + c] = X0[(b * L + rr - L) * vpr + c];
+      else if ((zero_halo >> b) & 1)
         seq[(C + rr - 2 * L) * vpr + c] = make_uint4(0, 0, 0, 0);
     }
   }
@@ -168,16 +170,19 @@ __global__ __launch_bounds__(64 * WAVES) void decode_swiglu_kernel(
   *reinterpret_cast<uint2*>(Z + m * f + f0 + 4 * q) = out;
 }
 
-// O[b][t][c] = Z[b][t] · W_cur[b][c] for the L <= 16 new rows of session b.
-// Workgroup = 16 output channels of one session; WAVES waves split k = f.
+// O[b][t][c] = Z[b][t] · W_cur[b][c] for the L <= 16 new rows of each session
+// b in `mask`.  Workgroup = 16 output channels of one session; WAVES waves
+// split k = f.
 template <int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void decode_down_kernel(
     const uint16_t* __restrict__ Z, const uint16_t* __restrict__ Wc, uint16_t* __restrict__ O,
-    int64_t L, int64_t d, int64_t f) {
+    int64_t L, int64_t d, int64_t f, uint64_t mask) {
   __shared__ floatx4_t red[WAVES][64];
+  const int64_t b = blockIdx.y;
+  if (!((mask >> b) & 1)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, q = lane >> 4;
-  const int64_t b = blockIdx.y, c0 = (int64_t)blockIdx.x * kDecRows;
+  const int64_t c0 = (int64_t)blockIdx.x * kDecRows;
   const uint16_t* w = Wc + (b * d + c0 + r) * f + 16 * q;
   const bool zv = r < L;
   const uint16_t* z = Z + (b * L + (zv ? r : 0)) * f + 16 * q;
@@ -247,19 +252,21 @@ unsigned grid_cap(int64_t n, int64_t per_block, int64_t cap) {
 
 hipError_t launch_decode_swiglu(const void* H, int64_t M, const void* Wg, const void* Wu, void* Z,
                                 int64_t d, int64_t f, const void* X0, void* carry, int64_t B,
-                                int64_t L, int64_t n_pend, int64_t C, bool zero_halo,
-                                hipStream_t s) {
+                                int64_t L, const int64_t* n_pend, int64_t C, uint64_t mask,
+                                uint64_t zero_halo, hipStream_t s) {
+  if (B > kDecodeMaxSessions) return hipErrorInvalidValue;
   CarryAppend app;
   app.H = static_cast<const uint4*>(H);
   app.X0 = static_cast<const uint4*>(X0);
   app.carry = static_cast<uint4*>(carry);
   app.B = B;
   app.L = L;
-  app.n_pend = n_pend;
   app.C = C;
   app.vpr = d * 2 / 16;
-  app.zero_halo = zero_halo ? 1 : 0;
-  const int64_t items = B * (2 * L + (zero_halo ? kHaloRows : 0)) * app.vpr;
+  app.mask = mask;
+  app.zero_halo = zero_halo;
+  for (int64_t b = 0; b < kDecodeMaxSessions; ++b) app.n_pend[b] = b < B ? (int32_t)n_pend[b] : 0;
+  const int64_t items = B * (2 * L + kHaloRows) * app.vpr;
   const dim3 grid((unsigned)(f / kDecRows + grid_cap(items, 512, 64)));
   const auto h = static_cast<const uint16_t*>(H);
   const auto g = static_cast<const uint16_t*>(Wg);
@@ -275,10 +282,11 @@ hipError_t launch_decode_swiglu(const void* H, int64_t M, const void* Wg, const 
 }
 
 hipError_t launch_decode_down(const void* Z, const void* Wc, void* O, int64_t B, int64_t L,
-                              int64_t d, int64_t f, hipStream_t s) {
+                              int64_t d, int64_t f, uint64_t mask, hipStream_t s) {
+  if (B > kDecodeMaxSessions) return hipErrorInvalidValue;
   hipLaunchKernelGGL((decode_down_kernel<8>), dim3((unsigned)(d / kDecRows), (unsigned)B),
                      dim3(512), 0, s, static_cast<const uint16_t*>(Z),
-                     static_cast<const uint16_t*>(Wc), static_cast<uint16_t*>(O), L, d, f);
+                     static_cast<const uint16_t*>(Wc), static_cast<uint16_t*>(O), L, d, f, mask);
   return hipGetLastError();
 }
 

@@ -85,15 +85,17 @@ hipError_t launch_stream_save(const Dims& dv, const void* Hv, const void* X0v, c
                               void* out, int64_t c_new, int64_t C, hipStream_t s);
 
 // Decode kernels (bf16 only).  Z[M][f] = SiLU(H W_gateᵀ) ⊙ (H W_upᵀ) for M <= 64
-// rows, with the new H and X0 rows of the B sessions appended to the carry's
-// pending chunk in the same launch; O[b][L][d] = Z[b][L] W_cur[b]ᵀ for L <= 16
-// rows per session; W_cur = bf16(W_state).
+// rows, with the new H and X0 rows of the sessions in `mask` appended to their
+// carries' pending chunks (at n_pend[b]; a zero halo for those in zero_halo)
+// in the same launch; O[b][L][d] = Z[b][L] W_cur[b]ᵀ for L <= 16 rows of each
+// session in `mask`; W_cur = bf16(W_state).  At most kDecodeMaxSessions sessions.
+constexpr int kDecodeMaxSessions = 64;
 hipError_t launch_decode_swiglu(const void* H, int64_t M, const void* Wg, const void* Wu, void* Z,
                                 int64_t d, int64_t f, const void* X0, void* carry, int64_t B,
-                                int64_t L, int64_t n_pend, int64_t C, bool zero_halo,
-                                hipStream_t s);
+                                int64_t L, const int64_t* n_pend, int64_t C, uint64_t mask,
+                                uint64_t zero_halo, hipStream_t s);
 hipError_t launch_decode_down(const void* Z, const void* Wc, void* O, int64_t B, int64_t L,
-                              int64_t d, int64_t f, hipStream_t s);
+                              int64_t d, int64_t f, uint64_t mask, hipStream_t s);
 hipError_t launch_state_to_bf16(const float* W, void* out, int64_t n, hipStream_t s);
 
 // Backward-pass kernels (backward.hip).

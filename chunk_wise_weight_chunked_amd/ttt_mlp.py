@@ -65,6 +65,7 @@ EXPORTS = (
     "ttt_mlp_forward_batched", "ttt_fastweight_state_reset", "ttt_last_error",
     "ttt_profile_enable", "ttt_profile_read", "ttt_stage_name",
     "ttt_mlp_carry_size", "ttt_mlp_stream_workspace_size", "ttt_mlp_forward_stream",
+    "ttt_mlp_forward_stream_ragged",
     "ttt_mlp_backward_workspace_size", "ttt_mlp_backward_batched",
 )
 
@@ -107,6 +108,8 @@ def load(path: str | None = None):
     lib.ttt_mlp_stream_workspace_size.restype = sz
     lib.ttt_mlp_forward_stream.argtypes = [dp, i64, ctypes.c_int32] + [vp] * 11 + [sz, vp]
     lib.ttt_mlp_forward_stream.restype = ctypes.c_int
+    lib.ttt_mlp_forward_stream_ragged.argtypes = [dp, vp, vp] + [vp] * 11 + [sz, vp]
+    lib.ttt_mlp_forward_stream_ragged.restype = ctypes.c_int
     lib.ttt_mlp_backward_workspace_size.argtypes = [dp]
     lib.ttt_mlp_backward_workspace_size.restype = sz
     lib.ttt_mlp_backward_batched.argtypes = [dp] + [vp] * 18 + [vp, sz, vp]
@@ -304,6 +307,24 @@ def forward_batched(H, X0, W_gate, W_up, W_down0, conv_taps, W_target, eta, chun
     ttt_mlp_forward_batched(desc, H, X0, W_gate, W_up, W_down0 if init else None, conv_taps,
                             W_target, O, W_state, ws, stream=stream)
     return O, W_state
+
+
+def ttt_mlp_forward_stream_ragged(desc, pos, last, H, X0, W_gate, W_up, W_down0, conv_taps,
+                                  W_target, O, W_state, carry, ws, ws_bytes=None,
+                                  stream=None) -> None:
+    """pos, last: sequences of B ints (each session's position and closing flag)."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    B = desc.batch
+    if len(pos) != B or len(last) != B:
+        raise ValueError(f"pos and last need {B} entries")
+    p = (ctypes.c_int64 * B)(*[int(x) for x in pos])
+    l_ = (ctypes.c_int32 * B)(*[int(x) for x in last])
+    _check(load().ttt_mlp_forward_stream_ragged(
+        ctypes.byref(desc), ctypes.cast(p, ctypes.c_void_p), ctypes.cast(l_, ctypes.c_void_p),
+        _ptr(H), _ptr(X0), _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(conv_taps),
+        _ptr(W_target), _ptr(O), _ptr(W_state), _ptr(carry), _ptr(ws), int(ws_bytes),
+        _stream(stream)))
 
 
 def ttt_mlp_backward_workspace_size(desc: ttt_mlp_desc_t) -> int:

@@ -232,6 +232,22 @@ ttt_status_t ttt_mlp_forward_stream(const ttt_mlp_desc_t* desc, int64_t pos, int
                                     const void* W_target, void* O, float* W_state, void* carry,
                                     void* ws, size_t ws_bytes, void* stream);
 
+/* Ragged batches: the same call with each session's own position pos[b] and
+ * closing flag last[b] (host arrays of B entries), as a server batching
+ * sessions that joined and end at different times needs.  A slot whose
+ * session closed may start a new one at pos 0 in the next call (its state is
+ * set from W_down0 when init_from_w0 = 1, its carry restarts).  Sessions the
+ * decode rule above admits are served together by the decode kernels; the
+ * others by the full path, one pass per run of consecutive sessions with equal
+ * position and flag.  ttt_mlp_forward_stream is this call with every pos[b] =
+ * pos and last[b] = last.  ws as for ttt_mlp_forward_stream. */
+ttt_status_t ttt_mlp_forward_stream_ragged(const ttt_mlp_desc_t* desc, const int64_t* pos,
+                                           const int32_t* last, const void* H, const void* X0,
+                                           const void* W_gate, const void* W_up,
+                                           const void* W_down0, const void* conv_taps,
+                                           const void* W_target, void* O, float* W_state,
+                                           void* carry, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- Backward pass ----
  * Gradients of a loss L through the layer, given dO = dL/dO and (optionally)
  * dW_final = dL/dW_state after the call, for B sequences laid out as in

@@ -389,3 +389,32 @@ def test_backward_workspace_and_validation(lib):
     assert call_backward(lib, d, dict(p, dH=p["dH"] + 8)) == tm.TTT_ERR_INVALID_ARGUMENT
     assert "aligned" in tm.ttt_last_error()
     assert call_backward(lib, d, dict(p, d_eta=p["d_eta"] + 2)) == tm.TTT_ERR_INVALID_ARGUMENT
+
+
+def test_stream_ragged_validation(lib):
+    d = desc(batch=3, seq_len=16, chunk=64)
+    w1 = tm.ttt_mlp_stream_workspace_size(d, 1)
+    p = stream_ptrs(d, w1 - 256)
+
+    def call(pos, last, q=p):
+        P = (ctypes.c_int64 * 3)(*pos)
+        L = (ctypes.c_int32 * 3)(*last)
+        return lib.ttt_mlp_forward_stream_ragged(
+            ctypes.byref(d), ctypes.cast(P, ctypes.c_void_p), ctypes.cast(L, ctypes.c_void_p),
+            q["H"], q["X0"], q["W_gate"], q["W_up"], q["W_down0"], q["taps"], q["W_target"],
+            q["O"], q["W"], q["carry"], q["ws"], q["ws_bytes"], None)
+
+    assert call([0, 64, 7], [0, 1, 0]) == tm.TTT_ERR_WORKSPACE_TOO_SMALL, tm.ttt_last_error()
+    assert call([0, -1, 7], [0, 0, 0]) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert "session 1" in tm.ttt_last_error()
+    assert call([0, 1, 7], [0, 0, 3]) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert "last" in tm.ttt_last_error()
+    # every session closing from the start: no carry needed; W_down0 only
+    # needed while some session starts at 0 with init_from_w0
+    assert call([0, 0, 0], [1, 1, 1], dict(p, carry=None)) == tm.TTT_ERR_WORKSPACE_TOO_SMALL
+    assert call([0, 5, 0], [1, 1, 1], dict(p, carry=None)) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert call([8, 5, 9], [0, 1, 0], dict(p, W_down0=None)) == tm.TTT_ERR_WORKSPACE_TOO_SMALL
+    assert call([8, 0, 9], [0, 1, 0], dict(p, W_down0=None)) == tm.TTT_ERR_INVALID_ARGUMENT
+    assert lib.ttt_mlp_forward_stream_ragged(ctypes.byref(d), None, None, *[p[k] for k in (
+        "H", "X0", "W_gate", "W_up", "W_down0", "taps", "W_target", "O", "W", "carry", "ws")],
+        p["ws_bytes"], None) == tm.TTT_ERR_INVALID_ARGUMENT

@@ -160,3 +160,72 @@ def test_stream_rejects_bad_arguments():
     with pytest.raises(tm.TTTError) as e:
         tm.ttt_mlp_forward_stream(desc, 0, 0, *args, carry, ws, ws_bytes=1024)
     assert e.value.status == tm.TTT_ERR_WORKSPACE_TOO_SMALL
+
+
+# Three slots over eight calls of L tokens: slot 0 runs sequence 0 (40 tokens)
+# then sequence 3 (24 tokens) from a fresh start; slot 1 runs sequence 1 (64
+# tokens); slot 2 runs two one-call sequences (4, 5) and then sequence 2 (48
+# tokens).  Each call passes every slot's own position and closing flag.
+RAGGED_SLOTS = [[(0, 40), (3, 24)], [(1, 64)], [(4, 8), (5, 8), (2, 48)]]
+
+
+@pytest.mark.parametrize("dtype,L,C", [(torch.bfloat16, 8, 16), (torch.float32, 8, 16),
+                                       (torch.bfloat16, 24, 16)],
+                         ids=["bf16-decode", "f32", "bf16-L24"])
+def test_ragged_sessions_equal_their_own_runs(dtype, L, C):
+    d, f, K = 128, 192, 4
+    scale = L // 8
+    slots = [[(q, n * scale) for q, n in s] for s in RAGGED_SLOTS]
+    B = len(slots)
+    inp = synth.make_inputs(6, 64 * scale, d, f, K, dtype, seed=95)
+    dev = to_device(inp)
+    eta = 2e-2
+    w = (dev["W_gate"], dev["W_up"], dev["W_down0"], dev["taps"], dev["W_target"])
+    ref = {}
+    for q in range(6):
+        n = max(m for s in slots for (qq, m) in s if qq == q)
+        ref[q] = tm.forward_batched(dev["H"][q:q + 1, :n].contiguous(),
+                                    dev["X0"][q:q + 1, :n].contiguous(), *w, eta, C)
+    calls = sum(m for _, m in slots[0]) // L
+    desc = tm.make_desc(B, L, d, f, C, K, eta, dtype)
+    ws = torch.empty(tm.ttt_mlp_stream_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    carry = torch.empty(tm.ttt_mlp_carry_size(desc), dtype=torch.uint8, device="cuda")
+    state = torch.empty((B, d, f), dtype=torch.float32, device="cuda")
+    outs = {q: [] for q in range(6)}
+    finals, dec_rows = {}, {q: [] for q in range(6)}
+    cursor = [[0, 0] for _ in range(B)]  # (index of the slot's sequence, its position)
+    for j in range(calls):
+        pos, last, hs, xs, seqs = [], [], [], [], []
+        for b in range(B):
+            k, p = cursor[b]
+            q, n = slots[b][k]
+            pos.append(p)
+            last.append(1 if p + L == n else 0)
+            hs.append(dev["H"][q, p:p + L])
+            xs.append(dev["X0"][q, p:p + L])
+            seqs.append(q)
+            n_pend = 0 if p == 0 else p - (p - 1) // C * C
+            dec = dtype == torch.bfloat16 and L <= 16 and B * L <= 64 and not last[-1] \
+                and n_pend + L <= C
+            dec_rows[q] += [dec] * L
+        O = torch.empty((B, L, d), dtype=dtype, device="cuda")
+        tm.ttt_mlp_forward_stream_ragged(desc, pos, last, torch.stack(hs).contiguous(),
+                                         torch.stack(xs).contiguous(), *w, O, state, carry, ws)
+        for b in range(B):
+            outs[seqs[b]].append(O[b].clone())
+            if last[b]:
+                finals[seqs[b]] = state[b].clone()
+                cursor[b] = [cursor[b][0] + 1, 0]
+            else:
+                cursor[b][1] += L
+    torch.cuda.synchronize()
+    for q in range(6):
+        Oq = torch.cat(outs[q])
+        O1, W1 = ref[q]
+        assert torch.equal(finals[q], W1[0]), q
+        dec = torch.tensor(dec_rows[q], device="cuda")
+        assert torch.equal(Oq[~dec], O1[0][~dec]), q
+        if dec.any():
+            e = rel(Oq[dec].double().cpu().numpy(), O1[0][dec].double().cpu().numpy())
+            assert e <= 1e-2, (q, e)
+    print(f"  decode rows: {sum(sum(v) for v in dec_rows.values())}", flush=True)
