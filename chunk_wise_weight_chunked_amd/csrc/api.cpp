@@ -720,7 +720,9 @@ namespace {
 // own regions, 256-byte aligned.
 struct BackwardPlan {
   ttt::WorkspacePlan fwd;
-  size_t wst, u, v, ag, au, ztr, dotr, sslots, dz, da, wgu, g, gf, du, tpart, dpart, blas, total;
+  size_t wst, u, v, ag, au, ztr, dotr, sslots, dz, da, wgu, g, gf, du, tpart, dpart, wtpart,
+      blas, total;
+  int64_t wt_slices;  // token slices of the dW_target product (split over K = B*T)
 };
 
 constexpr size_t kBlasWorkspace = (size_t)32 << 20;
@@ -752,6 +754,10 @@ BackwardPlan plan_backward(const ttt::Dims& dm) {
   p.du = take(dm.proj ? BT * d * 4 : 0);                  // dU (fp32)
   p.tpart = take((size_t)ttt::target_backward_ranges(dm) * 8 * d * 4);
   p.dpart = take((size_t)ttt::kDotPartials * 4);
+  // dW_target = Uᵀ dV^ is d x d with K = B*T: one product per slice of about
+  // 2048 tokens keeps the GPU busy, the slices are then added in order
+  p.wt_slices = dm.proj ? std::max<int64_t>(1, std::min<int64_t>(16, (int64_t)BT / 2048)) : 0;
+  p.wtpart = take((size_t)p.wt_slices * d * d * 4);
   p.blas = take(kBlasWorkspace);
   p.total = off;
   return p;
@@ -964,9 +970,22 @@ ttt_status_t ttt_mlp_backward_batched(
   //    the conv's transpose (or dX0 = dU without the conv)
   if (dm.proj) {
     gemm(false, true, BTi, Di, Di, dm.eta, G, Di, 0, W_target, Di, 0, 0.f, dU, Di, 0, 1, f32);
-    gemm(true, false, Di, Di, BTi, dm.eta, U, Di, 0, G, Di, 0, 0.f, dW_target, Di, 0, 1, f32);
+    // split over token slices: slices - 1 of `rows` tokens, the last the rest
+    const int64_t S = bp.wt_slices, rows = BTi / S, rest = BTi - (S - 1) * rows;
+    float* wtp = reinterpret_cast<float*>(base + bp.wtpart);
+    if (S > 1)
+      gemm(true, false, Di, Di, rows, dm.eta, U, Di, rows * Di, G, Di, rows * Di, 0.f, wtp, Di,
+           Di * Di, S - 1, f32);
+    gemm(true, false, Di, Di, rest, dm.eta, static_cast<const char*>(U) + (S - 1) * rows * Di * es,
+         Di, 0, static_cast<const char*>(G) + (S - 1) * rows * Di * es, Di, 0, 0.f,
+         wtp + (S - 1) * Di * Di, Di, 0, 1, f32);
   }
   if (gemm.st != rocblas_status_success) return fail(TTT_ERR_HIP, "rocblas gemm failed (%d)", (int)gemm.st);
+  if (dm.proj) {
+    e = ttt::launch_sum_slices(reinterpret_cast<float*>(base + bp.wtpart), dW_target, Di * Di,
+                               (int)bp.wt_slices, s);
+    if (e != hipSuccess) return hip_fail(e, "backward");
+  }
   e = dm.proj ? ttt::launch_target_backward(dU, 1.0f, X0, tapsT, dX0, tpart, dtaps, dm, s)
               : ttt::launch_target_backward(Gf, dm.eta, X0, tapsT, dX0, tpart, dtaps, dm, s);
   if (e != hipSuccess) return hip_fail(e, "backward");

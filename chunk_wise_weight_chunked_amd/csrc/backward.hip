@@ -239,6 +239,17 @@ __global__ void from_f32_kernel(const float* __restrict__ in, T* __restrict__ ou
     Elem<T>::store(out + i, in[i]);
 }
 
+// out[i] = sum over s (in order) of part[s][i].
+__global__ void sum_slices_kernel(const float* __restrict__ part, float* __restrict__ out,
+                                  int64_t n, int slices) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    float s = 0.f;
+    for (int k = 0; k < slices; ++k) s += part[(int64_t)k * n + i];
+    out[i] = s;
+  }
+}
+
 // out[i] = v.
 __global__ void fill_f32_kernel(float* __restrict__ out, int64_t n, float v) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -333,6 +344,13 @@ hipError_t launch_from_f32(const float* in, void* out, int64_t n, Dtype dt, hipS
                        static_cast<uint16_t*>(out), n);
   else
     hipLaunchKernelGGL(from_f32_kernel<float>, g, dim3(256), 0, s, in, static_cast<float*>(out), n);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_slices(const float* part, float* out, int64_t n, int slices,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(sum_slices_kernel, dim3(grid_cap(n, 256, 16384)), dim3(256), 0, s, part, out,
+                     n, slices);
   return hipGetLastError();
 }
 

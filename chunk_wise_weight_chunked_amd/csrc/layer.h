@@ -127,5 +127,8 @@ hipError_t launch_dot(const void* a, const float* b, int64_t n, Dtype dt, float 
                       float* out, hipStream_t s);
 hipError_t launch_from_f32(const float* in, void* out, int64_t n, Dtype dt, hipStream_t s);
 hipError_t launch_fill_f32(float* out, int64_t n, float v, hipStream_t s);
+// out[i] = sum over s < slices (in order) of part[s * n + i].
+hipError_t launch_sum_slices(const float* part, float* out, int64_t n, int slices,
+                             hipStream_t s);
 
 }  // namespace ttt
