@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(BUILD, "libttt_mlp.so")
-SOURCES = ["kernels.hip", "decode.hip", "backward.hip", "api.cpp"]
+SOURCES = ["kernels.hip", "decode.hip", "backward.hip", "api.cpp", "backward_api.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
