@@ -36,38 +36,49 @@ unsigned grid_cap(int64_t n, int64_t per_block, int64_t cap) {
 // dst = the rows of src ([B][T][R] row-major) in the k-blocked token-major
 // layout [P/TB][R][TB] (TB = 128 bytes of tokens: 64 bf16, 32 fp32), with the
 // chunks of every sequence in reverse order if `reverse`, and zeros in the
-// padding columns.  One TB-token x 64-row tile per workgroup, through LDS.
+// padding columns.  One TB-token x 64-row tile per workgroup, through LDS;
+// global reads and writes are 16 bytes per lane.
 template <typename T>
 __global__ __launch_bounds__(256) void to_kblocked_kernel(const T* __restrict__ src,
                                                           T* __restrict__ dst, Dims dm, int64_t R,
                                                           int32_t reverse) {
   constexpr int TB = kRowBytes / (int)sizeof(T);
-  __shared__ float tile[TB][65];
-  const int64_t q = blockIdx.x;                 // TB-token block of the reversed layout
+  constexpr int EPC = 16 / (int)sizeof(T);   // values per 16-byte chunk
+  constexpr int IN_CHUNKS = 64 / EPC;         // chunks of a token's 64 rows
+  constexpr int OUT_CHUNKS = TB / EPC;        // chunks of a row's TB tokens (8)
+  __shared__ __attribute__((aligned(16))) T tile[TB][64 + EPC];  // [token][row], padded
+  const int64_t q = blockIdx.x;                 // TB-token block of the layout
   const int64_t r0 = (int64_t)blockIdx.y * 64;  // first row of the tile
   const int64_t tiles_per_chunk = dm.Cp / TB;
   const int64_t chunk_rev = q / tiles_per_chunk, jb = q - chunk_rev * tiles_per_chunk;
   const int64_t b = chunk_rev / dm.N, i_dst = chunk_rev - b * dm.N;
   const int64_t i = reverse ? dm.N - 1 - i_dst : i_dst;
   const int64_t len = std::min<int64_t>(dm.C, dm.T - i * dm.C);  // tokens of chunk i
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int e = ty; e < TB; e += 4) {  // token e of the block, row r0 + tx
-    const int64_t j = jb * TB + e;
-    float v = 0.f;
-    if (j < len && r0 + tx < R) v = ld_f32<T>(src + (b * dm.T + i * dm.C + j) * R + r0 + tx);
-    tile[e][tx] = v;
+  for (int it = threadIdx.x; it < TB * IN_CHUNKS; it += 256) {
+    const int e = it / IN_CHUNKS, cc = it % IN_CHUNKS;  // token e, chunk cc of its rows
+    const int64_t j = jb * TB + e, r = r0 + cc * EPC;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (j < len && r < R)
+      v = *reinterpret_cast<const uint4*>(src + (b * dm.T + i * dm.C + j) * R + r);
+    *reinterpret_cast<uint4*>(&tile[e][cc * EPC]) = v;
   }
   __syncthreads();
-  if (tx >= TB) return;
-  for (int rr = ty; rr < 64; rr += 4) {  // row r0 + rr, token tx
-    if (r0 + rr < R) Elem<T>::store(dst + (q * R + r0 + rr) * TB + tx, tile[tx][rr]);
+  for (int it = threadIdx.x; it < 64 * OUT_CHUNKS; it += 256) {
+    const int rr = it / OUT_CHUNKS, oc = it % OUT_CHUNKS;  // row rr, tokens oc*EPC..
+    if (r0 + rr >= R) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (sizeof(T) == 2)
+        w[k] = (uint32_t)tile[oc * EPC + 2 * k][rr] | ((uint32_t)tile[oc * EPC + 2 * k + 1][rr] << 16);
+      else
+        w[k] = __float_as_uint(tile[oc * EPC + k][rr]);
+    }
+    *reinterpret_cast<uint4*>(dst + (q * R + r0 + rr) * TB + oc * EPC) =
+        make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
-// SwiGLU derivative.  With Z = SiLU(A_g) * A_u and s = sigmoid(A_g):
-//   dA_g = dZ * A_u * s * (1 + A_g (1 - s)),  dA_u = dZ * A_g * s.
-// Row t of the output holds [dA_g[t][0..f) | dA_u[t][0..f)] (the A operand
-// of dH = [dA_g | dA_u] [W_gate; W_up]).
 // Z = SiLU(A_g) * A_u from the fp32 pre-activations, in the activation type
 // (the same SiLU as the forward's epilogue).  4 values per item.
 template <typename T>
