@@ -3,7 +3,7 @@
 Imported only by tests, the smoke check and the benchmark's CPU-baseline leg.
 """
 from .oracle import (ALIGNS, TARGETS, build, final_weight_grid, forward, gated_activations, lm_target,
-                     num_threads, set_num_threads)
+                     num_threads, set_num_threads, set_progress)
 
 __all__ = ["ALIGNS", "TARGETS", "build", "final_weight_grid", "forward", "gated_activations", "lm_target",
-           "num_threads", "set_num_threads"]
+           "num_threads", "set_num_threads", "set_progress"]

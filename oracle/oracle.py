@@ -79,6 +79,7 @@ def _load():
         lib.oracle_final_weight_grid.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_progress.argtypes = [i64]
         _lib = lib
     return _lib
 
@@ -95,6 +96,12 @@ def _f32(a) -> np.ndarray:
 
 def _ptr(a: np.ndarray, ctype):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def set_progress(every: int) -> None:
+    """Print a progress line on stderr every `every` chunks of the sequential
+    form (0: silent)."""
+    _load().oracle_set_progress(int(every))
 
 
 def num_threads() -> int:

@@ -43,6 +43,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -146,6 +147,12 @@ int oracle_lm_target(int64_t B, int64_t T, int64_t d, int32_t K, const float* X0
  *   first   O[r][m] = sum_n Z[r][n] W[m][n]            (output with W^(i-1))
  *   then    W[m][n] += eta * sum_r V^[r][m] Z[r][n]    (W^(i) = W^(i-1) + eta V^_i^T Z_i)
  */
+/* Progress report (for runs of minutes): a line on stderr every
+ * g_progress_every chunks of the sequential form; 0 = silent.  No effect on
+ * the arithmetic. */
+static int64_t g_progress_every = 0;
+void oracle_set_progress(int64_t every) { g_progress_every = every; }
+
 static int sequential_one(int64_t T, int64_t d, int64_t f, int64_t C, int32_t K,
                           double eta, const float* H, const float* X0, const float* Wg,
                           const float* Wu, const float* taps, const float* Wt,
@@ -180,6 +187,12 @@ static int sequential_one(int64_t T, int64_t d, int64_t f, int64_t C, int32_t K,
         for (int64_t r = 0; r < rows; ++r) s += Vc[r * d + m] * Zc[r * f + n];
         W[m * f + n] += eta * s;
       }
+    }
+    const int64_t done = r0 / C + 1;
+    if (g_progress_every > 0 && done % g_progress_every == 0) {
+      fprintf(stderr, "[oracle] chunk %lld of %lld\n", (long long)done,
+              (long long)((T + C - 1) / C));
+      fflush(stderr);
     }
   }
   free(Zc); free(Uc); free(Vc);
