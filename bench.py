@@ -447,22 +447,26 @@ def main() -> int:
     torch.cuda.synchronize()
     tm.ttt_profile_read()  # drop anything recorded so far
     tm.ttt_profile_enable(True)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # an event between steps (no synchronisation) gives each step's time too
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for k in range(args.steps):
         step()
-    end.record(stream)
+        marks[k + 1].record(stream)
     torch.cuda.synchronize()
     tm.ttt_profile_enable(False)
-    ms_total = start.elapsed_time(end)
+    ms_total = marks[0].elapsed_time(marks[-1])
+    per_step = sorted(marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps))
+    ms_median = per_step[len(per_step) // 2] if len(per_step) % 2 else \
+        0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
     stages = tm.ttt_profile_read()
     ms_step = ms_total / args.steps
     tokens = w.tokens
     value = tokens / (ms_step / 1e3)
     dtype = "bf16" if w.dtype == torch.bfloat16 else "f32"
     peak = PEAK_TFLOPS[dtype]
-    log(f"[bench] {ms_step:.3f} ms/step, {value / 1e6:.3f} M tokens/s")
+    log(f"[bench] {ms_step:.3f} ms/step (median {ms_median:.3f}), {value / 1e6:.3f} M tokens/s")
 
     work = stage_work(w, group)
     proj = args.target in ("conv_proj", "proj")
@@ -507,6 +511,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_median": ms_median,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
