@@ -398,7 +398,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the layer's multi-GPU sharding is described in DESIGN.md, not built)",
+              "(the library runs the layer on one GPU; sharding across GPUs is not built)",
               file=sys.stderr)
         return 2
 
