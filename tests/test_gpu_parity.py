@@ -301,3 +301,42 @@ def test_full_workload_prefix_and_final_weight(name):
     e_w, e_dw = rel(Wgpu, Wg), rel(Wgpu - W0, Wg - W0)
     print(f"  seq {b} W_final sample rel {e_w:.3e}, dW rel {e_dw:.3e}", flush=True)
     assert e_w <= tol_for(w.dtype) and e_dw <= tol_for(w.dtype)
+
+
+# ------------------------------------------------- coherent-accumulation stress
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_repeated_block_stress(dtype):
+    """An induction-head-like input: every token's H and X0 rows come from a
+    table of 48 rows, in a block of 64 tokens that repeats, so every chunk's
+    increment points the same way and the fast weight grows linearly with the
+    chunk index instead of like its square root.  Checks range and tolerance
+    (and prints the worst chunk of O)."""
+    B, T, d, f, K, C = 1, 4096, 256, 512, 4, 256
+    g = torch.Generator().manual_seed(71)
+    table_h = torch.randn((48, d), generator=g)
+    table_x = torch.randn((48, d), generator=g)
+    block = torch.randint(0, 48, (64,), generator=g)
+    idx = block.repeat(T // 64)
+    inp = synth.make_inputs(B, T, d, f, K, dtype, seed=72)
+    inp["H"] = table_h[idx][None].to(dtype)
+    inp["X0"] = table_x[idx][None].to(dtype)
+    dev = to_device(inp)
+    eta = 2e-3
+    O, W = tm.forward_batched(dev["H"], dev["X0"], dev["W_gate"], dev["W_up"], dev["W_down0"],
+                              dev["taps"], dev["W_target"], eta, C)
+    torch.cuda.synchronize()
+    assert torch.isfinite(O.float()).all() and torch.isfinite(W).all()
+    ni = numpy_inputs(inp)
+    Oo, Wo = oracle.forward(ni["H"], ni["X0"], ni["W_gate"], ni["W_up"], ni["W_down0"],
+                            ni["taps"], ni["W_target"], eta, C)
+    Og, Wg = O.float().cpu().numpy()[0], W.cpu().numpy()[0]
+    Oo, Wo = Oo[0], Wo[0]
+    W0 = ni["W_down0"].astype(np.float64)
+    grow = np.linalg.norm(Wo - W0) / np.linalg.norm(W0)
+    e_o, e_dw = rel(Og, Oo), rel(Wg - W0, Wo - W0)
+    worst = max(rel(Og[i:i + C], Oo[i:i + C]) for i in range(0, T, C))
+    print(f"  |W_final - W0| / |W0| = {grow:.1f}; rel O {e_o:.2e} (worst chunk {worst:.2e}), "
+          f"rel dW {e_dw:.2e}", flush=True)
+    assert grow > 1.0  # the update dominates the starting weight
+    tol = tol_for(dtype)
+    assert e_o <= tol and e_dw <= tol and worst <= tol, (e_o, e_dw, worst)
