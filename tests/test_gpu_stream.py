@@ -229,3 +229,72 @@ def test_ragged_sessions_equal_their_own_runs(dtype, L, C):
             e = rel(Oq[dec].double().cpu().numpy(), O1[0][dec].double().cpu().numpy())
             assert e <= 1e-2, (q, e)
     print(f"  decode rows: {sum(sum(v) for v in dec_rows.values())}", flush=True)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_ragged_random_schedule(seed):
+    """Four slots over 30 calls with a random number of new tokens per call
+    (1..20, the same for every slot) and sequences that end at random (or at
+    their drawn length) and are replaced by new ones; each finished sequence
+    is compared with its own one-call run."""
+    import random
+    rnd = random.Random(seed)
+    B, d, f, K, C, dtype = 4, 128, 192, 4, 16, torch.bfloat16
+    eta = 2e-2
+    n_seq, max_len, calls = 4 + 4 * 30, 160, 30
+    inp = synth.make_inputs(n_seq, max_len, d, f, K, dtype, seed=96 + seed)
+    dev = to_device(inp)
+    w = (dev["W_gate"], dev["W_up"], dev["W_down0"], dev["taps"], dev["W_target"])
+    length = [rnd.randint(1, max_len) for _ in range(n_seq)]
+    desc_max = tm.make_desc(B, 20, d, f, C, K, eta, dtype)
+    ws = torch.empty(tm.ttt_mlp_stream_workspace_size(desc_max), dtype=torch.uint8,
+                     device="cuda")
+    carry = torch.empty(tm.ttt_mlp_carry_size(desc_max), dtype=torch.uint8, device="cuda")
+    state = torch.empty((B, d, f), dtype=torch.float32, device="cuda")
+    slot = [[b, 0] for b in range(B)]  # (sequence, position)
+    nxt = B
+    outs = {q: [] for q in range(n_seq)}
+    dec_rows = {q: [] for q in range(n_seq)}
+    finals = {}
+    for _ in range(calls):
+        L = rnd.randint(1, min(20, min(max_len - p for _, p in slot)))
+        pos, last, hs, xs = [], [], [], []
+        for b in range(B):
+            q, p = slot[b]
+            closing = p + L >= length[q] or rnd.random() < 0.15
+            if closing:
+                length[q] = p + L
+            pos.append(p)
+            last.append(1 if closing else 0)
+            hs.append(dev["H"][q, p:p + L])
+            xs.append(dev["X0"][q, p:p + L])
+            n_pend = 0 if p == 0 else p - (p - 1) // C * C
+            dec_rows[q] += [B * L <= 64 and L <= 16 and not closing and n_pend + L <= C] * L
+        desc = tm.make_desc(B, L, d, f, C, K, eta, dtype)
+        O = torch.empty((B, L, d), dtype=dtype, device="cuda")
+        tm.ttt_mlp_forward_stream_ragged(desc, pos, last, torch.stack(hs).contiguous(),
+                                         torch.stack(xs).contiguous(), *w, O, state, carry, ws)
+        for b in range(B):
+            q, p = slot[b]
+            outs[q].append(O[b].clone())
+            if last[b]:
+                finals[q] = state[b].clone()
+                slot[b] = [nxt, 0]
+                nxt += 1
+            else:
+                slot[b][1] = p + L
+    torch.cuda.synchronize()
+    assert len(finals) >= 6
+    for q, Wq in finals.items():
+        n = length[q]
+        O1, W1 = tm.forward_batched(dev["H"][q:q + 1, :n].contiguous(),
+                                    dev["X0"][q:q + 1, :n].contiguous(), *w, eta, C)
+        Oq = torch.cat(outs[q])
+        assert Oq.shape[0] == n, (q, Oq.shape, n)
+        assert torch.equal(Wq, W1[0]), q
+        dec = torch.tensor(dec_rows[q], device="cuda")
+        assert torch.equal(Oq[~dec], O1[0][~dec]), q
+        if dec.any():
+            assert rel(Oq[dec].double().cpu().numpy(), O1[0][dec].double().cpu().numpy()) <= 1e-2
+    print(f"  {len(finals)} sequences finished, "
+          f"{sum(sum(dec_rows[q]) for q in finals)} of their rows decoded", flush=True)
