@@ -20,7 +20,7 @@ namespace {
 // own regions, 256-byte aligned.
 struct BackwardPlan {
   ttt::WorkspacePlan fwd;
-  size_t wst, u, v, ag, au, ztr, dotr, sslots, dz, da, wgu, g, gf, du, tpart, dpart, wtpart,
+  size_t wst, u, v, agu, ztr, dotr, sslots, dz, da, wgu, g, gf, du, tpart, dpart, wtpart,
       blas, total;
   int64_t wt_slices;  // token slices of the dW_target product (split over K = B*T)
 };
@@ -41,8 +41,7 @@ BackwardPlan plan_backward(const ttt::Dims& dm) {
   p.wst = take((size_t)dm.B * d * f * 4);                 // fp32 state of the forward scan
   p.u = take(dm.conv ? BT * d * es : 0);                  // conv output U
   p.v = take(dm.proj ? BT * d * es : 0);                  // V^ = U W_target, row-major
-  p.ag = take(BT * f * 4);                                // A_g = H W_gateᵀ (fp32)
-  p.au = take(BT * f * 4);                                // A_u = H W_upᵀ (fp32)
+  p.agu = take(BT * 2 * f * 4);                           // [A_g | A_u] per row (fp32)
   p.ztr = take(f * (size_t)dm.P * es);                    // Zt, chunks reversed
   p.dotr = take(d * (size_t)dm.P * es);                   // dOᵀ k-blocked, chunks reversed
   p.sslots = take((size_t)dm.N * dm.B * d * f * es);      // S_j, reversed chunk order
@@ -175,8 +174,8 @@ ttt_status_t ttt_mlp_backward_batched(
   float* Wst = reinterpret_cast<float*>(base + bp.wst);
   void* U = dm.conv ? static_cast<void*>(base + bp.u) : const_cast<void*>(X0);
   void* V = dm.proj ? static_cast<void*>(base + bp.v) : U;
-  float* Ag = reinterpret_cast<float*>(base + bp.ag);
-  float* Au = reinterpret_cast<float*>(base + bp.au);
+  float* Ag = reinterpret_cast<float*>(base + bp.agu);  // row t at t * 2f
+  float* Au = Ag + f;
   void* Ztr = base + bp.ztr;
   void* dOtr = base + bp.dotr;
   char* Sslots = base + bp.sslots;
@@ -200,7 +199,8 @@ ttt_status_t ttt_mlp_backward_batched(
   if (e != hipSuccess) return hip_fail(e, "backward");
 
   // 2. The plain GEMMs run in rocBLAS (fp32 accumulation): first the fp32
-  //    pre-activations A_g = H W_gateᵀ, A_u = H W_upᵀ and V^ = U W_target.
+  //    pre-activations [A_g | A_u] = H [W_gate; W_up]ᵀ in one GEMM (row t
+  //    holds both, 2f wide) and V^ = U W_target.
   if (rocblas_set_stream(h, s) != rocblas_status_success ||
       rocblas_set_workspace(h, base + bp.blas, kBlasWorkspace) != rocblas_status_success)
     return fail(TTT_ERR_HIP, "rocblas set-up failed");
@@ -209,8 +209,7 @@ ttt_status_t ttt_mlp_backward_batched(
   Gemm gemm{h, ab};
   const int64_t B = dm.B, T = dm.T, C = dm.C, N = dm.N, sl = (int64_t)(B * d * f);
   const int64_t Di = (int64_t)d, Fi = (int64_t)f, BTi = (int64_t)BT;
-  gemm(false, true, BTi, Fi, Di, 1.f, H, Di, 0, W_gate, Di, 0, 0.f, Ag, Fi, 0, 1, f32);
-  gemm(false, true, BTi, Fi, Di, 1.f, H, Di, 0, W_up, Di, 0, 0.f, Au, Fi, 0, 1, f32);
+  gemm(false, true, BTi, 2 * Fi, Di, 1.f, H, Di, 0, Wgu, Di, 0, 0.f, Ag, 2 * Fi, 0, 1, f32);
   if (dm.proj)
     gemm(false, false, BTi, Di, Di, 1.f, U, Di, 0, W_target, Di, 0, 0.f, V, Di, 0, 1, ab);
   if (gemm.st != rocblas_status_success) return fail(TTT_ERR_HIP, "rocblas gemm failed (%d)", (int)gemm.st);
@@ -220,7 +219,7 @@ ttt_status_t ttt_mlp_backward_batched(
   //    one launch, the forward's scan (slot j = W^(j-1)) and the same scan
   //    over dOᵀ and Z in reverse chunk order from dW_final (slot j = S_j; its
   //    final state is the gradient of the starting weight).
-  e = ttt::launch_swiglu_rows(Ag, Au, Z, dm, s);
+  e = ttt::launch_swiglu_rows(Ag, Au, 2 * Fi, Z, dm, s);
   if (e == hipSuccess) e = ttt::launch_to_kblocked(Z, Zt, dm, dm.f, false, s);
   if (e == hipSuccess) e = ttt::launch_to_kblocked(Z, Ztr, dm, dm.f, true, s);
   if (e == hipSuccess) e = ttt::launch_to_kblocked(dO, dOtr, dm, dm.d, true, s);
@@ -260,7 +259,7 @@ ttt_status_t ttt_mlp_backward_batched(
   // 4. eta's gradient sum_t <V^[t], G[t]>; the SwiGLU derivative; dH and the
   //    gated MLP's weight gradients
   e = ttt::launch_dot(V, Gf, BTi * Di, dm.dt, 1.0f, dpart, d_eta, s);
-  if (e == hipSuccess) e = ttt::launch_swiglu_backward(dZ, Ag, Au, dA, dm, s);
+  if (e == hipSuccess) e = ttt::launch_swiglu_backward(dZ, Ag, Au, 2 * Fi, dA, dm, s);
   if (e == hipSuccess && dm.proj) e = ttt::launch_from_f32(Gf, G, BTi * Di, dm.dt, s);
   if (e != hipSuccess) return hip_fail(e, "backward");
   gemm(false, false, BTi, Di, 2 * Fi, 1.f, dA, 2 * Fi, 0, Wgu, Di, 0, 0.f, dH, Di, 0, 1, ab);

@@ -105,16 +105,18 @@ constexpr int kDotPartials = 1024;        // partial sums of the learning rate's
 // reversed if `reverse`), zeros in the padding columns.
 hipError_t launch_to_kblocked(const void* src, void* dst, const Dims& dm, int64_t R, bool reverse,
                               hipStream_t s);
-// Z [B*T][f] = SiLU(A_g) * A_u (activation type) from fp32 pre-activations.
-hipError_t launch_swiglu_rows(const float* Ag, const float* Au, void* Z, const Dims& dm,
-                              hipStream_t s);
+// Z [B*T][f] = SiLU(A_g) * A_u (activation type) from fp32 pre-activations
+// (row t of A_g and A_u at t * ld).
+hipError_t launch_swiglu_rows(const float* Ag, const float* Au, int64_t ld, void* Z,
+                              const Dims& dm, hipStream_t s);
 // The scans of two independent problems (same shapes) in one launch.
 hipError_t launch_dual_scan(const Dims& d1, const void* Vt1, const void* Zt1, float* W1,
                             void* slots1, const Dims& d2, const void* Vt2, const void* Zt2,
                             float* W2, void* slots2, hipStream_t s);
-// dA [B*T][2f] = [dA_g | dA_u] from dZ, A_g, A_u (fp32 [B*T][f]).
-hipError_t launch_swiglu_backward(const float* dZ, const float* Ag, const float* Au, void* dA,
-                                  const Dims& dm, hipStream_t s);
+// dA [B*T][2f] = [dA_g | dA_u] from dZ (fp32 [B*T][f]) and A_g, A_u (fp32,
+// row t at t * ld).
+hipError_t launch_swiglu_backward(const float* dZ, const float* Ag, const float* Au, int64_t ld,
+                                  void* dA, const Dims& dm, hipStream_t s);
 // dX0 and dtaps from dU = scale * src (fp32 [B*T][d]); `part` holds
 // target_backward_ranges(dm) * 8 * d floats.
 int64_t target_backward_ranges(const Dims& dm);
