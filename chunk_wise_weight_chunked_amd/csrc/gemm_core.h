@@ -204,6 +204,50 @@ struct Mma<uint16_t, S> {
       }
     }
   }
+  // The same k-tile with the fragment reads of step s+1 spread between the
+  // MFMAs of step s (read m after MFMA m) and a hook after every MFMA, called
+  // with the MFMA's index in the k-tile (a constant once unrolled); the
+  // mainloop issues the next k-tile's global reads from it.  Issued in one
+  // group, the reads and loads of all eight waves queue behind each other and
+  // hold up the MFMAs that follow them.
+  template <class Hook>
+  __device__ __forceinline__ static void ktile_spread(Accum<S>& acc, const lds_char* sA,
+                                                      const lds_char* sB, const LanePos& p,
+                                                      Hook&& after_mfma) {
+    constexpr int kPerStep = S::MB * S::NB;
+    const int r = p.lane & 31, h = p.lane >> 5;
+    Frag f[2];
+    read(f[0], sA, sB, p, 0);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      const Frag& c = f[s & 1];
+      Frag& n = f[(s + 1) & 1];
+#pragma unroll
+      for (int i = 0; i < S::MB; ++i)
+#pragma unroll
+        for (int j = 0; j < S::NB; ++j) {
+          acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.a[i], c.b[j], acc.v[i][j], 0, 0, 0);
+          const int m = i * S::NB + j;
+          if (s + 1 < kSteps) {
+            // fragment reads of step s+1 due after this MFMA (the last MFMA
+            // of the step takes whatever is left)
+#pragma unroll
+            for (int q = 0; q < S::MB + S::NB; ++q) {
+              if (q == m || (m == kPerStep - 1 && q > m)) {
+                if (q < S::MB)
+                  n.a[q] = lds_load<bf16x8_t>(sA + lds_offset(p.wave_m0 + 32 * q + r, 2 * (s + 1) + h));
+                else
+                  n.b[q - S::MB] = lds_load<bf16x8_t>(
+                      sB + lds_offset(p.wave_n0 + 32 * (q - S::MB) + r, 2 * (s + 1) + h));
+              }
+            }
+          }
+          after_mfma(s * kPerStep + m);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+  }
 };
 
 template <class S>
@@ -313,13 +357,21 @@ struct DirectLoader {
       voff[q] = (uint32_t)(row * row_stride + c * 16);
     }
   }
+  // Descriptor of k-tile kt; live = false gives an empty range (every read
+  // returns zero).
+  __device__ __forceinline__ rsrc_t rsrc(int64_t kt, bool live = true) const {
+    return make_rsrc(base + kt * kt_stride, live ? valid_bytes - kt * kt_shrink : 0);
+  }
+  // Instruction q (0..kPer-1) of a k-tile: 8 rows into `stage`.
+  __device__ __forceinline__ void issue_one(rsrc_t r, lds_char* stage, int q) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(stage + (lds_row0 + 8 * q) * kRowBytes), 16,
+        voff[q], 0, 0, 0);
+  }
   __device__ __forceinline__ void issue(int64_t kt, lds_char* stage) {
-    const rsrc_t r = make_rsrc(base + kt * kt_stride, valid_bytes - kt * kt_shrink);
+    const rsrc_t r = rsrc(kt);
 #pragma unroll
-    for (int q = 0; q < kPer; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(stage + (lds_row0 + 8 * q) * kRowBytes), 16,
-          voff[q], 0, 0, 0);
+    for (int q = 0; q < kPer; ++q) issue_one(r, stage, q);
   }
   __device__ __forceinline__ void commit(lds_char*) const {}
 };
@@ -370,18 +422,54 @@ struct RegLoader {
 // ---------------------------------------------------------------- mainloop
 // Runs k-tiles [0, nk) through a two-stage LDS pipeline.  Entering k-tile kt
 // (after a barrier), stage kt&1 holds k-tile kt and the other stage is free:
-// direct loaders start k-tile kt+1 into it at once; staged loaders write the
+// direct loaders start k-tile kt+1 into it (bf16 with kSpread: spread over
+// kt's MFMAs; otherwise at once, in one group); staged loaders write the
 // registers they fetched one k-tile earlier halfway through kt's MFMAs and
 // then fetch k-tile kt+2.  Before the closing barrier every wave waits for
 // its own direct reads of k-tile kt+1 (the staged fetches, issued later, may
 // stay in flight).  after_ktile(kt) runs once every wave has finished k-tile
 // kt and no direct read is in flight (it may use registers and global memory,
 // not LDS).
-template <typename T, class S, class LA, class LB, class Hook>
+template <typename T, class S, bool kSpread = true, class LA, class LB, class Hook>
 __device__ __forceinline__ void mainloop(Accum<S>& acc, LA& la, LB& lb, int64_t nk, lds_char* smem,
                                          const LanePos& p, Hook&& after_ktile) {
   constexpr int kStaged = LA::kStagedLoads + LB::kStagedLoads;
   if (nk <= 0) return;
+  if constexpr (kSpread && sizeof(T) == 2 && kStaged == 0) {
+    // bf16, direct loaders: k-tile kt+1's load instructions are spread over
+    // k-tile kt's MFMAs, one every kEvery MFMAs from the first (every second
+    // when they then still end in the first half of the k-tile).  After the
+    // last k-tile they read an empty range into the idle stage; the closing
+    // wait drains them before the caller touches LDS.
+    using M = Mma<T, S>;
+    constexpr int kLoads = LA::kPer + LB::kPer;
+    constexpr int kMfmas = M::kSteps * S::MB * S::NB;
+    constexpr int kEvery = 2 * kLoads <= kMfmas / 2 ? 2 : 1;
+    static_assert(kLoads <= kMfmas, "one load instruction per MFMA at most");
+    la.issue(0, smem);
+    lb.issue(0, smem + S::BM * kRowBytes);
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int64_t kt = 0; kt < nk; ++kt) {
+      const lds_char* cur = smem + (kt & 1) * S::kStageBytes;
+      lds_char* nxt = smem + ((kt + 1) & 1) * S::kStageBytes;
+      const bool more = kt + 1 < nk;
+      const rsrc_t ra = la.rsrc(kt + 1, more), rb = lb.rsrc(kt + 1, more);
+      M::ktile_spread(acc, cur, cur + S::BM * kRowBytes, p, [&](int idx) {
+        if (idx % kEvery == 0 && idx / kEvery < kLoads) {
+          const int q = idx / kEvery;
+          if (q < LA::kPer)
+            la.issue_one(ra, nxt, q);
+          else
+            lb.issue_one(rb, nxt + S::BM * kRowBytes, q - LA::kPer);
+        }
+      });
+      wait_vmcnt<0>();
+      __syncthreads();
+      after_ktile(kt);
+    }
+    return;
+  }
   lds_char* const stage0 = smem;
   la.issue(0, stage0);
   lb.issue(0, stage0 + S::BM * kRowBytes);
