@@ -511,6 +511,56 @@ __device__ __forceinline__ void mainloop(Accum<S>& acc, LA& la, LB& lb, int64_t 
   }
 }
 
+// A workgroup barrier for LDS only.  __syncthreads() also releases global
+// memory, and the compiler puts a wait for every outstanding vector memory
+// operation (stores included) in front of it.  Here: this wave's LDS
+// operations complete (lgkmcnt(0)), then s_barrier, with compiler-level
+// memory barriers on both sides so no access moves across.  Direct-to-LDS
+// loads are not covered: callers wait for them (vmcnt) before calling.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt not waited
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The one-group-issue mainloop for a tile that stores part of its
+// accumulator to global memory between k-tiles.  before_ktile(kt) runs once
+// k-tile kt+1's loads are issued and before kt's MFMAs, while the accumulator
+// holds the sum over k-tiles [0, kt); it returns whether it issued kStores
+// store instructions.  One counter covers vector loads and stores, and they
+// complete in issue order, so after such a k-tile the closing wait leaves the
+// last min(kStores, 63) operations -- the stores -- in flight: they drain
+// during the MFMAs instead of holding up the barrier, and the loads they wait
+// behind are only those of the following k-tile.
+template <typename T, class S, int kStores, class LA, class LB, class Hook>
+__device__ __forceinline__ void mainloop_with_stores(Accum<S>& acc, LA& la, LB& lb, int64_t nk,
+                                                     lds_char* smem, const LanePos& p,
+                                                     Hook&& before_ktile) {
+  static_assert(LA::kStagedLoads == 0 && LB::kStagedLoads == 0, "direct loaders");
+  constexpr int kLeave = kStores < 63 ? kStores : 63;
+  if (nk <= 0) return;
+  la.issue(0, smem);
+  lb.issue(0, smem + S::BM * kRowBytes);
+  wait_vmcnt<0>();
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const lds_char* cur = smem + (kt & 1) * S::kStageBytes;
+    lds_char* nxt = smem + ((kt + 1) & 1) * S::kStageBytes;
+    if (kt + 1 < nk) {
+      la.issue(kt + 1, nxt);
+      lb.issue(kt + 1, nxt + S::BM * kRowBytes);
+    }
+    const bool stored = before_ktile(kt);
+    Mma<T, S>::ktile(acc, cur, cur + S::BM * kRowBytes, p, [] {});
+    if (stored)
+      wait_vmcnt<kLeave>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+  }
+}
+
 // ------------------------------------------------------- block -> tile map
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2): hardware block b runs on XCD b % 8.  xcd_remap gives every XCD a

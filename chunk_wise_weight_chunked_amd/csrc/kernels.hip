@@ -57,8 +57,12 @@ using PrefixTile = Tile;
   __attribute__((amdgpu_waves_per_eu(TTT_GEMM_WPE, TTT_GEMM_WPE)))
 
 // ------------------------------------------------------------ chunk columns
+// Token row -> column of the token-major layouts (chunks padded to Cp
+// columns).  ident: no padding and whole chunks (Cp = C, N C = T), where the
+// column is the row itself.
 struct ChunkMap {
   int32_t T, C, N, Cp;
+  bool ident;
   __device__ __forceinline__ int64_t col(int32_t row) const {
     const int32_t b = row / T, s = row - b * T, i = s / C;
     return ((int64_t)b * N + i) * Cp + (s - i * C);
@@ -71,6 +75,7 @@ __device__ __forceinline__ ChunkMap chunk_map(const Dims& dm) {
   m.C = (int32_t)dm.C;
   m.N = (int32_t)dm.N;
   m.Cp = (int32_t)dm.Cp;
+  m.ident = dm.Cp == dm.C && dm.N * dm.C == dm.T;
   return m;
 }
 
@@ -121,9 +126,13 @@ struct Stage {
       if (c >= ncols || row >= rows_total) continue;
       const lds_char* src = lds + c * kStride + tok * (int)sizeof(T);
       const int64_t n = col_base + c;
-      const int32_t b = row / cm.T, sq = row - b * cm.T, i = sq / cm.C, j = sq - i * cm.C;
-      const int64_t p0 = ((int64_t)b * cm.N + i) * cm.Cp + j;
-      const int32_t room = min(cm.C - j, cm.T - sq);
+      int64_t p0 = row;  // identity map: 8 rows of a whole chunk (T and C multiples of 64)
+      int32_t room = 8;
+      if (!cm.ident) {
+        const int32_t b = row / cm.T, sq = row - b * cm.T, i = sq / cm.C, j = sq - i * cm.C;
+        p0 = ((int64_t)b * cm.N + i) * cm.Cp + j;
+        room = min(cm.C - j, cm.T - sq);
+      }
       if (room >= 8 && (p0 & 7) == 0) {
         T* d = dst + kblock_index<T>(n, p0, R);
         if constexpr (sizeof(T) == 2) {
@@ -175,6 +184,59 @@ __device__ __forceinline__ float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
+// Lanes hold 4 consecutive rows (e = 0..3) of one column; an even/odd lane
+// pair (adjacent columns c, c+1) swaps two values (DPP) so that each lane
+// holds two 32-bit bf16 pairs of adjacent columns: the even lane rows 0 and 1,
+// the odd lane rows 2 and 3.  w[r] is row (odd ? 2 : 0) + r, columns
+// (c & ~1, (c & ~1) + 1).
+__device__ __forceinline__ void pair_pack(const float z[4], bool odd, uint32_t w[2]) {
+  const float s0 = odd ? z[0] : z[2], s1 = odd ? z[1] : z[3];
+  const float r0 = __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s0), 0xB1, 0xF, 0xF, false));
+  const float r1 = __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s1), 0xB1, 0xF, 0xF, false));
+  w[0] = odd ? pack_bf16x2(r0, z[2]) : pack_bf16x2(z[0], r0);
+  w[1] = odd ? pack_bf16x2(r1, z[3]) : pack_bf16x2(z[1], r1);
+}
+
+// bf16 row-major staging of a 256-token x 128-feature tile for the
+// row-major Z output: rows of 256 bytes at a 288-byte stride, written as the
+// 32-bit column pairs of pair_pack.  The stride (72 dwords: +16 banks per two rows)
+// keeps the four rows one write instruction touches on distinct banks, and
+// the flush reads each row as 16-byte runs.
+struct RowStage {
+  static constexpr int kRowStride = 288;
+  static constexpr int kToks = 256;
+  static constexpr int kCols = 128;
+  static constexpr int kBytes = kToks * kRowStride;
+
+  // z[e] = value of (tok0 + e, col), e = 0..3; col = this lane's feature.
+  __device__ __forceinline__ static void put4(lds_char* lds, int col, int tok0, const float z[4],
+                                              bool odd) {
+    uint32_t w[2];
+    pair_pack(z, odd, w);
+    lds_char* q = lds + (tok0 + (odd ? 2 : 0)) * kRowStride + (col & ~1) * 2;
+    lds_store<uint32_t>(q, w[0]);
+    lds_store<uint32_t>(q + kRowStride, w[1]);
+  }
+
+  // Rows [0, rows_valid), columns [0, ncols) (ncols a multiple of 8) to
+  // dst[(dst_row0 + t) * ld + col_base + c], 16 bytes per lane.
+  template <int NTHREADS>
+  __device__ __forceinline__ static void flush(const lds_char* lds, uint16_t* __restrict__ dst,
+                                               int64_t dst_row0, int64_t ld, int64_t col_base,
+                                               int ncols, int32_t rows_valid) {
+    constexpr int kRuns = kCols / 8;
+    for (int it = threadIdx.x; it < kToks * kRuns; it += NTHREADS) {
+      const int t = it / kRuns, c = (it % kRuns) * 8;
+      if (t >= rows_valid || c >= ncols) continue;
+      const u32x4_t v = lds_load<u32x4_t>(lds + t * kRowStride + c * 2);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst + (dst_row0 + t) * ld +
+                                                                 col_base + c));
+    }
+  }
+};
+
 // Put tile columns [64 q, 64 q + 64) into the stage (values transformed by
 // `fn`); only the waves owning those columns write.
 template <typename T, class S, class F>
@@ -209,7 +271,11 @@ TTT_GEMM_KERNEL void swiglu_kernel(Dims dm, const T* __restrict__ H, const T* __
                                    T* __restrict__ Z, T* __restrict__ Zt) {
   using S = Tile;
   static_assert(S::NB % 2 == 0, "gate/up block pairs");
-  __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
+  // the pipeline's two stages, or (bf16) the two epilogue stages, whichever is larger
+  constexpr int kLds = sizeof(T) == 2 && Stage<T, S::kThreads, S::BN / 2>::kBytes + RowStage::kBytes > S::kLdsBytes
+                           ? Stage<T, S::kThreads, S::BN / 2>::kBytes + RowStage::kBytes
+                           : S::kLdsBytes;
+  __shared__ __attribute__((aligned(16))) char smem_raw[kLds];
   lds_char* smem = (lds_char*)smem_raw;
   const int32_t BT = (int32_t)(dm.B * dm.T);
   const int64_t d = dm.d, f = dm.f;
@@ -234,13 +300,17 @@ TTT_GEMM_KERNEL void swiglu_kernel(Dims dm, const T* __restrict__ H, const T* __
   const LanePos p = lane_pos<S>();
   mainloop<T, S>(acc, la, lb, ld / kRowBytes, smem, p, [](int64_t) {});
 
-  // z = silu(gate) * up, staged through LDS and written to Zt and Z: all 128
-  // features in one pass for bf16 (every wave computes at once), two passes
-  // of 64 for fp32 (the staging would not fit the LDS otherwise).
+  // z = silu(gate) * up, staged through LDS and written to Zt and Z.  bf16:
+  // all 128 features in one pass, into a token-run stage for Zt and a
+  // row-major stage for Z (both in LDS at once); fp32: two passes of 64
+  // features through the token-run stage, read back as column runs for Z.
   const ChunkMap cm = chunk_map(dm);
   constexpr int kPass = sizeof(T) == 2 ? kFeat : 64;  // features per pass
   using St = Stage<T, S::kThreads, kPass>;
-  static_assert(St::kBytes <= S::kLdsBytes, "staging fits the pipeline's LDS");
+  static_assert(St::kBytes + (sizeof(T) == 2 ? RowStage::kBytes : 0) <= kLds,
+                "staging fits the kernel's LDS");
+  lds_char* const rows_stage = smem + St::kBytes;
+  const bool odd = p.lane & 1;
 #pragma unroll
   for (int h = 0; h < kFeat / kPass; ++h) {
 #pragma unroll
@@ -257,13 +327,19 @@ TTT_GEMM_KERNEL void swiglu_kernel(Dims dm, const T* __restrict__ H, const T* __
           for (int e = 0; e < 4; ++e)
             z[e] = silu(acc.v[i][2 * jp][4 * rq + e]) * acc.v[i][2 * jp + 1][4 * rq + e];
           St::put4(smem, fcol + (p.lane & 31), p.row(i, 4 * rq), z);
+          if constexpr (sizeof(T) == 2)
+            RowStage::put4(rows_stage, fcol + (p.lane & 31), p.row(i, 4 * rq), z, odd);
         }
     }
     __syncthreads();
     const int64_t cb = feat0 + kPass * h;
     const int ncols = (int)max<int64_t>(0, min<int64_t>(kPass, f - cb));
     St::flush_tokens(smem, Zt, f, cb, ncols, row0, BT, cm);
-    St::flush_rows(smem, Z, row0, f, cb, ncols, 0, min(BT - row0, S::BM));
+    if constexpr (sizeof(T) == 2)
+      RowStage::flush<S::kThreads>(rows_stage, reinterpret_cast<uint16_t*>(Z), row0, f, cb, ncols,
+                                   min(BT - row0, S::BM));
+    else
+      St::flush_rows(smem, Z, row0, f, cb, ncols, 0, min(BT - row0, S::BM));
     __syncthreads();
   }
 }
@@ -483,6 +559,15 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
     }
 
   const int64_t slot_stride = dm.B * d * f;
+  // bf16 slots leave as 32-bit column pairs (pair_pack): half the store
+  // instructions, so that all of them fit the wait counter's range
+  const bool odd = p.lane & 1;
+  uint32_t lane_pair[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    lane_pair[r] = (uint32_t)((p.wave_m0 + 4 * (p.lane >> 5) + (odd ? 2 : 0) + r) * f +
+                              p.wave_n0 + ((p.lane & 31) & ~1)) * 2u;
+  constexpr int kSlotStores = S::MB * 4 * S::NB * (sizeof(T) == 2 ? 2 : 4);
   auto write_slot = [&](int64_t jj) {
     const int64_t js = dm.reverse_slots ? gc - 1 - jj : jj;
     const rsrc_t sr = make_rsrc(slots + js * slot_stride + b * d * f + corner,
@@ -492,18 +577,26 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t so = (uint32_t)(32 * i + 8 * q) * fu * (uint32_t)sizeof(T);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
+        if constexpr (sizeof(T) == 2) {
 #pragma unroll
           for (int j = 0; j < S::NB; ++j) {
-            const uint32_t vo = (lane_e[e] + 32 * j) * (uint32_t)sizeof(T);
-            if constexpr (sizeof(T) == 2)
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(acc.v[i][j][4 * q + e]), sr,
-                                                    vo, so, 0);
-            else
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.v[i][j][4 * q + e]), sr,
-                                                    vo, so, 0);
+            float z[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[e] = acc.v[i][j][4 * q + e];
+            uint32_t w[2];
+            pair_pack(z, odd, w);
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+              __builtin_amdgcn_raw_buffer_store_b32(w[r], sr, lane_pair[r] + 64 * j, so, 0);
           }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int j = 0; j < S::NB; ++j)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.v[i][j][4 * q + e]), sr,
+                                                    (lane_e[e] + 32 * j) * 4, so, 0);
+        }
         // one row group at a time: keeps the compiler from hoisting every
         // accumulator read (and conversion) ahead of the stores
         __builtin_amdgcn_sched_barrier(0);
@@ -517,11 +610,17 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
   // still written
   const bool skip = dm.skip_last && g0 + gc == dm.N;
   const int64_t nk = (skip ? gc - 1 : gc) * kt_per_chunk;
-  // (the loads issued in one group measure faster here than spread: both
-  // operands are token-major k-blocks, each instruction one contiguous KB)
-  mainloop<T, S, false>(acc, la, lb, nk, smem, p, [&](int64_t kt) {
-    const int64_t done = kt + 1;
-    if (done % kt_per_chunk == 0 && done < nk) write_slot(done / kt_per_chunk);
+  // Slot jj (the weight after jj chunks) is stored before the MFMAs of the
+  // chunk's first k-tile and drains while they run.  (The loads are issued in
+  // one group: both operands are token-major k-blocks, each instruction one
+  // contiguous KB, and spreading them measured slower here.)
+  int64_t next_slot = 1, next_slot_kt = kt_per_chunk;  // counters, not a division per k-tile
+  mainloop_with_stores<T, S, kSlotStores>(acc, la, lb, nk, smem, p, [&](int64_t kt) {
+    if (kt != next_slot_kt) return false;
+    write_slot(next_slot);
+    ++next_slot;
+    next_slot_kt += kt_per_chunk;
+    return true;
   });
   if (skip && gc > 1) write_slot(gc - 1);
 
