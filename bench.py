@@ -57,17 +57,28 @@ def _per_launch(scan, apply, toks) -> dict:
     return out
 
 
-def stage_work(w, group: int) -> dict:
-    """Algorithmic flops per launch of each kernel."""
+def _split_tokens(w, group: int) -> int:
+    """Tokens (all sequences) the target stage projects when the rest of the
+    projection runs next to the first group's scan (scan_target)."""
+    return w.batch * min(w.seq_len, group * w.chunk)
+
+
+def stage_work(w, group: int, split: bool = False) -> dict:
+    """Algorithmic flops per launch of each kernel.  split: the first group's
+    scan ran next to the projection of the later tokens (scan_target)."""
     B, T, d, f = w.batch, w.seq_len, w.d_model, w.d_ff
     tok = B * T
     out = {"swiglu": 4.0 * tok * d * f, "target": 2.0 * tok * d * d}
     out.update(_per_launch(lambda t: 2.0 * t * d * f, lambda t: 2.0 * t * d * f,
                            _group_tokens(w, group)))
+    if split:
+        t0 = _split_tokens(w, group)
+        out["target"] = 2.0 * t0 * d * d
+        out["scan_target"] = out.pop("prefix_update") + 2.0 * (tok - t0) * d * d
     return out
 
 
-def stage_bytes(w, group: int) -> dict:
+def stage_bytes(w, group: int, split: bool = False) -> dict:
     """Algorithmic HBM bytes per launch of each kernel: every operand read once
     and every result written once (the fp32 state once per group)."""
     B, T, C, d, f = w.batch, w.seq_len, w.chunk, w.d_model, w.d_ff
@@ -85,6 +96,10 @@ def stage_bytes(w, group: int) -> dict:
     out.update(_per_launch(lambda t: e * t * (d + f) + e * slots(t) * d * f + 8 * B * d * f,
                            lambda t: e * t * (f + d) + e * slots(t) * d * f,
                            _group_tokens(w, group)))
+    if split:
+        t0 = _split_tokens(w, group)
+        out["target"] = e * t0 * 2 * d + e * d * d
+        out["scan_target"] = out.pop("prefix_update") + e * (tok - t0) * 2 * d + e * d * d
     return out
 
 
@@ -101,6 +116,7 @@ STAGE_KERNELS = {
     "swiglu": "void ttt::swiglu_kernel",
     "target": "void ttt::target_kernel",
     "scan_apply": "void ttt::scan_apply_kernel",
+    "scan_target": "void ttt::scan_target_kernel",
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
@@ -468,7 +484,8 @@ def main() -> int:
     peak = PEAK_TFLOPS[dtype]
     log(f"[bench] {ms_step:.3f} ms/step (median {ms_median:.3f}), {value / 1e6:.3f} M tokens/s")
 
-    work = stage_work(w, group)
+    split = stages.get("scan_target", (0.0, 0))[1] > 0
+    work = stage_work(w, group, split)
     proj = args.target in ("conv_proj", "proj")
     if not proj:
         work.pop("target")  # no projection GEMM: the stage only moves rows
@@ -492,7 +509,7 @@ def main() -> int:
                 "traffic": traffic_for(dom, w.name) if default_config else None,
                 "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "flops_per_launch": work[dom],
-                "algorithmic_bytes_per_launch": stage_bytes(w, group)[dom],
+                "algorithmic_bytes_per_launch": stage_bytes(w, group, split)[dom],
                 "ms_per_launch": per_stage[dom]["ms_per_launch"]}
     layer_flops = w.flops() - (0 if proj else 2.0 * w.tokens * d * d)
     layer_frac = layer_flops / (ms_step / 1e3) / (peak * 1e12)

@@ -47,8 +47,8 @@ namespace {
 // ---------------------------------------------------------------- profiling
 const char* const kStageNames[TTT_NUM_STAGES] = {
     "state_reset", "weight_prep", "pad_fill", "swiglu", "target", "prefix_update", "down_proj",
-    "scan_apply"};
-enum Stage { kReset = 0, kPrep, kPad, kSwiglu, kTarget, kPrefix, kDown, kScanApply };
+    "scan_apply", "scan_target"};
+enum Stage { kReset = 0, kPrep, kPad, kSwiglu, kTarget, kPrefix, kDown, kScanApply, kScanTarget };
 
 struct Profiler {
   std::mutex mu;
@@ -213,6 +213,7 @@ ttt_status_t run_layer(const ttt::Dims& dm, ttt_mode_t mode, bool reset, const v
   const ttt::WorkspacePlan wp = ttt::plan_workspace(dm, G);
   char* base = static_cast<char*>(ws);
   void* Z = base + wp.z_off;
+  void* U = base + wp.u_off;
   void* Zt = base + wp.zt_off;
   void* Vt = base + wp.vt_off;
   void* WgU = base + wp.wgu_off;
@@ -234,14 +235,21 @@ ttt_status_t run_layer(const ttt::Dims& dm, ttt_mode_t mode, bool reset, const v
     e = staged(kPad, s, [&] { return ttt::launch_pad_fill(Zt, Vt, dm, s); });
     if (e != hipSuccess) return hip_fail(e, "pad_fill");
   }
-  // S2 first: its conv output U lives in the Z region until S1 overwrites it
-  e = staged(kTarget, s, [&] { return ttt::launch_target(dm, X0, tapsT, WtT, Z, Vt, s); });
+  // S2 (the conv into U, the projection into Vt), then S1.  With a
+  // projection and more than one group, S2 projects only the first group's
+  // token rows here: the rest runs next to the first group's scan, whose
+  // tiles alone fill about 1.5 waves of the chip.
+  const int64_t groups = (dm.N + G - 1) / G;
+  const bool split = groups > 1 && ttt::scan_target_fits(dm);
+  const int64_t t_split = split ? G * dm.C : dm.T;  // 0 < t_split < T when split
+  e = staged(kTarget, s, [&] {
+    return ttt::launch_target(dm, X0, tapsT, WtT, U, Vt, s, split ? t_split : -1);
+  });
   if (e != hipSuccess) return hip_fail(e, "target");
   e = staged(kSwiglu, s, [&] { return ttt::launch_swiglu(dm, H, WgU, Z, Zt, s); });
   if (e != hipSuccess) return hip_fail(e, "swiglu");
   // Group pipeline: launch g scans group g (slot set g & 1) and computes the
   // outputs of group g - 1 (the other set, completed by launch g - 1).
-  const int64_t groups = (dm.N + G - 1) / G;
   const size_t set_bytes = (size_t)G * wp.slot_bytes;
   for (int64_t g = 0; g <= groups; ++g) {
     const int64_t g0 = g * G, gc = g < groups ? std::min<int64_t>(G, dm.N - g0) : 0;
@@ -249,6 +257,14 @@ ttt_status_t run_layer(const ttt::Dims& dm, ttt_mode_t mode, bool reset, const v
     char* scan_slots = static_cast<char*>(slots) + (g & 1) * (wp.slot_sets > 1 ? set_bytes : 0);
     const char* apply_slots =
         static_cast<char*>(slots) + ((g - 1) & 1) * (wp.slot_sets > 1 ? set_bytes : 0);
+    if (g == 0 && split) {
+      e = staged(kScanTarget, s, [&] {
+        return ttt::launch_scan_target(dm, Vt, Zt, W_state, scan_slots, gc, dm.conv ? U : X0, WtT,
+                                       t_split, s);
+      });
+      if (e != hipSuccess) return hip_fail(e, "scan_target");
+      continue;
+    }
     const int stage = gc > 0 && ac > 0 ? kScanApply : gc > 0 ? kPrefix : kDown;
     e = staged(stage, s, [&] {
       return ttt::launch_scan_apply(dm, Vt, Zt, W_state, scan_slots, g0, gc, Z, apply_slots, O, a0,

@@ -199,18 +199,20 @@ __device__ __forceinline__ void pair_pack(const float z[4], bool odd, uint32_t w
   w[1] = odd ? pack_bf16x2(r1, z[3]) : pack_bf16x2(z[1], r1);
 }
 
-// bf16 row-major staging of a 256-token x 128-feature tile for the
-// row-major Z output: rows of 256 bytes at a 288-byte stride, written as the
-// 32-bit column pairs of pair_pack.  The stride (72 dwords: +16 banks per two rows)
-// keeps the four rows one write instruction touches on distinct banks, and
-// the flush reads each row as 16-byte runs.
+// bf16 row-major staging of a 256-row x COLS-column tile for row-major
+// outputs: rows of 2 COLS bytes at a stride of 2 COLS + 32, written as the
+// 32-bit column pairs of pair_pack.  The stride (8 mod 64 dwords: +16 banks
+// per two rows) keeps the four rows one write instruction touches on
+// distinct banks, and the flush reads each row as 16-byte runs.
+template <int COLS>
 struct RowStage {
-  static constexpr int kRowStride = 288;
+  static constexpr int kCols = COLS;
   static constexpr int kToks = 256;
-  static constexpr int kCols = 128;
+  static constexpr int kRowStride = 2 * COLS + 32;
   static constexpr int kBytes = kToks * kRowStride;
+  static_assert((kRowStride / 4) % 64 == 8, "bank spread of the pair writes");
 
-  // z[e] = value of (tok0 + e, col), e = 0..3; col = this lane's feature.
+  // z[e] = value of (tok0 + e, col), e = 0..3; col = this lane's column.
   __device__ __forceinline__ static void put4(lds_char* lds, int col, int tok0, const float z[4],
                                               bool odd) {
     uint32_t w[2];
@@ -220,16 +222,16 @@ struct RowStage {
     lds_store<uint32_t>(q + kRowStride, w[1]);
   }
 
-  // Rows [0, rows_valid), columns [0, ncols) (ncols a multiple of 8) to
+  // Rows [rows_lo, rows_valid), columns [0, ncols) (ncols a multiple of 8) to
   // dst[(dst_row0 + t) * ld + col_base + c], 16 bytes per lane.
   template <int NTHREADS>
   __device__ __forceinline__ static void flush(const lds_char* lds, uint16_t* __restrict__ dst,
                                                int64_t dst_row0, int64_t ld, int64_t col_base,
-                                               int ncols, int32_t rows_valid) {
+                                               int ncols, int32_t rows_lo, int32_t rows_valid) {
     constexpr int kRuns = kCols / 8;
     for (int it = threadIdx.x; it < kToks * kRuns; it += NTHREADS) {
       const int t = it / kRuns, c = (it % kRuns) * 8;
-      if (t >= rows_valid || c >= ncols) continue;
+      if (t < rows_lo || t >= rows_valid || c >= ncols) continue;
       const u32x4_t v = lds_load<u32x4_t>(lds + t * kRowStride + c * 2);
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst + (dst_row0 + t) * ld +
                                                                  col_base + c));
@@ -237,17 +239,16 @@ struct RowStage {
   }
 };
 
-// Put tile columns [64 q, 64 q + 64) into the stage (values transformed by
+// Put tile columns [W q, W q + W) into the stage (values transformed by
 // `fn`); only the waves owning those columns write.
-template <typename T, class S, class F>
-__device__ __forceinline__ void stage_cols64(lds_char* lds, const Accum<S>& acc, const LanePos& p,
-                                             int q, F&& fn) {
-  static_assert(S::WN % 64 == 0 || 64 % S::WN == 0, "64-column passes");
-  constexpr int kBlk = 64 / 32;  // block columns per pass
+template <typename T, class S, int W = 64, class F>
+__device__ __forceinline__ void stage_cols(lds_char* lds, const Accum<S>& acc, const LanePos& p,
+                                           int q, F&& fn) {
+  static_assert(W % 32 == 0, "whole 32-column blocks per pass");
 #pragma unroll
   for (int j = 0; j < S::NB; ++j) {
     const int col = p.wave_n0 + 32 * j;  // first tile column of block j
-    if (col < 64 * q || col >= 64 * q + 64) continue;
+    if (col < W * q || col >= W * q + W) continue;
 #pragma unroll
     for (int i = 0; i < S::MB; ++i)
 #pragma unroll
@@ -255,10 +256,9 @@ __device__ __forceinline__ void stage_cols64(lds_char* lds, const Accum<S>& acc,
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = fn(acc.v[i][j][4 * rq + e]);
-        Stage<T, S::kThreads>::put4(lds, col - 64 * q + (p.lane & 31), p.row(i, 4 * rq), v);
+        Stage<T, S::kThreads, W>::put4(lds, col - W * q + (p.lane & 31), p.row(i, 4 * rq), v);
       }
   }
-  (void)kBlk;
 }
 
 // ===================================================================== S1
@@ -272,8 +272,9 @@ TTT_GEMM_KERNEL void swiglu_kernel(Dims dm, const T* __restrict__ H, const T* __
   using S = Tile;
   static_assert(S::NB % 2 == 0, "gate/up block pairs");
   // the pipeline's two stages, or (bf16) the two epilogue stages, whichever is larger
-  constexpr int kLds = sizeof(T) == 2 && Stage<T, S::kThreads, S::BN / 2>::kBytes + RowStage::kBytes > S::kLdsBytes
-                           ? Stage<T, S::kThreads, S::BN / 2>::kBytes + RowStage::kBytes
+  using Rows = RowStage<S::BN / 2>;
+  constexpr int kLds = sizeof(T) == 2 && Stage<T, S::kThreads, S::BN / 2>::kBytes + Rows::kBytes > S::kLdsBytes
+                           ? Stage<T, S::kThreads, S::BN / 2>::kBytes + Rows::kBytes
                            : S::kLdsBytes;
   __shared__ __attribute__((aligned(16))) char smem_raw[kLds];
   lds_char* smem = (lds_char*)smem_raw;
@@ -307,7 +308,7 @@ TTT_GEMM_KERNEL void swiglu_kernel(Dims dm, const T* __restrict__ H, const T* __
   const ChunkMap cm = chunk_map(dm);
   constexpr int kPass = sizeof(T) == 2 ? kFeat : 64;  // features per pass
   using St = Stage<T, S::kThreads, kPass>;
-  static_assert(St::kBytes + (sizeof(T) == 2 ? RowStage::kBytes : 0) <= kLds,
+  static_assert(St::kBytes + (sizeof(T) == 2 ? Rows::kBytes : 0) <= kLds,
                 "staging fits the kernel's LDS");
   lds_char* const rows_stage = smem + St::kBytes;
   const bool odd = p.lane & 1;
@@ -328,7 +329,7 @@ TTT_GEMM_KERNEL void swiglu_kernel(Dims dm, const T* __restrict__ H, const T* __
             z[e] = silu(acc.v[i][2 * jp][4 * rq + e]) * acc.v[i][2 * jp + 1][4 * rq + e];
           St::put4(smem, fcol + (p.lane & 31), p.row(i, 4 * rq), z);
           if constexpr (sizeof(T) == 2)
-            RowStage::put4(rows_stage, fcol + (p.lane & 31), p.row(i, 4 * rq), z, odd);
+            Rows::put4(rows_stage, fcol + (p.lane & 31), p.row(i, 4 * rq), z, odd);
         }
     }
     __syncthreads();
@@ -336,8 +337,8 @@ TTT_GEMM_KERNEL void swiglu_kernel(Dims dm, const T* __restrict__ H, const T* __
     const int ncols = (int)max<int64_t>(0, min<int64_t>(kPass, f - cb));
     St::flush_tokens(smem, Zt, f, cb, ncols, row0, BT, cm);
     if constexpr (sizeof(T) == 2)
-      RowStage::flush<S::kThreads>(rows_stage, reinterpret_cast<uint16_t*>(Z), row0, f, cb, ncols,
-                                   min(BT - row0, S::BM));
+      Rows::template flush<S::kThreads>(rows_stage, reinterpret_cast<uint16_t*>(Z), row0, f, cb,
+                                        ncols, 0, min(BT - row0, S::BM));
     else
       St::flush_rows(smem, Z, row0, f, cb, ncols, 0, min(BT - row0, S::BM));
     __syncthreads();
@@ -424,25 +425,39 @@ __global__ __launch_bounds__(256) void conv_kernel(Dims dm, const T* __restrict_
 }
 
 // eta * V^ = eta * U W_target over all token rows, written token-major to Vt.
+// LDS of the projection tile: the pipeline's stages, or the epilogue stage
+// (all 256 columns at once for bf16, 128 for fp32), whichever is larger.
 template <typename T>
-TTT_GEMM_KERNEL void target_kernel(Dims dm, const T* __restrict__ U, const T* __restrict__ WtT,
-                                   T* __restrict__ Vt) {
+struct TargetLds {
+  static constexpr int kPass = sizeof(T) == 2 ? Tile::BN : Tile::BN / 2;
+  using St = Stage<T, Tile::kThreads, kPass>;
+  static constexpr int kBytes = St::kBytes > Tile::kLdsBytes ? St::kBytes : Tile::kLdsBytes;
+};
+
+// Tile `blk` of `nblk` of the projection of token rows [t_lo, t_hi) of every
+// sequence (tiles do not straddle sequences).
+template <typename T>
+__device__ __forceinline__ void target_tile(const Dims& dm, const T* __restrict__ U,
+                                            const T* __restrict__ WtT, T* __restrict__ Vt,
+                                            int64_t t_lo, int64_t t_hi, int blk, int nblk,
+                                            lds_char* smem) {
   using S = Tile;
-  __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
-  lds_char* smem = (lds_char*)smem_raw;
-  const int32_t BT = (int32_t)(dm.B * dm.T);
+  constexpr int kPass = TargetLds<T>::kPass;
+  using St = typename TargetLds<T>::St;
   const int64_t d = dm.d;
   const int64_t ld = d * (int64_t)sizeof(T);
-  const int tiles_m = (BT + S::BM - 1) / S::BM;
+  const int tiles_seq = (int)((t_hi - t_lo + S::BM - 1) / S::BM);
+  const int tiles_m = tiles_seq * (int)dm.B;
   const int tiles_n = (int)((d + S::BN - 1) / S::BN);
-  const TileCoord tc =
-      grouped_tile(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, 8);
-  const int32_t row0 = tc.m * S::BM;
+  const TileCoord tc = grouped_tile(xcd_remap(blk, nblk), tiles_m, tiles_n, 8);
+  const int64_t b = tc.m / tiles_seq;
+  const int32_t row0 = (int32_t)(b * dm.T + t_lo + (int64_t)(tc.m - b * tiles_seq) * S::BM);
+  const int32_t row_end = (int32_t)(b * dm.T + t_hi);  // rows of this sequence end here
   const int64_t col0 = (int64_t)tc.n * S::BN;
 
   DirectLoader<S::BM, S::kWaves> la;
-  la.init(reinterpret_cast<const char*>(U) + row0 * ld, ld, kRowBytes, (BT - row0) * ld,
-          kRowBytes);
+  la.init(reinterpret_cast<const char*>(U) + (int64_t)row0 * ld, ld, kRowBytes,
+          (int64_t)(row_end - row0) * ld, kRowBytes);
   DirectLoader<S::BN, S::kWaves> lb;
   lb.init(reinterpret_cast<const char*>(WtT) + col0 * ld, ld, kRowBytes, (d - col0) * ld,
           kRowBytes);
@@ -452,19 +467,25 @@ TTT_GEMM_KERNEL void target_kernel(Dims dm, const T* __restrict__ U, const T* __
   const LanePos p = lane_pos<S>();
   mainloop<T, S>(acc, la, lb, ld / kRowBytes, smem, p, [](int64_t) {});
 
-  // eta * acc to Vt through the stage, four passes of 64 columns.
+  // eta * acc to Vt through the stage, kPass columns per pass.
   const ChunkMap cm = chunk_map(dm);
   const float eta = dm.eta;
 #pragma unroll
-  for (int q = 0; q < S::BN / 64; ++q) {
-    stage_cols64<T, S>(smem, acc, p, q, [&](float x) { return eta * x; });
+  for (int q = 0; q < S::BN / kPass; ++q) {
+    if (q > 0) __syncthreads();  // the previous pass's flush has read the stage
+    stage_cols<T, S, kPass>(smem, acc, p, q, [&](float x) { return eta * x; });
     __syncthreads();
-    const int64_t cb = col0 + 64 * q;
-    Stage<T, S::kThreads>::flush_tokens(smem, Vt, d, cb,
-                                        (int)max<int64_t>(0, min<int64_t>(64, d - cb)), row0, BT,
-                                        cm);
-    __syncthreads();
+    const int64_t cb = col0 + kPass * q;
+    St::flush_tokens(smem, Vt, d, cb, (int)max<int64_t>(0, min<int64_t>(kPass, d - cb)), row0,
+                     row_end, cm);
   }
+}
+
+template <typename T>
+TTT_GEMM_KERNEL void target_kernel(Dims dm, const T* __restrict__ U, const T* __restrict__ WtT,
+                                   T* __restrict__ Vt, int64_t t_lo, int64_t t_hi) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[TargetLds<T>::kBytes];
+  target_tile<T>(dm, U, WtT, Vt, t_lo, t_hi, blockIdx.x, gridDim.x, (lds_char*)smem_raw);
 }
 
 // eta * R (R [B*T][d] row-major: X0 or U) into Vt, for the targets without a
@@ -694,7 +715,7 @@ __device__ __forceinline__ void down_proj_tile(const Dims& dm, const T* __restri
   const int64_t out_T = dm.out_T > 0 ? dm.out_T : T_seq;
 #pragma unroll
   for (int q = 0; q < S::BN / 64; ++q) {
-    stage_cols64<T, S>(smem, acc, p, q, [](float x) { return x; });
+    stage_cols<T, S>(smem, acc, p, q, [](float x) { return x; });
     __syncthreads();
     const int64_t cbase = n0 + 64 * q;
     Stage<T, S::kThreads>::flush_rows(smem, O, b * out_T + srow - dm.out_skip, d, cbase,
@@ -736,6 +757,34 @@ TTT_GEMM_KERNEL void scan_apply_kernel(Dims dm, const T* __restrict__ Vt, const 
   }
   down_proj_tile<T>(dm, Z, apply_slots, O, a0, ac, b - scan_pad, (int)gridDim.x - scan_pad,
                     (lds_char*)smem_raw);
+}
+
+// The first launch of the group pipeline when the projection of later
+// chunks is still to do: workgroups [0, scan_blocks) scan chunks g0.. (as in
+// scan_apply_kernel), the rest project token rows [t_lo, T) of every
+// sequence.  The scan tiles alone fill about 1.5 waves of the chip; the
+// projection tiles fill the rest.  The scan reads the target columns of
+// chunks g0 .. g0 + gc - 1, the projection writes those of chunks from t_lo
+// on: disjoint 64-token blocks.
+template <typename T>
+TTT_GEMM_KERNEL void scan_target_kernel(Dims dm, const T* __restrict__ Vt,
+                                        const T* __restrict__ Zt, float* __restrict__ W_state,
+                                        T* __restrict__ scan_slots, int64_t g0, int64_t gc,
+                                        int scan_blocks, int scan_pad, const T* __restrict__ rows,
+                                        const T* __restrict__ WtT, T* __restrict__ Vt_out,
+                                        int64_t t_lo) {
+  constexpr int kLds = TargetLds<T>::kBytes > PrefixTile::kLdsBytes ? TargetLds<T>::kBytes
+                                                                    : PrefixTile::kLdsBytes;
+  __shared__ __attribute__((aligned(16))) char smem_raw[kLds];
+  const int b = blockIdx.x;
+  if (b < scan_pad) {
+    if (b < scan_blocks)
+      prefix_update_tile<T, PrefixTile>(dm, Vt, Zt, W_state, scan_slots, g0, gc, b, scan_blocks,
+                                        (lds_char*)smem_raw);
+    return;
+  }
+  target_tile<T>(dm, rows, WtT, Vt_out, t_lo, dm.T, b - scan_pad, (int)gridDim.x - scan_pad,
+                 (lds_char*)smem_raw);
 }
 
 // Two independent scans of all N chunks (the backward's forward weights and
@@ -902,8 +951,10 @@ WorkspacePlan plan_workspace(const Dims& dm, int64_t group) {
   const size_t es = dtype_bytes(dm.dt);
   WorkspacePlan w;
   size_t off = 0;
-  w.z_off = off;  // Z, and before S1 runs, U of S2
-  off = align256(off + (size_t)(dm.B * dm.T) * std::max(dm.f, dm.d) * es);
+  w.z_off = off;  // Z
+  off = align256(off + (size_t)(dm.B * dm.T) * dm.f * es);
+  w.u_off = off;  // U of S2 (the conv output the projection reads)
+  off = align256(off + (size_t)(dm.B * dm.T) * dm.d * es);
   w.zt_off = off;
   off = align256(off + (size_t)dm.f * dm.P * es);
   w.vt_off = off;
@@ -995,7 +1046,7 @@ hipError_t launch_swiglu(const Dims& dm, const void* H, const void* WgU, void* Z
 
 template <typename T>
 static void launch_target_t(const Dims& dm, const T* X0, const float* tapsT, const T* WtT, T* U,
-                            T* Vt, hipStream_t s) {
+                            T* Vt, int64_t t_hi, hipStream_t s) {
   const int64_t BT = dm.B * dm.T;
   const T* rows = X0;  // the rows the projection (or the copy into Vt) reads
   if (dm.conv) {
@@ -1008,9 +1059,10 @@ static void launch_target_t(const Dims& dm, const T* X0, const float* tapsT, con
     rows = U;
   }
   if (dm.proj) {
-    const int64_t tiles = ((BT + Tile::BM - 1) / Tile::BM) * ((dm.d + Tile::BN - 1) / Tile::BN);
+    if (t_hi <= 0) return;
+    const int64_t tiles = ((t_hi + Tile::BM - 1) / Tile::BM) * dm.B * ((dm.d + Tile::BN - 1) / Tile::BN);
     hipLaunchKernelGGL(target_kernel<T>, dim3((unsigned)tiles), dim3(Tile::kThreads), 0, s, dm,
-                       rows, WtT, Vt);
+                       rows, WtT, Vt, (int64_t)0, t_hi);
   } else {
     hipLaunchKernelGGL(rows_to_vt_kernel<T>, dim3((unsigned)((BT + 255) / 256), (unsigned)((dm.d + 63) / 64)),
                        dim3(256), 0, s, dm, rows, Vt);
@@ -1018,15 +1070,51 @@ static void launch_target_t(const Dims& dm, const T* X0, const float* tapsT, con
 }
 
 hipError_t launch_target(const Dims& dm, const void* X0, const void* tapsT, const void* WtT,
-                         void* U, void* Vt, hipStream_t s) {
+                         void* U, void* Vt, hipStream_t s, int64_t t_hi) {
+  if (t_hi < 0) t_hi = dm.T;
   if (dm.dt == Dtype::BF16)
     launch_target_t<uint16_t>(dm, static_cast<const uint16_t*>(X0),
                               static_cast<const float*>(tapsT), static_cast<const uint16_t*>(WtT),
-                              static_cast<uint16_t*>(U), static_cast<uint16_t*>(Vt), s);
+                              static_cast<uint16_t*>(U), static_cast<uint16_t*>(Vt), t_hi, s);
   else
     launch_target_t<float>(dm, static_cast<const float*>(X0), static_cast<const float*>(tapsT),
                            static_cast<const float*>(WtT), static_cast<float*>(U),
-                           static_cast<float*>(Vt), s);
+                           static_cast<float*>(Vt), t_hi, s);
+  return hipGetLastError();
+}
+
+template <typename T>
+static void launch_scan_target_t(const Dims& dm, const T* Vt, const T* Zt, float* W_state,
+                                 T* scan_slots, int64_t gc, const T* rows, const T* WtT,
+                                 int64_t t_lo, hipStream_t s) {
+  const int64_t scan = (dm.d / PrefixTile::BM) * (dm.f / PrefixTile::BN) * dm.B;
+  const int64_t pad = (scan + 7) / 8 * 8;
+  const int64_t tiles =
+      ((dm.T - t_lo + Tile::BM - 1) / Tile::BM) * dm.B * ((dm.d + Tile::BN - 1) / Tile::BN);
+  hipLaunchKernelGGL(scan_target_kernel<T>, dim3((unsigned)(pad + tiles)), dim3(Tile::kThreads), 0,
+                     s, dm, Vt, Zt, W_state, scan_slots, (int64_t)0, gc, (int)scan, (int)pad, rows,
+                     WtT, const_cast<T*>(Vt), t_lo);
+}
+
+bool scan_target_fits(const Dims& dm) {
+  return dm.proj && dm.d % PrefixTile::BM == 0 && dm.f % PrefixTile::BN == 0;
+}
+
+hipError_t launch_scan_target(const Dims& dm, void* Vt, const void* Zt, float* W_state,
+                              void* scan_slots, int64_t gc, const void* rows, const void* WtT,
+                              int64_t t_lo, hipStream_t s) {
+  if (!scan_target_fits(dm) || t_lo <= 0 || t_lo >= dm.T) return hipErrorInvalidValue;
+  if (dm.dt == Dtype::BF16)
+    launch_scan_target_t<uint16_t>(dm, static_cast<const uint16_t*>(Vt),
+                                   static_cast<const uint16_t*>(Zt), W_state,
+                                   static_cast<uint16_t*>(scan_slots), gc,
+                                   static_cast<const uint16_t*>(rows),
+                                   static_cast<const uint16_t*>(WtT), t_lo, s);
+  else
+    launch_scan_target_t<float>(dm, static_cast<const float*>(Vt), static_cast<const float*>(Zt),
+                                W_state, static_cast<float*>(scan_slots), gc,
+                                static_cast<const float*>(rows), static_cast<const float*>(WtT),
+                                t_lo, s);
   return hipGetLastError();
 }
 

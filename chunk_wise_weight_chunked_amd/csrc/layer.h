@@ -41,7 +41,7 @@ struct Dims {
 // groups: the scan of group g+1 writes one set while the outputs of group g
 // read the other.
 struct WorkspacePlan {
-  size_t z_off, zt_off, vt_off, wgu_off, wtt_off, taps_off, slots_off;
+  size_t z_off, u_off, zt_off, vt_off, wgu_off, wtt_off, taps_off, slots_off;
   size_t slot_bytes;   // one chunk slot for all B sequences: B * d * f * es
   size_t fixed_bytes;  // everything except the slots
   int64_t group;       // chunks per group G
@@ -62,9 +62,20 @@ hipError_t launch_swiglu(const Dims& dm, const void* H, const void* WgU, void* Z
                          hipStream_t s);
 // eta * V^ into Vt: the conv of X0 into U (scratch of B*T x d elements) if
 // dm.conv, then the projection by W_target if dm.proj (each part left out is
-// the identity).
+// the identity).  With a projection, t_hi >= 0 projects only token rows
+// [0, t_hi) of each sequence (the conv always covers all rows).
 hipError_t launch_target(const Dims& dm, const void* X0, const void* taps, const void* WtT,
-                         void* U, void* Vt, hipStream_t s);
+                         void* U, void* Vt, hipStream_t s, int64_t t_hi = -1);
+// Whether launch_scan_target serves these dims (a projection, and the scan
+// tiles divide the weight).
+bool scan_target_fits(const Dims& dm);
+// The first pipeline launch together with the rest of the projection: scan of
+// chunks [0, gc) (slots into scan_slots, state in W_state) and projection of
+// token rows [t_lo, T) of every sequence from `rows` (U, or X0 without a
+// conv) into Vt.  0 < t_lo < T, and the chunks [0, gc) end at or before t_lo.
+hipError_t launch_scan_target(const Dims& dm, void* Vt, const void* Zt, float* W_state,
+                              void* scan_slots, int64_t gc, const void* rows, const void* WtT,
+                              int64_t t_lo, hipStream_t s);
 // One step of the group pipeline: the scan (S4) of chunks [g0, g0 + gc) into
 // scan_slots, and the outputs (S3) of chunks [a0, a0 + ac) from apply_slots;
 // gc == 0 or ac == 0 leaves that part out.  Both parts run in one launch

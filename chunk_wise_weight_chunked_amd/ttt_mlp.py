@@ -27,7 +27,7 @@ TTT_ERR_WORKSPACE_TOO_SMALL = -3
 TTT_ERR_HIP = -4
 TTT_MODE_AUTO, TTT_MODE_SEQUENTIAL, TTT_MODE_CHUNK_PARALLEL = 0, 1, 2
 TTT_TARGET_CONV_PROJ, TTT_TARGET_PROJ, TTT_TARGET_CONV, TTT_TARGET_EMBED = 0, 1, 2, 3
-TTT_NUM_STAGES = 8
+TTT_NUM_STAGES = 9
 
 _MODES = {"auto": TTT_MODE_AUTO, "sequential": TTT_MODE_SEQUENTIAL,
           "chunk_parallel": TTT_MODE_CHUNK_PARALLEL}

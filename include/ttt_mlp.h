@@ -295,8 +295,10 @@ const char* ttt_last_error(void);
  * 0 state_reset, 1 weight_prep, 2 pad_fill, 3 swiglu (S1), 4 target (S2),
  * 5 prefix_update (the first group's scan, S4/S5), 6 down_proj (the last
  * group's outputs, S3), 7 scan_apply (a group's scan next to the previous
- * group's outputs). */
-#define TTT_NUM_STAGES 8
+ * group's outputs), 8 scan_target (the first group's scan next to the
+ * projection of the later groups' tokens; with a projection and more than one
+ * group, stage 4 then projects the first group's tokens only). */
+#define TTT_NUM_STAGES 9
 ttt_status_t ttt_profile_enable(int enable);
 int ttt_profile_read(double* ms_total, int64_t* launches, int max_stages);
 const char* ttt_stage_name(int stage);

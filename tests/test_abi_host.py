@@ -75,22 +75,22 @@ def test_workspace_plan():
 
 
 def test_workspace_fixed_part_matches_layout():
-    # Z [T][f] + Zt [f][P] + Vt [d][P] + WgU [2f][d] + WtT [d][d] + tapsT [8][d] fp32
-    # + 2 slot sets of 1
+    # Z [T][f] + U [T][d] + Zt [f][P] + Vt [d][P] + WgU [2f][d] + WtT [d][d]
+    # + tapsT [8][d] fp32 + 2 slot sets of 1
     d = desc(seq_len=1000, chunk=100)  # padded chunks: Cp = 128, P = 10 * 128
     es = 2
-    parts = [1000 * 512 * es, 512 * 1280 * es, 256 * 1280 * es, 2 * 512 * 256 * es,
-             256 * 256 * es, 8 * 256 * 4, 2 * 256 * 512 * es]
+    parts = [1000 * 512 * es, 1000 * 256 * es, 512 * 1280 * es, 256 * 1280 * es,
+             2 * 512 * 256 * es, 256 * 256 * es, 8 * 256 * 4, 2 * 256 * 512 * es]
     expect = sum((p + 255) // 256 * 256 for p in parts)
     assert tm.ttt_mlp_workspace_size(d, 1) == expect
 
 
-def test_workspace_z_region_holds_conv_output():
-    # the Z region also holds the conv output U [T][d] before S1 runs: max(d, f) columns
+def test_workspace_conv_output_has_its_own_region():
+    # d > f: Z keeps f columns, the conv output U [T][d] its own region
     d = desc(d_model=512, d_ff=256, seq_len=1000, chunk=100)
     es = 2
-    parts = [1000 * 512 * es, 256 * 1280 * es, 512 * 1280 * es, 2 * 256 * 512 * es,
-             512 * 512 * es, 8 * 512 * 4, 2 * 512 * 256 * es]
+    parts = [1000 * 256 * es, 1000 * 512 * es, 256 * 1280 * es, 512 * 1280 * es,
+             2 * 256 * 512 * es, 512 * 512 * es, 8 * 512 * 4, 2 * 512 * 256 * es]
     expect = sum((p + 255) // 256 * 256 for p in parts)
     assert tm.ttt_mlp_workspace_size(d, 1) == expect
 
@@ -249,7 +249,7 @@ def test_last_error_is_per_thread(lib):
 def test_stage_names(lib):
     names = [tm.ttt_stage_name(i) for i in range(tm.TTT_NUM_STAGES)]
     assert names == ["state_reset", "weight_prep", "pad_fill", "swiglu", "target",
-                     "prefix_update", "down_proj", "scan_apply"]
+                     "prefix_update", "down_proj", "scan_apply", "scan_target"]
     header = open(os.path.join(ROOT, "include", "ttt_mlp.h")).read()
     assert f"#define TTT_NUM_STAGES {tm.TTT_NUM_STAGES}" in header
     assert tm.ttt_stage_name(99) == ""
