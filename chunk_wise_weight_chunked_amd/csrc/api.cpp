@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -202,6 +203,23 @@ ttt_status_t plan_group(const ttt::Dims& dm, ttt_mode_t mode, size_t ws_bytes, i
   return TTT_OK;
 }
 
+// Compute units of the current device (cached per device; 256 if the query
+// fails).
+int64_t compute_units() {
+  static std::mutex mu;
+  static std::map<int, int64_t> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  cache[dev] = n;
+  return n;
+}
+
 // The whole layer for B sequences whose starting weights are in W_state.
 ttt_status_t run_layer(const ttt::Dims& dm, ttt_mode_t mode, bool reset, const void* H,
                        const void* X0, const void* Wg, const void* Wu, const void* W0,
@@ -236,11 +254,15 @@ ttt_status_t run_layer(const ttt::Dims& dm, ttt_mode_t mode, bool reset, const v
     if (e != hipSuccess) return hip_fail(e, "pad_fill");
   }
   // S2 (the conv into U, the projection into Vt), then S1.  With a
-  // projection and more than one group, S2 projects only the first group's
-  // token rows here: the rest runs next to the first group's scan, whose
-  // tiles alone fill about 1.5 waves of the chip.
+  // projection and more than one group, S2 may project only the first
+  // group's token rows here and the rest next to the first group's scan: when
+  // the scan's tiles leave CUs idle (at most two waves of them) and are long
+  // enough (G·C >= 2 d tokens: twice a projection tile's k-loop) for
+  // projection tiles to fit beside them.
   const int64_t groups = (dm.N + G - 1) / G;
-  const bool split = groups > 1 && ttt::scan_target_fits(dm);
+  const int64_t scan_tiles = dm.B * (dm.d / 256) * (dm.f / 256);
+  const bool split = groups > 1 && ttt::scan_target_fits(dm) && G * dm.C >= 2 * dm.d &&
+                     scan_tiles <= 2 * compute_units();
   const int64_t t_split = split ? G * dm.C : dm.T;  // 0 < t_split < T when split
   e = staged(kTarget, s, [&] {
     return ttt::launch_target(dm, X0, tapsT, WtT, U, Vt, s, split ? t_split : -1);

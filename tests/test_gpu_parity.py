@@ -109,29 +109,40 @@ def test_modes_and_group_sizes_bitwise_equal(dtype):
         assert np.array_equal(O, ref[0]) and np.array_equal(W, ref[1]), (mode, g)
 
 
-@pytest.mark.parametrize("target,C,dtype", [("conv_proj", 64, torch.bfloat16),
-                                            ("proj", 100, torch.bfloat16),
-                                            ("conv_proj", 100, torch.float32)])
-def test_projection_split_bitwise_equal(target, C, dtype):
-    """With 256-divisible weights and more than one group, the projection of
-    the tokens after the first group runs inside the first pipeline launch;
-    with one group it runs whole before the scans.  Both give the same bits,
-    over several sequences, padded chunks and a ragged last tile."""
-    B, T, d, f = 2, 600, 256, 512
+@pytest.mark.parametrize("target,T,C,dtype,split_group",
+                         [("conv_proj", 1300, 64, torch.bfloat16, 8),
+                          ("proj", 1300, 100, torch.bfloat16, 6),
+                          ("conv_proj", 1300, 100, torch.float32, 6)])
+def test_projection_split_bitwise_equal(target, T, C, dtype, split_group):
+    """With 256-divisible weights, more than one group and a first group of at
+    least 2 d tokens, the projection of the later tokens runs inside the first
+    pipeline launch (stage scan_target); otherwise it runs whole before the
+    scans.  Both give the same bits, over several sequences, padded chunks and
+    a ragged last tile.  (Chunk-parallel mode takes one group of all chunks
+    when the workspace holds them, so split_group < N / 2 forces groups of
+    split_group.)"""
+    B, d, f = 2, 256, 512
     dev = to_device(synth.make_inputs(B, T, d, f, 4, dtype, seed=41))
     if target == "proj":
         dev["taps"] = None
 
     def run(mode, g):
+        tm.ttt_profile_read()
+        tm.ttt_profile_enable(True)
         O, W = tm.forward_batched(dev["H"], dev["X0"], dev["W_gate"], dev["W_up"],
                                   dev["W_down0"], dev["taps"], dev["W_target"], 1e-2, C,
                                   mode=mode, max_group=g, target=target)
         torch.cuda.synchronize()
-        return O.float().cpu().numpy(), W.cpu().numpy()
+        tm.ttt_profile_enable(False)
+        split = tm.ttt_profile_read()["scan_target"][1] > 0
+        return O.float().cpu().numpy(), W.cpu().numpy(), split
 
     ref = run("chunk_parallel", 0)  # one group: no split
-    for mode, g in (("sequential", 0), ("chunk_parallel", 2), ("auto", 0)):
-        O, W = run(mode, g)
+    assert not ref[2]
+    for mode, g, expect_split in (("chunk_parallel", split_group, True), ("sequential", 0, False),
+                                  ("auto", 0, False)):
+        O, W, split = run(mode, g)
+        assert split == expect_split, (mode, g)
         assert np.array_equal(O, ref[0]) and np.array_equal(W, ref[1]), (mode, g)
 
 
