@@ -53,6 +53,32 @@ def test_forward_graph_replays_equal_eager():
     _replays(g, [O, W], [O_ref, W_ref], torch.ones(1 << 20, device="cuda"))
 
 
+def test_forward_with_projection_split_graph_replays_equal_eager():
+    # groups of 8 chunks of 64 tokens (512 >= 2 d): the later rows' projection
+    # runs inside the first pipeline launch
+    B, T, d, f, K, C = 1, 1300, 256, 512, 4, 64
+    inp = to_device(synth.make_inputs(B, T, d, f, K, torch.bfloat16, seed=65))
+    desc = tm.make_desc(B, T, d, f, C, K, 1e-2, torch.bfloat16, "chunk_parallel")
+    ws = tm.alloc_workspace(desc, 8)
+    O = torch.empty_like(inp["H"])
+    W = torch.empty((B, d, f), dtype=torch.float32, device="cuda")
+    args = (desc, inp["H"], inp["X0"], inp["W_gate"], inp["W_up"], inp["W_down0"], inp["taps"],
+            inp["W_target"], O, W, ws)
+    tm.ttt_profile_read()
+    tm.ttt_profile_enable(True)
+    tm.ttt_mlp_forward_batched(*args)
+    torch.cuda.synchronize()
+    tm.ttt_profile_enable(False)
+    assert tm.ttt_profile_read()["scan_target"][1] == 1
+    O_ref, W_ref = O.clone(), W.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            tm.ttt_mlp_forward_batched(*args, stream=s)
+    _replays(g, [O, W], [O_ref, W_ref], torch.ones(1 << 20, device="cuda"))
+
+
 def test_decode_call_graph_replays_equal_eager():
     B, L, d, f, K, C = 4, 1, 256, 512, 4, 64
     inp = to_device(synth.make_inputs(B, 40, d, f, K, torch.bfloat16, seed=62))
