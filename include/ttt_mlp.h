@@ -75,7 +75,9 @@ typedef enum {
  *   CHUNK_PARALLEL  G as large as the workspace holds, up to all chunks (the
  *                   three-step form of section 3.2);
  *   AUTO            chunk-parallel in four groups (fewer if the workspace is
- *                   smaller), so that scans and outputs share launches. */
+ *                   smaller), so that scans and outputs share launches; one
+ *                   group when one scan already has B * ceil(d / 256) *
+ *                   ceil(f / 256) >= 1024 weight tiles (many sequences). */
 typedef enum {
   TTT_MODE_AUTO = 0,
   TTT_MODE_SEQUENTIAL = 1,

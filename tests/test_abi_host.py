@@ -74,6 +74,20 @@ def test_workspace_plan():
     assert tm.ttt_mlp_group_size(one, tm.ttt_mlp_workspace_size(one, 0)) == 1
 
 
+def test_auto_mode_takes_one_group_for_many_sequences():
+    # the scan of one group has B * ceil(d/256) * ceil(f/256) weight tiles:
+    # from 1024 tiles on, auto takes one group of all chunks, else four
+    many = desc(batch=16, seq_len=8192, d_model=2560, d_ff=9728, chunk=512)  # 6080 tiles
+    few = desc(batch=2, seq_len=8192, d_model=2560, d_ff=9728, chunk=512)    # 760 tiles
+    assert tm.ttt_mlp_workspace_size(many, 0) == tm.ttt_mlp_workspace_size(many, 16)
+    assert tm.ttt_mlp_group_size(many, tm.ttt_mlp_workspace_size(many, 0)) == 16
+    assert tm.ttt_mlp_group_size(few, tm.ttt_mlp_workspace_size(few, 0)) == 4
+    edge = desc(batch=64, d_model=1024, d_ff=1024)  # 64 * 4 * 4 = 1024 tiles, N = 8
+    assert tm.ttt_mlp_group_size(edge, tm.ttt_mlp_workspace_size(edge, 0)) == 8
+    below = desc(batch=63, d_model=1024, d_ff=1024)
+    assert tm.ttt_mlp_group_size(below, tm.ttt_mlp_workspace_size(below, 0)) == 2
+
+
 def test_workspace_fixed_part_matches_layout():
     # Z [T][f] + U [T][d] + Zt [f][P] + Vt [d][P] + WgU [2f][d] + WtT [d][d]
     # + tapsT [8][d] fp32 + 2 slot sets of 1
