@@ -267,13 +267,15 @@ ttt_status_t run_layer(const ttt::Dims& dm, ttt_mode_t mode, bool reset, const v
   // S2 (the conv into U, the projection into Vt), then S1.  With a
   // projection and more than one group, S2 may project only the first
   // group's token rows here and the rest next to the first group's scan: when
-  // the scan's tiles leave CUs idle (at most two waves of them) and are long
-  // enough (G·C >= 2 d tokens: twice a projection tile's k-loop) for
-  // projection tiles to fit beside them.
+  // the scan's tiles leave CUs idle (at most two waves of them, a quarter of
+  // the CUs or more idle in the last) and are long enough (G·C >= 2 d tokens:
+  // twice a projection tile's k-loop) for projection tiles to fit beside them.
   const int64_t groups = (dm.N + G - 1) / G;
   const int64_t scan_tiles = dm.B * (dm.d / 256) * (dm.f / 256);
+  const int64_t cus = compute_units();
+  const int64_t scan_waves = (scan_tiles + cus - 1) / cus;
   const bool split = groups > 1 && ttt::scan_target_fits(dm) && G * dm.C >= 2 * dm.d &&
-                     scan_tiles <= 2 * compute_units();
+                     scan_waves <= 2 && scan_waves * cus - scan_tiles >= cus / 4;
   const int64_t t_split = split ? G * dm.C : dm.T;  // 0 < t_split < T when split
   e = staged(kTarget, s, [&] {
     return ttt::launch_target(dm, X0, tapsT, WtT, U, Vt, s, split ? t_split : -1);
