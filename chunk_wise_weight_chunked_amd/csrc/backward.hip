@@ -158,9 +158,10 @@ __device__ __forceinline__ float4 fma4v(float4 a, float4 x, float4 y) {
 // (U[t][c] = sum_k taps[c][k] X0[t + shift - k][c]):
 //   dX0[s][c] = sum_k taps[c][k] dU[s - shift + k][c]   (rows of the same sequence)
 //   part[r][k][c] = sum over the rows of range r of dU[t][c] X0[t + shift - k][c]
-// without it dX0 = dU.  Thread = four consecutive features, looping over the
-// rows of its token range (blockIdx.y); partial tap sums are reduced in a
-// second pass.
+// without it dX0 = dU.  Thread = four consecutive features, walking the rows
+// of its token range (blockIdx.y) with the K rows of src and of X0 each row
+// needs held in register windows that slide by one row per step (one new row
+// of each is read per step); partial tap sums are reduced in a second pass.
 template <typename T>
 __global__ __launch_bounds__(256) void target_backward_kernel(
     const float* __restrict__ src, float scale, const T* __restrict__ X0,
@@ -171,36 +172,74 @@ __global__ __launch_bounds__(256) void target_backward_kernel(
   const int64_t d = dm.d, BT = dm.B * dm.T, T_seq = dm.T;
   const int64_t r0 = (int64_t)blockIdx.y * rows_per_range;
   const int64_t r1 = std::min<int64_t>(BT, r0 + rows_per_range);
-  const int K = dm.conv ? dm.K : 0;
-  float4 tp[8], acc[8];
-  for (int k = 0; k < 8; ++k) {
-    tp[k] = k < K ? *reinterpret_cast<const float4*>(tapsT + k * d + c)
-                  : make_float4(0.f, 0.f, 0.f, 0.f);
-    acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  for (int64_t t = r0; t < r1; ++t) {
-    const int64_t b = t / T_seq, s = t - b * T_seq;
-    const float4 du0 = *reinterpret_cast<const float4*>(src + t * d + c);
-    if (!dm.conv) {
+  const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (!dm.conv) {
+    for (int64_t t = r0; t < r1; ++t) {
+      const float4 du0 = *reinterpret_cast<const float4*>(src + t * d + c);
       st4<T>(dX0 + t * d + c, make_float4(scale * du0.x, scale * du0.y, scale * du0.z,
                                           scale * du0.w));
-      continue;
     }
-    float4 dx = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < K; ++k) {
-      const int64_t xs = s + dm.shift - k;  // X0 row tap k of output row s reads
-      if (xs >= 0 && xs < T_seq) acc[k] = fma4(scale, fma4v(du0, ld4<T>(X0 + (b * T_seq + xs) * d + c),
-                                                            make_float4(0.f, 0.f, 0.f, 0.f)),
-                                               acc[k]);
-      const int64_t us = s - dm.shift + k;  // output row whose tap k reads X0 row s
-      if (us >= 0 && us < T_seq)
-        dx = fma4v(tp[k], *reinterpret_cast<const float4*>(src + (b * T_seq + us) * d + c), dx);
+    return;
+  }
+  const int K = dm.K, shift = (int)dm.shift;
+  float4 tp[8], acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    tp[k] = k < K ? *reinterpret_cast<const float4*>(tapsT + k * d + c) : zero;
+    acc[k] = zero;
+  }
+  // src row s - shift + k of sequence b (zero outside it), and X0 row s + shift - k
+  auto src_row = [&](int64_t b, int64_t u) {
+    return (u >= 0 && u < T_seq) ? *reinterpret_cast<const float4*>(src + (b * T_seq + u) * d + c)
+                                 : zero;
+  };
+  auto x0_row = [&](int64_t b, int64_t x) {
+    return (x >= 0 && x < T_seq) ? ld4<T>(X0 + (b * T_seq + x) * d + c) : zero;
+  };
+  float4 uwin[8], xwin[8];  // uwin[k] = src row s - shift + k, xwin[k] = X0 row s + shift - k
+  int64_t b = r0 / T_seq, s = r0 - b * T_seq;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    uwin[k] = k < K ? src_row(b, s - shift + k) : zero;
+    xwin[k] = k < K ? x0_row(b, s + shift - k) : zero;
+  }
+  for (int64_t t = r0; t < r1; ++t) {
+    const float4 du0 = shift < K ? (shift == 0 ? uwin[0] : uwin[1]) : src_row(b, s);
+    float4 dx = zero;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k < K) {
+        acc[k] = fma4(scale, fma4v(du0, xwin[k], zero), acc[k]);
+        dx = fma4v(tp[k], uwin[k], dx);
+      }
     }
     st4<T>(dX0 + t * d + c, make_float4(scale * dx.x, scale * dx.y, scale * dx.z, scale * dx.w));
+    // next row: a new sequence restarts both windows, else each slides by one
+    if (++s == T_seq) {
+      ++b;
+      s = 0;
+      if (t + 1 < r1) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          uwin[k] = k < K ? src_row(b, s - shift + k) : zero;
+          xwin[k] = k < K ? x0_row(b, s + shift - k) : zero;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 7; ++k) uwin[k] = uwin[k + 1];
+#pragma unroll
+      for (int k = 7; k > 0; --k) xwin[k] = xwin[k - 1];
+      const float4 un = src_row(b, s - shift + K - 1), xn = x0_row(b, s + shift);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k == K - 1) uwin[k] = un;
+      xwin[0] = xn;
+    }
   }
-  if (dm.conv)
-    for (int k = 0; k < K; ++k)
-      *reinterpret_cast<float4*>(part + ((int64_t)blockIdx.y * 8 + k) * d + c) = acc[k];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (k < K) *reinterpret_cast<float4*>(part + ((int64_t)blockIdx.y * 8 + k) * d + c) = acc[k];
 }
 
 // dtaps[c][k] = sum over ranges r (in order) of part[r][k][c].
