@@ -352,7 +352,7 @@ TTT_GEMM_KERNEL void swiglu_kernel(Dims dm, const T* __restrict__ H, const T* __
 // rows, with the X0 window of those rows (kConvRows + KMAX - 1 rows) in
 // registers; consecutive threads take consecutive chunks of a row group, so
 // every access is a coalesced 16-byte load or store.
-constexpr int kConvRows = 4;
+constexpr int kConvRows = 8;
 template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void conv_kernel(Dims dm, const T* __restrict__ X0,
                                                    const float* __restrict__ tapsT,
