@@ -162,8 +162,10 @@ ttt_status_t make_dims(const ttt_mlp_desc_t* desc, ttt::Dims* dm) {
   if (d.d * d.f > kMaxInt32) return fail(TTT_ERR_UNSUPPORTED, "d_model * d_ff must be < 2^31");
   if (d.B * d.N > kMaxInt32 / d.Cp) return fail(TTT_ERR_UNSUPPORTED, "padded token count must be < 2^31");
   d.P = d.B * d.N * d.Cp;
-  // fast-weight tiles address 256 rows of f fp32 values with 32-bit byte offsets
+  // the GEMM tiles address 256 rows of d or f values (up to 4 bytes each)
+  // with 32-bit byte offsets from the tile's corner
   if (d.f > (int64_t)1 << 20) return fail(TTT_ERR_UNSUPPORTED, "d_ff must be <= 2^20");
+  if (d.d > (int64_t)1 << 20) return fail(TTT_ERR_UNSUPPORTED, "d_model must be <= 2^20");
   *dm = d;
   return TTT_OK;
 }

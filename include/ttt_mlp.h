@@ -115,7 +115,8 @@ typedef enum {
 /* Shapes and scalars of one call.
  *   batch    B >= 1 independent sequences (ttt_mlp_forward requires B == 1);
  *   seq_len  T >= 1 tokens per sequence;
- *   d_model  d, a multiple of 64;  d_ff  f, a multiple of 64, at most 2^20;
+ *   d_model  d, a multiple of 64, at most 2^20;
+ *   d_ff     f, a multiple of 64, at most 2^20;
  *            (B*T, d*f and B*ceil(T/C)*ceil64(C) must each stay below 2^31);
  *   chunk    C >= 1 tokens per chunk (the last chunk may be shorter);
  *   conv_k   K taps, 1 <= K <= 8;

@@ -125,6 +125,9 @@ BAD_DESCS = [
     (dict(target=4), tm.TTT_ERR_INVALID_ARGUMENT, "target"),
     (dict(align=2), tm.TTT_ERR_INVALID_ARGUMENT, "align"),
     (dict(batch=1 << 20, seq_len=1 << 12), tm.TTT_ERR_UNSUPPORTED, "2^31"),
+    # each below the d*f bound, but a 256-row tile would need offsets past 2^31
+    (dict(d_ff=(1 << 20) + 64), tm.TTT_ERR_UNSUPPORTED, "d_ff must be <= 2^20"),
+    (dict(d_model=1 << 24, d_ff=64), tm.TTT_ERR_UNSUPPORTED, "d_model must be <= 2^20"),
 ]
 
 
