@@ -489,6 +489,9 @@ def main() -> int:
     proj = args.target in ("conv_proj", "proj")
     if not proj:
         work.pop("target")  # no projection GEMM: the stage only moves rows
+    nbytes = stage_bytes(w, group, split)
+    if not proj:  # the stage reads X0 and writes one row per token, no weight
+        nbytes["target"] = (2 if dtype == "bf16" else 4) * w.tokens * 2 * d
     per_stage = {}
     for name, (ms, n) in stages.items():
         if n == 0:
@@ -498,18 +501,28 @@ def main() -> int:
         if name in work:
             tf = work[name] / (avg / 1e3) / 1e12
             entry.update({"tflops": tf, "frac_of_peak": tf / peak})
+        if name in nbytes:
+            gbs = nbytes[name] / (avg / 1e3) / 1e9
+            entry.update({"gbps": gbs, "frac_of_hbm": gbs / HBM_PEAK_GBS})
         per_stage[name] = entry
         log(f"  {name:14s} {avg:9.3f} ms x {n / args.steps:g}/step  "
-            + (f"{entry['tflops']:8.1f} TFLOP/s ({entry['frac_of_peak']:.1%})" if "tflops" in entry else ""))
+            + (f"{entry['tflops']:8.1f} TFLOP/s ({entry['frac_of_peak']:.1%})" if "tflops" in entry else "")
+            + (f"  {entry['gbps']:7.0f} GB/s ({entry['frac_of_hbm']:.1%})" if "gbps" in entry else ""))
     dom = max((k for k in per_stage if k in work),
               key=lambda k: per_stage[k]["ms_per_launch"] * per_stage[k]["launches_per_step"])
-    ach = per_stage[dom]["tflops"]
-    roofline = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": peak,
-                "unit": "TFLOP/s", "frac": ach / peak,
+    # the dominant kernel's bound: MFMA when its algorithmic intensity is above
+    # the ridge (peak flop/s over peak HBM bytes/s), else HBM
+    hbm_bound = work[dom] / nbytes[dom] < peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if hbm_bound:
+        ach, pk, unit = per_stage[dom]["gbps"], HBM_PEAK_GBS, "GB/s"
+    else:
+        ach, pk, unit = per_stage[dom]["tflops"], peak, "TFLOP/s"
+    roofline = {"kernel": dom, "bound": "hbm" if hbm_bound else "mfma", "achieved": ach,
+                "peak": pk, "unit": unit, "frac": ach / pk,
                 "traffic": traffic_for(dom, w.name) if default_config else None,
                 "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "flops_per_launch": work[dom],
-                "algorithmic_bytes_per_launch": stage_bytes(w, group, split)[dom],
+                "algorithmic_bytes_per_launch": nbytes[dom],
                 "ms_per_launch": per_stage[dom]["ms_per_launch"]}
     layer_flops = w.flops() - (0 if proj else 2.0 * w.tokens * d * d)
     layer_frac = layer_flops / (ms_step / 1e3) / (peak * 1e12)
