@@ -103,6 +103,12 @@ def stage_bytes(w, group: int, split: bool = False) -> dict:
     return out
 
 
+def hbm_bound(flops: float, nbytes: float, dtype: str) -> bool:
+    """A kernel is HBM-bound when its algorithmic flops per byte are below the
+    ridge: the MFMA peak for its dtype over the HBM peak."""
+    return flops / nbytes < PEAK_TFLOPS[dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+
+
 def torch_bf16():
     import torch
     return torch.bfloat16
@@ -510,14 +516,12 @@ def main() -> int:
             + (f"  {entry['gbps']:7.0f} GB/s ({entry['frac_of_hbm']:.1%})" if "gbps" in entry else ""))
     dom = max((k for k in per_stage if k in work),
               key=lambda k: per_stage[k]["ms_per_launch"] * per_stage[k]["launches_per_step"])
-    # the dominant kernel's bound: MFMA when its algorithmic intensity is above
-    # the ridge (peak flop/s over peak HBM bytes/s), else HBM
-    hbm_bound = work[dom] / nbytes[dom] < peak * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if hbm_bound:
+    is_hbm = hbm_bound(work[dom], nbytes[dom], dtype)
+    if is_hbm:
         ach, pk, unit = per_stage[dom]["gbps"], HBM_PEAK_GBS, "GB/s"
     else:
         ach, pk, unit = per_stage[dom]["tflops"], peak, "TFLOP/s"
-    roofline = {"kernel": dom, "bound": "hbm" if hbm_bound else "mfma", "achieved": ach,
+    roofline = {"kernel": dom, "bound": "hbm" if is_hbm else "mfma", "achieved": ach,
                 "peak": pk, "unit": unit, "frac": ach / pk,
                 "traffic": traffic_for(dom, w.name) if default_config else None,
                 "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
