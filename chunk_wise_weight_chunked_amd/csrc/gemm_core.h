@@ -528,11 +528,15 @@ __device__ __forceinline__ void lds_barrier() {
 // accumulator to global memory between k-tiles.  before_ktile(kt) runs once
 // k-tile kt+1's loads are issued and before kt's MFMAs, while the accumulator
 // holds the sum over k-tiles [0, kt); it returns whether it issued kStores
-// store instructions.  One counter covers vector loads and stores, and they
-// complete in issue order, so after such a k-tile the closing wait leaves the
-// last min(kStores, 63) operations -- the stores -- in flight: they drain
-// during the MFMAs instead of holding up the barrier, and the loads they wait
-// behind are only those of the following k-tile.
+// store instructions.  One counter (vmcnt) covers vector loads, direct-to-LDS
+// loads and stores, and they retire in issue order -- the model gfx950's
+// compiler itself uses: for a direct-to-LDS load, three stores and a barrier
+// before the LDS is read it emits vmcnt(3).  So after such a k-tile the
+// closing wait leaves the last min(kStores, 63) operations -- the stores -- in
+// flight: they drain during the MFMAs instead of holding up the barrier, and
+// the loads they wait behind are only those of the following k-tile.  kStores
+// must not exceed the stores actually issued, or loads would stay in flight
+// past the barrier (the compiled scan kernels are checked for this).
 template <typename T, class S, int kStores, class LA, class LB, class Hook>
 __device__ __forceinline__ void mainloop_with_stores(Accum<S>& acc, LA& la, LB& lb, int64_t nk,
                                                      lds_char* smem, const LanePos& p,

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle.backward import _conv as oracle_conv
 from oracle.backward import backward as oracle_backward
 from chunk_wise_weight_chunked_amd import synth
 from chunk_wise_weight_chunked_amd import ttt_mlp as tm
@@ -37,6 +38,41 @@ CASES = [
     (2, 70, 64, 128, 4, 1, torch.float32, "conv_proj", "next", False, True),    # C = 1
     (1, 130, 128, 64, 1, 65, torch.bfloat16, "conv_proj", "self", False, True),  # K = 1, C odd
 ]
+
+
+def _bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).double().numpy()
+
+
+def bf16_rounded_deta(ni, eta, C, dO, dWN, target, align):
+    """eta's gradient sum_j <S_j, V^_jᵀ Z_j> in fp64 from the bf16 roundings a
+    bf16 pipeline makes of its operands: Z, U (with a conv and a projection),
+    eta * V^ and each S_j (the reversed scan's bf16 slots).  How far this moves
+    from the exact value measures how much those roundings alone shift the
+    gradient, whose terms cancel."""
+    conv = target in ("conv_proj", "conv")
+    proj = target in ("conv_proj", "proj")
+    shift = 1 if align == "next" else 0
+    H, X0 = ni["H"].astype(np.float64), ni["X0"].astype(np.float64)
+    Wg, Wu = ni["W_gate"].astype(np.float64), ni["W_up"].astype(np.float64)
+    B, T, d = H.shape
+    f = Wg.shape[0]
+    N = -(-T // C)
+    total = 0.0
+    for b in range(B):
+        Ag, Au = H[b] @ Wg.T, H[b] @ Wu.T
+        Z = _bf16(Ag / (1.0 + np.exp(-Ag)) * Au)
+        U = oracle_conv(X0[b], ni["taps"].astype(np.float64), shift) if conv else X0[b]
+        if conv and proj:
+            U = _bf16(U)
+        V = U @ ni["W_target"].astype(np.float64) if proj else U
+        Vr = _bf16(eta * V) / eta
+        S = np.zeros((d, f)) if dWN is None else dWN[b].astype(np.float64).copy()
+        for j in reversed(range(N)):
+            r = slice(j * C, min(T, (j + 1) * C))
+            total += float(np.sum(Vr[r] * (Z[r] @ _bf16(S).T)))
+            S = S + dO[b][r].T.astype(np.float64) @ Z[r]
+    return total
 
 
 def _id(c):
@@ -86,13 +122,20 @@ def test_backward_matches_oracle(case):
     # (V^ = 0, e.g. one token whose only tap reads the next one: eta's gradient is 0)
     e_eta = d_eta / ref["eta_scale"] if ref["eta_scale"] > 0 else d_eta
     e_eta_plain = d_eta / max(abs(ref["eta"]), 1e-30)
+    bound = 1e-3
+    if dtype == torch.bfloat16:
+        # the plain relative bound: a few times what the bf16 roundings of the
+        # operands alone move eta's gradient (0.03%-10% at these shapes)
+        moved = abs(bf16_rounded_deta(ni, eta, C, dO.float().numpy(),
+                                      None if dWN is None else dWN.numpy(), target, align)
+                    - ref["eta"]) / max(abs(ref["eta"]), 1e-30)
+        bound = 3.0 * moved + 2e-3
     print("  " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()) +
-          f"  eta {e_eta:.2e} (plain relative {e_eta_plain:.2e})", flush=True)
+          f"  eta {e_eta:.2e} (plain relative {e_eta_plain:.2e}, bound {bound:.2e})", flush=True)
     for k, v in errs.items():
         assert v <= tol, (k, v)
     assert e_eta <= tol, e_eta
-    if dtype == torch.float32:
-        assert e_eta_plain <= 1e-3, e_eta_plain
+    assert e_eta_plain <= bound, (e_eta_plain, bound)
 
 
 def test_backward_is_deterministic():

@@ -40,6 +40,14 @@ def run_gpu(inp_dev, eta, C, mode="auto", max_group=0, W_state=None):
     return O.float().cpu().numpy(), W.cpu().numpy()
 
 
+def worst_chunk(O, Oo, C):
+    """The largest relative error of one chunk of one sequence's outputs (late
+    chunks have larger outputs and dominate the global norm; this catches an
+    error confined to a few chunks)."""
+    B, T = Oo.shape[:2]
+    return max(rel(O[b, i:i + C], Oo[b, i:i + C]) for b in range(B) for i in range(0, T, C))
+
+
 def check_against_oracle(inp, eta, C, dtype, mode="auto", max_group=0, label=""):
     print(f"[parity] {label} B,T,d,f,K={tuple(inp['H'].shape)},{inp['W_gate'].shape[0]},"
           f"{inp['taps'].shape[1]} C={C} eta={eta} mode={mode} G={max_group}", flush=True)
@@ -51,8 +59,10 @@ def check_against_oracle(inp, eta, C, dtype, mode="auto", max_group=0, label="")
     tol = tol_for(dtype)
     W0 = ni["W_down0"].astype(np.float64)
     e_o, e_w, e_dw = rel(O, Oo), rel(W, Wo), rel(W - W0, Wo - W0)
-    print(f"  rel O {e_o:.3e}  W {e_w:.3e}  dW {e_dw:.3e}  (tol {tol})", flush=True)
-    assert e_o <= tol and e_w <= tol, (e_o, e_w)
+    worst = worst_chunk(O, Oo, C)
+    print(f"  rel O {e_o:.3e} (worst chunk {worst:.3e})  W {e_w:.3e}  dW {e_dw:.3e}  (tol {tol})",
+          flush=True)
+    assert e_o <= tol and e_w <= tol and worst <= tol, (e_o, e_w, worst)
     if eta != 0.0:
         assert e_dw <= tol, e_dw
     else:
@@ -298,7 +308,9 @@ def test_reconstruction_alignment(case):
 
 # --------------------------------------------------------------- full-size workloads
 FULL = ["qwen3_4b_32k", "qwen3_4b_128k", "multi_session_16x8k", "small_4x128k"]
-PREFIX_CHUNKS = {"qwen3_4b_32k": 2, "qwen3_4b_128k": 1, "multi_session_16x8k": 1,
+# two chunks everywhere: chunk 1's outputs come from a weight the scan has
+# updated, at the benchmark's chunk size, group and launch shapes
+PREFIX_CHUNKS = {"qwen3_4b_32k": 2, "qwen3_4b_128k": 2, "multi_session_16x8k": 2,
                  "small_4x128k": 2}
 PREFIX_SEQS = {"multi_session_16x8k": (0, 15), "small_4x128k": (0, 3)}
 
@@ -324,9 +336,18 @@ def test_full_workload_prefix_and_final_weight(name):
     for b in seqs:
         Oo, _ = oracle.forward(ni["H"][b, :m], ni["X0"][b, :m], ni["W_gate"], ni["W_up"],
                                ni["W_down0"], ni["taps"], ni["W_target"], w.eta, w.chunk)
-        e = rel(O[b, :m].float().cpu().numpy(), Oo)
-        print(f"  seq {b} O[0:{m}] rel {e:.3e}", flush=True)
-        assert e <= tol_for(w.dtype)
+        Og = O[b, :m].float().cpu().numpy()
+        e = rel(Og, Oo)
+        per_chunk = [rel(Og[i:i + w.chunk], Oo[i:i + w.chunk]) for i in range(0, m, w.chunk)]
+        print(f"  seq {b} O[0:{m}] rel {e:.3e}, per chunk "
+              + " ".join(f"{x:.3e}" for x in per_chunk), flush=True)
+        assert e <= tol_for(w.dtype) and max(per_chunk) <= tol_for(w.dtype)
+        # chunk 1 used an updated weight: its outputs differ from W_down0's
+        Ostatic = oracle.gated_activations(ni["H"][b, w.chunk:m], ni["W_gate"], ni["W_up"]) \
+            @ ni["W_down0"].astype(np.float64).T
+        moved = rel(Ostatic, Oo[w.chunk:m])
+        print(f"  seq {b} chunk 1 with W_down0 instead: rel {moved:.3e}", flush=True)
+        assert moved > 10 * per_chunk[1]
     rng = np.random.default_rng(0)
     ms = np.sort(rng.choice(w.d_model, 3, replace=False))
     ns = np.sort(rng.choice(w.d_ff, 6, replace=False))
