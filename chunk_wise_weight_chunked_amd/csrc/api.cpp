@@ -233,11 +233,47 @@ int64_t compute_units() {
   return n;
 }
 
+// The fast-weight-independent part of the layer: the prepared weights, S2
+// (the conv into U, the projection into Vt: token rows [0, t_split) of each
+// sequence when t_split < T, the rest left to the first scan launch) and S1
+// (Z and Zt), in the workspace regions of `wp`.
+ttt_status_t run_activations(const ttt::Dims& dm, const ttt::WorkspacePlan& wp, const void* H,
+                             const void* X0, const void* Wg, const void* Wu, const void* taps,
+                             const void* Wt, void* ws, int64_t t_split, hipStream_t s) {
+  char* base = static_cast<char*>(ws);
+  void* Z = base + wp.z_off;
+  void* U = base + wp.u_off;
+  void* Zt = base + wp.zt_off;
+  void* Vt = base + wp.vt_off;
+  void* WgU = base + wp.wgu_off;
+  void* WtT = base + wp.wtt_off;
+  float* tapsT = reinterpret_cast<float*>(base + wp.taps_off);
+  hipError_t e = staged(kPrep, s, [&] {
+    return ttt::launch_weight_prep(dm, Wg, Wu, Wt, taps, WgU, WtT, tapsT, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "weight_prep");
+  const bool padded = dm.Cp != dm.C || dm.T % dm.C != 0;
+  if (padded) {
+    e = staged(kPad, s, [&] { return ttt::launch_pad_fill(Zt, Vt, dm, s); });
+    if (e != hipSuccess) return hip_fail(e, "pad_fill");
+  }
+  e = staged(kTarget, s, [&] {
+    return ttt::launch_target(dm, X0, tapsT, WtT, U, Vt, s, t_split < dm.T ? t_split : -1);
+  });
+  if (e != hipSuccess) return hip_fail(e, "target");
+  e = staged(kSwiglu, s, [&] { return ttt::launch_swiglu(dm, H, WgU, Z, Zt, s); });
+  if (e != hipSuccess) return hip_fail(e, "swiglu");
+  return TTT_OK;
+}
+
 // The whole layer for B sequences whose starting weights are in W_state.
+// acts_ready: the workspace already holds S1's and S2's results for these
+// inputs (a share's increment call made them), so only the scans and outputs
+// run.
 ttt_status_t run_layer(const ttt::Dims& dm, ttt_mode_t mode, bool reset, const void* H,
                        const void* X0, const void* Wg, const void* Wu, const void* W0,
                        const void* taps, const void* Wt, void* O, float* W_state, void* ws,
-                       size_t ws_bytes, hipStream_t s) {
+                       size_t ws_bytes, hipStream_t s, bool acts_ready = false) {
   int64_t G = 1;
   ttt_status_t st = plan_group(dm, mode, ws_bytes, &G);
   if (st) return st;
@@ -247,24 +283,13 @@ ttt_status_t run_layer(const ttt::Dims& dm, ttt_mode_t mode, bool reset, const v
   void* U = base + wp.u_off;
   void* Zt = base + wp.zt_off;
   void* Vt = base + wp.vt_off;
-  void* WgU = base + wp.wgu_off;
   void* WtT = base + wp.wtt_off;
-  float* tapsT = reinterpret_cast<float*>(base + wp.taps_off);
   void* slots = base + wp.slots_off;
 
   hipError_t e;
   if (reset) {
     e = staged(kReset, s, [&] { return ttt::launch_state_reset(W_state, W0, dm.dt, dm.B, dm.d, dm.f, s); });
     if (e != hipSuccess) return hip_fail(e, "state_reset");
-  }
-  e = staged(kPrep, s, [&] {
-    return ttt::launch_weight_prep(dm, Wg, Wu, Wt, taps, WgU, WtT, tapsT, s);
-  });
-  if (e != hipSuccess) return hip_fail(e, "weight_prep");
-  const bool padded = dm.Cp != dm.C || dm.T % dm.C != 0;
-  if (padded) {
-    e = staged(kPad, s, [&] { return ttt::launch_pad_fill(Zt, Vt, dm, s); });
-    if (e != hipSuccess) return hip_fail(e, "pad_fill");
   }
   // S2 (the conv into U, the projection into Vt), then S1.  With a
   // projection and more than one group, S2 may project only the first
@@ -276,15 +301,14 @@ ttt_status_t run_layer(const ttt::Dims& dm, ttt_mode_t mode, bool reset, const v
   const int64_t scan_tiles = dm.B * (dm.d / 256) * (dm.f / 256);
   const int64_t cus = compute_units();
   const int64_t scan_waves = (scan_tiles + cus - 1) / cus;
-  const bool split = groups > 1 && ttt::scan_target_fits(dm) && G * dm.C >= 2 * dm.d &&
-                     scan_waves <= 2 && scan_waves * cus - scan_tiles >= cus / 4;
+  const bool split = !acts_ready && groups > 1 && ttt::scan_target_fits(dm) &&
+                     G * dm.C >= 2 * dm.d && scan_waves <= 2 &&
+                     scan_waves * cus - scan_tiles >= cus / 4;
   const int64_t t_split = split ? G * dm.C : dm.T;  // 0 < t_split < T when split
-  e = staged(kTarget, s, [&] {
-    return ttt::launch_target(dm, X0, tapsT, WtT, U, Vt, s, split ? t_split : -1);
-  });
-  if (e != hipSuccess) return hip_fail(e, "target");
-  e = staged(kSwiglu, s, [&] { return ttt::launch_swiglu(dm, H, WgU, Z, Zt, s); });
-  if (e != hipSuccess) return hip_fail(e, "swiglu");
+  if (!acts_ready) {
+    const ttt_status_t st_a = run_activations(dm, wp, H, X0, Wg, Wu, taps, Wt, ws, t_split, s);
+    if (st_a) return st_a;
+  }
   // Group pipeline: launch g scans group g (slot set g & 1) and computes the
   // outputs of group g - 1 (the other set, completed by launch g - 1).
   const size_t set_bytes = (size_t)G * wp.slot_bytes;
@@ -320,14 +344,18 @@ struct Buffers {
   size_t ws_bytes;
 };
 
-ttt_status_t check_buffers(const ttt::Dims& dm, const Buffers& b, bool need_w0) {
+// Null, alignment and overlap checks of a call's buffers.  need_o = false:
+// the call writes no O (b.O is ignored).  `extra` inputs (halo rows) join the
+// overlap check against every output.
+ttt_status_t check_buffers(const ttt::Dims& dm, const Buffers& b, bool need_w0, bool need_o = true,
+                           const std::vector<Range>& extra = {}) {
   struct P {
     const char* name;
     const void* p;
     bool needed;
   } ptrs[] = {{"H", b.H, true},       {"X0", b.X0, true},     {"W_gate", b.Wg, true},
               {"W_up", b.Wu, true},   {"W_down0", b.W0, need_w0}, {"conv_taps", b.taps, dm.conv},
-              {"W_target", b.Wt, dm.proj}, {"O", b.O, true},     {"W_state", b.W, true},
+              {"W_target", b.Wt, dm.proj}, {"O", b.O, need_o},   {"W_state", b.W, true},
               {"ws", b.ws, true}};
   for (const P& q : ptrs) {
     if (!q.needed) continue;
@@ -344,7 +372,8 @@ ttt_status_t check_buffers(const ttt::Dims& dm, const Buffers& b, bool need_w0) 
   if (dm.conv) ins.push_back(range("conv_taps", b.taps, (size_t)dm.d * dm.K * es));
   if (dm.proj) ins.push_back(range("W_target", b.Wt, (size_t)dm.d * dm.d * es));
   if (need_w0) ins.push_back(range("W_down0", b.W0, (size_t)dm.d * dm.f * es));
-  const Range outs[] = {range("O", b.O, act),
+  ins.insert(ins.end(), extra.begin(), extra.end());
+  const Range outs[] = {range("O", need_o ? b.O : nullptr, need_o ? act : 0),
                         range("W_state", b.W, (size_t)dm.B * dm.d * dm.f * sizeof(float)),
                         range("ws", b.ws, b.ws_bytes)};
   for (const Range& o : outs)
@@ -492,6 +521,96 @@ ttt_status_t ttt_mlp_forward_batched(const ttt_mlp_desc_t* desc, const void* H, 
   if (st) return st;
   return run_layer(dm, desc->mode, init, H, X0, W_gate, W_up, W_down0, conv_taps, W_target, O,
                    W_state, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// A share's descriptor and halo rows: validates them and sets the conv's
+// halo pointers in dm (the left halo is read as the streaming halo of
+// kHaloRows rows before each session's first row).
+ttt_status_t share_dims(const ttt_mlp_desc_t* desc, const ttt_share_t* share, ttt::Dims* dm,
+                        std::vector<Range>* halos) {
+  ttt_status_t st = make_dims(desc, dm);
+  if (st) return st;
+  if (!share) return fail(TTT_ERR_INVALID_ARGUMENT, "share is NULL");
+  const size_t row = (size_t)dm->d * ttt::dtype_bytes(dm->dt);
+  if (share->X0_left) {
+    if (!aligned(share->X0_left, 16))
+      return fail(TTT_ERR_INVALID_ARGUMENT, "X0_left is not 16-byte aligned");
+    dm->halo = share->X0_left;
+    dm->halo_stride = ttt::kHaloRows * dm->d;
+    halos->push_back(range("X0_left", share->X0_left, (size_t)dm->B * ttt::kHaloRows * row));
+  }
+  if (share->X0_right) {
+    if (!aligned(share->X0_right, 16))
+      return fail(TTT_ERR_INVALID_ARGUMENT, "X0_right is not 16-byte aligned");
+    if (dm->T % dm->C != 0)
+      return fail(TTT_ERR_INVALID_ARGUMENT,
+                  "a share followed by more tokens (X0_right given) must hold whole chunks "
+                  "(seq_len %lld, chunk %lld)", (long long)dm->T, (long long)dm->C);
+    dm->halo_r = share->X0_right;
+    dm->halo_r_stride = dm->d;
+    halos->push_back(range("X0_right", share->X0_right, (size_t)dm->B * row));
+  }
+  return TTT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ttt_status_t ttt_mlp_share_increment(const ttt_mlp_desc_t* desc, const ttt_share_t* share,
+                                     const void* H, const void* X0, const void* W_gate,
+                                     const void* W_up, const void* conv_taps,
+                                     const void* W_target, float* S, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  ttt::Dims dm;
+  std::vector<Range> halos;
+  ttt_status_t st = share_dims(desc, share, &dm, &halos);
+  if (st) return st;
+  const Buffers b{H, X0, W_gate, W_up, nullptr, conv_taps, W_target, nullptr, S, ws, ws_bytes};
+  st = check_buffers(dm, b, false, false, halos);
+  if (st) return st;
+  const ttt::WorkspacePlan wp = ttt::plan_workspace(dm, 1);
+  if (ws_bytes < wp.total_bytes)
+    return fail(TTT_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is below the minimum %zu",
+                ws_bytes, wp.total_bytes);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_activations(dm, wp, H, X0, W_gate, W_up, conv_taps, W_target, ws, dm.T, s);
+  if (st) return st;
+  // the scan of every chunk from a zero state, without weight slots: the
+  // accumulator ends as the sum of the share's increments
+  char* base = static_cast<char*>(ws);
+  hipError_t e = ttt::launch_fill_f32(S, dm.B * dm.d * dm.f, 0.0f, s);
+  if (e == hipSuccess)
+    e = staged(kPrefix, s, [&] {
+      return ttt::launch_scan_apply(dm, base + wp.vt_off, base + wp.zt_off, S, nullptr, 0, dm.N,
+                                    nullptr, nullptr, nullptr, 0, 0, s);
+    });
+  if (e != hipSuccess) return hip_fail(e, "share increment");
+  return ok();
+}
+
+ttt_status_t ttt_mlp_share_forward(const ttt_mlp_desc_t* desc, const ttt_share_t* share,
+                                   int32_t reuse, const void* H, const void* X0,
+                                   const void* W_gate, const void* W_up, const void* conv_taps,
+                                   const void* W_target, void* O, float* W_state, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  ttt::Dims dm;
+  std::vector<Range> halos;
+  ttt_status_t st = share_dims(desc, share, &dm, &halos);
+  if (st) return st;
+  if (reuse != 0 && reuse != 1) return fail(TTT_ERR_INVALID_ARGUMENT, "reuse must be 0 or 1");
+  const Buffers b{H, X0, W_gate, W_up, nullptr, conv_taps, W_target, O, W_state, ws, ws_bytes};
+  st = check_buffers(dm, b, false, true, halos);
+  if (st) return st;
+  int64_t g;
+  st = plan_group(dm, desc->mode, ws_bytes, &g);
+  if (st) return st;
+  return run_layer(dm, desc->mode, false, H, X0, W_gate, W_up, nullptr, conv_taps, W_target, O,
+                   W_state, ws, ws_bytes, static_cast<hipStream_t>(stream), reuse == 1);
 }
 
 size_t ttt_mlp_carry_size(const ttt_mlp_desc_t* desc) {

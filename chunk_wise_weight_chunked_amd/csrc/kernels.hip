@@ -398,7 +398,15 @@ __global__ __launch_bounds__(256) void conv_kernel(Dims dm, const T* __restrict_
 #pragma unroll
       for (int k = 0; k < KMAX; ++k) {
         const int64_t src = sq + dm.shift - k;  // X0 row of tap k, inside the sequence
-        if (k >= K || src >= T_seq) continue;
+        if (k >= K) continue;
+        if (src >= T_seq) {  // after the sequence: zero, or the share's right halo row
+          if (dm.halo_r == nullptr || src > T_seq) continue;
+          const uint4 hv = *reinterpret_cast<const uint4*>(
+              static_cast<const T*>(dm.halo_r) + (o / T_seq) * dm.halo_r_stride + c * EPC);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) u[e] = fmaf(tp[k][e], chunk_value<T>(hv, e), u[e]);
+          continue;
+        }
         if (src < 0) {  // before the sequence: zero, or the streaming halo
           if (dm.halo == nullptr || src < -kHaloRows) continue;
           const uint4 hv = *reinterpret_cast<const uint4*>(
@@ -624,7 +632,8 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
       }
   };
 
-  write_slot(0);
+  const bool with_slots = slots != nullptr;  // none: the increments' sum only
+  if (with_slots) write_slot(0);
   const int64_t kt_per_chunk = dm.Cp / TB;
   // a streaming call leaves the sequence's last chunk out of the state (its
   // last token's target needs the next call's first token); its slot is
@@ -637,13 +646,13 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
   // contiguous KB, and spreading them measured slower here.)
   int64_t next_slot = 1, next_slot_kt = kt_per_chunk;  // counters, not a division per k-tile
   mainloop_with_stores<T, S, kSlotStores>(acc, la, lb, nk, smem, p, [&](int64_t kt) {
-    if (kt != next_slot_kt) return false;
+    if (kt != next_slot_kt || !with_slots) return false;
     write_slot(next_slot);
     ++next_slot;
     next_slot_kt += kt_per_chunk;
     return true;
   });
-  if (skip && gc > 1) write_slot(gc - 1);
+  if (skip && gc > 1 && with_slots) write_slot(gc - 1);
 
 #pragma unroll
   for (int i = 0; i < S::MB; ++i)

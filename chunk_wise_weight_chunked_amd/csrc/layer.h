@@ -30,6 +30,10 @@ struct Dims {
   // Streaming continuation (defaults give the one-shot layer):
   const void* halo = nullptr;  // [B][halo_stride]: kHaloRows X0 rows before each session's row 0
   int64_t halo_stride = 0;     // elements between sessions in `halo`
+  // A share of a longer sequence (context parallelism): the X0 row after each
+  // session's last row (null: the sequence ends there, zero padding).
+  const void* halo_r = nullptr;  // [B][halo_r_stride]
+  int64_t halo_r_stride = 0;
   bool skip_last = false;      // leave the last chunk's update out of the state
   bool reverse_slots = false;  // the scan writes chunk jj's slot at gc - 1 - jj
   int64_t out_skip = 0;        // rows [0, out_skip) of each session are not output ...

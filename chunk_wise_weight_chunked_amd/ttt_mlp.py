@@ -60,6 +60,13 @@ class ttt_mlp_desc_t(ctypes.Structure):
     ]
 
 
+class ttt_share_t(ctypes.Structure):
+    _fields_ = [
+        ("X0_left", ctypes.c_void_p),
+        ("X0_right", ctypes.c_void_p),
+    ]
+
+
 EXPORTS = (
     "ttt_mlp_workspace_size", "ttt_mlp_group_size", "ttt_mlp_forward",
     "ttt_mlp_forward_batched", "ttt_fastweight_state_reset", "ttt_last_error",
@@ -67,6 +74,7 @@ EXPORTS = (
     "ttt_mlp_carry_size", "ttt_mlp_stream_workspace_size", "ttt_mlp_forward_stream",
     "ttt_mlp_forward_stream_ragged",
     "ttt_mlp_backward_workspace_size", "ttt_mlp_backward_batched",
+    "ttt_mlp_share_increment", "ttt_mlp_share_forward",
 )
 
 _lib = None
@@ -114,6 +122,11 @@ def load(path: str | None = None):
     lib.ttt_mlp_backward_workspace_size.restype = sz
     lib.ttt_mlp_backward_batched.argtypes = [dp] + [vp] * 18 + [vp, sz, vp]
     lib.ttt_mlp_backward_batched.restype = ctypes.c_int
+    shp = ctypes.POINTER(ttt_share_t)
+    lib.ttt_mlp_share_increment.argtypes = [dp, shp] + [vp] * 7 + [vp, sz, vp]
+    lib.ttt_mlp_share_increment.restype = ctypes.c_int
+    lib.ttt_mlp_share_forward.argtypes = [dp, shp, ctypes.c_int32] + [vp] * 8 + [vp, sz, vp]
+    lib.ttt_mlp_share_forward.restype = ctypes.c_int
     lib.ttt_fastweight_state_reset.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp]
     lib.ttt_fastweight_state_reset.restype = ctypes.c_int
     lib.ttt_last_error.restype = ctypes.c_char_p
@@ -229,6 +242,31 @@ def ttt_mlp_forward_stream(desc, pos, last, H, X0, W_gate, W_up, W_down0, conv_t
         ctypes.byref(desc), int(pos), int(last), _ptr(H), _ptr(X0), _ptr(W_gate), _ptr(W_up),
         _ptr(W_down0), _ptr(conv_taps), _ptr(W_target), _ptr(O), _ptr(W_state), _ptr(carry),
         _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def make_share(X0_left=None, X0_right=None) -> ttt_share_t:
+    """The halo rows of a share: X0_left [B][7][d] (the 7 X0 rows before the
+    share) and X0_right [B][d] (the row after it), device tensors or None."""
+    return ttt_share_t(_ptr(X0_left), _ptr(X0_right))
+
+
+def ttt_mlp_share_increment(desc, share, H, X0, W_gate, W_up, conv_taps, W_target, S, ws,
+                            ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(load().ttt_mlp_share_increment(
+        ctypes.byref(desc), ctypes.byref(share), _ptr(H), _ptr(X0), _ptr(W_gate), _ptr(W_up),
+        _ptr(conv_taps), _ptr(W_target), _ptr(S), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def ttt_mlp_share_forward(desc, share, reuse, H, X0, W_gate, W_up, conv_taps, W_target, O,
+                          W_state, ws, ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(load().ttt_mlp_share_forward(
+        ctypes.byref(desc), ctypes.byref(share), int(reuse), _ptr(H), _ptr(X0), _ptr(W_gate),
+        _ptr(W_up), _ptr(conv_taps), _ptr(W_target), _ptr(O), _ptr(W_state), _ptr(ws),
+        int(ws_bytes), _stream(stream)))
 
 
 def ttt_fastweight_state_reset(W_state, W_down0, w0_dtype, batch, d_model, d_ff,

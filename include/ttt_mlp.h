@@ -251,6 +251,69 @@ ttt_status_t ttt_mlp_forward_stream_ragged(const ttt_mlp_desc_t* desc, const int
                                            const void* W_target, void* O, float* W_state,
                                            void* carry, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- A share of a long sequence (context parallelism) ----
+ * The chunk-wise update splits over devices (section 3.2, the note that
+ * block-wise updates fit context parallelism): each device takes a
+ * contiguous range of whole chunks of the sequences, computes the sum of its
+ * own chunks' increments, one exclusive prefix sum over the devices gives
+ * each its starting weight, and each then produces its outputs.  These two
+ * calls are the per-device parts, on the device's share at its real shape;
+ * the prefix sum between them (a collective across devices) is the
+ * caller's.  With shares r = 0..R-1 of a sequence, S_r from
+ * ttt_mlp_share_increment and W_state of share r set to
+ * W_down0 + S_0 + ... + S_{r-1}, ttt_mlp_share_forward gives the outputs of
+ * one ttt_mlp_forward_batched call over the whole sequence, and the last
+ * share's W_state the final weight (equal up to fp32 summation order; the
+ * bf16 weight slots may round differently where the fp32 sums differ).
+ *
+ * desc describes the share: seq_len = its T_r tokens of each of B
+ * sequences, chunk = C (chunks are counted from the share's first token, so a
+ * share must start on a chunk boundary of its sequence), and the other
+ * fields as for the whole sequence.  H, X0 [B][T_r][d] are the share's rows.
+ * The conv's window reaches outside the share; the rows it needs come in
+ * ttt_share_t:
+ *   X0_left   [B][7][d]: the 7 X0 rows before the share's first token (row 6
+ *             is the token just before it); only the last K-2 (alignment
+ *             NEXT) or K-1 (SELF) rows are read.  NULL when the share starts
+ *             its sequences (zero padding).
+ *   X0_right  [B][d]: the X0 row of the token after the share's last token
+ *             (the last target looks one token ahead).  NULL when the share
+ *             ends its sequences; when given, seq_len must be a multiple of
+ *             chunk (the next share starts on a chunk boundary).
+ * Both are device pointers, 16-byte aligned, and must not overlap outputs. */
+typedef struct {
+  const void* X0_left;
+  const void* X0_right;
+} ttt_share_t;
+
+/* Step 1 of section 3.2 on one device: S [B][d][f] fp32 (overwritten) gets
+ * eta * sum over the share's chunks of V^_iᵀ Z_i, the change the share makes
+ * to each sequence's fast weight, computed without writing any weight slot.
+ * ws: at least ttt_mlp_workspace_size(desc, 1) bytes; on return it holds the
+ * share's activations (gated activations and targets in the scans' layouts)
+ * for a following ttt_mlp_share_forward with reuse = 1.  W_down0 is not an
+ * input: the sum does not depend on the weight. */
+ttt_status_t ttt_mlp_share_increment(const ttt_mlp_desc_t* desc, const ttt_share_t* share,
+                                     const void* H, const void* X0, const void* W_gate,
+                                     const void* W_up, const void* conv_taps,
+                                     const void* W_target, float* S, void* ws, size_t ws_bytes,
+                                     void* stream);
+
+/* Step 3 of section 3.2 on one device: the share's outputs O [B][T_r][d]
+ * from W_state [B][d][f] fp32 (in/out: on entry the weight at the share's
+ * first token -- W_down0 plus the increments of every earlier share --, on
+ * exit the weight after the share).  reuse = 1: ws holds this share's
+ * activations from the ttt_mlp_share_increment call just before it, made on
+ * the same stream with the same desc, share rows and weights and not
+ * modified since; S1 and S2 are then skipped.  reuse = 0 recomputes them.
+ * ws as for ttt_mlp_forward_batched (its size sets the group; keep the same
+ * buffer for reuse).  desc.init_from_w0 is ignored. */
+ttt_status_t ttt_mlp_share_forward(const ttt_mlp_desc_t* desc, const ttt_share_t* share,
+                                   int32_t reuse, const void* H, const void* X0,
+                                   const void* W_gate, const void* W_up, const void* conv_taps,
+                                   const void* W_target, void* O, float* W_state, void* ws,
+                                   size_t ws_bytes, void* stream);
+
 /* ---- Backward pass ----
  * Gradients of a loss L through the layer, given dO = dL/dO and (optionally)
  * dW_final = dL/dW_state after the call, for B sequences laid out as in

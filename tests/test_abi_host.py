@@ -435,3 +435,73 @@ def test_stream_ragged_validation(lib):
     assert lib.ttt_mlp_forward_stream_ragged(ctypes.byref(d), None, None, *[p[k] for k in (
         "H", "X0", "W_gate", "W_up", "W_down0", "taps", "W_target", "O", "W", "carry", "ws")],
         p["ws_bytes"], None) == tm.TTT_ERR_INVALID_ARGUMENT
+
+
+# ------------------------------------------------ shares (context parallelism)
+def _share_ptrs(d):
+    p = fake_ptrs(d)
+    es = 2 if d.dtype == tm.TTT_BF16 else 4
+    top = max(v for k, v in p.items() if k != "ws_bytes") + (1 << 32)
+    p["left"] = top
+    p["right"] = top + (d.batch * 7 * d.d_model * es + 4095) // 4096 * 4096 + 4096
+    return p
+
+
+def _share_calls(lib, d, p, share, reuse=0):
+    inc = lib.ttt_mlp_share_increment(ctypes.byref(d), share, p["H"], p["X0"], p["W_gate"],
+                                      p["W_up"], p["taps"], p["W_target"], p["W"], p["ws"],
+                                      p["ws_bytes"], None)
+    msg = tm.ttt_last_error()
+    fwd = lib.ttt_mlp_share_forward(ctypes.byref(d), share, reuse, p["H"], p["X0"],
+                                    p["W_gate"], p["W_up"], p["taps"], p["W_target"], p["O"],
+                                    p["W"], p["ws"], p["ws_bytes"], None)
+    return inc, msg, fwd, tm.ttt_last_error()
+
+
+def test_share_rejects_bad_arguments(lib):
+    d = desc(seq_len=1000, chunk=128)  # not whole chunks
+    p = _share_ptrs(d)
+    # a share followed by more tokens must end on a chunk boundary
+    sh = tm.ttt_share_t(p["left"], p["right"])
+    inc, m1, fwd, m2 = _share_calls(lib, d, p, ctypes.byref(sh))
+    assert inc == fwd == tm.TTT_ERR_INVALID_ARGUMENT and "whole chunks" in m1 and "whole chunks" in m2
+    # the last share of a sequence may end on a partial chunk: the call gets
+    # past validation and stops at the (too small) workspace
+    p["ws_bytes"] = 1024
+    sh = tm.ttt_share_t(p["left"], None)
+    inc, m1, fwd, m2 = _share_calls(lib, d, p, ctypes.byref(sh))
+    assert inc == fwd == tm.TTT_ERR_WORKSPACE_TOO_SMALL, (m1, m2)
+    # NULL share descriptor, misaligned halo, halo overlapping an output, bad reuse
+    inc, m1, fwd, m2 = _share_calls(lib, d, p, None)
+    assert inc == fwd == tm.TTT_ERR_INVALID_ARGUMENT and "share is NULL" in m1
+    sh = tm.ttt_share_t(p["left"] + 8, None)
+    inc, m1, fwd, m2 = _share_calls(lib, d, p, ctypes.byref(sh))
+    assert inc == fwd == tm.TTT_ERR_INVALID_ARGUMENT and "X0_left" in m1 and "aligned" in m1
+    sh = tm.ttt_share_t(p["O"], None)  # the halo inside O: O overlaps an input
+    _, _, fwd, m2 = _share_calls(lib, d, p, ctypes.byref(sh))
+    assert fwd == tm.TTT_ERR_INVALID_ARGUMENT and "overlaps" in m2
+    sh = tm.ttt_share_t(p["W"], None)  # the halo inside S / W_state
+    inc, m1, fwd, m2 = _share_calls(lib, d, p, ctypes.byref(sh))
+    assert inc == fwd == tm.TTT_ERR_INVALID_ARGUMENT and "overlaps" in m1
+    _, _, fwd, m2 = _share_calls(lib, d, p, ctypes.byref(tm.ttt_share_t(None, None)), reuse=2)
+    assert fwd == tm.TTT_ERR_INVALID_ARGUMENT and "reuse" in m2
+
+
+def test_share_increment_needs_no_o_and_no_w_down0(lib):
+    """The increment call writes no output rows and reads no starting weight:
+    NULL O and W_down0 pass validation (the call stops at the workspace)."""
+    d = desc(seq_len=1024, chunk=128)
+    p = _share_ptrs(d)
+    p["O"] = None
+    p["W_down0"] = None
+    p["ws_bytes"] = tm.ttt_mlp_workspace_size(d, 1) - 256
+    sh = tm.ttt_share_t(p["left"], p["right"])
+    st = lib.ttt_mlp_share_increment(ctypes.byref(d), ctypes.byref(sh), p["H"], p["X0"],
+                                     p["W_gate"], p["W_up"], p["taps"], p["W_target"], p["W"],
+                                     p["ws"], p["ws_bytes"], None)
+    assert st == tm.TTT_ERR_WORKSPACE_TOO_SMALL, tm.ttt_last_error()
+    p["W"] = None
+    st = lib.ttt_mlp_share_increment(ctypes.byref(d), ctypes.byref(sh), p["H"], p["X0"],
+                                     p["W_gate"], p["W_up"], p["taps"], p["W_target"], p["W"],
+                                     p["ws"], p["ws_bytes"], None)
+    assert st == tm.TTT_ERR_INVALID_ARGUMENT and "W_state is NULL" in tm.ttt_last_error()
