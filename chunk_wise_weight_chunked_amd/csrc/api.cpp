@@ -705,17 +705,40 @@ ttt_status_t stream_full(const ttt_mlp_desc_t* desc, int64_t b0, int64_t nb, int
   return TTT_OK;
 }
 
-// A stream call with per-session positions and closing flags.
+// A stream call with per-session positions and closing flags.  noalloc:
+// every session must be one the decode kernels serve, and their gated
+// activations go to the library's static scratch instead of ws.
 ttt_status_t stream_call(const ttt_mlp_desc_t* desc, const int64_t* pos, const int32_t* last,
                          const void* H, const void* X0, const void* W_gate, const void* W_up,
                          const void* W_down0, const void* conv_taps, const void* W_target,
                          void* O, float* W_state, void* carry, void* ws, size_t ws_bytes,
-                         void* stream) {
+                         void* stream, bool noalloc = false) {
   ttt::Dims du;  // the call's own L tokens (user buffers)
   ttt_status_t st = make_dims(desc, &du);
   if (st) return st;
   if (!pos || !last) return fail(TTT_ERR_INVALID_ARGUMENT, "pos and last must be non-NULL");
   const int64_t B = du.B;
+  if (noalloc) {
+    if (!decode_shape(du))
+      return fail(TTT_ERR_UNSUPPORTED,
+                  "the allocation-free call serves decode calls only: bf16, at most %lld new "
+                  "rows per session and %lld in all", (long long)kDecodeMaxRows,
+                  (long long)kDecodeMaxTotal);
+    for (int64_t b = 0; b < B; ++b)
+      if (pos[b] < 0 || last[b] != 0 ||
+          !decode_session(du.T, desc->chunk, pending_tokens(pos[b], desc->chunk), 0))
+        return fail(TTT_ERR_UNSUPPORTED,
+                    "session %lld needs the full path (closing call, or its new rows go past "
+                    "its pending chunk): use ttt_mlp_forward_stream_ragged with a workspace",
+                    (long long)b);
+    if ((size_t)(B * du.T) * du.f * 2 > ttt::kDecodeScratchBytes)
+      return fail(TTT_ERR_UNSUPPORTED,
+                  "the gated activations of %lld rows of d_ff %lld exceed the %zu-byte scratch",
+                  (long long)(B * du.T), (long long)du.f, ttt::kDecodeScratchBytes);
+    const hipError_t e = ttt::decode_scratch_ptr(&ws);
+    if (e != hipSuccess) return hip_fail(e, "scratch address");
+    ws_bytes = ttt::kDecodeScratchBytes;
+  }
   bool need_carry = false, need_w0 = false;
   for (int64_t b = 0; b < B; ++b) {
     if (pos[b] < 0)
@@ -741,9 +764,11 @@ ttt_status_t stream_call(const ttt_mlp_desc_t* desc, const int64_t* pos, const i
     for (const Range& o : others)
       if (overlaps(c, o)) return fail(TTT_ERR_INVALID_ARGUMENT, "carry overlaps %s", o.name);
   }
-  StreamPlan sp;
-  st = plan_stream(desc, 0, ws_bytes, &sp);  // the whole batch: the largest sub-call fits
-  if (st) return st;
+  if (!noalloc) {
+    StreamPlan sp;
+    st = plan_stream(desc, 0, ws_bytes, &sp);  // the whole batch: the largest sub-call fits
+    if (st) return st;
+  }
 
   const int64_t C = desc->chunk, L = du.T, d = du.d, f = du.f;
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -846,6 +871,15 @@ ttt_status_t ttt_fastweight_state_reset(float* W_state, const void* W_down0, ttt
   });
   if (e != hipSuccess) return hip_fail(e, "state_reset");
   return ok();
+}
+
+ttt_status_t ttt_mlp_forward_stream_decode_noalloc(
+    const ttt_mlp_desc_t* desc, const int64_t* pos, const int32_t* last, const void* H,
+    const void* X0, const void* W_gate, const void* W_up, const void* W_down0,
+    const void* conv_taps, const void* W_target, void* O, float* W_state, void* carry,
+    void* stream) {
+  return stream_call(desc, pos, last, H, X0, W_gate, W_up, W_down0, conv_taps, W_target, O,
+                     W_state, carry, nullptr, 0, stream, true);
 }
 
 const char* ttt_last_error(void) { return g_err.c_str(); }

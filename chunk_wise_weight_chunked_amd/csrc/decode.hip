@@ -21,6 +21,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
 
 #include "gemm_core.h"
 #include "layer.h"
@@ -295,6 +297,33 @@ hipError_t launch_state_to_bf16(const float* W, void* out, int64_t n, hipStream_
   hipLaunchKernelGGL(state_to_bf16_kernel, dim3(grid_cap(n8, 256, 16384)), dim3(256), 0, s, W,
                      static_cast<uint16_t*>(out), n8);
   return hipGetLastError();
+}
+
+// ------------------------------------------------- allocation-free scratch
+// The gated activations of a decode call for callers that cannot allocate: a
+// file-scope device array (each GPU holds its own copy until the process
+// ends).  Host code never passes the array's name to a kernel or a copy (on
+// the host it is only a stand-in for the device symbol): it takes the
+// device's address of it once per device and hands that out.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch_ptr(void** out) {
+  static std::mutex mu;
+  static std::map<int, void*> by_device;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = by_device.find(dev);
+  if (it == by_device.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    it = by_device.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return hipSuccess;
 }
 
 }  // namespace ttt

@@ -112,6 +112,12 @@ hipError_t launch_decode_swiglu(const void* H, int64_t M, const void* Wg, const 
 hipError_t launch_decode_down(const void* Z, const void* Wc, void* O, int64_t B, int64_t L,
                               int64_t d, int64_t f, uint64_t mask, hipStream_t s);
 hipError_t launch_state_to_bf16(const float* W, void* out, int64_t n, hipStream_t s);
+// The allocation-free decode call's scratch for its gated activations (at
+// most kDecodeMaxSessions rows of d_ff bf16 values in all: 64 rows of up to
+// 32768 features): the calling thread's current device's address of a static
+// device array, looked up once per device.
+constexpr size_t kDecodeScratchBytes = (size_t)4 << 20;
+hipError_t decode_scratch_ptr(void** out);
 
 // Backward-pass kernels (backward.hip).
 constexpr int kTargetBackwardRows = 256;  // token rows per partial sum of the taps' gradient

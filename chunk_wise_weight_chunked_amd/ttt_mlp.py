@@ -75,6 +75,7 @@ EXPORTS = (
     "ttt_mlp_forward_stream_ragged",
     "ttt_mlp_backward_workspace_size", "ttt_mlp_backward_batched",
     "ttt_mlp_share_increment", "ttt_mlp_share_forward",
+    "ttt_mlp_forward_stream_decode_noalloc",
 )
 
 _lib = None
@@ -122,6 +123,8 @@ def load(path: str | None = None):
     lib.ttt_mlp_backward_workspace_size.restype = sz
     lib.ttt_mlp_backward_batched.argtypes = [dp] + [vp] * 18 + [vp, sz, vp]
     lib.ttt_mlp_backward_batched.restype = ctypes.c_int
+    lib.ttt_mlp_forward_stream_decode_noalloc.argtypes = [dp, vp, vp] + [vp] * 10 + [vp]
+    lib.ttt_mlp_forward_stream_decode_noalloc.restype = ctypes.c_int
     shp = ctypes.POINTER(ttt_share_t)
     lib.ttt_mlp_share_increment.argtypes = [dp, shp] + [vp] * 7 + [vp, sz, vp]
     lib.ttt_mlp_share_increment.restype = ctypes.c_int
@@ -363,6 +366,21 @@ def ttt_mlp_forward_stream_ragged(desc, pos, last, H, X0, W_gate, W_up, W_down0,
         _ptr(H), _ptr(X0), _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(conv_taps),
         _ptr(W_target), _ptr(O), _ptr(W_state), _ptr(carry), _ptr(ws), int(ws_bytes),
         _stream(stream)))
+
+
+def ttt_mlp_forward_stream_decode_noalloc(desc, pos, last, H, X0, W_gate, W_up, W_down0,
+                                          conv_taps, W_target, O, W_state, carry,
+                                          stream=None) -> None:
+    """The allocation-free decode call (no workspace); pos, last: B ints."""
+    B = desc.batch
+    if len(pos) != B or len(last) != B:
+        raise ValueError(f"pos and last need {B} entries")
+    p = (ctypes.c_int64 * B)(*[int(x) for x in pos])
+    l_ = (ctypes.c_int32 * B)(*[int(x) for x in last])
+    _check(load().ttt_mlp_forward_stream_decode_noalloc(
+        ctypes.byref(desc), ctypes.cast(p, ctypes.c_void_p), ctypes.cast(l_, ctypes.c_void_p),
+        _ptr(H), _ptr(X0), _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(conv_taps),
+        _ptr(W_target), _ptr(O), _ptr(W_state), _ptr(carry), _stream(stream)))
 
 
 def ttt_mlp_backward_workspace_size(desc: ttt_mlp_desc_t) -> int:

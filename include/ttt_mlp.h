@@ -251,6 +251,26 @@ ttt_status_t ttt_mlp_forward_stream_ragged(const ttt_mlp_desc_t* desc, const int
                                            const void* W_target, void* O, float* W_state,
                                            void* carry, void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the decode
+ * form of ttt_mlp_forward_stream_ragged without a workspace argument.  It
+ * serves only calls the decode kernels serve -- bf16, last[b] = 0 for every
+ * session, at most 16 new rows per session and 64 in all, every session's new
+ * rows inside its pending chunk, and B * L * d_ff * 2 <= 4 MiB -- and returns
+ * TTT_ERR_UNSUPPORTED (nothing written) for any other call, which needs
+ * ttt_mlp_forward_stream_ragged with a workspace.  Its outputs, state and
+ * carry equal that call's bit for bit.  The gated activations go to a
+ * library-owned static device buffer of 4 MiB, one per GPU, held until the
+ * process ends; it calls no allocator.  All calls on one GPU share that
+ * buffer: calls that overlap in time on one GPU (on different streams) race
+ * and must be serialised by the caller.  Other arguments as for
+ * ttt_mlp_forward_stream_ragged. */
+ttt_status_t ttt_mlp_forward_stream_decode_noalloc(
+    const ttt_mlp_desc_t* desc, const int64_t* pos, const int32_t* last, const void* H,
+    const void* X0, const void* W_gate, const void* W_up, const void* W_down0,
+    const void* conv_taps, const void* W_target, void* O, float* W_state, void* carry,
+    void* stream);
+
 /* ---- A share of a long sequence (context parallelism) ----
  * The chunk-wise update splits over devices (section 3.2, the note that
  * block-wise updates fit context parallelism): each device takes a

@@ -505,3 +505,24 @@ def test_share_increment_needs_no_o_and_no_w_down0(lib):
                                      p["W_gate"], p["W_up"], p["taps"], p["W_target"], p["W"],
                                      p["ws"], p["ws_bytes"], None)
     assert st == tm.TTT_ERR_INVALID_ARGUMENT and "W_state is NULL" in tm.ttt_last_error()
+
+
+def test_noalloc_decode_rejects_calls_it_does_not_serve():
+    """Through the binding (argument count and order) with fake pointers: an
+    fp32 call, a closing call and a call past the pending chunk are refused
+    before anything touches the device."""
+    for kw, pos, last, word in ((dict(dtype=tm.TTT_F32), 0, 0, "at most"),
+                                (dict(), 0, 1, "full path"),
+                                (dict(seq_len=16, chunk=16), 16, 0, "full path"),
+                                (dict(seq_len=17), 0, 0, "at most")):
+        base = dict(batch=2, seq_len=8, chunk=64)
+        base.update(kw)
+        d = desc(**base)
+        p = fake_ptrs(d)
+        with pytest.raises(tm.TTTError) as e:
+            tm.ttt_mlp_forward_stream_decode_noalloc(
+                d, [pos] * 2, [last] * 2, *[p[k] for k in (
+                    "H", "X0", "W_gate", "W_up", "W_down0", "taps", "W_target", "O", "W")],
+                p["ws"], stream=0)
+        assert e.value.status == tm.TTT_ERR_UNSUPPORTED and word in str(e.value), str(e.value)
+
