@@ -29,7 +29,7 @@ constexpr size_t kBlasWorkspace = (size_t)32 << 20;
 
 BackwardPlan plan_backward(const ttt::Dims& dm) {
   BackwardPlan p;
-  p.fwd = ttt::plan_workspace(dm, dm.N);
+  p.fwd = ttt::plan_workspace(dm, dm.N, true);
   const size_t es = ttt::dtype_bytes(dm.dt), BT = (size_t)(dm.B * dm.T);
   const size_t d = dm.d, f = dm.f;
   size_t off = p.fwd.total_bytes;

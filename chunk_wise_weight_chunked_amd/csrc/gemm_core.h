@@ -105,6 +105,14 @@ __device__ __forceinline__ uint32_t lds_offset(int row, int chunk) {
   return (uint32_t)row * kRowBytes + (uint32_t)((chunk ^ lds_swz(row)) << 4);
 }
 
+// A k-major operand tile (rows = k, 128-byte rows of 64 m-values) is read with
+// transposed loads that take four consecutive rows at a time; this swizzle
+// puts rows r and r + 2 (same bank half) on opposite halves of the 8 chunk
+// slots, so each half-wave of such a load hits every bank once.
+__device__ __forceinline__ int lds_swz_tr(int row) {
+  return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
 // ------------------------------------------------------------- tile shapes
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct TileShape {
@@ -161,18 +169,53 @@ __device__ __forceinline__ LanePos lane_pos() {
 template <typename T, class S>
 struct Mma;
 
-template <class S>
-struct Mma<uint16_t, S> {
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// A fragment i of step s from a k-major A tile: stage row R = (m / 64) * 64 + k
+// holds the 64 m-values [64 (m / 64), + 64) of k-tile column k, chunk c at
+// c ^ lds_swz_tr(R).  ds_read_b64_tr_b16 works on groups of 16 lanes: lane j
+// of a group gives the address of 4 consecutive values, and lane j receives
+// value j % 4 of the words lanes j / 4, 4 + j / 4, 8 + j / 4 and 12 + j / 4
+// addressed.  With lane j addressing k-row kb + j / 4 at m-values
+// mb + 4 (j % 4) .. + 3, lane j receives k-rows kb .. kb + 3 of column mb + j.
+// Lane l of the wave needs row m = l % 32 of the fragment and k values
+// 8 (l / 32) .. + 7: group g = l / 16 takes mb = 16 (g % 2) and kb = 8 (g / 2),
+// two loads (kb and kb + 4) per fragment.
+__device__ __forceinline__ bf16x8_t read_a_tr(const lds_char* sA, int m0, int lane, int s) {
+  const int g = lane >> 4, j = lane & 15;
+  const int m = m0 + 16 * (g & 1) + 4 * (j & 3);  // m-values m .. m + 3 of this lane's word
+  const int k = 16 * s + 8 * (g >> 1) + (j >> 2);
+  bf16x4_t v[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int R = (m >> 6) * 64 + k + 4 * h;
+    const uint32_t off = (uint32_t)R * kRowBytes +
+                         (uint32_t)(((((m & 63) >> 3) ^ lds_swz_tr(R))) << 4) + (uint32_t)((m & 7) * 2);
+    v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4_t*)(sA + off));
+  }
+  return bf16x8_t{v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+}
+
+template <class S, bool kTrA = false>
+struct Mma16 {
   static constexpr int kSteps = 4;  // 16 K values per step, 64 per k-tile
   struct Frag {
     bf16x8_t a[S::MB], b[S::NB];
   };
+  __device__ __forceinline__ static bf16x8_t read_a(const lds_char* sA, const LanePos& p, int i,
+                                                    int s) {
+    if constexpr (kTrA)
+      return read_a_tr(sA, p.wave_m0 + 32 * i, p.lane, s);
+    else
+      return lds_load<bf16x8_t>(sA + lds_offset(p.wave_m0 + 32 * i + (p.lane & 31),
+                                                2 * s + (p.lane >> 5)));
+  }
   __device__ __forceinline__ static void read(Frag& f, const lds_char* sA, const lds_char* sB,
                                               const LanePos& p, int s) {
     const int r = p.lane & 31, h = p.lane >> 5;
 #pragma unroll
-    for (int i = 0; i < S::MB; ++i)
-      f.a[i] = lds_load<bf16x8_t>(sA + lds_offset(p.wave_m0 + 32 * i + r, 2 * s + h));
+    for (int i = 0; i < S::MB; ++i) f.a[i] = read_a(sA, p, i, s);
 #pragma unroll
     for (int j = 0; j < S::NB; ++j)
       f.b[j] = lds_load<bf16x8_t>(sB + lds_offset(p.wave_n0 + 32 * j + r, 2 * s + h));
@@ -236,7 +279,7 @@ struct Mma<uint16_t, S> {
             for (int q = 0; q < S::MB + S::NB; ++q) {
               if (q == m || (m == kPerStep - 1 && q > m)) {
                 if (q < S::MB)
-                  n.a[q] = lds_load<bf16x8_t>(sA + lds_offset(p.wave_m0 + 32 * q + r, 2 * (s + 1) + h));
+                  n.a[q] = read_a(sA, p, q, s + 1);
                 else
                   n.b[q - S::MB] = lds_load<bf16x8_t>(
                       sB + lds_offset(p.wave_n0 + 32 * (q - S::MB) + r, 2 * (s + 1) + h));
@@ -249,6 +292,9 @@ struct Mma<uint16_t, S> {
     }
   }
 };
+
+template <class S>
+struct Mma<uint16_t, S> : Mma16<S, false> {};
 
 template <class S>
 struct Mma<float, S> {
@@ -376,6 +422,53 @@ struct DirectLoader {
   __device__ __forceinline__ void commit(lds_char*) const {}
 };
 
+// KMajorLoader: a k-major A tile (see read_a_tr) from a k-blocked token-major
+// matrix [cols / 64][R][64] (R rows of 64 token columns per block): the
+// tile's m = 256 token columns are 4 consecutive blocks, and k-tile kt is rows
+// [64 kt, 64 kt + 64) of each.  Stage row Rs = (m / 64) * 64 + k is block
+// m / 64's row 64 kt + k, 128 bytes, stored with lds_swz_tr.  Reads at or
+// beyond valid_bytes from the first block return zero.
+template <int WAVES>
+struct KMajorLoader {
+  static constexpr int kStagedLoads = 0;
+  static constexpr int kRowsPerWave = 256 / WAVES;
+  static constexpr int kPer = kRowsPerWave / 8;
+  const char* base;
+  int64_t valid_bytes;
+  uint32_t voff[kPer];
+  uint32_t lds_row0;
+
+  // base: row 0 of the first of the 4 blocks; block_bytes: R * 128.
+  __device__ __forceinline__ void init(const void* base_, int64_t block_bytes,
+                                       int64_t valid_bytes_) {
+    base = static_cast<const char*>(base_);
+    valid_bytes = valid_bytes_;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    lds_row0 = (uint32_t)(wave * kRowsPerWave);
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int row = (int)lds_row0 + 8 * q + (lane >> 3);
+      const int c = (lane & 7) ^ lds_swz_tr(row);
+      voff[q] = (uint32_t)((row >> 6) * block_bytes + (row & 63) * kRowBytes + c * 16);
+    }
+  }
+  __device__ __forceinline__ rsrc_t rsrc(int64_t kt, bool live = true) const {
+    return make_rsrc(base + kt * 64 * kRowBytes, live ? valid_bytes - kt * 64 * kRowBytes : 0);
+  }
+  __device__ __forceinline__ void issue_one(rsrc_t r, lds_char* stage, int q) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(stage + (lds_row0 + 8 * q) * kRowBytes), 16,
+        voff[q], 0, 0, 0);
+  }
+  __device__ __forceinline__ void issue(int64_t kt, lds_char* stage) {
+    const rsrc_t r = rsrc(kt);
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) issue_one(r, stage, q);
+  }
+  __device__ __forceinline__ void commit(lds_char*) const {}
+};
+
 // RegLoader: the same addressing as DirectLoader, through registers (global ->
 // VGPR with buffer loads in issue(), VGPR -> swizzled LDS in commit()).
 template <int ROWS, int WAVES>
@@ -430,10 +523,15 @@ struct RegLoader {
 // stay in flight).  after_ktile(kt) runs once every wave has finished k-tile
 // kt and no direct read is in flight (it may use registers and global memory,
 // not LDS).
-template <typename T, class S, bool kSpread = true, class LA, class LB, class Hook>
+// kTrA (bf16 only): the A tile is k-major (see read_a_tr) and its fragments
+// are read with transposed loads.
+template <typename T, class S, bool kSpread = true, bool kTrA = false, class LA, class LB,
+          class Hook>
 __device__ __forceinline__ void mainloop(Accum<S>& acc, LA& la, LB& lb, int64_t nk, lds_char* smem,
                                          const LanePos& p, Hook&& after_ktile) {
   constexpr int kStaged = LA::kStagedLoads + LB::kStagedLoads;
+  static_assert(!kTrA || (sizeof(T) == 2 && kSpread && kStaged == 0),
+                "transposed A fragments: bf16, direct loaders, spread issue");
   if (nk <= 0) return;
   if constexpr (kSpread && sizeof(T) == 2 && kStaged == 0) {
     // bf16, direct loaders: k-tile kt+1's load instructions are spread over
@@ -441,7 +539,7 @@ __device__ __forceinline__ void mainloop(Accum<S>& acc, LA& la, LB& lb, int64_t 
     // when they then still end in the first half of the k-tile).  After the
     // last k-tile they read an empty range into the idle stage; the closing
     // wait drains them before the caller touches LDS.
-    using M = Mma<T, S>;
+    using M = Mma16<S, kTrA>;
     constexpr int kLoads = LA::kPer + LB::kPer;
     constexpr int kMfmas = M::kSteps * S::MB * S::NB;
     constexpr int kEvery = 2 * kLoads <= kMfmas / 2 ? 2 : 1;

@@ -199,46 +199,6 @@ __device__ __forceinline__ void pair_pack(const float z[4], bool odd, uint32_t w
   w[1] = odd ? pack_bf16x2(r1, z[3]) : pack_bf16x2(z[1], r1);
 }
 
-// bf16 row-major staging of a 256-row x COLS-column tile for row-major
-// outputs: rows of 2 COLS bytes at a stride of 2 COLS + 32, written as the
-// 32-bit column pairs of pair_pack.  The stride (8 mod 64 dwords: +16 banks
-// per two rows) keeps the four rows one write instruction touches on
-// distinct banks, and the flush reads each row as 16-byte runs.
-template <int COLS>
-struct RowStage {
-  static constexpr int kCols = COLS;
-  static constexpr int kToks = 256;
-  static constexpr int kRowStride = 2 * COLS + 32;
-  static constexpr int kBytes = kToks * kRowStride;
-  static_assert((kRowStride / 4) % 64 == 8, "bank spread of the pair writes");
-
-  // z[e] = value of (tok0 + e, col), e = 0..3; col = this lane's column.
-  __device__ __forceinline__ static void put4(lds_char* lds, int col, int tok0, const float z[4],
-                                              bool odd) {
-    uint32_t w[2];
-    pair_pack(z, odd, w);
-    lds_char* q = lds + (tok0 + (odd ? 2 : 0)) * kRowStride + (col & ~1) * 2;
-    lds_store<uint32_t>(q, w[0]);
-    lds_store<uint32_t>(q + kRowStride, w[1]);
-  }
-
-  // Rows [rows_lo, rows_valid), columns [0, ncols) (ncols a multiple of 8) to
-  // dst[(dst_row0 + t) * ld + col_base + c], 16 bytes per lane.
-  template <int NTHREADS>
-  __device__ __forceinline__ static void flush(const lds_char* lds, uint16_t* __restrict__ dst,
-                                               int64_t dst_row0, int64_t ld, int64_t col_base,
-                                               int ncols, int32_t rows_lo, int32_t rows_valid) {
-    constexpr int kRuns = kCols / 8;
-    for (int it = threadIdx.x; it < kToks * kRuns; it += NTHREADS) {
-      const int t = it / kRuns, c = (it % kRuns) * 8;
-      if (t < rows_lo || t >= rows_valid || c >= ncols) continue;
-      const u32x4_t v = lds_load<u32x4_t>(lds + t * kRowStride + c * 2);
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst + (dst_row0 + t) * ld +
-                                                                 col_base + c));
-    }
-  }
-};
-
 // Put tile columns [W q, W q + W) into the stage (values transformed by
 // `fn`); only the waves owning those columns write.
 template <typename T, class S, int W = 64, class F>
@@ -266,16 +226,15 @@ __device__ __forceinline__ void stage_cols(lds_char* lds, const Accum<S>& acc, c
 // is WgU, whose 32-row blocks alternate gate and up rows of the same 32
 // features, so each wave holds the gate and up sums of the same (token,
 // feature) in the same lane and register (block columns 2q and 2q+1).
+// Output: Zt (token-major, k-blocked), which both the scan and (bf16, with
+// transposed reads) the outputs read; fp32 also writes the row-major Z its
+// outputs read.
 template <typename T>
 TTT_GEMM_KERNEL void swiglu_kernel(Dims dm, const T* __restrict__ H, const T* __restrict__ WgU,
                                    T* __restrict__ Z, T* __restrict__ Zt) {
   using S = Tile;
   static_assert(S::NB % 2 == 0, "gate/up block pairs");
-  // the pipeline's two stages, or (bf16) the two epilogue stages, whichever is larger
-  using Rows = RowStage<S::BN / 2>;
-  constexpr int kLds = sizeof(T) == 2 && Stage<T, S::kThreads, S::BN / 2>::kBytes + Rows::kBytes > S::kLdsBytes
-                           ? Stage<T, S::kThreads, S::BN / 2>::kBytes + Rows::kBytes
-                           : S::kLdsBytes;
+  constexpr int kLds = S::kLdsBytes;
   __shared__ __attribute__((aligned(16))) char smem_raw[kLds];
   lds_char* smem = (lds_char*)smem_raw;
   const int32_t BT = (int32_t)(dm.B * dm.T);
@@ -301,17 +260,13 @@ TTT_GEMM_KERNEL void swiglu_kernel(Dims dm, const T* __restrict__ H, const T* __
   const LanePos p = lane_pos<S>();
   mainloop<T, S>(acc, la, lb, ld / kRowBytes, smem, p, [](int64_t) {});
 
-  // z = silu(gate) * up, staged through LDS and written to Zt and Z.  bf16:
-  // all 128 features in one pass, into a token-run stage for Zt and a
-  // row-major stage for Z (both in LDS at once); fp32: two passes of 64
+  // z = silu(gate) * up, staged through LDS and written to Zt (and for fp32
+  // to Z).  bf16: all 128 features in one pass; fp32: two passes of 64
   // features through the token-run stage, read back as column runs for Z.
   const ChunkMap cm = chunk_map(dm);
   constexpr int kPass = sizeof(T) == 2 ? kFeat : 64;  // features per pass
   using St = Stage<T, S::kThreads, kPass>;
-  static_assert(St::kBytes + (sizeof(T) == 2 ? Rows::kBytes : 0) <= kLds,
-                "staging fits the kernel's LDS");
-  lds_char* const rows_stage = smem + St::kBytes;
-  const bool odd = p.lane & 1;
+  static_assert(St::kBytes <= kLds, "staging fits the kernel's LDS");
 #pragma unroll
   for (int h = 0; h < kFeat / kPass; ++h) {
 #pragma unroll
@@ -328,20 +283,14 @@ TTT_GEMM_KERNEL void swiglu_kernel(Dims dm, const T* __restrict__ H, const T* __
           for (int e = 0; e < 4; ++e)
             z[e] = silu(acc.v[i][2 * jp][4 * rq + e]) * acc.v[i][2 * jp + 1][4 * rq + e];
           St::put4(smem, fcol + (p.lane & 31), p.row(i, 4 * rq), z);
-          if constexpr (sizeof(T) == 2)
-            Rows::put4(rows_stage, fcol + (p.lane & 31), p.row(i, 4 * rq), z, odd);
         }
     }
     __syncthreads();
     const int64_t cb = feat0 + kPass * h;
     const int ncols = (int)max<int64_t>(0, min<int64_t>(kPass, f - cb));
     St::flush_tokens(smem, Zt, f, cb, ncols, row0, BT, cm);
-    if constexpr (sizeof(T) == 2)
-      Rows::template flush<S::kThreads>(rows_stage, reinterpret_cast<uint16_t*>(Z), row0, f, cb,
-                                        ncols, 0, min(BT - row0, S::BM));
-    else
-      St::flush_rows(smem, Z, row0, f, cb, ncols, 0, min(BT - row0, S::BM));
-    __syncthreads();
+    if constexpr (sizeof(T) == 4) St::flush_rows(smem, Z, row0, f, cb, ncols, 0, min(BT - row0, S::BM));
+    if (h + 1 < kFeat / kPass) __syncthreads();
   }
 }
 
@@ -682,8 +631,12 @@ __global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::
 // O_i = Z_i slot_i^T for every chunk of the group and every sequence.
 // Tile `blk` of `nblk` (the launch's workgroups [first, first + nblk), first a
 // multiple of 8 so that the XCD of workgroup first + blk is blk % 8).
+// Zs: bf16 -- the token-major Zt the scan reads, taken as a k-major A tile
+// (a tile's 256 token rows are 4 consecutive 64-token blocks) and read with
+// transposed fragment loads, so S1 writes Z in this one layout; fp32 -- the
+// row-major Z.
 template <typename T>
-__device__ __forceinline__ void down_proj_tile(const Dims& dm, const T* __restrict__ Z,
+__device__ __forceinline__ void down_proj_tile(const Dims& dm, const T* __restrict__ Zs,
                                                const T* __restrict__ slots, T* __restrict__ O,
                                                int64_t g0, int64_t gc, int blk, int nblk,
                                                lds_char* smem) {
@@ -704,16 +657,29 @@ __device__ __forceinline__ void down_proj_tile(const Dims& dm, const T* __restri
   const int64_t row0 = b * T_seq + c_begin + m0;  // first token row of the tile
   const T* slot = slots + (jj * dm.B + b) * d * f;
 
-  DirectLoader<S::BM, S::kWaves> la;
-  la.init(reinterpret_cast<const char*>(Z) + row0 * ld, ld, kRowBytes, (c_len - m0) * ld,
-          kRowBytes);
   DirectLoader<S::BN, S::kWaves> lb;
   lb.init(reinterpret_cast<const char*>(slot) + n0 * ld, ld, kRowBytes, (d - n0) * ld, kRowBytes);
 
   Accum<S> acc;
   acc.zero();
   const LanePos p = lane_pos<S>();
-  mainloop<T, S>(acc, la, lb, ld / kRowBytes, smem, p, [](int64_t) {});
+  if constexpr (sizeof(T) == 2) {
+    static_assert(S::BM == 256, "four 64-token blocks per tile");
+    // token column of tile row 0; rows past the chunk read the next chunk's
+    // columns (or zeros past the end), which only reach output rows that are
+    // not stored
+    const int64_t col0 = (b * dm.N + chunk) * dm.Cp + m0;
+    const int64_t block_bytes = f * kRowBytes;
+    KMajorLoader<S::kWaves> la;
+    la.init(reinterpret_cast<const char*>(Zs) + (col0 / kTokenAlign) * block_bytes, block_bytes,
+            (dm.P - col0) / kTokenAlign * block_bytes);
+    mainloop<T, S, true, true>(acc, la, lb, ld / kRowBytes, smem, p, [](int64_t) {});
+  } else {
+    DirectLoader<S::BM, S::kWaves> la;
+    la.init(reinterpret_cast<const char*>(Zs) + row0 * ld, ld, kRowBytes, (c_len - m0) * ld,
+            kRowBytes);
+    mainloop<T, S>(acc, la, lb, ld / kRowBytes, smem, p, [](int64_t) {});
+  }
 
   // O through the stage, four passes of 64 columns, written row-major; rows
   // beyond the chunk are skipped, and so are the first out_skip rows of each
@@ -956,12 +922,12 @@ __global__ void stream_save_kernel(const T* __restrict__ Hv, const T* __restrict
 // ================================================================ launchers
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-WorkspacePlan plan_workspace(const Dims& dm, int64_t group) {
+WorkspacePlan plan_workspace(const Dims& dm, int64_t group, bool row_z) {
   const size_t es = dtype_bytes(dm.dt);
   WorkspacePlan w;
   size_t off = 0;
-  w.z_off = off;  // Z
-  off = align256(off + (size_t)(dm.B * dm.T) * dm.f * es);
+  w.z_off = off;  // Z row-major (fp32 outputs and the backward read it)
+  if (row_z || dm.dt == Dtype::F32) off = align256(off + (size_t)(dm.B * dm.T) * dm.f * es);
   w.u_off = off;  // U of S2 (the conv output the projection reads)
   off = align256(off + (size_t)(dm.B * dm.T) * dm.d * es);
   w.zt_off = off;
@@ -1131,6 +1097,7 @@ template <typename T>
 static void launch_scan_apply_t(const Dims& dm, const T* Vt, const T* Zt, float* W_state,
                                 T* scan_slots, int64_t g0, int64_t gc, const T* Z,
                                 const T* apply_slots, T* O, int64_t a0, int64_t ac, hipStream_t s) {
+  if (sizeof(T) == 2) Z = Zt;  // bf16 outputs read the token-major Z (down_proj_tile)
   const int64_t down_tiles = ac > 0 ? ((dm.C + Tile::BM - 1) / Tile::BM) *
                                           ((dm.d + Tile::BN - 1) / Tile::BN) * ac * dm.B
                                     : 0;

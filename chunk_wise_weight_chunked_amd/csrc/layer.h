@@ -53,7 +53,9 @@ struct WorkspacePlan {
   size_t total_bytes;  // fixed_bytes + slot_sets * group * slot_bytes
 };
 
-WorkspacePlan plan_workspace(const Dims& dm, int64_t group);
+// row_z: keep a row-major Z region even for bf16 (the backward builds Z there;
+// the bf16 forward writes Z only token-major).
+WorkspacePlan plan_workspace(const Dims& dm, int64_t group, bool row_z = false);
 
 // Kernel launchers (asynchronous on `s`; return hipGetLastError()).
 hipError_t launch_state_reset(float* W_state, const void* W0, Dtype w0_dt, int64_t B, int64_t d,

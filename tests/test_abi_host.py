@@ -89,21 +89,24 @@ def test_auto_mode_takes_one_group_for_many_sequences():
 
 
 def test_workspace_fixed_part_matches_layout():
-    # Z [T][f] + U [T][d] + Zt [f][P] + Vt [d][P] + WgU [2f][d] + WtT [d][d]
-    # + tapsT [8][d] fp32 + 2 slot sets of 1
+    # bf16: U [T][d] + Zt [f][P] + Vt [d][P] + WgU [2f][d] + WtT [d][d]
+    # + tapsT [8][d] fp32 + 2 slot sets of 1 (Z is kept only token-major);
+    # fp32 adds the row-major Z [T][f] in front
     d = desc(seq_len=1000, chunk=100)  # padded chunks: Cp = 128, P = 10 * 128
-    es = 2
-    parts = [1000 * 512 * es, 1000 * 256 * es, 512 * 1280 * es, 256 * 1280 * es,
-             2 * 512 * 256 * es, 256 * 256 * es, 8 * 256 * 4, 2 * 256 * 512 * es]
-    expect = sum((p + 255) // 256 * 256 for p in parts)
-    assert tm.ttt_mlp_workspace_size(d, 1) == expect
+    for es, dt in ((2, tm.TTT_BF16), (4, tm.TTT_F32)):
+        parts = [1000 * 256 * es, 512 * 1280 * es, 256 * 1280 * es,
+                 2 * 512 * 256 * es, 256 * 256 * es, 8 * 256 * 4, 2 * 256 * 512 * es]
+        if es == 4:
+            parts.insert(0, 1000 * 512 * es)
+        expect = sum((p + 255) // 256 * 256 for p in parts)
+        assert tm.ttt_mlp_workspace_size(desc(seq_len=1000, chunk=100, dtype=dt), 1) == expect
 
 
 def test_workspace_conv_output_has_its_own_region():
-    # d > f: Z keeps f columns, the conv output U [T][d] its own region
+    # d > f: the conv output U [T][d] has its own region (Zt keeps f rows)
     d = desc(d_model=512, d_ff=256, seq_len=1000, chunk=100)
     es = 2
-    parts = [1000 * 256 * es, 1000 * 512 * es, 256 * 1280 * es, 512 * 1280 * es,
+    parts = [1000 * 512 * es, 256 * 1280 * es, 512 * 1280 * es,
              2 * 256 * 512 * es, 512 * 512 * es, 8 * 512 * 4, 2 * 512 * 256 * es]
     expect = sum((p + 255) // 256 * 256 for p in parts)
     assert tm.ttt_mlp_workspace_size(d, 1) == expect
