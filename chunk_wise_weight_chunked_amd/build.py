@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(BUILD, "libttt_mlp.so")
-SOURCES = ["kernels.hip", "decode.hip", "backward.hip", "api.cpp", "backward_api.cpp"]
+SOURCES = ["kernels.hip", "decode.hip", "backward.hip", "gemm.hip", "api.cpp",
+           "backward_api.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -30,9 +31,7 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
-
-# rocBLAS serves the plain GEMMs of the backward pass
-LINK_FLAGS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
+LINK_FLAGS: list = []
 
 
 def hipcc() -> str:

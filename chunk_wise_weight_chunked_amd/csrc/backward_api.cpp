@@ -1,8 +1,8 @@
 // backward_api.cpp -- C ABI of the layer's backward pass: validation,
-// workspace planning and the launch sequence (own kernels and rocBLAS GEMMs)
-// on the caller's stream.  Semantics in include/ttt_mlp.h.
+// workspace planning and the launch sequence (the library's own kernels and
+// its batched MFMA GEMM) on the caller's stream.  Semantics in
+// include/ttt_mlp.h.
 #include <hip/hip_runtime.h>
-#include <rocblas/rocblas.h>
 
 #include <algorithm>
 #include <string>
@@ -20,12 +20,10 @@ namespace {
 // own regions, 256-byte aligned.
 struct BackwardPlan {
   ttt::WorkspacePlan fwd;
-  size_t wst, u, v, agu, ztr, dotr, sslots, dz, da, wgu, g, gf, du, tpart, dpart, wtpart,
-      blas, total;
+  size_t wst, u, v, agu, ztr, dotr, sslots, dz, da, wgu, g, gf, du, tpart, dpart, wtpart, dak,
+      hk, uk, gk, wgut, total;
   int64_t wt_slices;  // token slices of the dW_target product (split over K = B*T)
 };
-
-constexpr size_t kBlasWorkspace = (size_t)32 << 20;
 
 BackwardPlan plan_backward(const ttt::Dims& dm) {
   BackwardPlan p;
@@ -57,37 +55,57 @@ BackwardPlan plan_backward(const ttt::Dims& dm) {
   // 2048 tokens keeps the GPU busy, the slices are then added in order
   p.wt_slices = dm.proj ? std::max<int64_t>(1, std::min<int64_t>(16, (int64_t)BT / 2048)) : 0;
   p.wtpart = take((size_t)p.wt_slices * d * d * 4);
-  p.blas = take(kBlasWorkspace);
+  // k-blocked token-major copies of the operands of the products over all
+  // tokens (dW_gate, dW_up, dW_target), and [W_gate; W_up]ᵀ for dH
+  p.dak = take(2 * f * (size_t)dm.P * es);
+  p.hk = take(d * (size_t)dm.P * es);
+  p.uk = take(dm.proj ? d * (size_t)dm.P * es : 0);
+  p.gk = take(dm.proj ? d * (size_t)dm.P * es : 0);
+  p.wgut = take(2 * f * d * es);
   p.total = off;
   return p;
 }
 
-// One rocBLAS handle per host thread, kept for the life of the process.
-rocblas_handle blas_handle() {
-  thread_local rocblas_handle h = nullptr;
-  if (!h && rocblas_create_handle(&h) != rocblas_status_success) h = nullptr;
-  return h;
-}
-
-// Row-major C[M][N] (ldc) = alpha op(A) op(B) + beta C, op(A) [M][K], op(B)
-// [K][N]: A is stored [M][K] (lda), or [K][M] when ta; B is [K][N] (ldb), or
-// [N][K] when tb.  rocBLAS is column-major, so it computes Cᵀ = op(B)ᵀ op(A)ᵀ.
-// `batch` products at the given element strides.
+// C = alpha A' B'ᵀ (+ C when accumulate) on the library's batched GEMM, with
+// each operand's layout (ttt::GemmLayout, see layer.h); the first failure is
+// kept.
 struct Gemm {
-  rocblas_handle h;
-  rocblas_datatype ab;  // type of A and B
-  rocblas_status st = rocblas_status_success;
-  void operator()(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
-                  int64_t lda, int64_t sa, const void* B, int64_t ldb, int64_t sb, float beta,
-                  void* C, int64_t ldc, int64_t sc, int64_t batch, rocblas_datatype ctype) {
-    if (st != rocblas_status_success || M == 0 || N == 0) return;
-    st = rocblas_gemm_strided_batched_ex_64(
-        h, tb ? rocblas_operation_transpose : rocblas_operation_none,
-        ta ? rocblas_operation_transpose : rocblas_operation_none, N, M, K, &alpha, B, ab, ldb, sb,
-        A, ab, lda, sa, &beta, C, ctype, ldc, sc, C, ctype, ldc, sc, batch, rocblas_datatype_f32_r,
-        rocblas_gemm_algo_standard, 0, 0);
+  ttt::Dtype dt;
+  hipStream_t s;
+  hipError_t err = hipSuccess;
+  void operator()(int32_t la, int32_t lb, int64_t M, int64_t N, int64_t K, float alpha,
+                  const void* A, int64_t lda, int64_t sa, const void* B, int64_t ldb, int64_t sb,
+                  bool accumulate, void* C, int64_t ldc, int64_t sc, int64_t batch, bool c_f32,
+                  int64_t K_last = -1) {
+    if (err != hipSuccess || M == 0 || N == 0) return;
+    ttt::GemmArgs g{};
+    g.dt = dt;
+    g.A = A;
+    g.lda = lda;
+    g.sa = sa;
+    g.a_layout = la;
+    g.B = B;
+    g.ldb = ldb;
+    g.sb = sb;
+    g.b_layout = lb;
+    g.C = C;
+    g.ldc = ldc;
+    g.sc = sc;
+    g.c_f32 = c_f32 ? 1 : 0;
+    g.accumulate = accumulate ? 1 : 0;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.K_last = K_last < 0 ? K : K_last;
+    g.batch = batch;
+    g.alpha = alpha;
+    err = ttt::launch_gemm(g, s);
   }
 };
+
+using ttt::kKBlocked;
+using ttt::kKMajor;
+using ttt::kRowK;
 
 }  // namespace
 
@@ -158,9 +176,6 @@ ttt_status_t ttt_mlp_backward_batched(
   if (ws_bytes < bp.total)
     return fail(TTT_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is below the minimum %zu",
                 ws_bytes, bp.total);
-  const rocblas_handle h = blas_handle();
-  if (!h) return fail(TTT_ERR_HIP, "rocblas_create_handle failed");
-
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
   const ttt::WorkspacePlan& wp = bp.fwd;
@@ -198,27 +213,34 @@ ttt_status_t ttt_mlp_backward_batched(
   if (e == hipSuccess) e = hipMemcpyAsync(Wgu + f * d * es, W_up, f * d * es, hipMemcpyDeviceToDevice, s);
   if (e != hipSuccess) return hip_fail(e, "backward");
 
-  // 2. The plain GEMMs run in rocBLAS (fp32 accumulation): first the fp32
-  //    pre-activations [A_g | A_u] = H [W_gate; W_up]ᵀ in one GEMM (row t
-  //    holds both, 2f wide) and V^ = U W_target.
-  if (rocblas_set_stream(h, s) != rocblas_status_success ||
-      rocblas_set_workspace(h, base + bp.blas, kBlasWorkspace) != rocblas_status_success)
-    return fail(TTT_ERR_HIP, "rocblas set-up failed");
-  const rocblas_datatype ab = dm.dt == ttt::Dtype::BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
-  const rocblas_datatype f32 = rocblas_datatype_f32_r;
-  Gemm gemm{h, ab};
+  // 2. The plain GEMMs (the library's batched MFMA GEMM, fp32 accumulation):
+  //    first the fp32 pre-activations [A_g | A_u] = H [W_gate; W_up]ᵀ in one
+  //    GEMM (row t holds both, 2f wide) and V^ = U W_target.
+  Gemm gemm{dm.dt, s};
+  const bool f32 = true, act_f32 = dm.dt == ttt::Dtype::F32;  // output types
   const int64_t B = dm.B, T = dm.T, C = dm.C, N = dm.N, sl = (int64_t)(B * d * f);
   const int64_t Di = (int64_t)d, Fi = (int64_t)f, BTi = (int64_t)BT;
-  gemm(false, true, BTi, 2 * Fi, Di, 1.f, H, Di, 0, Wgu, Di, 0, 0.f, Ag, 2 * Fi, 0, 1, f32);
+  gemm(kRowK, kRowK, BTi, 2 * Fi, Di, 1.f, H, Di, 0, Wgu, Di, 0, false, Ag, 2 * Fi, 0, 1, f32);
   if (dm.proj)
-    gemm(false, false, BTi, Di, Di, 1.f, U, Di, 0, W_target, Di, 0, 0.f, V, Di, 0, 1, ab);
-  if (gemm.st != rocblas_status_success) return fail(TTT_ERR_HIP, "rocblas gemm failed (%d)", (int)gemm.st);
+    gemm(kRowK, kRowK, BTi, Di, Di, 1.f, U, Di, 0, WtT, Di, 0, false, V, Di, 0, 1, act_f32);
+  if (gemm.err != hipSuccess) return hip_fail(gemm.err, "backward gemm");
+  // operands of the later products in the layouts they are read in
+  void* dAk = base + bp.dak;
+  void* Hk = base + bp.hk;
+  void* Uk = base + bp.uk;
+  void* Gk = base + bp.gk;
+  void* WguT = base + bp.wgut;
+  e = ttt::launch_to_kblocked(H, Hk, dm, dm.d, false, s);
+  if (e == hipSuccess) e = ttt::launch_transpose(Wgu, WguT, 2 * Fi, Di, dm.dt, s);
+  if (e == hipSuccess && dm.proj) e = ttt::launch_to_kblocked(U, Uk, dm, dm.d, false, s);
+  if (e != hipSuccess) return hip_fail(e, "backward");
 
   // 3. Z from them, in row-major and in the scans' k-blocked layout (chunks in
   //    order and reversed); dOᵀ k-blocked with the chunks reversed.  Then, in
-  //    one launch, the forward's scan (slot j = W^(j-1)) and the same scan
-  //    over dOᵀ and Z in reverse chunk order from dW_final (slot j = S_j; its
-  //    final state is the gradient of the starting weight).
+  //    one launch, the forward's scan (slot j = W^(j-1), written transposed)
+  //    and the same scan over dOᵀ and Z in reverse chunk order from dW_final
+  //    (slot j = S_j; its final state is the gradient of the starting
+  //    weight).
   e = ttt::launch_swiglu_rows(Ag, Au, 2 * Fi, Z, dm, s);
   if (e == hipSuccess) e = ttt::launch_to_kblocked(Z, Zt, dm, dm.f, false, s);
   if (e == hipSuccess) e = ttt::launch_to_kblocked(Z, Ztr, dm, dm.f, true, s);
@@ -233,7 +255,8 @@ ttt_status_t ttt_mlp_backward_batched(
   if (e != hipSuccess) return hip_fail(e, "backward");
 
   // per chunk j: dZ_j = dO_j W^(j-1) + eta V^_j S_j and G_j = Z_j S_jᵀ, with
-  // W^(j-1) and S_j in slot j.  The full chunks of a sequence are one batch
+  // W^(j-1) (transposed: K = d contiguous) and S_j (row-major, read k-major
+  // for dZ) in slot j.  The full chunks of a sequence are one batch
   // (rows C apart, slots B*d*f apart); a ragged last chunk is one batch over
   // the sequences.
   const char* Zc = static_cast<const char*>(Z);
@@ -242,47 +265,55 @@ ttt_status_t ttt_mlp_backward_batched(
   auto chunk_gemms = [&](int64_t j, int64_t rows, int64_t b0, int64_t count, int64_t row_stride,
                          int64_t slot_stride) {
     const int64_t r = b0 * T + j * C;  // first row
-    const char* Wj = Wslots + (size_t)(j * sl + b0 * Di * Fi) * es;
+    const char* WjT = Wslots + (size_t)(j * sl + b0 * Di * Fi) * es;
     const char* Sj = Sslots + (size_t)(j * sl + b0 * Di * Fi) * es;
-    gemm(false, false, rows, Fi, Di, 1.f, dOc + r * d * es, Di, row_stride * Di, Wj, Fi,
-         slot_stride, 0.f, dZ + r * f, Fi, row_stride * Fi, count, f32);
-    gemm(false, false, rows, Fi, Di, dm.eta, Vc + r * d * es, Di, row_stride * Di, Sj, Fi,
-         slot_stride, 1.f, dZ + r * f, Fi, row_stride * Fi, count, f32);
-    gemm(false, true, rows, Di, Fi, 1.f, Zc + r * f * es, Fi, row_stride * Fi, Sj, Fi,
-         slot_stride, 0.f, Gf + r * d, Di, row_stride * Di, count, f32);
+    gemm(kRowK, kRowK, rows, Fi, Di, 1.f, dOc + r * d * es, Di, row_stride * Di, WjT, Di,
+         slot_stride, false, dZ + r * f, Fi, row_stride * Fi, count, f32);
+    gemm(kRowK, kKMajor, rows, Fi, Di, dm.eta, Vc + r * d * es, Di, row_stride * Di, Sj, Fi,
+         slot_stride, true, dZ + r * f, Fi, row_stride * Fi, count, f32);
+    gemm(kRowK, kRowK, rows, Di, Fi, 1.f, Zc + r * f * es, Fi, row_stride * Fi, Sj, Fi,
+         slot_stride, false, Gf + r * d, Di, row_stride * Di, count, f32);
   };
   const int64_t full = T / C;
   if (full > 0)
     for (int64_t b = 0; b < B; ++b) chunk_gemms(0, C, b, full, C, sl);
   if (full < N) chunk_gemms(full, T - full * C, 0, B, T, Di * Fi);
-  if (gemm.st != rocblas_status_success) return fail(TTT_ERR_HIP, "rocblas gemm failed (%d)", (int)gemm.st);
+  if (gemm.err != hipSuccess) return hip_fail(gemm.err, "backward gemm");
   // 4. eta's gradient sum_t <V^[t], G[t]>; the SwiGLU derivative; dH and the
   //    gated MLP's weight gradients
   e = ttt::launch_dot(V, Gf, BTi * Di, dm.dt, 1.0f, dpart, d_eta, s);
   if (e == hipSuccess) e = ttt::launch_swiglu_backward(dZ, Ag, Au, 2 * Fi, dA, dm, s);
   if (e == hipSuccess && dm.proj) e = ttt::launch_from_f32(Gf, G, BTi * Di, dm.dt, s);
   if (e != hipSuccess) return hip_fail(e, "backward");
-  gemm(false, false, BTi, Di, 2 * Fi, 1.f, dA, 2 * Fi, 0, Wgu, Di, 0, 0.f, dH, Di, 0, 1, ab);
-  gemm(true, false, Fi, Di, BTi, 1.f, dA, 2 * Fi, 0, H, Di, 0, 0.f, dW_gate, Di, 0, 1, f32);
-  gemm(true, false, Fi, Di, BTi, 1.f, dA + f * es, 2 * Fi, 0, H, Di, 0, 0.f, dW_up, Di, 0, 1, f32);
+  e = ttt::launch_to_kblocked(dA, dAk, dm, 2 * dm.f, false, s);
+  if (e == hipSuccess && dm.proj) e = ttt::launch_to_kblocked(G, Gk, dm, dm.d, false, s);
+  if (e != hipSuccess) return hip_fail(e, "backward");
+  const int64_t tb = 128 / (int64_t)es, P = dm.P;  // tokens per 128-byte block row
+  gemm(kRowK, kRowK, BTi, Di, 2 * Fi, 1.f, dA, 2 * Fi, 0, WguT, 2 * Fi, 0, false, dH, Di, 0, 1,
+       act_f32);
+  // dW_gate and dW_up (dA_gᵀ H, dA_uᵀ H over every token column) as one
+  // launch of two products: the second's A starts f rows into each block and
+  // its C is the other output buffer (element distance as the batch stride)
+  const int64_t gu = (int64_t)(reinterpret_cast<intptr_t>(dW_up) -
+                               reinterpret_cast<intptr_t>(dW_gate)) / (int64_t)sizeof(float);
+  gemm(kKBlocked, kKBlocked, Fi, Di, P, 1.f, dAk, 2 * Fi, Fi * tb, Hk, Di, 0, false, dW_gate, Di,
+       gu, 2, f32);
   // 5. the target: dV^ = eta G; dU = dV^ W_targetᵀ, dW_target = Uᵀ dV^; then
   //    the conv's transpose (or dX0 = dU without the conv)
+  int64_t slices = 0;
   if (dm.proj) {
-    gemm(false, true, BTi, Di, Di, dm.eta, G, Di, 0, W_target, Di, 0, 0.f, dU, Di, 0, 1, f32);
-    // split over token slices: slices - 1 of `rows` tokens, the last the rest
-    const int64_t S = bp.wt_slices, rows = BTi / S, rest = BTi - (S - 1) * rows;
+    gemm(kRowK, kRowK, BTi, Di, Di, dm.eta, G, Di, 0, W_target, Di, 0, false, dU, Di, 0, 1, f32);
+    // split over token slices of whole 64-token blocks, summed in order below
+    const int64_t nb = P / tb, per = (nb + bp.wt_slices - 1) / bp.wt_slices;
+    slices = (nb + per - 1) / per;
     float* wtp = reinterpret_cast<float*>(base + bp.wtpart);
-    if (S > 1)
-      gemm(true, false, Di, Di, rows, dm.eta, U, Di, rows * Di, G, Di, rows * Di, 0.f, wtp, Di,
-           Di * Di, S - 1, f32);
-    gemm(true, false, Di, Di, rest, dm.eta, static_cast<const char*>(U) + (S - 1) * rows * Di * es,
-         Di, 0, static_cast<const char*>(G) + (S - 1) * rows * Di * es, Di, 0, 0.f,
-         wtp + (S - 1) * Di * Di, Di, 0, 1, f32);
+    gemm(kKBlocked, kKBlocked, Di, Di, per * tb, dm.eta, Uk, Di, per * Di * tb, Gk, Di,
+         per * Di * tb, false, wtp, Di, Di * Di, slices, f32, (nb - (slices - 1) * per) * tb);
   }
-  if (gemm.st != rocblas_status_success) return fail(TTT_ERR_HIP, "rocblas gemm failed (%d)", (int)gemm.st);
+  if (gemm.err != hipSuccess) return hip_fail(gemm.err, "backward gemm");
   if (dm.proj) {
     e = ttt::launch_sum_slices(reinterpret_cast<float*>(base + bp.wtpart), dW_target, Di * Di,
-                               (int)bp.wt_slices, s);
+                               (int)slices, s);
     if (e != hipSuccess) return hip_fail(e, "backward");
   }
   e = dm.proj ? ttt::launch_target_backward(dU, 1.0f, X0, tapsT, dX0, tpart, dtaps, dm, s)

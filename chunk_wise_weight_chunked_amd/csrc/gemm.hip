@@ -1,0 +1,236 @@
+// gemm.hip -- batched GEMM on the library's MFMA mainloop (gemm_core.h), for
+// the plain products of the layer's backward pass.
+//
+// C[b] = alpha * A[b] B[b]ᵀ (or C[b] += ...), with A [M][K] and B [N][K] in
+// the mainloop's "both operands K-contiguous" sense.  Either operand may
+// instead be stored k-major -- [K][M] (resp. [K][N]) row-major -- and is then
+// loaded as k-major tiles (KMajorLoader) and read with transposed fragment
+// loads (bf16) or one value per lane (fp32), so no operand is ever copied to
+// another layout.  The batch index walks independent products (the chunks of
+// a sequence, or the K slices of a split product whose partial results the
+// caller adds in order).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "gemm_core.h"
+#include "layer.h"
+
+namespace ttt {
+namespace {
+
+using GTile = TileShape<256, 256, 2, 4>;
+
+// Rows [0, 256) x columns [64 q, 64 q + 64) of the accumulator into an LDS
+// stage of fp32 values, then out to C in 8-element runs.  Row stride 72
+// floats: the two half-waves of a put (rows 4 apart) land on opposite halves
+// of the 64 banks.
+constexpr int kEpiCols = 64;
+constexpr int kEpiStride = kEpiCols + 8;  // floats per staged row
+
+template <typename Tc>
+__device__ __forceinline__ void store8(Tc* dst, const float v[8], bool accumulate);
+template <>
+__device__ __forceinline__ void store8<float>(float* dst, const float v[8], bool accumulate) {
+  float4 lo = make_float4(v[0], v[1], v[2], v[3]), hi = make_float4(v[4], v[5], v[6], v[7]);
+  if (accumulate) {
+    const float4 a = *reinterpret_cast<const float4*>(dst);
+    const float4 b = *reinterpret_cast<const float4*>(dst + 4);
+    lo = make_float4(a.x + lo.x, a.y + lo.y, a.z + lo.z, a.w + lo.w);
+    hi = make_float4(b.x + hi.x, b.y + hi.y, b.z + hi.z, b.w + hi.w);
+  }
+  *reinterpret_cast<float4*>(dst) = lo;
+  *reinterpret_cast<float4*>(dst + 4) = hi;
+}
+template <>
+__device__ __forceinline__ void store8<uint16_t>(uint16_t* dst, const float v[8], bool) {
+  *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                              pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+}
+
+template <class S, typename Tc>
+__device__ __forceinline__ void gemm_epilogue(const Accum<S>& acc, const LanePos& p, lds_char* smem,
+                                              Tc* __restrict__ C, int64_t ldc, int64_t m0,
+                                              int64_t n0, int64_t M, int64_t N, float alpha,
+                                              bool accumulate) {
+  for (int q = 0; q < S::BN / kEpiCols; ++q) {
+    __syncthreads();  // the mainloop's (or the previous pass's) reads of LDS are done
+#pragma unroll
+    for (int j = 0; j < S::NB; ++j) {
+      const int col = p.wave_n0 + 32 * j;
+      if (col < kEpiCols * q || col >= kEpiCols * q + kEpiCols) continue;
+      const int c = col - kEpiCols * q + (p.lane & 31);
+#pragma unroll
+      for (int i = 0; i < S::MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          lds_store<float>(smem + ((uint32_t)p.row(i, r) * kEpiStride + c) * 4,
+                           alpha * acc.v[i][j][r]);
+    }
+    __syncthreads();
+    const int64_t cb = n0 + kEpiCols * q;
+    for (int it = threadIdx.x; it < S::BM * (kEpiCols / 8); it += S::kThreads) {
+      const int t = it / (kEpiCols / 8), c = (it % (kEpiCols / 8)) * 8;
+      if (m0 + t >= M || cb + c >= N) continue;
+      const floatx4_t lo = lds_load<floatx4_t>(smem + ((uint32_t)t * kEpiStride + c) * 4);
+      const floatx4_t hi = lds_load<floatx4_t>(smem + ((uint32_t)t * kEpiStride + c + 4) * 4);
+      const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      store8<Tc>(C + (m0 + t) * ldc + cb + c, v, accumulate);
+    }
+  }
+}
+
+template <typename T, int kLA, int kLB>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(
+    GemmArgs g) {
+  constexpr bool kKA = kLA == kKMajor, kKB = kLB == kKMajor;
+  using S = GTile;
+  static_assert(S::kLdsBytes >= S::BM * kEpiStride * 4, "epilogue stage fits the pipeline's LDS");
+  __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
+  lds_char* smem = (lds_char*)smem_raw;
+  constexpr int64_t es = sizeof(T);
+  constexpr int TB = kRowBytes / (int)sizeof(T);
+  const int tiles_m = (int)((g.M + S::BM - 1) / S::BM);
+  const int tiles_n = (int)((g.N + S::BN - 1) / S::BN);
+  const int per_batch = tiles_m * tiles_n;
+  const int L = xcd_remap(blockIdx.x, (int)gridDim.x);
+  const int64_t b = L / per_batch;
+  const TileCoord tc = grouped_tile(L - (int)b * per_batch, tiles_m, tiles_n, 8);
+  const int64_t m0 = (int64_t)tc.m * S::BM, n0 = (int64_t)tc.n * S::BN;
+  const int64_t K = b + 1 == g.batch ? g.K_last : g.K;
+  const char* A = static_cast<const char*>(g.A) + b * g.sa * es;
+  const char* B = static_cast<const char*>(g.B) + b * g.sb * es;
+
+  Accum<S> acc;
+  acc.zero();
+  const LanePos p = lane_pos<S>();
+  const int64_t nk = (K + TB - 1) / TB;
+  auto run = [&](auto& la, auto& lb) {
+    mainloop<T, S, true, kKA, kKB>(acc, la, lb, nk, smem, p, [](int64_t) {});
+  };
+  // row-major [M][lda] with K contiguous: rows beyond M read zero (K is a
+  // multiple of TB here); k-major [K][lda]: rows beyond K read zero -- the
+  // range ends with row K - 1 of the batch's matrix, whose first column may
+  // sit partway across a stored row (a batch offset that is not whole rows)
+  // k-blocked: rows beyond the block's ld rows read zero (a batch's row offset
+  // counted); K is whole blocks
+  auto make_a = [&]() {
+    if constexpr (kLA == kKMajor) {
+      const int64_t col = (b * g.sa) % g.lda + m0;  // column of the tile's first m
+      KMajorLoader<T, S::kWaves> l;
+      l.init(A + m0 * es, kRowBytes, g.lda * es, TB * g.lda * es, (K * g.lda - col) * es);
+      return l;
+    } else if constexpr (kLA == kKBlocked) {
+      const int64_t row = (b * g.sa / TB) % g.lda + m0;
+      DirectLoader<S::BM, S::kWaves> l;
+      l.init(A + m0 * kRowBytes, kRowBytes, g.lda * kRowBytes, (g.lda - row) * kRowBytes, 0);
+      return l;
+    } else {
+      DirectLoader<S::BM, S::kWaves> l;
+      l.init(A + m0 * g.lda * es, g.lda * es, kRowBytes, (g.M - m0) * g.lda * es, kRowBytes);
+      return l;
+    }
+  };
+  auto make_b = [&]() {
+    if constexpr (kLB == kKMajor) {
+      const int64_t col = (b * g.sb) % g.ldb + n0;
+      KMajorLoader<T, S::kWaves> l;
+      l.init(B + n0 * es, kRowBytes, g.ldb * es, TB * g.ldb * es, (K * g.ldb - col) * es);
+      return l;
+    } else if constexpr (kLB == kKBlocked) {
+      const int64_t row = (b * g.sb / TB) % g.ldb + n0;
+      DirectLoader<S::BN, S::kWaves> l;
+      l.init(B + n0 * kRowBytes, kRowBytes, g.ldb * kRowBytes, (g.ldb - row) * kRowBytes, 0);
+      return l;
+    } else {
+      DirectLoader<S::BN, S::kWaves> l;
+      l.init(B + n0 * g.ldb * es, g.ldb * es, kRowBytes, (g.N - n0) * g.ldb * es, kRowBytes);
+      return l;
+    }
+  };
+  auto la = make_a();
+  auto lb = make_b();
+  run(la, lb);
+  if (g.c_f32)
+    gemm_epilogue<S, float>(acc, p, smem, static_cast<float*>(g.C) + b * g.sc, g.ldc, m0, n0, g.M,
+                            g.N, g.alpha, g.accumulate != 0);
+  else
+    gemm_epilogue<S, T>(acc, p, smem, static_cast<T*>(g.C) + b * g.sc, g.ldc, m0, n0, g.M, g.N,
+                        g.alpha, false);
+}
+
+template <typename T>
+hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s) {
+  const int64_t tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
+  const dim3 grid((unsigned)tiles), block(512);
+  const int32_t combo = g.a_layout * 3 + g.b_layout;
+  switch (combo) {
+    case kRowK * 3 + kRowK:
+      hipLaunchKernelGGL((gemm_kernel<T, kRowK, kRowK>), grid, block, 0, s, g);
+      break;
+    case kRowK * 3 + kKMajor:
+      hipLaunchKernelGGL((gemm_kernel<T, kRowK, kKMajor>), grid, block, 0, s, g);
+      break;
+    case kKMajor * 3 + kRowK:
+      hipLaunchKernelGGL((gemm_kernel<T, kKMajor, kRowK>), grid, block, 0, s, g);
+      break;
+    case kKMajor * 3 + kKMajor:
+      hipLaunchKernelGGL((gemm_kernel<T, kKMajor, kKMajor>), grid, block, 0, s, g);
+      break;
+    case kKBlocked * 3 + kKBlocked:
+      hipLaunchKernelGGL((gemm_kernel<T, kKBlocked, kKBlocked>), grid, block, 0, s, g);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// dst[j][i] = src[i][j], through a 64 x 64 LDS tile (padded against bank
+// conflicts); 256 threads, 4 rows per pass.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_rect_kernel(T* __restrict__ dst,
+                                                             const T* __restrict__ src,
+                                                             int64_t rows, int64_t cols) {
+  __shared__ T tile[64][65];
+  const int64_t i0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int64_t i = i0 + r, j = j0 + tx;
+    if (i < rows && j < cols) tile[r][tx] = src[i * cols + j];
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int64_t j = j0 + r, i = i0 + tx;
+    if (i < rows && j < cols) dst[j * rows + i] = tile[tx][r];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
+  const int64_t tb = 128 / (int64_t)dtype_bytes(g.dt);
+  // K-contiguous and k-blocked operands are read in whole k-tiles; the N runs
+  // of the epilogue are 8 wide
+  if ((g.a_layout != kKMajor || g.b_layout != kKMajor) && (g.K % tb != 0 || g.K_last % tb != 0))
+    return hipErrorInvalidValue;
+  if (g.N % 8 != 0 || g.K <= 0 || g.K_last <= 0) return hipErrorInvalidValue;
+  if (g.dt == Dtype::BF16) return launch_gemm_t<uint16_t>(g, s);
+  return launch_gemm_t<float>(g, s);
+}
+
+hipError_t launch_transpose(const void* src, void* dst, int64_t rows, int64_t cols, Dtype dt,
+                            hipStream_t s) {
+  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  if (dt == Dtype::BF16)
+    hipLaunchKernelGGL(transpose_rect_kernel<uint16_t>, grid, dim3(256), 0, s,
+                       static_cast<uint16_t*>(dst), static_cast<const uint16_t*>(src), rows, cols);
+  else
+    hipLaunchKernelGGL(transpose_rect_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<float*>(dst), static_cast<const float*>(src), rows, cols);
+  return hipGetLastError();
+}
+
+}  // namespace ttt

@@ -197,7 +197,7 @@ __device__ __forceinline__ bf16x8_t read_a_tr(const lds_char* sA, int m0, int la
   return bf16x8_t{v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
 }
 
-template <class S, bool kTrA = false>
+template <class S, bool kTrA = false, bool kTrB = false>
 struct Mma16 {
   static constexpr int kSteps = 4;  // 16 K values per step, 64 per k-tile
   struct Frag {
@@ -211,14 +211,20 @@ struct Mma16 {
       return lds_load<bf16x8_t>(sA + lds_offset(p.wave_m0 + 32 * i + (p.lane & 31),
                                                 2 * s + (p.lane >> 5)));
   }
+  __device__ __forceinline__ static bf16x8_t read_b(const lds_char* sB, const LanePos& p, int j,
+                                                    int s) {
+    if constexpr (kTrB)
+      return read_a_tr(sB, p.wave_n0 + 32 * j, p.lane, s);
+    else
+      return lds_load<bf16x8_t>(sB + lds_offset(p.wave_n0 + 32 * j + (p.lane & 31),
+                                                2 * s + (p.lane >> 5)));
+  }
   __device__ __forceinline__ static void read(Frag& f, const lds_char* sA, const lds_char* sB,
                                               const LanePos& p, int s) {
-    const int r = p.lane & 31, h = p.lane >> 5;
 #pragma unroll
     for (int i = 0; i < S::MB; ++i) f.a[i] = read_a(sA, p, i, s);
 #pragma unroll
-    for (int j = 0; j < S::NB; ++j)
-      f.b[j] = lds_load<bf16x8_t>(sB + lds_offset(p.wave_n0 + 32 * j + r, 2 * s + h));
+    for (int j = 0; j < S::NB; ++j) f.b[j] = read_b(sB, p, j, s);
   }
   // The fragments of step s+1 are read while the MFMAs of step s run.  The
   // scheduling barriers pin that order (otherwise the compiler sinks each read
@@ -258,7 +264,6 @@ struct Mma16 {
                                                       const lds_char* sB, const LanePos& p,
                                                       Hook&& after_mfma) {
     constexpr int kPerStep = S::MB * S::NB;
-    const int r = p.lane & 31, h = p.lane >> 5;
     Frag f[2];
     read(f[0], sA, sB, p, 0);
 #pragma unroll
@@ -281,8 +286,7 @@ struct Mma16 {
                 if (q < S::MB)
                   n.a[q] = read_a(sA, p, q, s + 1);
                 else
-                  n.b[q - S::MB] = lds_load<bf16x8_t>(
-                      sB + lds_offset(p.wave_n0 + 32 * (q - S::MB) + r, 2 * (s + 1) + h));
+                  n.b[q - S::MB] = read_b(sB, p, q - S::MB, s + 1);
               }
             }
           }
@@ -296,38 +300,71 @@ struct Mma16 {
 template <class S>
 struct Mma<uint16_t, S> : Mma16<S, false> {};
 
-template <class S>
-struct Mma<float, S> {
+// fp32: v_mfma_f32_32x32x2_f32, eight per 16 K values; lane l feeds K value
+// 16 s + 8 (l / 32) + e of its row to MFMA e of step s, on both sides.  A
+// k-major tile (rows = k, 128-byte rows of 32 m-values: stage row
+// R = (m / 32) * 32 + k, chunk c at c ^ lds_swz_tr(R)) is read one value per
+// lane and MFMA.
+template <class S, bool kTrA = false, bool kTrB = false>
+struct Mma32 {
   static constexpr int kSteps = 2;  // 16 K values per step, 32 per k-tile
+  template <bool kKMajor>
+  __device__ __forceinline__ static void read8(float v[8], const lds_char* sX, int row, int lane,
+                                               int s) {
+    const int h = lane >> 5;
+    if constexpr (kKMajor) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int R = (row >> 5) * 32 + 16 * s + 8 * h + e;
+        v[e] = lds_load<float>(sX + (uint32_t)R * kRowBytes +
+                               (uint32_t)((((row & 31) >> 2) ^ lds_swz_tr(R)) << 4) +
+                               (uint32_t)((row & 3) * 4));
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const floatx4_t x = lds_load<floatx4_t>(sX + lds_offset(row, 4 * s + 2 * h + q));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+      }
+    }
+  }
   template <class Mid>
   __device__ __forceinline__ static void ktile(Accum<S>& acc, const lds_char* sA,
                                                const lds_char* sB, const LanePos& p, Mid&& mid) {
-    const int r = p.lane & 31, h = p.lane >> 5;
+    const int r = p.lane & 31;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      floatx4_t a[S::MB][2], b[S::NB][2];
+      float a[S::MB][8], b[S::NB][8];
 #pragma unroll
-      for (int i = 0; i < S::MB; ++i)
+      for (int i = 0; i < S::MB; ++i) read8<kTrA>(a[i], sA, p.wave_m0 + 32 * i + r, p.lane, s);
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-          a[i][q] = lds_load<floatx4_t>(sA + lds_offset(p.wave_m0 + 32 * i + r, 4 * s + 2 * h + q));
-#pragma unroll
-      for (int j = 0; j < S::NB; ++j)
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-          b[j][q] = lds_load<floatx4_t>(sB + lds_offset(p.wave_n0 + 32 * j + r, 4 * s + 2 * h + q));
+      for (int j = 0; j < S::NB; ++j) read8<kTrB>(b[j], sB, p.wave_n0 + 32 * j + r, p.lane, s);
 #pragma unroll
       for (int i = 0; i < S::MB; ++i)
 #pragma unroll
         for (int j = 0; j < S::NB; ++j)
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e >> 2][e & 3],
-                                                               b[j][e >> 2][e & 3],
-                                                               acc.v[i][j], 0, 0, 0);
+            acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc.v[i][j], 0, 0, 0);
       if (s == kSteps / 2 - 1) mid();
     }
   }
+};
+
+template <class S>
+struct Mma<float, S> : Mma32<S, false, false> {};
+
+// The fragment reader of element type T with the given operand forms.
+template <typename T, class S, bool kTrA, bool kTrB>
+struct MmaSel;
+template <class S, bool kTrA, bool kTrB>
+struct MmaSel<uint16_t, S, kTrA, kTrB> {
+  using type = Mma16<S, kTrA, kTrB>;
+};
+template <class S, bool kTrA, bool kTrB>
+struct MmaSel<float, S, kTrA, kTrB> {
+  using type = Mma32<S, kTrA, kTrB>;
 };
 
 // ------------------------------------------------------------- row loaders
@@ -422,26 +459,34 @@ struct DirectLoader {
   __device__ __forceinline__ void commit(lds_char*) const {}
 };
 
-// KMajorLoader: a k-major A tile (see read_a_tr) from a k-blocked token-major
-// matrix [cols / 64][R][64] (R rows of 64 token columns per block): the
-// tile's m = 256 token columns are 4 consecutive blocks, and k-tile kt is rows
-// [64 kt, 64 kt + 64) of each.  Stage row Rs = (m / 64) * 64 + k is block
-// m / 64's row 64 kt + k, 128 bytes, stored with lds_swz_tr.  Reads at or
-// beyond valid_bytes from the first block return zero.
-template <int WAVES>
+// KMajorLoader: a k-major operand tile of 256 m-values (m: the tile's output
+// rows or columns) and one k-tile of TB = 128 / sizeof(T) k-values.  Stage
+// row R = (m / TB) * TB + k holds the TB values m = TB (R / TB) .. + TB - 1 of
+// k-tile row k (128 bytes), chunk c at c ^ lds_swz_tr(R); the fragment readers
+// with kTrA / kTrB read it.  Source addressing, in bytes from base:
+//   m-block mb = m / TB, k-tile kt, row k  ->  mb * block_stride + kt * kt_stride
+//                                             + k * row_stride,
+// e.g. a row-major [K][ld] matrix: block_stride = 128, row_stride = ld bytes,
+// kt_stride = TB * row_stride; the k-blocked token-major layouts (blocks of
+// 64 token columns, R rows of 128 bytes each): block_stride = R * 128,
+// row_stride = 128, kt_stride = 64 * 128.  Reads at or beyond valid_bytes -
+// kt * kt_stride from base + kt * kt_stride return zero.
+template <typename T, int WAVES>
 struct KMajorLoader {
+  static constexpr int TB = kRowBytes / (int)sizeof(T);
   static constexpr int kStagedLoads = 0;
   static constexpr int kRowsPerWave = 256 / WAVES;
   static constexpr int kPer = kRowsPerWave / 8;
   const char* base;
-  int64_t valid_bytes;
+  int64_t kt_stride, valid_bytes;
   uint32_t voff[kPer];
   uint32_t lds_row0;
 
-  // base: row 0 of the first of the 4 blocks; block_bytes: R * 128.
-  __device__ __forceinline__ void init(const void* base_, int64_t block_bytes,
+  __device__ __forceinline__ void init(const void* base_, int64_t block_stride,
+                                       int64_t row_stride, int64_t kt_stride_,
                                        int64_t valid_bytes_) {
     base = static_cast<const char*>(base_);
+    kt_stride = kt_stride_;
     valid_bytes = valid_bytes_;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -450,11 +495,11 @@ struct KMajorLoader {
     for (int q = 0; q < kPer; ++q) {
       const int row = (int)lds_row0 + 8 * q + (lane >> 3);
       const int c = (lane & 7) ^ lds_swz_tr(row);
-      voff[q] = (uint32_t)((row >> 6) * block_bytes + (row & 63) * kRowBytes + c * 16);
+      voff[q] = (uint32_t)((row / TB) * block_stride + (row % TB) * row_stride + c * 16);
     }
   }
   __device__ __forceinline__ rsrc_t rsrc(int64_t kt, bool live = true) const {
-    return make_rsrc(base + kt * 64 * kRowBytes, live ? valid_bytes - kt * 64 * kRowBytes : 0);
+    return make_rsrc(base + kt * kt_stride, live ? valid_bytes - kt * kt_stride : 0);
   }
   __device__ __forceinline__ void issue_one(rsrc_t r, lds_char* stage, int q) const {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -525,13 +570,13 @@ struct RegLoader {
 // not LDS).
 // kTrA (bf16 only): the A tile is k-major (see read_a_tr) and its fragments
 // are read with transposed loads.
-template <typename T, class S, bool kSpread = true, bool kTrA = false, class LA, class LB,
-          class Hook>
+template <typename T, class S, bool kSpread = true, bool kTrA = false, bool kTrB = false,
+          class LA, class LB, class Hook>
 __device__ __forceinline__ void mainloop(Accum<S>& acc, LA& la, LB& lb, int64_t nk, lds_char* smem,
                                          const LanePos& p, Hook&& after_ktile) {
   constexpr int kStaged = LA::kStagedLoads + LB::kStagedLoads;
-  static_assert(!kTrA || (sizeof(T) == 2 && kSpread && kStaged == 0),
-                "transposed A fragments: bf16, direct loaders, spread issue");
+  static_assert(sizeof(T) == 4 || !(kTrA || kTrB) || (kSpread && kStaged == 0),
+                "bf16 k-major fragments: direct loaders, spread issue");
   if (nk <= 0) return;
   if constexpr (kSpread && sizeof(T) == 2 && kStaged == 0) {
     // bf16, direct loaders: k-tile kt+1's load instructions are spread over
@@ -539,7 +584,7 @@ __device__ __forceinline__ void mainloop(Accum<S>& acc, LA& la, LB& lb, int64_t 
     // when they then still end in the first half of the k-tile).  After the
     // last k-tile they read an empty range into the idle stage; the closing
     // wait drains them before the caller touches LDS.
-    using M = Mma16<S, kTrA>;
+    using M = Mma16<S, kTrA, kTrB>;
     constexpr int kLoads = LA::kPer + LB::kPer;
     constexpr int kMfmas = M::kSteps * S::MB * S::NB;
     constexpr int kEvery = 2 * kLoads <= kMfmas / 2 ? 2 : 1;
@@ -588,7 +633,7 @@ __device__ __forceinline__ void mainloop(Accum<S>& acc, LA& la, LB& lb, int64_t 
       if constexpr (LA::kStagedLoads == 0) la.issue(kt + 1, nxt);
       if constexpr (LB::kStagedLoads == 0) lb.issue(kt + 1, nxt + S::BM * kRowBytes);
     }
-    Mma<T, S>::ktile(acc, cur, cur + S::BM * kRowBytes, p, [&] {
+    MmaSel<T, S, kTrA, kTrB>::type::ktile(acc, cur, cur + S::BM * kRowBytes, p, [&] {
       if constexpr (kStaged > 0) {
         if (kt + 1 < nk) {
           la.commit(nxt);

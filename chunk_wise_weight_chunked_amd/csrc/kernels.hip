@@ -483,12 +483,17 @@ __global__ __launch_bounds__(256) void rows_to_vt_kernel(Dims dm, const T* __res
 // result does not depend on how the chunks are grouped.  The tile shape S
 // divides d and f exactly (the host picks it), so every tile is full.
 // Tile `blk` of `nblk` (workgroups [0, nblk) of the launch are these tiles).
-template <typename T, class S>
+// kSlots: which slot layouts are written -- bit 0: `slots` [G][B][d][f] (what
+// the outputs read); bit 1: `slots_t` [G][B][f][d], the weights transposed
+// (the backward's products that contract over d read them with K
+// contiguous).
+template <typename T, class S, int kSlots = 1>
 __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __restrict__ Vt,
                                                    const T* __restrict__ Zt,
                                                    float* __restrict__ W_state,
                                                    T* __restrict__ slots, int64_t g0, int64_t gc,
-                                                   int blk, int nblk, lds_char* smem) {
+                                                   int blk, int nblk, lds_char* smem,
+                                                   T* __restrict__ slots_t = nullptr) {
   constexpr int TB = kRowBytes / (int)sizeof(T);
   const int64_t d = dm.d, f = dm.f;
   const int tiles_m = (int)(d / S::BM);
@@ -545,9 +550,44 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
   for (int r = 0; r < 2; ++r)
     lane_pair[r] = (uint32_t)((p.wave_m0 + 4 * (p.lane >> 5) + (odd ? 2 : 0) + r) * f +
                               p.wave_n0 + ((p.lane & 31) & ~1)) * 2u;
-  constexpr int kSlotStores = S::MB * 4 * S::NB * (sizeof(T) == 2 ? 2 : 4);
+  // store instructions per lane of one slot: row-major pairs (bf16) or
+  // values (fp32); transposed, 4 consecutive rows of a column in one store
+  constexpr int kSlotStores = ((kSlots & 1) ? S::MB * 4 * S::NB * (sizeof(T) == 2 ? 2 : 4) : 0) +
+                              ((kSlots & 2) ? S::MB * 4 * S::NB : 0);
+  const uint32_t lane_t = (uint32_t)(((p.wave_n0 + (p.lane & 31)) * d + p.wave_m0 +
+                                      4 * (p.lane >> 5)) * (int64_t)sizeof(T));
+  const uint32_t du = (uint32_t)d;
+  auto write_slot_t = [&](int64_t js) {
+    const rsrc_t sr = make_rsrc(slots_t + js * slot_stride + b * d * f + n0 * d + m0,
+                                ((f - n0) * d - m0) * (int64_t)sizeof(T));
+#pragma unroll
+    for (int i = 0; i < S::MB; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int j = 0; j < S::NB; ++j) {
+          const uint32_t so = (uint32_t)(32 * j * du + 32 * i + 8 * q) * (uint32_t)sizeof(T);
+          float z[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[e] = acc.v[i][j][4 * q + e];
+          if constexpr (sizeof(T) == 2) {
+            typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+            __builtin_amdgcn_raw_buffer_store_b64(u2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])},
+                                                  sr, lane_t, so, 0);
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b128(
+                u32x4_t{__float_as_uint(z[0]), __float_as_uint(z[1]), __float_as_uint(z[2]),
+                        __float_as_uint(z[3])},
+                sr, lane_t, so, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
   auto write_slot = [&](int64_t jj) {
     const int64_t js = dm.reverse_slots ? gc - 1 - jj : jj;
+    if constexpr ((kSlots & 2) != 0) write_slot_t(js);
+    if constexpr ((kSlots & 1) == 0) return;
     const rsrc_t sr = make_rsrc(slots + js * slot_stride + b * d * f + corner,
                                 span * (int64_t)sizeof(T));
 #pragma unroll
@@ -581,7 +621,8 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
       }
   };
 
-  const bool with_slots = slots != nullptr;  // none: the increments' sum only
+  // none: the increments' sum only
+  const bool with_slots = (kSlots & 1) ? slots != nullptr : slots_t != nullptr;
   if (with_slots) write_slot(0);
   const int64_t kt_per_chunk = dm.Cp / TB;
   // a streaming call leaves the sequence's last chunk out of the state (its
@@ -618,13 +659,13 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
     }
 }
 
-template <typename T, class S>
+template <typename T, class S, int kSlots = 1>
 __global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::kWaves / 4, S::kWaves / 4))) void prefix_update_kernel(
     Dims dm, const T* __restrict__ Vt, const T* __restrict__ Zt, float* __restrict__ W_state,
-    T* __restrict__ slots, int64_t g0, int64_t gc) {
+    T* __restrict__ slots, int64_t g0, int64_t gc, T* __restrict__ slots_t) {
   __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
-  prefix_update_tile<T, S>(dm, Vt, Zt, W_state, slots, g0, gc, blockIdx.x, gridDim.x,
-                           (lds_char*)smem_raw);
+  prefix_update_tile<T, S, kSlots>(dm, Vt, Zt, W_state, slots, g0, gc, blockIdx.x, gridDim.x,
+                                   (lds_char*)smem_raw, slots_t);
 }
 
 // ===================================================================== S3
@@ -670,9 +711,9 @@ __device__ __forceinline__ void down_proj_tile(const Dims& dm, const T* __restri
     // not stored
     const int64_t col0 = (b * dm.N + chunk) * dm.Cp + m0;
     const int64_t block_bytes = f * kRowBytes;
-    KMajorLoader<S::kWaves> la;
+    KMajorLoader<T, S::kWaves> la;
     la.init(reinterpret_cast<const char*>(Zs) + (col0 / kTokenAlign) * block_bytes, block_bytes,
-            (dm.P - col0) / kTokenAlign * block_bytes);
+            kRowBytes, kTokenAlign * kRowBytes, (dm.P - col0) / kTokenAlign * block_bytes);
     mainloop<T, S, true, true>(acc, la, lb, ld / kRowBytes, smem, p, [](int64_t) {});
   } else {
     DirectLoader<S::BM, S::kWaves> la;
@@ -764,10 +805,11 @@ TTT_GEMM_KERNEL void scan_target_kernel(Dims dm, const T* __restrict__ Vt,
 
 // Two independent scans of all N chunks (the backward's forward weights and
 // its chunk-reversed gradient sums) in one launch: one group of all chunks
-// gives ~1.5 waves of tiles per scan, two together fill the chip better.
+// gives ~1.5 waves of tiles per scan, two together fill the chip better.  The
+// first writes its slots transposed (slots1t), the second row-major (slots2).
 template <typename T>
 TTT_GEMM_KERNEL void dual_scan_kernel(Dims d1, const T* __restrict__ Vt1, const T* __restrict__ Zt1,
-                                      float* __restrict__ W1, T* __restrict__ slots1, Dims d2,
+                                      float* __restrict__ W1, T* __restrict__ slots1t, Dims d2,
                                       const T* __restrict__ Vt2, const T* __restrict__ Zt2,
                                       float* __restrict__ W2, T* __restrict__ slots2, int blocks,
                                       int pad) {
@@ -775,11 +817,11 @@ TTT_GEMM_KERNEL void dual_scan_kernel(Dims d1, const T* __restrict__ Vt1, const 
   const int b = blockIdx.x;
   if (b < pad) {
     if (b < blocks)
-      prefix_update_tile<T, PrefixTile>(d1, Vt1, Zt1, W1, slots1, 0, d1.N, b, blocks,
-                                        (lds_char*)smem_raw);
+      prefix_update_tile<T, PrefixTile, 2>(d1, Vt1, Zt1, W1, nullptr, 0, d1.N, b, blocks,
+                                           (lds_char*)smem_raw, slots1t);
   } else if (b - pad < blocks) {
-    prefix_update_tile<T, PrefixTile>(d2, Vt2, Zt2, W2, slots2, 0, d2.N, b - pad, blocks,
-                                      (lds_char*)smem_raw);
+    prefix_update_tile<T, PrefixTile, 1>(d2, Vt2, Zt2, W2, slots2, 0, d2.N, b - pad, blocks,
+                                         (lds_char*)smem_raw);
   }
 }
 
@@ -1116,7 +1158,8 @@ static void launch_scan_apply_t(const Dims& dm, const T* Vt, const T* Zt, float*
   if (gc > 0)
     hipLaunchKernelGGL((prefix_update_kernel<T, Small>),
                        dim3((unsigned)((dm.d / Small::BM) * (dm.f / Small::BN) * dm.B)),
-                       dim3(Small::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, g0, gc);
+                       dim3(Small::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, g0, gc,
+                       static_cast<T*>(nullptr));
   if (down_tiles > 0)
     hipLaunchKernelGGL(down_proj_kernel<T>, dim3((unsigned)down_tiles), dim3(Tile::kThreads), 0, s,
                        dm, Z, apply_slots, O, a0, ac);
@@ -1141,29 +1184,41 @@ hipError_t launch_scan_apply(const Dims& dm, const void* Vt, const void* Zt, flo
   return hipGetLastError();
 }
 
-hipError_t launch_dual_scan(const Dims& d1, const void* Vt1, const void* Zt1, float* W1,
-                            void* slots1, const Dims& d2, const void* Vt2, const void* Zt2,
-                            float* W2, void* slots2, hipStream_t s) {
+template <typename T>
+static void launch_dual_scan_t(const Dims& d1, const T* Vt1, const T* Zt1, float* W1, T* slots1t,
+                               const Dims& d2, const T* Vt2, const T* Zt2, float* W2, T* slots2,
+                               hipStream_t s) {
   if (d1.d % PrefixTile::BM != 0 || d1.f % PrefixTile::BN != 0) {
-    hipError_t e = launch_scan_apply(d1, Vt1, Zt1, W1, slots1, 0, d1.N, nullptr, nullptr, nullptr,
-                                     0, 0, s);
-    if (e != hipSuccess) return e;
-    return launch_scan_apply(d2, Vt2, Zt2, W2, slots2, 0, d2.N, nullptr, nullptr, nullptr, 0, 0, s);
+    // 64 x 64 tiles when 256 does not divide the weight: two launches
+    using Small = TileShape<64, 64, 2, 2>;
+    const dim3 grid((unsigned)((d1.d / Small::BM) * (d1.f / Small::BN) * d1.B));
+    hipLaunchKernelGGL((prefix_update_kernel<T, Small, 2>), grid, dim3(Small::kThreads), 0, s, d1,
+                       Vt1, Zt1, W1, static_cast<T*>(nullptr), (int64_t)0, d1.N, slots1t);
+    hipLaunchKernelGGL((prefix_update_kernel<T, Small, 1>), grid, dim3(Small::kThreads), 0, s, d2,
+                       Vt2, Zt2, W2, slots2, (int64_t)0, d2.N, static_cast<T*>(nullptr));
+    return;
   }
   const int blocks = (int)((d1.d / PrefixTile::BM) * (d1.f / PrefixTile::BN) * d1.B);
   const int pad = (blocks + 7) / 8 * 8;  // the second scan starts on XCD 0
+  hipLaunchKernelGGL(dual_scan_kernel<T>, dim3((unsigned)(pad + blocks)), dim3(Tile::kThreads), 0,
+                     s, d1, Vt1, Zt1, W1, slots1t, d2, Vt2, Zt2, W2, slots2, blocks, pad);
+}
+
+hipError_t launch_dual_scan(const Dims& d1, const void* Vt1, const void* Zt1, float* W1,
+                            void* slots1t, const Dims& d2, const void* Vt2, const void* Zt2,
+                            float* W2, void* slots2, hipStream_t s) {
   if (d1.dt == Dtype::BF16)
-    hipLaunchKernelGGL(dual_scan_kernel<uint16_t>, dim3((unsigned)(pad + blocks)),
-                       dim3(Tile::kThreads), 0, s, d1, static_cast<const uint16_t*>(Vt1),
-                       static_cast<const uint16_t*>(Zt1), W1, static_cast<uint16_t*>(slots1), d2,
-                       static_cast<const uint16_t*>(Vt2), static_cast<const uint16_t*>(Zt2), W2,
-                       static_cast<uint16_t*>(slots2), blocks, pad);
+    launch_dual_scan_t<uint16_t>(d1, static_cast<const uint16_t*>(Vt1),
+                                 static_cast<const uint16_t*>(Zt1), W1,
+                                 static_cast<uint16_t*>(slots1t), d2,
+                                 static_cast<const uint16_t*>(Vt2),
+                                 static_cast<const uint16_t*>(Zt2), W2,
+                                 static_cast<uint16_t*>(slots2), s);
   else
-    hipLaunchKernelGGL(dual_scan_kernel<float>, dim3((unsigned)(pad + blocks)),
-                       dim3(Tile::kThreads), 0, s, d1, static_cast<const float*>(Vt1),
-                       static_cast<const float*>(Zt1), W1, static_cast<float*>(slots1), d2,
-                       static_cast<const float*>(Vt2), static_cast<const float*>(Zt2), W2,
-                       static_cast<float*>(slots2), blocks, pad);
+    launch_dual_scan_t<float>(d1, static_cast<const float*>(Vt1), static_cast<const float*>(Zt1),
+                              W1, static_cast<float*>(slots1t), d2,
+                              static_cast<const float*>(Vt2), static_cast<const float*>(Zt2), W2,
+                              static_cast<float*>(slots2), s);
   return hipGetLastError();
 }
 

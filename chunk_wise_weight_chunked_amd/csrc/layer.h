@@ -121,6 +121,39 @@ hipError_t launch_state_to_bf16(const float* W, void* out, int64_t n, hipStream_
 constexpr size_t kDecodeScratchBytes = (size_t)4 << 20;
 hipError_t decode_scratch_ptr(void** out);
 
+// Batched GEMM on the library's mainloop (gemm.hip):
+//   C[b] = alpha * A[b] B[b]ᵀ   (accumulate: C[b] += ...)
+// over b < batch, A [M][K] and B [N][K] of element type dt; C [M][ldc] fp32
+// (c_f32) or of type dt.  Operand layouts (X = A or B, rows = M or N, ld = lda
+// or ldb, TB = 128 / element bytes):
+//   kRowK     X[r][k] at r * ld + k                  (K contiguous)
+//   kKMajor   X[r][k] at k * ld + r                  ([K][ld] row-major)
+//   kKBlocked X[r][k] at ((k / TB) * ld + r) * TB + k % TB  (ld = rows per
+//             block: the k-blocked token-major layouts, K = token columns)
+// Element offsets between batches sa, sb, sc (for kKBlocked, a row offset
+// r0 * TB or whole blocks); the last batch contracts K_last values (split
+// products: batch = K slice).  kRowK and kKBlocked need K and K_last to be
+// multiples of TB; N a multiple of 8.
+enum GemmLayout : int32_t { kRowK = 0, kKMajor = 1, kKBlocked = 2 };
+struct GemmArgs {
+  Dtype dt;
+  const void* A;
+  int64_t lda, sa;
+  int32_t a_layout;
+  const void* B;
+  int64_t ldb, sb;
+  int32_t b_layout;
+  void* C;
+  int64_t ldc, sc;
+  int32_t c_f32, accumulate;
+  int64_t M, N, K, K_last, batch;
+  float alpha;
+};
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
+// dst [cols][rows] = srcᵀ for src [rows][cols] of element type dt.
+hipError_t launch_transpose(const void* src, void* dst, int64_t rows, int64_t cols, Dtype dt,
+                            hipStream_t s);
+
 // Backward-pass kernels (backward.hip).
 constexpr int kTargetBackwardRows = 256;  // token rows per partial sum of the taps' gradient
 constexpr int kDotPartials = 1024;        // partial sums of the learning rate's gradient
@@ -132,9 +165,11 @@ hipError_t launch_to_kblocked(const void* src, void* dst, const Dims& dm, int64_
 // (row t of A_g and A_u at t * ld).
 hipError_t launch_swiglu_rows(const float* Ag, const float* Au, int64_t ld, void* Z,
                               const Dims& dm, hipStream_t s);
-// The scans of two independent problems (same shapes) in one launch.
+// The scans of two independent problems (same shapes) in one launch: the
+// first writes its slots transposed ([N][B][f][d], slots1t), the second
+// row-major (slots2).
 hipError_t launch_dual_scan(const Dims& d1, const void* Vt1, const void* Zt1, float* W1,
-                            void* slots1, const Dims& d2, const void* Vt2, const void* Zt2,
+                            void* slots1t, const Dims& d2, const void* Vt2, const void* Zt2,
                             float* W2, void* slots2, hipStream_t s);
 // dA [B*T][2f] = [dA_g | dA_u] from dZ (fp32 [B*T][f]) and A_g, A_u (fp32,
 // row t at t * ld).

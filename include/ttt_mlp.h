@@ -29,9 +29,10 @@
  *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
  *     Calls only enqueue work and return; the caller synchronises.
  *   - The caller owns every buffer (inputs, outputs, state, workspace).  The
- *     library allocates no device memory and keeps no device state.  Inputs are
- *     never written.  Outputs and the workspace must not overlap inputs or each
- *     other (checked on address ranges).
+ *     library allocates no device memory and keeps no device state, apart from
+ *     the static 4 MiB buffer per GPU of ttt_mlp_forward_stream_decode_noalloc.
+ *     Inputs are never written.  Outputs and the workspace must not overlap
+ *     inputs or each other (checked on address ranges).
  *   - Arguments are validated on the host before anything is enqueued; on any
  *     error status nothing has been written.  TTT_ERR_HIP means a launch failed
  *     after validation; outputs are then undefined.  ttt_last_error() returns a
@@ -359,8 +360,8 @@ ttt_status_t ttt_mlp_share_forward(const ttt_mlp_desc_t* desc, const ttt_share_t
  *             (with init_from_w0 = 1 the gradient of W_down0 is their sum)
  *   d_eta     one fp32 value in device memory
  *   ws        ttt_mlp_backward_workspace_size(desc) bytes, 256-byte aligned
- * desc.mode is ignored.  The plain GEMMs run in rocBLAS (one handle per host
- * thread, created on first use, working in a slice of ws). */
+ * desc.mode is ignored.  Every product runs in the library's own MFMA kernels,
+ * in ws; like the forward, the call keeps no state and allocates nothing. */
 size_t ttt_mlp_backward_workspace_size(const ttt_mlp_desc_t* desc);
 ttt_status_t ttt_mlp_backward_batched(
     const ttt_mlp_desc_t* desc, const void* H, const void* X0, const void* W_gate,
