@@ -367,6 +367,119 @@ struct MmaSel<float, S, kTrA, kTrB> {
   using type = Mma32<S, kTrA, kTrB>;
 };
 
+// ------------------------------------------------- 16 x 16 x 32 MFMA policy
+// bf16 with v_mfma_f32_16x16x32_bf16: each wave's sub-tile is (WM / 16) x
+// (WN / 16) blocks of 16 x 16; a k-tile is 2 steps of 32 K values.  Lane l
+// feeds row (l % 16) of its block and K values 8 (l / 16) .. + 7 of the step,
+// on both sides.  Accumulator element e (0..3) of block (i, j) in lane l sits
+// at
+//     row = 16 i + 4 (l / 16) + e,   col = 16 j + (l % 16)
+// of the wave's sub-tile: four consecutive rows of one column per lane.
+template <class S>
+struct Accum16 {
+  static constexpr int MB = S::WM / 16, NB = S::WN / 16;
+  floatx4_t v[MB][NB];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) v[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+};
+
+// Row of accumulator element (i, j, e) of this lane in the BM x BN tile, and
+// its column.
+__device__ __forceinline__ int row16(const LanePos& p, int i, int e) {
+  return p.wave_m0 + 16 * i + 4 * (p.lane >> 4) + e;
+}
+__device__ __forceinline__ int col16(const LanePos& p, int j) {
+  return p.wave_n0 + 16 * j + (p.lane & 15);
+}
+
+// Fragment of the 16-row block at m0 of a k-major tile (see read_a_tr): lane
+// group g = l / 16 takes K values 8 g .. + 7 of step s, lane j of the group
+// row m0 + j: two transposed loads (k-rows 8 g + 4 h .. + 3).
+__device__ __forceinline__ bf16x8_t read_tr16(const lds_char* sX, int m0, int lane, int s) {
+  const int g = lane >> 4, j = lane & 15;
+  const int m = m0 + 4 * (j & 3);
+  const int k = 32 * s + 8 * g + (j >> 2);
+  bf16x4_t v[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int R = (m >> 6) * 64 + k + 4 * h;
+    const uint32_t off = (uint32_t)R * kRowBytes +
+                         (uint32_t)((((m & 63) >> 3) ^ lds_swz_tr(R)) << 4) + (uint32_t)((m & 7) * 2);
+    v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4_t*)(sX + off));
+  }
+  return bf16x8_t{v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+}
+
+template <class S, bool kTrA = false, bool kTrB = false>
+struct Mma16x16 {
+  static constexpr int kSteps = 2;  // 32 K values per step, 64 per k-tile
+  static constexpr int MB = S::WM / 16, NB = S::WN / 16;
+  struct Frag {
+    bf16x8_t a[MB], b[NB];
+  };
+  __device__ __forceinline__ static bf16x8_t read_a(const lds_char* sA, const LanePos& p, int i,
+                                                    int s) {
+    if constexpr (kTrA)
+      return read_tr16(sA, p.wave_m0 + 16 * i, p.lane, s);
+    else
+      return lds_load<bf16x8_t>(sA + lds_offset(p.wave_m0 + 16 * i + (p.lane & 15),
+                                                4 * s + (p.lane >> 4)));
+  }
+  __device__ __forceinline__ static bf16x8_t read_b(const lds_char* sB, const LanePos& p, int j,
+                                                    int s) {
+    if constexpr (kTrB)
+      return read_tr16(sB, p.wave_n0 + 16 * j, p.lane, s);
+    else
+      return lds_load<bf16x8_t>(sB + lds_offset(p.wave_n0 + 16 * j + (p.lane & 15),
+                                                4 * s + (p.lane >> 4)));
+  }
+  // Fragment reads of step s+1 spread between the MFMAs of step s (the
+  // reads of fragment q after MFMA q), and a hook after every MFMA with its
+  // index in the k-tile.
+  template <class Hook>
+  __device__ __forceinline__ static void ktile_spread(Accum16<S>& acc, const lds_char* sA,
+                                                      const lds_char* sB, const LanePos& p,
+                                                      Hook&& after_mfma) {
+    constexpr int kPerStep = MB * NB;
+    Frag f[2];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) f[0].a[i] = read_a(sA, p, i, 0);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) f[0].b[j] = read_b(sB, p, j, 0);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      const Frag& c = f[s & 1];
+      Frag& n = f[(s + 1) & 1];
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.a[i], c.b[j], acc.v[i][j], 0, 0, 0);
+          const int m = i * NB + j;
+          if (s + 1 < kSteps) {
+#pragma unroll
+            for (int q = 0; q < MB + NB; ++q) {
+              if (q == m || (m == kPerStep - 1 && q > m)) {
+                if (q < MB)
+                  n.a[q] = read_a(sA, p, q, s + 1);
+                else
+                  n.b[q - MB] = read_b(sB, p, q - MB, s + 1);
+              }
+            }
+          }
+          after_mfma(s * kPerStep + m);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+  }
+};
+
 // ------------------------------------------------------------- row loaders
 // Global reads use buffer loads: a scalar resource (base, byte range) per
 // operand and k-tile, a per-lane 32-bit offset.  Reads at or beyond the range
@@ -649,6 +762,42 @@ __device__ __forceinline__ void mainloop(Accum<S>& acc, LA& la, LB& lb, int64_t 
       wait_vmcnt<kStaged>();
     else
       wait_vmcnt<0>();
+    __syncthreads();
+    after_ktile(kt);
+  }
+}
+
+// The bf16 mainloop of the 16 x 16 x 32 policy (direct loaders, k-tile kt+1's
+// loads spread over k-tile kt's MFMAs, as in mainloop's bf16 path).
+template <class S, bool kTrA = false, bool kTrB = false, class LA, class LB, class Hook>
+__device__ __forceinline__ void mainloop16(Accum16<S>& acc, LA& la, LB& lb, int64_t nk,
+                                           lds_char* smem, const LanePos& p, Hook&& after_ktile) {
+  static_assert(LA::kStagedLoads == 0 && LB::kStagedLoads == 0, "direct loaders");
+  using M = Mma16x16<S, kTrA, kTrB>;
+  constexpr int kLoads = LA::kPer + LB::kPer;
+  constexpr int kMfmas = M::kSteps * M::MB * M::NB;
+  constexpr int kEvery = 2 * kLoads <= kMfmas / 2 ? 2 : 1;
+  static_assert(kLoads <= kMfmas, "one load instruction per MFMA at most");
+  if (nk <= 0) return;
+  la.issue(0, smem);
+  lb.issue(0, smem + S::BM * kRowBytes);
+  wait_vmcnt<0>();
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const lds_char* cur = smem + (kt & 1) * S::kStageBytes;
+    lds_char* nxt = smem + ((kt + 1) & 1) * S::kStageBytes;
+    const bool more = kt + 1 < nk;
+    const rsrc_t ra = la.rsrc(kt + 1, more), rb = lb.rsrc(kt + 1, more);
+    M::ktile_spread(acc, cur, cur + S::BM * kRowBytes, p, [&](int idx) {
+      if (idx % kEvery == 0 && idx / kEvery < kLoads) {
+        const int q = idx / kEvery;
+        if (q < LA::kPer)
+          la.issue_one(ra, nxt, q);
+        else
+          lb.issue_one(rb, nxt + S::BM * kRowBytes, q - LA::kPer);
+      }
+    });
+    wait_vmcnt<0>();
     __syncthreads();
     after_ktile(kt);
   }

@@ -336,6 +336,34 @@ __global__ __launch_bounds__(256) void conv_kernel(Dims dm, const T* __restrict_
                    ? *reinterpret_cast<const uint4*>(X0 + row * d + c * EPC)
                    : make_uint4(0, 0, 0, 0);
     }
+    // Interior items: all kConvRows rows in one sequence and every tap's row
+    // inside it -- the same sums in the same order without the per-row and
+    // per-tap position checks.
+    const int64_t sq0 = r0 % T_seq;
+    if (r0 + kConvRows <= BT && sq0 + dm.shift >= K - 1 && sq0 + kConvRows + dm.shift <= T_seq) {
+#pragma unroll
+      for (int jj = 0; jj < kConvRows; ++jj) {
+        float u[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) u[e] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+          if (k >= K) break;
+#pragma unroll
+          for (int e = 0; e < EPC; ++e)
+            u[e] = fmaf(tp[k][e], chunk_value<T>(win[jj + KMAX - 1 - k], e), u[e]);
+        }
+        uint4 out;
+        if constexpr (sizeof(T) == 2)
+          out = make_uint4(pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]),
+                           pack_bf16x2(u[4], u[5]), pack_bf16x2(u[6], u[7]));
+        else
+          out = make_uint4(__float_as_uint(u[0]), __float_as_uint(u[1]), __float_as_uint(u[2]),
+                           __float_as_uint(u[3]));
+        *reinterpret_cast<uint4*>(U + (r0 + jj) * d + c * EPC) = out;
+      }
+      continue;
+    }
 #pragma unroll
     for (int jj = 0; jj < kConvRows; ++jj) {
       const int64_t o = r0 + jj;
