@@ -77,7 +77,10 @@ struct Gemm {
                   const void* A, int64_t lda, int64_t sa, const void* B, int64_t ldb, int64_t sb,
                   bool accumulate, void* C, int64_t ldc, int64_t sc, int64_t batch, bool c_f32,
                   int64_t K_last = -1) {
-    if (err != hipSuccess || M == 0 || N == 0) return;
+    if (err != hipSuccess || M == 0 || N == 0) {
+      hold = pending = false;
+      return;
+    }
     ttt::GemmArgs g{};
     g.dt = dt;
     g.A = A;
@@ -99,12 +102,27 @@ struct Gemm {
     g.K_last = K_last < 0 ? K : K_last;
     g.batch = batch;
     g.alpha = alpha;
-    err = ttt::launch_gemm(g, s);
+    if (pending) {
+      err = ttt::launch_gemm2(g, first, s);
+      pending = false;
+    } else if (hold) {
+      first = g;
+      pending = true;
+      hold = false;
+    } else {
+      err = ttt::launch_gemm(g, s);
+    }
   }
+  // The next call's product is held and added into the one after it (one
+  // launch, C written once; its C and accumulate are ignored).
+  void fuse_next() { hold = true; }
+  ttt::GemmArgs first{};
+  bool hold = false, pending = false;
 };
 
 using ttt::kKBlocked;
-using ttt::kKMajor;
+using ttt::kTiledKMajor;
+using ttt::kTiledRowK;
 using ttt::kRowK;
 
 }  // namespace
@@ -254,9 +272,10 @@ ttt_status_t ttt_mlp_backward_batched(
     e = ttt::launch_dual_scan(dm, Vt, Zt, Wst, Wslots, dr, dOtr, Ztr, dW_start, Sslots, s);
   if (e != hipSuccess) return hip_fail(e, "backward");
 
-  // per chunk j: dZ_j = dO_j W^(j-1) + eta V^_j S_j and G_j = Z_j S_jᵀ, with
-  // W^(j-1) (transposed: K = d contiguous) and S_j (row-major, read k-major
-  // for dZ) in slot j.  The full chunks of a sequence are one batch
+  // per chunk j: dZ_j = dO_j W^(j-1) + eta V^_j S_j (one launch: both
+  // products on the same accumulators) and G_j = Z_j S_jᵀ, with W^(j-1)
+  // (transposed: K = d contiguous) and S_j (in TB x TB tiles: k-major tiles
+  // for dZ, K-contiguous tiles for G) in slot j.  The full chunks of a sequence are one batch
   // (rows C apart, slots B*d*f apart); a ragged last chunk is one batch over
   // the sequences.
   const char* Zc = static_cast<const char*>(Z);
@@ -267,11 +286,12 @@ ttt_status_t ttt_mlp_backward_batched(
     const int64_t r = b0 * T + j * C;  // first row
     const char* WjT = Wslots + (size_t)(j * sl + b0 * Di * Fi) * es;
     const char* Sj = Sslots + (size_t)(j * sl + b0 * Di * Fi) * es;
+    gemm.fuse_next();
+    gemm(kRowK, kTiledKMajor, rows, Fi, Di, dm.eta, Vc + r * d * es, Di, row_stride * Di, Sj,
+         Fi, slot_stride, false, nullptr, Fi, row_stride * Fi, count, f32);
     gemm(kRowK, kRowK, rows, Fi, Di, 1.f, dOc + r * d * es, Di, row_stride * Di, WjT, Di,
          slot_stride, false, dZ + r * f, Fi, row_stride * Fi, count, f32);
-    gemm(kRowK, kKMajor, rows, Fi, Di, dm.eta, Vc + r * d * es, Di, row_stride * Di, Sj, Fi,
-         slot_stride, true, dZ + r * f, Fi, row_stride * Fi, count, f32);
-    gemm(kRowK, kRowK, rows, Di, Fi, 1.f, Zc + r * f * es, Fi, row_stride * Fi, Sj, Fi,
+    gemm(kRowK, kTiledRowK, rows, Di, Fi, 1.f, Zc + r * f * es, Fi, row_stride * Fi, Sj, Fi,
          slot_stride, false, Gf + r * d, Di, row_stride * Di, count, f32);
   };
   const int64_t full = T / C;

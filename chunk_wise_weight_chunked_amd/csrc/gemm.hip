@@ -3,10 +3,12 @@
 //
 // C[b] = alpha * A[b] B[b]ᵀ (or C[b] += ...), with A [M][K] and B [N][K] in
 // the mainloop's "both operands K-contiguous" sense.  Either operand may
-// instead be stored k-major -- [K][M] (resp. [K][N]) row-major -- and is then
-// loaded as k-major tiles (KMajorLoader) and read with transposed fragment
-// loads (bf16) or one value per lane (fp32), so no operand is ever copied to
-// another layout.  The batch index walks independent products (the chunks of
+// instead be stored k-major -- [K][M] (resp. [K][N]) row-major, or in TB x TB
+// tiles of such a matrix -- and is then loaded as k-major tiles
+// (KMajorLoader) and read with transposed fragment loads (bf16) or one value
+// per lane (fp32).  The layouts are listed with GemmLayout (layer.h).  A
+// second product of the same output shape can share the accumulators:
+// C[b] = alpha (A[b] B[b]ᵀ + alpha2 A2[b] B2[b]ᵀ), written once.  The batch index walks independent products (the chunks of
 // a sequence, or the K slices of a split product whose partial results the
 // caller adds in order).
 #include <hip/hip_runtime.h>
@@ -81,10 +83,58 @@ __device__ __forceinline__ void gemm_epilogue(const Accum<S>& acc, const LanePos
   }
 }
 
-template <typename T, int kLA, int kLB>
+// Operand loaders of batch b for a tile starting at row r0 (m0 for A, n0 for
+// B), contracting K values:
+// row-major [rows][ld] with K contiguous: rows beyond the operand's row count
+// read zero (K is a multiple of TB here); k-major [K][ld]: rows beyond K read
+// zero -- the range ends with row K - 1 of the batch's matrix, whose first
+// column may sit partway across a stored row (a batch offset that is not
+// whole rows); k-blocked: rows beyond the block's ld rows read zero (a
+// batch's row offset counted), K is whole blocks; tiled (TB x TB tiles of
+// 128-byte rows, whole matrices per batch, row count and ld multiples of TB):
+// K-contiguous -- a k-tile of the tile's rows is one tile from each of its
+// TB-row blocks; k-major -- a k-tile is consecutive tiles of one tile row.
+template <typename T, int kL, int kRows>
+__device__ __forceinline__ auto make_loader(const char* X, int64_t ld, int64_t sx, int64_t b,
+                                            int64_t r0, int64_t rows, int64_t K) {
+  constexpr int64_t es = sizeof(T);
+  constexpr int TB = kRowBytes / (int)sizeof(T);
+  constexpr int64_t kTileBytes = (int64_t)TB * kRowBytes;
+  constexpr int kWaves = GTile::kWaves;
+  if constexpr (kL == kKMajor) {
+    const int64_t col = (b * sx) % ld + r0;  // column of the tile's first row
+    KMajorLoader<T, kWaves> l;
+    l.init(X + r0 * es, kRowBytes, ld * es, TB * ld * es, (K * ld - col) * es);
+    return l;
+  } else if constexpr (kL == kTiledKMajor) {
+    KMajorLoader<T, kWaves> l;
+    l.init(X + (r0 / TB) * kTileBytes, kTileBytes, kRowBytes, ld * kRowBytes,
+           (K * ld - r0 * TB) * es);
+    return l;
+  } else if constexpr (kL == kKBlocked) {
+    const int64_t row = (b * sx / TB) % ld + r0;
+    DirectLoader<kRows, kWaves> l;
+    l.init(X + r0 * kRowBytes, kRowBytes, ld * kRowBytes, (ld - row) * kRowBytes, 0);
+    return l;
+  } else if constexpr (kL == kTiledRowK) {
+    DirectLoader<kRows, kWaves> l;
+    l.init_blocked(X + (r0 / TB) * ld * kRowBytes, TB, ld * kRowBytes, kTileBytes,
+                   ((rows - r0) / TB) * ld * kRowBytes, kTileBytes);
+    return l;
+  } else {
+    DirectLoader<kRows, kWaves> l;
+    l.init(X + r0 * ld * es, ld * es, kRowBytes, (rows - r0) * ld * es, kRowBytes);
+    return l;
+  }
+}
+
+constexpr bool is_kmajor(int l) { return l == kKMajor || l == kTiledKMajor; }
+
+// kLA2 >= 0: the second product (g2's A, B, K and alpha; g's M, N and batch)
+// runs first on the same accumulators, which are then scaled by g2.alpha.
+template <typename T, int kLA, int kLB, int kLA2 = -1, int kLB2 = -1>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(
-    GemmArgs g) {
-  constexpr bool kKA = kLA == kKMajor, kKB = kLB == kKMajor;
+    GemmArgs g, GemmArgs g2) {
   using S = GTile;
   static_assert(S::kLdsBytes >= S::BM * kEpiStride * 4, "epilogue stage fits the pipeline's LDS");
   __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
@@ -98,60 +148,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t b = L / per_batch;
   const TileCoord tc = grouped_tile(L - (int)b * per_batch, tiles_m, tiles_n, 8);
   const int64_t m0 = (int64_t)tc.m * S::BM, n0 = (int64_t)tc.n * S::BN;
-  const int64_t K = b + 1 == g.batch ? g.K_last : g.K;
-  const char* A = static_cast<const char*>(g.A) + b * g.sa * es;
-  const char* B = static_cast<const char*>(g.B) + b * g.sb * es;
 
   Accum<S> acc;
   acc.zero();
   const LanePos p = lane_pos<S>();
-  const int64_t nk = (K + TB - 1) / TB;
-  auto run = [&](auto& la, auto& lb) {
-    mainloop<T, S, true, kKA, kKB>(acc, la, lb, nk, smem, p, [](int64_t) {});
-  };
-  // row-major [M][lda] with K contiguous: rows beyond M read zero (K is a
-  // multiple of TB here); k-major [K][lda]: rows beyond K read zero -- the
-  // range ends with row K - 1 of the batch's matrix, whose first column may
-  // sit partway across a stored row (a batch offset that is not whole rows)
-  // k-blocked: rows beyond the block's ld rows read zero (a batch's row offset
-  // counted); K is whole blocks
-  auto make_a = [&]() {
-    if constexpr (kLA == kKMajor) {
-      const int64_t col = (b * g.sa) % g.lda + m0;  // column of the tile's first m
-      KMajorLoader<T, S::kWaves> l;
-      l.init(A + m0 * es, kRowBytes, g.lda * es, TB * g.lda * es, (K * g.lda - col) * es);
-      return l;
-    } else if constexpr (kLA == kKBlocked) {
-      const int64_t row = (b * g.sa / TB) % g.lda + m0;
-      DirectLoader<S::BM, S::kWaves> l;
-      l.init(A + m0 * kRowBytes, kRowBytes, g.lda * kRowBytes, (g.lda - row) * kRowBytes, 0);
-      return l;
-    } else {
-      DirectLoader<S::BM, S::kWaves> l;
-      l.init(A + m0 * g.lda * es, g.lda * es, kRowBytes, (g.M - m0) * g.lda * es, kRowBytes);
-      return l;
-    }
-  };
-  auto make_b = [&]() {
-    if constexpr (kLB == kKMajor) {
-      const int64_t col = (b * g.sb) % g.ldb + n0;
-      KMajorLoader<T, S::kWaves> l;
-      l.init(B + n0 * es, kRowBytes, g.ldb * es, TB * g.ldb * es, (K * g.ldb - col) * es);
-      return l;
-    } else if constexpr (kLB == kKBlocked) {
-      const int64_t row = (b * g.sb / TB) % g.ldb + n0;
-      DirectLoader<S::BN, S::kWaves> l;
-      l.init(B + n0 * kRowBytes, kRowBytes, g.ldb * kRowBytes, (g.ldb - row) * kRowBytes, 0);
-      return l;
-    } else {
-      DirectLoader<S::BN, S::kWaves> l;
-      l.init(B + n0 * g.ldb * es, g.ldb * es, kRowBytes, (g.N - n0) * g.ldb * es, kRowBytes);
-      return l;
-    }
-  };
-  auto la = make_a();
-  auto lb = make_b();
-  run(la, lb);
+  if constexpr (kLA2 >= 0) {
+    const int64_t K2 = b + 1 == g2.batch ? g2.K_last : g2.K;
+    auto la = make_loader<T, kLA2, S::BM>(static_cast<const char*>(g2.A) + b * g2.sa * es, g2.lda,
+                                          g2.sa, b, m0, g.M, K2);
+    auto lb = make_loader<T, kLB2, S::BN>(static_cast<const char*>(g2.B) + b * g2.sb * es, g2.ldb,
+                                          g2.sb, b, n0, g.N, K2);
+    mainloop<T, S, true, is_kmajor(kLA2), is_kmajor(kLB2)>(acc, la, lb, (K2 + TB - 1) / TB, smem,
+                                                           p, [](int64_t) {});
+#pragma unroll
+    for (int i = 0; i < S::MB; ++i)
+#pragma unroll
+      for (int j = 0; j < S::NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc.v[i][j][r] *= g2.alpha;
+  }
+  const int64_t K = b + 1 == g.batch ? g.K_last : g.K;
+  auto la = make_loader<T, kLA, S::BM>(static_cast<const char*>(g.A) + b * g.sa * es, g.lda, g.sa,
+                                       b, m0, g.M, K);
+  auto lb = make_loader<T, kLB, S::BN>(static_cast<const char*>(g.B) + b * g.sb * es, g.ldb, g.sb,
+                                       b, n0, g.N, K);
+  mainloop<T, S, true, is_kmajor(kLA), is_kmajor(kLB)>(acc, la, lb, (K + TB - 1) / TB, smem, p,
+                                                       [](int64_t) {});
   if (g.c_f32)
     gemm_epilogue<S, float>(acc, p, smem, static_cast<float*>(g.C) + b * g.sc, g.ldc, m0, n0, g.M,
                             g.N, g.alpha, g.accumulate != 0);
@@ -161,30 +183,60 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 template <typename T>
-hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s) {
+hipError_t launch_gemm_t(const GemmArgs& g, const GemmArgs* g2, hipStream_t s) {
   const int64_t tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
   const dim3 grid((unsigned)tiles), block(512);
-  const int32_t combo = g.a_layout * 3 + g.b_layout;
+  const int32_t combo = g.a_layout * 8 + g.b_layout;
+  if (g2) {
+    // the fused pair the backward uses: dO W (K contiguous) + eta V^ S (tiles)
+    if (combo != kRowK * 8 + kRowK || g2->a_layout != kRowK || g2->b_layout != kTiledKMajor)
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_kernel<T, kRowK, kRowK, kRowK, kTiledKMajor>), grid, block, 0, s, g,
+                       *g2);
+    return hipGetLastError();
+  }
   switch (combo) {
-    case kRowK * 3 + kRowK:
-      hipLaunchKernelGGL((gemm_kernel<T, kRowK, kRowK>), grid, block, 0, s, g);
+    case kRowK * 8 + kRowK:
+      hipLaunchKernelGGL((gemm_kernel<T, kRowK, kRowK>), grid, block, 0, s, g, g);
       break;
-    case kRowK * 3 + kKMajor:
-      hipLaunchKernelGGL((gemm_kernel<T, kRowK, kKMajor>), grid, block, 0, s, g);
+    case kRowK * 8 + kKMajor:
+      hipLaunchKernelGGL((gemm_kernel<T, kRowK, kKMajor>), grid, block, 0, s, g, g);
       break;
-    case kKMajor * 3 + kRowK:
-      hipLaunchKernelGGL((gemm_kernel<T, kKMajor, kRowK>), grid, block, 0, s, g);
+    case kRowK * 8 + kTiledRowK:
+      hipLaunchKernelGGL((gemm_kernel<T, kRowK, kTiledRowK>), grid, block, 0, s, g, g);
       break;
-    case kKMajor * 3 + kKMajor:
-      hipLaunchKernelGGL((gemm_kernel<T, kKMajor, kKMajor>), grid, block, 0, s, g);
+    case kRowK * 8 + kTiledKMajor:
+      hipLaunchKernelGGL((gemm_kernel<T, kRowK, kTiledKMajor>), grid, block, 0, s, g, g);
       break;
-    case kKBlocked * 3 + kKBlocked:
-      hipLaunchKernelGGL((gemm_kernel<T, kKBlocked, kKBlocked>), grid, block, 0, s, g);
+    case kKMajor * 8 + kRowK:
+      hipLaunchKernelGGL((gemm_kernel<T, kKMajor, kRowK>), grid, block, 0, s, g, g);
+      break;
+    case kKMajor * 8 + kKMajor:
+      hipLaunchKernelGGL((gemm_kernel<T, kKMajor, kKMajor>), grid, block, 0, s, g, g);
+      break;
+    case kKBlocked * 8 + kKBlocked:
+      hipLaunchKernelGGL((gemm_kernel<T, kKBlocked, kKBlocked>), grid, block, 0, s, g, g);
       break;
     default:
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// Layout and size rules of one product (see GemmLayout).
+bool gemm_args_ok(const GemmArgs& g) {
+  const int64_t tb = 128 / (int64_t)dtype_bytes(g.dt);
+  // K-contiguous, k-blocked and tiled operands are read in whole k-tiles; the
+  // N runs of the epilogue are 8 wide
+  if ((g.a_layout != kKMajor || g.b_layout != kKMajor) && (g.K % tb != 0 || g.K_last % tb != 0))
+    return false;
+  if (g.N % 8 != 0 || g.K <= 0 || g.K_last <= 0) return false;
+  // tiled operands (B only): whole TB x TB tiles
+  if (g.a_layout == kTiledRowK || g.a_layout == kTiledKMajor) return false;
+  if ((g.b_layout == kTiledRowK || g.b_layout == kTiledKMajor) &&
+      (g.N % tb != 0 || g.ldb % tb != 0 || g.K_last != g.K))
+    return false;
+  return true;
 }
 
 // dst[j][i] = src[i][j], through a 64 x 64 LDS tile (padded against bank
@@ -211,14 +263,18 @@ __global__ __launch_bounds__(256) void transpose_rect_kernel(T* __restrict__ dst
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
-  const int64_t tb = 128 / (int64_t)dtype_bytes(g.dt);
-  // K-contiguous and k-blocked operands are read in whole k-tiles; the N runs
-  // of the epilogue are 8 wide
-  if ((g.a_layout != kKMajor || g.b_layout != kKMajor) && (g.K % tb != 0 || g.K_last % tb != 0))
+  if (!gemm_args_ok(g)) return hipErrorInvalidValue;
+  if (g.dt == Dtype::BF16) return launch_gemm_t<uint16_t>(g, nullptr, s);
+  return launch_gemm_t<float>(g, nullptr, s);
+}
+
+hipError_t launch_gemm2(const GemmArgs& g, const GemmArgs& g2, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
+  if (!gemm_args_ok(g) || !gemm_args_ok(g2) || g2.dt != g.dt || g2.M != g.M || g2.N != g.N ||
+      g2.batch != g.batch || g.accumulate)
     return hipErrorInvalidValue;
-  if (g.N % 8 != 0 || g.K <= 0 || g.K_last <= 0) return hipErrorInvalidValue;
-  if (g.dt == Dtype::BF16) return launch_gemm_t<uint16_t>(g, s);
-  return launch_gemm_t<float>(g, s);
+  if (g.dt == Dtype::BF16) return launch_gemm_t<uint16_t>(g, &g2, s);
+  return launch_gemm_t<float>(g, &g2, s);
 }
 
 hipError_t launch_transpose(const void* src, void* dst, int64_t rows, int64_t cols, Dtype dt,

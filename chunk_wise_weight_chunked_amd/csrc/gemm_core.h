@@ -553,6 +553,28 @@ struct DirectLoader {
       voff[q] = (uint32_t)(row * row_stride + c * 16);
     }
   }
+  // Rows grouped in blocks of `block_rows` rows of 128 bytes each, blocks
+  // `block_stride` bytes apart (tiled operands): row r at
+  // (r / block_rows) block_stride + (r % block_rows) 128.
+  __device__ __forceinline__ void init_blocked(const void* base_, int block_rows,
+                                               int64_t block_stride, int64_t kt_stride_,
+                                               int64_t valid_bytes_, int64_t kt_shrink_) {
+    base = static_cast<const char*>(base_);
+    kt_stride = kt_stride_;
+    valid_bytes = valid_bytes_;
+    kt_shrink = kt_shrink_;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    lds_row0 = (uint32_t)(wave * kRowsPerWave);
+    const int rr = lane >> 3;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int row = (int)lds_row0 + 8 * q + rr;
+      const int c = (lane & 7) ^ lds_swz(row);
+      voff[q] = (uint32_t)((row / block_rows) * block_stride + (row % block_rows) * kRowBytes +
+                           c * 16);
+    }
+  }
   // Descriptor of k-tile kt; live = false gives an empty range (every read
   // returns zero).
   __device__ __forceinline__ rsrc_t rsrc(int64_t kt, bool live = true) const {

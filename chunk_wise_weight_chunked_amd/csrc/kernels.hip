@@ -514,7 +514,11 @@ __global__ __launch_bounds__(256) void rows_to_vt_kernel(Dims dm, const T* __res
 // kSlots: which slot layouts are written -- bit 0: `slots` [G][B][d][f] (what
 // the outputs read); bit 1: `slots_t` [G][B][f][d], the weights transposed
 // (the backward's products that contract over d read them with K
-// contiguous).
+// contiguous); bit 2 (instead of bit 0): `slots` in TB x TB tiles, element
+// (m, n) of a slot at ((m / TB) (f / TB) + n / TB) TB^2 + (m % TB) TB + n % TB
+// with TB = 128 bytes of T -- every k-tile of a product that contracts over d
+// (k-major) or over f (rows of 128 bytes) is then whole 128-row blocks of
+// TB rows each, contiguous in memory.
 template <typename T, class S, int kSlots = 1>
 __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __restrict__ Vt,
                                                    const T* __restrict__ Zt,
@@ -580,8 +584,10 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
                               p.wave_n0 + ((p.lane & 31) & ~1)) * 2u;
   // store instructions per lane of one slot: row-major pairs (bf16) or
   // values (fp32); transposed, 4 consecutive rows of a column in one store
-  constexpr int kSlotStores = ((kSlots & 1) ? S::MB * 4 * S::NB * (sizeof(T) == 2 ? 2 : 4) : 0) +
-                              ((kSlots & 2) ? S::MB * 4 * S::NB : 0);
+  static_assert((kSlots & 5) != 5, "one layout in `slots`");
+  constexpr int kSlotStores =
+      ((kSlots & 5) ? S::MB * 4 * S::NB * (sizeof(T) == 2 ? 2 : 4) : 0) +
+      ((kSlots & 2) ? S::MB * 4 * S::NB : 0);
   const uint32_t lane_t = (uint32_t)(((p.wave_n0 + (p.lane & 31)) * d + p.wave_m0 +
                                       4 * (p.lane >> 5)) * (int64_t)sizeof(T));
   const uint32_t du = (uint32_t)d;
@@ -612,9 +618,64 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
         __builtin_amdgcn_sched_barrier(0);
       }
   };
+  // Tiled slots: the lane's part of the offset (its rows and columns inside a
+  // 32 x 32 block, and the wave's corner), and per block (i, q, j) a uniform
+  // part.  A wave's rows (columns) stay inside one tile row (column) of TB:
+  // the wave tiles start on multiples of TB, or a block of 32 is all a wave
+  // holds.
+  static_assert((32 * S::MB) % TB == 0 || S::MB == 1, "wave rows inside whole tiles");
+  static_assert((32 * S::NB) % TB == 0 || S::NB == 1, "wave columns inside whole tiles");
+  const int64_t fT = f / TB;
+  const int64_t corner_t = ((m0 / TB) * fT + n0 / TB) * TB * TB;
+  const uint32_t wave_t = (uint32_t)((p.wave_m0 / TB) * fT * TB * TB + (p.wave_m0 % TB) * TB +
+                                     (p.wave_n0 / TB) * TB * TB + p.wave_n0 % TB);
+  uint32_t lane_tl[4];  // bf16: pair rows r = 0, 1; fp32: rows e = 0..3
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    lane_tl[e] = sizeof(T) == 2
+                     ? wave_t + (uint32_t)((4 * (p.lane >> 5) + (odd ? 2 : 0) + (e & 1)) * TB +
+                                           ((p.lane & 31) & ~1))
+                     : wave_t + (uint32_t)((4 * (p.lane >> 5) + e) * TB + (p.lane & 31));
+  auto tiled_uniform = [&](int i, int q, int j) -> uint32_t {
+    const int r = 32 * i + 8 * q, c = 32 * j;
+    return (uint32_t)(((r / TB) * fT + c / TB) * TB * TB + (r % TB) * TB + c % TB);
+  };
+  auto write_slot_tiled = [&](int64_t js) {
+    const rsrc_t sr = make_rsrc(slots + js * slot_stride + b * d * f + corner_t,
+                                (d * f - corner_t) * (int64_t)sizeof(T));
+#pragma unroll
+    for (int i = 0; i < S::MB; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int j = 0; j < S::NB; ++j) {
+            const uint32_t so = tiled_uniform(i, q, j) * 2u;
+            float z[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[e] = acc.v[i][j][4 * q + e];
+            uint32_t w[2];
+            pair_pack(z, odd, w);
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+              __builtin_amdgcn_raw_buffer_store_b32(w[r], sr, lane_tl[r] * 2u, so, 0);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int j = 0; j < S::NB; ++j)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.v[i][j][4 * q + e]), sr,
+                                                    lane_tl[e] * 4u, tiled_uniform(i, q, j) * 4u,
+                                                    0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
   auto write_slot = [&](int64_t jj) {
     const int64_t js = dm.reverse_slots ? gc - 1 - jj : jj;
     if constexpr ((kSlots & 2) != 0) write_slot_t(js);
+    if constexpr ((kSlots & 4) != 0) write_slot_tiled(js);
     if constexpr ((kSlots & 1) == 0) return;
     const rsrc_t sr = make_rsrc(slots + js * slot_stride + b * d * f + corner,
                                 span * (int64_t)sizeof(T));
@@ -650,7 +711,7 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
   };
 
   // none: the increments' sum only
-  const bool with_slots = (kSlots & 1) ? slots != nullptr : slots_t != nullptr;
+  const bool with_slots = (kSlots & 5) ? slots != nullptr : slots_t != nullptr;
   if (with_slots) write_slot(0);
   const int64_t kt_per_chunk = dm.Cp / TB;
   // a streaming call leaves the sequence's last chunk out of the state (its
@@ -834,7 +895,8 @@ TTT_GEMM_KERNEL void scan_target_kernel(Dims dm, const T* __restrict__ Vt,
 // Two independent scans of all N chunks (the backward's forward weights and
 // its chunk-reversed gradient sums) in one launch: one group of all chunks
 // gives ~1.5 waves of tiles per scan, two together fill the chip better.  The
-// first writes its slots transposed (slots1t), the second row-major (slots2).
+// first writes its slots transposed (slots1t), the second in TB x TB tiles
+// (slots2; see prefix_update_tile).
 template <typename T>
 TTT_GEMM_KERNEL void dual_scan_kernel(Dims d1, const T* __restrict__ Vt1, const T* __restrict__ Zt1,
                                       float* __restrict__ W1, T* __restrict__ slots1t, Dims d2,
@@ -848,7 +910,7 @@ TTT_GEMM_KERNEL void dual_scan_kernel(Dims d1, const T* __restrict__ Vt1, const 
       prefix_update_tile<T, PrefixTile, 2>(d1, Vt1, Zt1, W1, nullptr, 0, d1.N, b, blocks,
                                            (lds_char*)smem_raw, slots1t);
   } else if (b - pad < blocks) {
-    prefix_update_tile<T, PrefixTile, 1>(d2, Vt2, Zt2, W2, slots2, 0, d2.N, b - pad, blocks,
+    prefix_update_tile<T, PrefixTile, 4>(d2, Vt2, Zt2, W2, slots2, 0, d2.N, b - pad, blocks,
                                          (lds_char*)smem_raw);
   }
 }
@@ -1222,7 +1284,7 @@ static void launch_dual_scan_t(const Dims& d1, const T* Vt1, const T* Zt1, float
     const dim3 grid((unsigned)((d1.d / Small::BM) * (d1.f / Small::BN) * d1.B));
     hipLaunchKernelGGL((prefix_update_kernel<T, Small, 2>), grid, dim3(Small::kThreads), 0, s, d1,
                        Vt1, Zt1, W1, static_cast<T*>(nullptr), (int64_t)0, d1.N, slots1t);
-    hipLaunchKernelGGL((prefix_update_kernel<T, Small, 1>), grid, dim3(Small::kThreads), 0, s, d2,
+    hipLaunchKernelGGL((prefix_update_kernel<T, Small, 4>), grid, dim3(Small::kThreads), 0, s, d2,
                        Vt2, Zt2, W2, slots2, (int64_t)0, d2.N, static_cast<T*>(nullptr));
     return;
   }

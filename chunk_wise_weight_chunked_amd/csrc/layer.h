@@ -130,11 +130,24 @@ hipError_t decode_scratch_ptr(void** out);
 //   kKMajor   X[r][k] at k * ld + r                  ([K][ld] row-major)
 //   kKBlocked X[r][k] at ((k / TB) * ld + r) * TB + k % TB  (ld = rows per
 //             block: the k-blocked token-major layouts, K = token columns)
+//   kTiledRowK   X[r][k] at ((r / TB) (ld / TB) + k / TB) TB^2 + (r % TB) TB
+//             + k % TB  (TB x TB tiles, K contiguous inside; ld = K)
+//   kTiledKMajor X[r][k] at ((k / TB) (ld / TB) + r / TB) TB^2 + (k % TB) TB
+//             + r % TB  (the same tiles of a [K][ld] matrix; ld = row count)
+// (a weight slot in tiles, [d/TB][f/TB][TB][TB], is kTiledRowK with r = d,
+// k = f and kTiledKMajor with k = d, r = f).  Tiled operands need their row
+// count and ld to be multiples of TB and whole matrices between batches.
 // Element offsets between batches sa, sb, sc (for kKBlocked, a row offset
 // r0 * TB or whole blocks); the last batch contracts K_last values (split
-// products: batch = K slice).  kRowK and kKBlocked need K and K_last to be
-// multiples of TB; N a multiple of 8.
-enum GemmLayout : int32_t { kRowK = 0, kKMajor = 1, kKBlocked = 2 };
+// products: batch = K slice).  kRowK, kKBlocked and the tiled layouts need K
+// and K_last to be multiples of TB; N a multiple of 8.
+enum GemmLayout : int32_t {
+  kRowK = 0,
+  kKMajor = 1,
+  kKBlocked = 2,
+  kTiledRowK = 3,
+  kTiledKMajor = 4
+};
 struct GemmArgs {
   Dtype dt;
   const void* A;
@@ -150,6 +163,11 @@ struct GemmArgs {
   float alpha;
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
+// C[b] = g.alpha (A[b] B[b]ᵀ + g2.alpha A2[b] B2[b]ᵀ) from g's and g2's
+// operands, g's output, M, N and batch (g2's must agree); the second product
+// runs first on the same accumulators and C is written once.  Only the pair
+// (kRowK, kRowK) + (kRowK, kTiledKMajor) is built.
+hipError_t launch_gemm2(const GemmArgs& g, const GemmArgs& g2, hipStream_t s);
 // dst [cols][rows] = srcᵀ for src [rows][cols] of element type dt.
 hipError_t launch_transpose(const void* src, void* dst, int64_t rows, int64_t cols, Dtype dt,
                             hipStream_t s);
@@ -166,8 +184,9 @@ hipError_t launch_to_kblocked(const void* src, void* dst, const Dims& dm, int64_
 hipError_t launch_swiglu_rows(const float* Ag, const float* Au, int64_t ld, void* Z,
                               const Dims& dm, hipStream_t s);
 // The scans of two independent problems (same shapes) in one launch: the
-// first writes its slots transposed ([N][B][f][d], slots1t), the second
-// row-major (slots2).
+// first writes its slots transposed ([N][B][f][d], slots1t), the second in
+// tiles of TB x TB (slots2: [N][B][d/TB][f/TB][TB][TB], TB = 128 bytes of the
+// type).
 hipError_t launch_dual_scan(const Dims& d1, const void* Vt1, const void* Zt1, float* W1,
                             void* slots1t, const Dims& d2, const void* Vt2, const void* Zt2,
                             float* W2, void* slots2, hipStream_t s);
