@@ -40,20 +40,38 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _group_tokens(w, group: int) -> list:
-    """Tokens (all sequences) in each group of `group` chunks."""
+def _launches(w, group: int, split: bool, per_chunk: bool) -> list:
+    """The group pipeline's launches in order, as the library issues them:
+    (stage, (scan tokens, scan chunks), (output tokens, output chunks)), token
+    and chunk counts over all sequences.  Launch g scans group g and computes
+    the outputs of group g - 1; sequential mode (per_chunk) scans one chunk
+    per launch, the first chunk's launch carrying the previous group's
+    outputs.  split: the first launch also projects the later tokens."""
     B, T, C, N = w.batch, w.seq_len, w.chunk, w.n_chunks
+
+    def toks(c0, cn):
+        return B * (min(T, (c0 + cn) * C) - c0 * C)
+
     groups = -(-N // group)
-    return [B * (min(T, (g + 1) * group * C) - g * group * C) for g in range(groups)]
-
-
-def _per_launch(scan, apply, toks) -> dict:
-    """Per-launch averages of the group pipeline's three launch kinds, given
-    the work of one group's scan and outputs as functions of its tokens."""
-    n = len(toks)
-    out = {"prefix_update": scan(toks[0]), "down_proj": apply(toks[-1])}
-    if n > 1:
-        out["scan_apply"] = sum(scan(toks[g]) + apply(toks[g - 1]) for g in range(1, n)) / (n - 1)
+    out = []
+    for g in range(groups + 1):
+        g0, a0 = g * group, (g - 1) * group
+        gc = min(group, N - g0) if g < groups else 0
+        ac = min(group, N - a0) if g > 0 else 0
+        apply = (toks(a0, ac), ac * B) if ac else (0, 0)
+        if per_chunk and gc > 1:
+            for j in range(gc):
+                o = apply if j == 0 else (0, 0)
+                kind = "scan_target" if (g == 0 and j == 0 and split) else \
+                    ("scan_apply" if o[0] else "prefix_update")
+                out.append((kind, (toks(g0 + j, 1), B), o))
+            continue
+        scan = (toks(g0, gc), gc * B) if gc else (0, 0)
+        if g == 0 and split:
+            kind = "scan_target"
+        else:
+            kind = "scan_apply" if gc and ac else ("prefix_update" if gc else "down_proj")
+        out.append((kind, scan, apply))
     return out
 
 
@@ -63,24 +81,35 @@ def _split_tokens(w, group: int) -> int:
     return w.batch * min(w.seq_len, group * w.chunk)
 
 
-def stage_work(w, group: int, split: bool = False) -> dict:
+def _pipeline_average(w, group, split, per_chunk, scan_cost, apply_cost) -> dict:
+    """Per-launch averages over each pipeline stage's launches."""
+    tot, cnt = {}, {}
+    for kind, scan, apply in _launches(w, group, split, per_chunk):
+        c = (scan_cost(*scan) if scan[0] else 0.0) + (apply_cost(*apply) if apply[0] else 0.0)
+        tot[kind] = tot.get(kind, 0.0) + c
+        cnt[kind] = cnt.get(kind, 0) + 1
+    return {k: tot[k] / cnt[k] for k in tot}
+
+
+def stage_work(w, group: int, split: bool = False, per_chunk: bool = False) -> dict:
     """Algorithmic flops per launch of each kernel.  split: the first group's
-    scan ran next to the projection of the later tokens (scan_target)."""
+    scan ran next to the projection of the later tokens (scan_target);
+    per_chunk: sequential mode's schedule."""
     B, T, d, f = w.batch, w.seq_len, w.d_model, w.d_ff
     tok = B * T
     out = {"swiglu": 4.0 * tok * d * f, "target": 2.0 * tok * d * d}
-    out.update(_per_launch(lambda t: 2.0 * t * d * f, lambda t: 2.0 * t * d * f,
-                           _group_tokens(w, group)))
+    out.update(_pipeline_average(w, group, split, per_chunk, lambda t, n: 2.0 * t * d * f,
+                                 lambda t, n: 2.0 * t * d * f))
     if split:
         t0 = _split_tokens(w, group)
         out["target"] = 2.0 * t0 * d * d
-        out["scan_target"] = out.pop("prefix_update") + 2.0 * (tok - t0) * d * d
+        out["scan_target"] += 2.0 * (tok - t0) * d * d
     return out
 
 
-def stage_bytes(w, group: int, split: bool = False) -> dict:
+def stage_bytes(w, group: int, split: bool = False, per_chunk: bool = False) -> dict:
     """Algorithmic HBM bytes per launch of each kernel: every operand read once
-    and every result written once (the fp32 state once per group)."""
+    and every result written once (the fp32 state once per scan launch)."""
     B, T, C, d, f = w.batch, w.seq_len, w.chunk, w.d_model, w.d_ff
     e = 2 if w.dtype == torch_bf16() else 4
     tok = B * T
@@ -89,17 +118,14 @@ def stage_bytes(w, group: int, split: bool = False) -> dict:
         "swiglu": e * tok * (d + f) + e * 2 * f * d,
         "target": e * tok * 2 * d + e * d * d,
     }
-
-    def slots(t):  # chunks (over all sequences) in a group of t tokens
-        return -(-t // (B * C)) * B
-
-    out.update(_per_launch(lambda t: e * t * (d + f) + e * slots(t) * d * f + 8 * B * d * f,
-                           lambda t: e * t * (f + d) + e * slots(t) * d * f,
-                           _group_tokens(w, group)))
+    out.update(_pipeline_average(
+        w, group, split, per_chunk,
+        lambda t, n: e * t * (d + f) + e * n * d * f + 8 * B * d * f,
+        lambda t, n: e * t * (f + d) + e * n * d * f))
     if split:
         t0 = _split_tokens(w, group)
         out["target"] = e * t0 * 2 * d + e * d * d
-        out["scan_target"] = out.pop("prefix_update") + e * (tok - t0) * 2 * d + e * d * d
+        out["scan_target"] += e * (tok - t0) * 2 * d + e * d * d
     return out
 
 
@@ -491,11 +517,12 @@ def main() -> int:
     log(f"[bench] {ms_step:.3f} ms/step (median {ms_median:.3f}), {value / 1e6:.3f} M tokens/s")
 
     split = stages.get("scan_target", (0.0, 0))[1] > 0
-    work = stage_work(w, group, split)
+    per_chunk = args.mode == "sequential"
+    work = stage_work(w, group, split, per_chunk)
     proj = args.target in ("conv_proj", "proj")
     if not proj:
         work.pop("target")  # no projection GEMM: the stage only moves rows
-    nbytes = stage_bytes(w, group, split)
+    nbytes = stage_bytes(w, group, split, per_chunk)
     if not proj:  # the stage reads X0 and writes one row per token, no weight
         nbytes["target"] = (2 if dtype == "bf16" else 4) * w.tokens * 2 * d
     per_stage = {}

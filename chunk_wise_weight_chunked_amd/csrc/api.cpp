@@ -195,8 +195,9 @@ constexpr int64_t kAutoGroups = 4;
 // descriptor needs does not depend on the device.
 constexpr int64_t kAutoOneGroupTiles = 1024;
 
+// Sequential mode takes auto's groups for its slots (the state itself still
+// goes through memory after every chunk; see run_layer).
 int64_t mode_group(const ttt::Dims& dm, ttt_mode_t mode) {
-  if (mode == TTT_MODE_SEQUENTIAL) return 1;
   if (mode == TTT_MODE_CHUNK_PARALLEL) return dm.N;
   const int64_t scan_tiles = dm.B * ((dm.d + 255) / 256) * ((dm.f + 255) / 256);
   if (scan_tiles >= kAutoOneGroupTiles) return dm.N;
@@ -311,6 +312,13 @@ ttt_status_t run_layer(const ttt::Dims& dm, ttt_mode_t mode, bool reset, const v
   }
   // Group pipeline: launch g scans group g (slot set g & 1) and computes the
   // outputs of group g - 1 (the other set, completed by launch g - 1).
+  // Sequential mode scans one chunk per launch instead -- the fp32 state is
+  // read from and written back to W_state for every chunk, as the sequential
+  // form of the recurrence has it -- and computes the outputs of group g - 1
+  // in the launch of group g's first chunk; with groups of one chunk the two
+  // schedules are the same.  Either way each chunk's slot holds the weight
+  // its outputs use, and the state's fp32 sums run in the same order.
+  const bool per_chunk = mode == TTT_MODE_SEQUENTIAL;
   const size_t set_bytes = (size_t)G * wp.slot_bytes;
   for (int64_t g = 0; g <= groups; ++g) {
     const int64_t g0 = g * G, gc = g < groups ? std::min<int64_t>(G, dm.N - g0) : 0;
@@ -318,6 +326,26 @@ ttt_status_t run_layer(const ttt::Dims& dm, ttt_mode_t mode, bool reset, const v
     char* scan_slots = static_cast<char*>(slots) + (g & 1) * (wp.slot_sets > 1 ? set_bytes : 0);
     const char* apply_slots =
         static_cast<char*>(slots) + ((g - 1) & 1) * (wp.slot_sets > 1 ? set_bytes : 0);
+    if (per_chunk && gc > 1) {
+      for (int64_t j = 0; j < gc; ++j) {
+        char* sj = scan_slots + j * (size_t)(dm.B * dm.d * dm.f) * ttt::dtype_bytes(dm.dt);
+        if (g == 0 && j == 0 && split) {
+          e = staged(kScanTarget, s, [&] {
+            return ttt::launch_scan_target(dm, Vt, Zt, W_state, sj, 1, dm.conv ? U : X0, WtT,
+                                           t_split, s);
+          });
+          if (e != hipSuccess) return hip_fail(e, "scan_target");
+          continue;
+        }
+        const int64_t jc = j == 0 ? ac : 0;  // outputs of group g - 1 with the first chunk
+        e = staged(jc > 0 ? kScanApply : kPrefix, s, [&] {
+          return ttt::launch_scan_apply(dm, Vt, Zt, W_state, sj, g0 + j, 1, Z, apply_slots, O, a0,
+                                        jc, s);
+        });
+        if (e != hipSuccess) return hip_fail(e, "scan_apply");
+      }
+      continue;
+    }
     if (g == 0 && split) {
       e = staged(kScanTarget, s, [&] {
         return ttt::launch_scan_target(dm, Vt, Zt, W_state, scan_slots, gc, dm.conv ? U : X0, WtT,

@@ -70,9 +70,13 @@ typedef enum {
  * the exclusive prefix of the per-chunk increments through the fp32 state and
  * writes the weight each chunk uses into a slot; the group's outputs are then
  * computed from its slots, in the same launch as the next group's scan.
- *   SEQUENTIAL      G = 1: output with the current state, then one
- *                   read-modify-write of the state per chunk (section 3.2
- *                   schedule);
+ *   SEQUENTIAL      one read-modify-write of the fp32 state in memory per
+ *                   chunk (the chunk-by-chunk schedule of section 3.2): each
+ *                   chunk's scan is a launch of its own, which writes the
+ *                   chunk's slot and the state; a group's outputs run in the
+ *                   launch of the next group's first chunk.  Groups as in
+ *                   AUTO (G = 1: outputs of chunk i - 1 beside the update of
+ *                   chunk i);
  *   CHUNK_PARALLEL  G as large as the workspace holds, up to all chunks (the
  *                   three-step form of section 3.2);
  *   AUTO            chunk-parallel in four groups (fewer if the workspace is
@@ -144,8 +148,8 @@ typedef struct {
 } ttt_mlp_desc_t;
 
 /* Workspace bytes needed for groups of up to `max_group` chunks (0 = the
- * mode's own group: 1 sequential, all ceil(T/C) chunks chunk-parallel, a
- * quarter of them (rounded up) auto).  The workspace holds the activations in
+ * mode's own group: all ceil(T/C) chunks chunk-parallel, a quarter of them
+ * (rounded up) auto and sequential).  The workspace holds the activations in
  * the layouts the kernels read, the prepared weights, and one weight slot
  * (B * d * f elements) per chunk of a group, twice over when there is more
  * than one group.  Returns 0 if the descriptor is invalid (see
@@ -153,7 +157,7 @@ typedef struct {
 size_t ttt_mlp_workspace_size(const ttt_mlp_desc_t* desc, int64_t max_group);
 
 /* Chunks per group the planner would use for this descriptor and workspace
- * size (1 in sequential mode), or a negative ttt_status_t. */
+ * size, or a negative ttt_status_t. */
 int64_t ttt_mlp_group_size(const ttt_mlp_desc_t* desc, size_t ws_bytes);
 
 /* One sequence (B == 1), starting from W_down0.

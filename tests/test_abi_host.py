@@ -55,7 +55,7 @@ def test_workspace_plan():
     assert tm.ttt_mlp_workspace_size(d, 3) == fixed + 2 * 3 * slot
     cp, seq = desc(mode="chunk_parallel"), desc(mode="sequential")
     assert tm.ttt_mlp_workspace_size(cp, 0) == w_all
-    assert tm.ttt_mlp_workspace_size(seq, 0) == w1
+    assert tm.ttt_mlp_workspace_size(seq, 0) == tm.ttt_mlp_workspace_size(d, 0)  # auto's groups
     # auto takes a quarter of the chunks at most
     assert tm.ttt_mlp_group_size(d, w_all) == 2
     assert tm.ttt_mlp_group_size(d, w1) == 1
@@ -64,7 +64,8 @@ def test_workspace_plan():
     assert tm.ttt_mlp_group_size(cp, w_all) == 8
     assert tm.ttt_mlp_group_size(cp, w_all - 1) == 3  # 7 slots: 2 sets of 3
     assert tm.ttt_mlp_group_size(cp, w1) == 1
-    assert tm.ttt_mlp_group_size(seq, w_all) == 1
+    assert tm.ttt_mlp_group_size(seq, w_all) == 2
+    assert tm.ttt_mlp_group_size(seq, w1) == 1
     with pytest.raises(tm.TTTError) as e:
         tm.ttt_mlp_group_size(d, w1 - 1)
     assert e.value.status == tm.TTT_ERR_WORKSPACE_TOO_SMALL

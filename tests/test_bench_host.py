@@ -37,6 +37,29 @@ def test_stage_work_and_bytes_of_the_benchmark_workload():
     assert sum(sw[k] for k in ("target", "scan_target")) == work["target"] + work["prefix_update"]
 
 
+def test_sequential_schedule_accounting():
+    """Sequential mode scans one chunk per launch (the fp32 state read and
+    written every time) and computes a group's outputs in the launch of the
+    next group's first chunk."""
+    w = synth.WORKLOADS["qwen3_4b_128k"]
+    d, f, C = w.d_model, w.d_ff, w.chunk
+    kinds = [k for k, _, _ in bench._launches(w, 32, False, True)]
+    assert len(kinds) == 128 + 1
+    assert kinds.count("scan_apply") == 3 and kinds.count("down_proj") == 1
+    assert kinds.count("prefix_update") == 125
+    work = bench.stage_work(w, 32, per_chunk=True)
+    nbytes = bench.stage_bytes(w, 32, per_chunk=True)
+    assert work["prefix_update"] == 2.0 * C * d * f
+    assert work["scan_apply"] == 2.0 * C * d * f + 2.0 * 32 * C * d * f
+    assert work["down_proj"] == 2.0 * 32 * C * d * f
+    assert nbytes["prefix_update"] == 2 * C * (d + f) + 2 * d * f + 8 * d * f
+    # with groups of one chunk the two schedules are the same
+    assert bench._launches(w, 1, False, True) == bench._launches(w, 1, False, False)
+    # split: the first chunk's launch projects the tokens after the first group
+    sw = bench.stage_work(w, 32, split=True, per_chunk=True)
+    assert sw["scan_target"] == 2.0 * C * d * f + 2.0 * (w.seq_len - 32 * C) * d * d
+
+
 @pytest.mark.parametrize("name,stage,hbm", [
     ("qwen3_4b_128k", "swiglu", False),
     ("qwen3_4b_128k", "scan_apply", False),   # C = 1024: about 650 flop/B

@@ -113,8 +113,10 @@ def _inp_small(dtype=torch.bfloat16, B=2, T=600, d=128, f=256, K=4, seed=5):
 def test_modes_and_group_sizes_bitwise_equal(dtype):
     dev = _inp_small(dtype)
     ref = run_gpu(dev, 1e-2, 64, mode="chunk_parallel")
-    for mode, g in (("sequential", 0), ("chunk_parallel", 1), ("chunk_parallel", 3),
-                    ("auto", 0)):
+    # sequential: groups of 3 (its default here: 10 chunks) and of 1 -- one
+    # launch per chunk's update either way, the outputs batched per group
+    for mode, g in (("sequential", 0), ("sequential", 1), ("chunk_parallel", 1),
+                    ("chunk_parallel", 3), ("auto", 0)):
         O, W = run_gpu(dev, 1e-2, 64, mode=mode, max_group=g)
         assert np.array_equal(O, ref[0]) and np.array_equal(W, ref[1]), (mode, g)
 
@@ -122,7 +124,8 @@ def test_modes_and_group_sizes_bitwise_equal(dtype):
 @pytest.mark.parametrize("target,T,C,dtype,split_group",
                          [("conv_proj", 1300, 64, torch.bfloat16, 8),
                           ("proj", 1300, 100, torch.bfloat16, 6),
-                          ("conv_proj", 1300, 100, torch.float32, 6)])
+                          ("conv_proj", 1300, 100, torch.float32, 6),
+                          ("conv_proj", 1300, 256, torch.bfloat16, 2)])
 def test_projection_split_bitwise_equal(target, T, C, dtype, split_group):
     """With 256-divisible weights, more than one group and a first group of at
     least 2 d tokens, the projection of the later tokens runs inside the first
@@ -149,8 +152,19 @@ def test_projection_split_bitwise_equal(target, T, C, dtype, split_group):
 
     ref = run("chunk_parallel", 0)  # one group: no split
     assert not ref[2]
-    for mode, g, expect_split in (("chunk_parallel", split_group, True), ("sequential", 0, False),
-                                  ("auto", 0, False)):
+    # auto and sequential mode take a quarter of the chunks per group at most
+    # (sequential scans them one chunk per launch; its first chunk's launch
+    # carries the projection); the split needs a group of 2 d tokens or more
+    N = -(-T // C)
+
+    def splits(g):
+        return g * C >= 2 * d and -(-N // g) > 1
+
+    quarter = -(-N // 4)
+    for mode, g, expect_split in (("chunk_parallel", split_group, True),
+                                  ("sequential", 0, splits(quarter)),
+                                  ("sequential", split_group, splits(min(quarter, split_group))),
+                                  ("auto", 0, splits(quarter))):
         O, W, split = run(mode, g)
         assert split == expect_split, (mode, g)
         assert np.array_equal(O, ref[0]) and np.array_equal(W, ref[1]), (mode, g)
