@@ -52,6 +52,7 @@ namespace ttt {
 #define TTT_GEMM_WPE (TTT_WAVES_M * TTT_WAVES_N / 4)
 using Tile = TileShape<256, 256, TTT_WAVES_M, TTT_WAVES_N>;
 using PrefixTile = Tile;
+using OneChunkTile = TileShape<128, 128, 2, 2>;  // single-chunk updates
 #define TTT_GEMM_KERNEL                                  \
   __global__ __launch_bounds__(TTT_GEMM_THREADS)          \
   __attribute__((amdgpu_waves_per_eu(TTT_GEMM_WPE, TTT_GEMM_WPE)))
@@ -748,8 +749,10 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
     }
 }
 
-template <typename T, class S, int kSlots = 1>
-__global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::kWaves / 4, S::kWaves / 4))) void prefix_update_kernel(
+// kOcc: workgroups meant to share a CU (the register budget follows).
+template <typename T, class S, int kSlots = 1, int kOcc = 1>
+__global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(
+    kOcc * S::kWaves / 4, kOcc * S::kWaves / 4))) void prefix_update_kernel(
     Dims dm, const T* __restrict__ Vt, const T* __restrict__ Zt, float* __restrict__ W_state,
     T* __restrict__ slots, int64_t g0, int64_t gc, T* __restrict__ slots_t) {
   __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
@@ -1233,6 +1236,16 @@ static void launch_scan_apply_t(const Dims& dm, const T* Vt, const T* Zt, float*
   const int64_t down_tiles = ac > 0 ? ((dm.C + Tile::BM - 1) / Tile::BM) *
                                           ((dm.d + Tile::BN - 1) / Tile::BN) * ac * dm.B
                                     : 0;
+  if (gc == 1 && ac == 0 && dm.d % OneChunkTile::BM == 0 && dm.f % OneChunkTile::BN == 0) {
+    // one chunk's update alone (sequential mode): 128 x 128 tiles, two
+    // workgroups per CU, so that one's state load and store overlap the
+    // other's MFMAs, and four times the tiles to spread over the CUs
+    hipLaunchKernelGGL((prefix_update_kernel<T, OneChunkTile, 1, 2>),
+                       dim3((unsigned)((dm.d / OneChunkTile::BM) * (dm.f / OneChunkTile::BN) * dm.B)),
+                       dim3(OneChunkTile::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, g0, gc,
+                       static_cast<T*>(nullptr));
+    return;
+  }
   if (dm.d % PrefixTile::BM == 0 && dm.f % PrefixTile::BN == 0) {
     const int64_t scan = gc > 0 ? (dm.d / PrefixTile::BM) * (dm.f / PrefixTile::BN) * dm.B : 0;
     const int64_t pad = (scan + 7) / 8 * 8;

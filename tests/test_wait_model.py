@@ -130,7 +130,11 @@ def test_scan_kernels_leave_only_stores_in_flight(tmp_path):
     src = os.path.join(hipbuild.CSRC, "kernels.hip")
     funcs = _functions(_compile(src, str(tmp_path / "kernels.s")))
     checked = 0
-    for key in SCAN_KERNELS:
+    # the scan launches, and every instantiation of the scan-only kernel
+    # (tile shapes, slot layouts, data types)
+    prefix = [n for n in funcs if "prefix_update_kernel" in n]
+    assert len(prefix) >= 4, prefix
+    for key in SCAN_KERNELS + prefix:
         body = _body(funcs, key)
         for i, line in enumerate(body):
             m = WAIT_VM.match(line)
@@ -152,5 +156,6 @@ def test_scan_kernels_leave_only_stores_in_flight(tmp_path):
             assert len(prev) == n and all(VMEM.match(l).group(2) == "store" for l in prev), (
                 key, i, n, [l.strip() for l in prev if VMEM.match(l).group(2) != "store"][:4])
             checked += 1
-    # every scan kernel (two data types, three launch forms) has its store wait
-    assert checked >= len(SCAN_KERNELS), checked
+    # every scan kernel (two data types, three launch forms, the scan-only
+    # instantiations) has its store wait
+    assert checked >= len(SCAN_KERNELS) + len(prefix), checked
