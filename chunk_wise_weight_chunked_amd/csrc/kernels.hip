@@ -842,29 +842,31 @@ TTT_GEMM_KERNEL void down_proj_kernel(Dims dm, const T* __restrict__ Z,
 }
 
 // ============================================================== S4 + S3
-// One launch of the group pipeline: workgroups [0, scan_blocks) run the scan
-// tiles of chunks g0.. (dispatched first: they are the long ones), workgroups
-// [scan_blocks, scan_pad) exit at once (scan_pad rounds up to a multiple of
-// 8), the rest compute the outputs of chunks a0.. of the previous group,
-// whose slots the previous launch completed.
+// One launch of the group pipeline: the scan tiles of chunks g0.. and the
+// outputs of chunks a0.. of the previous group, whose slots the previous
+// launch completed.  The longer kind of tile is dispatched first (the scan's
+// k-loop is the group's tokens, the outputs' is f): workgroups [0, n1) run
+// it, [n1, pad) exit at once (pad rounds n1 up to a multiple of 8, so the
+// second kind starts on XCD 0), the rest run the other kind.
 template <typename T>
 TTT_GEMM_KERNEL void scan_apply_kernel(Dims dm, const T* __restrict__ Vt, const T* __restrict__ Zt,
                                        float* __restrict__ W_state, T* __restrict__ scan_slots,
-                                       int64_t g0, int64_t gc, int scan_blocks, int scan_pad,
+                                       int64_t g0, int64_t gc, int n1, int pad, int outputs_first,
                                        const T* __restrict__ Z, const T* __restrict__ apply_slots,
                                        T* __restrict__ O, int64_t a0, int64_t ac) {
   static_assert(Tile::kThreads == PrefixTile::kThreads && Tile::kLdsBytes == PrefixTile::kLdsBytes,
                 "both parts share the launch shape");
   __shared__ __attribute__((aligned(16))) char smem_raw[Tile::kLdsBytes];
   const int b = blockIdx.x;
-  if (b < scan_pad) {
-    if (b < scan_blocks)
-      prefix_update_tile<T, PrefixTile>(dm, Vt, Zt, W_state, scan_slots, g0, gc, b, scan_blocks,
-                                        (lds_char*)smem_raw);
-    return;
-  }
-  down_proj_tile<T>(dm, Z, apply_slots, O, a0, ac, b - scan_pad, (int)gridDim.x - scan_pad,
-                    (lds_char*)smem_raw);
+  const int n2 = (int)gridDim.x - pad;
+  const bool first = b < pad;
+  if (first && b >= n1) return;
+  const int blk = first ? b : b - pad, nblk = first ? n1 : n2;
+  if (first != (outputs_first != 0))
+    prefix_update_tile<T, PrefixTile>(dm, Vt, Zt, W_state, scan_slots, g0, gc, blk, nblk,
+                                      (lds_char*)smem_raw);
+  else
+    down_proj_tile<T>(dm, Z, apply_slots, O, a0, ac, blk, nblk, (lds_char*)smem_raw);
 }
 
 // The first launch of the group pipeline when the projection of later
@@ -1248,11 +1250,15 @@ static void launch_scan_apply_t(const Dims& dm, const T* Vt, const T* Zt, float*
   }
   if (dm.d % PrefixTile::BM == 0 && dm.f % PrefixTile::BN == 0) {
     const int64_t scan = gc > 0 ? (dm.d / PrefixTile::BM) * (dm.f / PrefixTile::BN) * dm.B : 0;
-    const int64_t pad = (scan + 7) / 8 * 8;
-    if (pad + down_tiles == 0) return;
-    hipLaunchKernelGGL(scan_apply_kernel<T>, dim3((unsigned)(pad + down_tiles)),
-                       dim3(Tile::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, g0, gc,
-                       (int)scan, (int)pad, Z, apply_slots, O, a0, ac);
+    if (scan + down_tiles == 0) return;
+    // longest first: a scan tile runs over the group's gc * Cp tokens, an
+    // output tile over the f features
+    const bool outputs_first = down_tiles > 0 && scan > 0 && gc * dm.Cp < dm.f;
+    const int64_t n1 = outputs_first ? down_tiles : scan, n2 = outputs_first ? scan : down_tiles;
+    const int64_t pad = (n1 + 7) / 8 * 8;
+    hipLaunchKernelGGL(scan_apply_kernel<T>, dim3((unsigned)(pad + n2)), dim3(Tile::kThreads), 0,
+                       s, dm, Vt, Zt, W_state, scan_slots, g0, gc, (int)n1, (int)pad,
+                       outputs_first ? 1 : 0, Z, apply_slots, O, a0, ac);
     return;
   }
   // 64 x 64 scan tiles when 256 does not divide the weight (d and f are

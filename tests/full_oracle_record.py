@@ -6,7 +6,10 @@ default group pipeline), the oracle runs the sequential form over every token,
 and the relative errors of O, of the final weight and of its change are
 printed, with the worst chunk of O.
 
-    python tests/full_oracle_record.py [workload ...]
+    python tests/full_oracle_record.py [workload ...] [--sessions a:b]
+
+--sessions a:b compares sequences a..b-1 only (the GPU still runs the whole
+batch, as the benchmark does): the oracle's time is split over several runs.
 """
 import os
 import sys
@@ -28,8 +31,9 @@ from _common import numpy_inputs, rel, to_device, tol_for  # noqa: E402
 DEFAULT = ["qwen3_4b_32k", "qwen3_4b_128k", "multi_session_16x8k", "small_4x128k"]
 
 
-def record(name: str) -> bool:
+def record(name: str, sessions=None) -> bool:
     w = synth.WORKLOADS[name]
+    b0, b1 = sessions if sessions else (0, w.batch)
     print(f"[record] {name}: inputs", flush=True)
     inp = synth.workload_inputs(w)
     dev = to_device(inp)
@@ -41,8 +45,11 @@ def record(name: str) -> bool:
     del O, W, dev
     torch.cuda.empty_cache()
     ni = numpy_inputs(inp)
-    print(f"[record] {name}: oracle (sequential, fp64, {oracle.num_threads()} threads)",
-          flush=True)
+    if (b0, b1) != (0, w.batch):
+        ni = dict(ni, H=ni["H"][b0:b1], X0=ni["X0"][b0:b1])
+        O_gpu, W_gpu = O_gpu[b0:b1], W_gpu[b0:b1]
+    print(f"[record] {name}: sequences {b0}..{b1 - 1}: oracle (sequential, fp64, "
+          f"{oracle.num_threads()} threads)", flush=True)
     oracle.set_progress(max(1, w.n_chunks // 8))
     t0 = time.perf_counter()
     Oo, Wo = oracle.forward(ni["H"], ni["X0"], ni["W_gate"], ni["W_up"], ni["W_down0"],
@@ -54,7 +61,7 @@ def record(name: str) -> bool:
     e_o, e_w, e_dw = rel(O_gpu, Oo), rel(W_gpu, Wo), rel(W_gpu - W0, Wo - W0)
     C = w.chunk
     worst = max(rel(O_gpu[b, i:i + C], Oo[b, i:i + C])
-                for b in range(w.batch) for i in range(0, w.seq_len, C))
+                for b in range(b1 - b0) for i in range(0, w.seq_len, C))
     tol = tol_for(w.dtype)
     ok = max(e_o, e_w, e_dw) <= tol
     print(f"[record] {name}: rel O {e_o:.3e}  rel W_final {e_w:.3e}  rel dW {e_dw:.3e}  "
@@ -64,10 +71,17 @@ def record(name: str) -> bool:
 
 
 def main() -> int:
-    names = sys.argv[1:] or DEFAULT
+    args = sys.argv[1:]
+    sessions = None
+    if "--sessions" in args:
+        i = args.index("--sessions")
+        a, b = args[i + 1].split(":")
+        sessions = (int(a), int(b))
+        del args[i:i + 2]
+    names = args or DEFAULT
     oracle.build(force=False)
     tm.load()
-    results = [record(n) for n in names]
+    results = [record(n, sessions) for n in names]
     return 0 if all(results) else 1
 
 

@@ -125,37 +125,144 @@ def test_compiler_counts_loads_and_stores_in_issue_order(tmp_path):
 SCAN_KERNELS = ["scan_apply_kernelIt", "scan_apply_kernelIf", "scan_target_kernelIt",
                 "scan_target_kernelIf", "dual_scan_kernelIt", "dual_scan_kernelIf"]
 
+LABEL = re.compile(r"^(\.LBB\w+):")
+BRANCH = re.compile(r"^\s*s_(branch|cbranch\w*)\s+(\.LBB\w+)")
+END = re.compile(r"^\s*s_(endpgm|setpc_b64|trap)\b")
+VMEM_ANY = re.compile(r"^\s*(buffer|global|flat|scratch)_(\w+)")
+
+
+def _blocks(body):
+    """Basic blocks of a kernel body: [line indices], successor block indices."""
+    blocks, names = [[]], {}
+    for at, line in enumerate(body):
+        m = LABEL.match(line)
+        if m:
+            if blocks[-1]:
+                blocks.append([])
+            names[m.group(1)] = len(blocks) - 1
+            continue
+        blocks[-1].append(at)
+        if BRANCH.match(line) or END.match(line):
+            blocks.append([])
+    succ = []
+    for i, idx in enumerate(blocks):
+        last = body[idx[-1]] if idx else ""
+        m, out = BRANCH.match(last), []
+        if m:
+            out.append(names[m.group(2)])
+        if not END.match(last) and not (m and m.group(1) == "branch") and i + 1 < len(blocks):
+            out.append(i + 1)
+        succ.append(out)
+    return blocks, succ
+
+
+def _vmem_kind(line):
+    m = VMEM_ANY.match(line)
+    if not m:
+        return None
+    op = m.group(2)
+    return "L" if op.startswith(("load", "atomic")) else "S"
+
+
+def _barrier_waits(body):
+    """Every vmcnt(N > 0) wait that guards a barrier (no vector-memory
+    instruction between it and the s_barrier), with the vector-memory
+    operations that may still be in flight after it on some path: a dataflow
+    pass over the basic blocks in which each state is the sequence of
+    operations issued since the last full drain, and vmcnt(N) keeps the last
+    N of them (one counter, retired in issue order)."""
+    blocks, succ = _blocks(body)
+
+    def guards(at):  # the text after a wait, through fall-through labels
+        for nxt in body[at + 1:]:
+            if _vmem_kind(nxt) or BRANCH.match(nxt) or END.match(nxt):
+                return False
+            if "s_barrier" in nxt:
+                return True
+        return False
+
+    # each block as events: ("V", kind, run length) or ("W", n, line, guards)
+    events = []
+    for idx in blocks:
+        ev = []
+        for at in idx:
+            kind = _vmem_kind(body[at])
+            if kind:
+                if ev and ev[-1][0] == "V" and ev[-1][1] == kind:
+                    ev[-1] = ("V", kind, ev[-1][2] + 1)
+                else:
+                    ev.append(("V", kind, 1))
+                continue
+            m = WAIT_VM.match(body[at])
+            if m:
+                n = int(m.group(1))
+                ev.append(("W", n, at, bool(n) and guards(at)))
+        events.append(ev)
+
+    found = {}
+    seen = set()
+    work = [(0, ())]
+    while work:
+        i, st = work.pop()
+        if (i, st) in seen:
+            continue
+        seen.add((i, st))
+        for e in events[i]:
+            if e[0] == "V":
+                st = (st + (e[1],) * e[2])[-64:]
+            else:
+                n = e[1]
+                st = st[-n:] if n else ()
+                if e[3]:
+                    found.setdefault(e[2], set()).add(st)
+        for j in succ[i]:
+            if (j, st) not in seen:
+                work.append((j, st))
+    return found
+
 
 def test_scan_kernels_leave_only_stores_in_flight(tmp_path):
     src = os.path.join(hipbuild.CSRC, "kernels.hip")
     funcs = _functions(_compile(src, str(tmp_path / "kernels.s")))
-    checked = 0
     # the scan launches, and every instantiation of the scan-only kernel
     # (tile shapes, slot layouts, data types)
     prefix = [n for n in funcs if "prefix_update_kernel" in n]
     assert len(prefix) >= 4, prefix
     for key in SCAN_KERNELS + prefix:
         body = _body(funcs, key)
-        for i, line in enumerate(body):
-            m = WAIT_VM.match(line)
-            if not m or int(m.group(1)) == 0:
-                continue
-            n = int(m.group(1))
-            # does this wait guard a barrier (no vector-memory op in between)?
-            guards = False
-            for nxt in body[i + 1:]:
-                if VMEM.match(nxt):
-                    break
-                if "s_barrier" in nxt:
-                    guards = True
-                    break
-            if not guards:
-                continue
-            # the last n vector-memory instructions before it must all be stores
-            prev = [l for l in body[:i] if VMEM.match(l)][-n:]
-            assert len(prev) == n and all(VMEM.match(l).group(2) == "store" for l in prev), (
-                key, i, n, [l.strip() for l in prev if VMEM.match(l).group(2) != "store"][:4])
-            checked += 1
-    # every scan kernel (two data types, three launch forms, the scan-only
-    # instantiations) has its store wait
-    assert checked >= len(SCAN_KERNELS) + len(prefix), checked
+        waits = _barrier_waits(body)
+        leaves_stores = 0
+        for at, states in waits.items():
+            n = int(WAIT_VM.match(body[at]).group(1))
+            # what the wait leaves in flight is stores only, on every path of
+            # the control flow; or, where the pass cannot tell two tests of
+            # one condition apart (stores issued under `if (stored)`, the
+            # wait chosen by the same test further on), the n vector-memory
+            # instructions right before it in the text are all stores
+            if any("L" in st for st in states):
+                prev = [l for l in body[:at] if VMEM.match(l)][-n:]
+                assert len(prev) == n and all(VMEM.match(l).group(2) == "store" for l in prev), (
+                    key, at, n, [l.strip() for l in prev if VMEM.match(l).group(2) != "store"][:4])
+                leaves_stores += 1
+            elif any("S" in st for st in states):
+                leaves_stores += 1
+        # and the scan's own wait, which leaves slot stores in flight, is there
+        assert leaves_stores > 0, key
+
+
+def test_dataflow_sees_a_load_left_in_flight():
+    """The check itself: a wait that leaves a direct-to-LDS load in flight
+    across a barrier, on one of two paths, is found."""
+    body = ["\tbuffer_store_dword v1, v2, s[0:3], 0 offen",
+            "\ts_cbranch_scc1 .LBB0_2",
+            "\tbuffer_load_dword v3, s[4:7], 0 offen lds",
+            ".LBB0_2:",
+            "\ts_waitcnt vmcnt(1)",
+            "\ts_barrier",
+            "\ts_endpgm"]
+    waits = _barrier_waits(body)
+    states = set().union(*waits.values())
+    assert ("S",) in states and ("L",) in states
+    # with the load waited for (vmcnt(0)) nothing is left
+    body[4] = "\ts_waitcnt vmcnt(0)"
+    assert _barrier_waits(body) == {}
