@@ -52,6 +52,13 @@ namespace ttt {
 #define TTT_GEMM_WPE (TTT_WAVES_M * TTT_WAVES_N / 4)
 using Tile = TileShape<256, 256, TTT_WAVES_M, TTT_WAVES_N>;
 using PrefixTile = Tile;
+// Output tiles: waves 4 x 2 (64 token rows x 128 columns each), so that each
+// wave reads two transposed Z fragments per step (two 8-byte transposing LDS
+// reads each) against four with the 2 x 4 arrangement: the transposing reads
+// cost LDS instructions, the row-form weight fragments half as many.
+using OutTile = TileShape<256, 256, 4, 2>;
+static_assert(OutTile::kThreads == Tile::kThreads && OutTile::kLdsBytes == Tile::kLdsBytes,
+              "output and scan tiles share a launch");
 using OneChunkTile = TileShape<128, 128, 2, 2>;  // single-chunk updates
 #define TTT_GEMM_KERNEL                                  \
   __global__ __launch_bounds__(TTT_GEMM_THREADS)          \
@@ -773,7 +780,7 @@ __device__ __forceinline__ void down_proj_tile(const Dims& dm, const T* __restri
                                                const T* __restrict__ slots, T* __restrict__ O,
                                                int64_t g0, int64_t gc, int blk, int nblk,
                                                lds_char* smem) {
-  using S = Tile;
+  using S = OutTile;
   const int64_t d = dm.d, f = dm.f, C = dm.C, T_seq = dm.T;
   const int64_t ld = f * (int64_t)sizeof(T);
   const int tiles_m = (int)((C + S::BM - 1) / S::BM);
