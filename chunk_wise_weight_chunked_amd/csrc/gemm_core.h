@@ -367,119 +367,6 @@ struct MmaSel<float, S, kTrA, kTrB> {
   using type = Mma32<S, kTrA, kTrB>;
 };
 
-// ------------------------------------------------- 16 x 16 x 32 MFMA policy
-// bf16 with v_mfma_f32_16x16x32_bf16: each wave's sub-tile is (WM / 16) x
-// (WN / 16) blocks of 16 x 16; a k-tile is 2 steps of 32 K values.  Lane l
-// feeds row (l % 16) of its block and K values 8 (l / 16) .. + 7 of the step,
-// on both sides.  Accumulator element e (0..3) of block (i, j) in lane l sits
-// at
-//     row = 16 i + 4 (l / 16) + e,   col = 16 j + (l % 16)
-// of the wave's sub-tile: four consecutive rows of one column per lane.
-template <class S>
-struct Accum16 {
-  static constexpr int MB = S::WM / 16, NB = S::WN / 16;
-  floatx4_t v[MB][NB];
-  __device__ __forceinline__ void zero() {
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) v[i][j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-};
-
-// Row of accumulator element (i, j, e) of this lane in the BM x BN tile, and
-// its column.
-__device__ __forceinline__ int row16(const LanePos& p, int i, int e) {
-  return p.wave_m0 + 16 * i + 4 * (p.lane >> 4) + e;
-}
-__device__ __forceinline__ int col16(const LanePos& p, int j) {
-  return p.wave_n0 + 16 * j + (p.lane & 15);
-}
-
-// Fragment of the 16-row block at m0 of a k-major tile (see read_a_tr): lane
-// group g = l / 16 takes K values 8 g .. + 7 of step s, lane j of the group
-// row m0 + j: two transposed loads (k-rows 8 g + 4 h .. + 3).
-__device__ __forceinline__ bf16x8_t read_tr16(const lds_char* sX, int m0, int lane, int s) {
-  const int g = lane >> 4, j = lane & 15;
-  const int m = m0 + 4 * (j & 3);
-  const int k = 32 * s + 8 * g + (j >> 2);
-  bf16x4_t v[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int R = (m >> 6) * 64 + k + 4 * h;
-    const uint32_t off = (uint32_t)R * kRowBytes +
-                         (uint32_t)((((m & 63) >> 3) ^ lds_swz_tr(R)) << 4) + (uint32_t)((m & 7) * 2);
-    v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (__attribute__((address_space(3))) bf16x4_t*)(sX + off));
-  }
-  return bf16x8_t{v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
-}
-
-template <class S, bool kTrA = false, bool kTrB = false>
-struct Mma16x16 {
-  static constexpr int kSteps = 2;  // 32 K values per step, 64 per k-tile
-  static constexpr int MB = S::WM / 16, NB = S::WN / 16;
-  struct Frag {
-    bf16x8_t a[MB], b[NB];
-  };
-  __device__ __forceinline__ static bf16x8_t read_a(const lds_char* sA, const LanePos& p, int i,
-                                                    int s) {
-    if constexpr (kTrA)
-      return read_tr16(sA, p.wave_m0 + 16 * i, p.lane, s);
-    else
-      return lds_load<bf16x8_t>(sA + lds_offset(p.wave_m0 + 16 * i + (p.lane & 15),
-                                                4 * s + (p.lane >> 4)));
-  }
-  __device__ __forceinline__ static bf16x8_t read_b(const lds_char* sB, const LanePos& p, int j,
-                                                    int s) {
-    if constexpr (kTrB)
-      return read_tr16(sB, p.wave_n0 + 16 * j, p.lane, s);
-    else
-      return lds_load<bf16x8_t>(sB + lds_offset(p.wave_n0 + 16 * j + (p.lane & 15),
-                                                4 * s + (p.lane >> 4)));
-  }
-  // Fragment reads of step s+1 spread between the MFMAs of step s (the
-  // reads of fragment q after MFMA q), and a hook after every MFMA with its
-  // index in the k-tile.
-  template <class Hook>
-  __device__ __forceinline__ static void ktile_spread(Accum16<S>& acc, const lds_char* sA,
-                                                      const lds_char* sB, const LanePos& p,
-                                                      Hook&& after_mfma) {
-    constexpr int kPerStep = MB * NB;
-    Frag f[2];
-#pragma unroll
-    for (int i = 0; i < MB; ++i) f[0].a[i] = read_a(sA, p, i, 0);
-#pragma unroll
-    for (int j = 0; j < NB; ++j) f[0].b[j] = read_b(sB, p, j, 0);
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      __builtin_amdgcn_sched_barrier(0);
-      const Frag& c = f[s & 1];
-      Frag& n = f[(s + 1) & 1];
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.a[i], c.b[j], acc.v[i][j], 0, 0, 0);
-          const int m = i * NB + j;
-          if (s + 1 < kSteps) {
-#pragma unroll
-            for (int q = 0; q < MB + NB; ++q) {
-              if (q == m || (m == kPerStep - 1 && q > m)) {
-                if (q < MB)
-                  n.a[q] = read_a(sA, p, q, s + 1);
-                else
-                  n.b[q - MB] = read_b(sB, p, q - MB, s + 1);
-              }
-            }
-          }
-          after_mfma(s * kPerStep + m);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-  }
-};
-
 // ------------------------------------------------------------- row loaders
 // Global reads use buffer loads: a scalar resource (base, byte range) per
 // operand and k-tile, a per-lane 32-bit offset.  Reads at or beyond the range
@@ -494,10 +381,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n,
                                            0x00020000);
 }
-__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
 
 // s_waitcnt on the vector-memory counter only: vmcnt(N), N a constant.
 template <int N>
@@ -506,12 +389,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Loader interface used by the mainloop:
-//   issue(kt, stage)  start the global reads of k-tile kt (into `stage` for
-//                     direct loaders, into registers for staged ones);
-//   commit(stage)     staged loaders write their registers to `stage`;
-//   kStagedLoads      vector-memory instructions one staged issue() makes
-//                     (0 for direct loaders).
+// Loader interface used by the mainloops: issue(kt, stage) starts the
+// direct-to-LDS reads of k-tile kt into `stage`; rsrc(kt, live) and
+// issue_one(r, stage, q) issue them one instruction at a time.
 //
 // DirectLoader moves one operand's k-tile (ROWS rows x 128 bytes) with
 // buffer_load ... lds (no registers): wave w of WAVES fills rows
@@ -528,7 +408,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 // kt_stride = rows * 128, kt_shrink = 0.
 template <int ROWS, int WAVES>
 struct DirectLoader {
-  static constexpr int kStagedLoads = 0;
   static constexpr int kRowsPerWave = ROWS / WAVES;
   static constexpr int kPer = kRowsPerWave / 8;  // instructions per wave per k-tile
   const char* base;
@@ -591,7 +470,6 @@ struct DirectLoader {
 #pragma unroll
     for (int q = 0; q < kPer; ++q) issue_one(r, stage, q);
   }
-  __device__ __forceinline__ void commit(lds_char*) const {}
 };
 
 // KMajorLoader: a k-major operand tile of 256 m-values (m: the tile's output
@@ -609,7 +487,6 @@ struct DirectLoader {
 template <typename T, int WAVES>
 struct KMajorLoader {
   static constexpr int TB = kRowBytes / (int)sizeof(T);
-  static constexpr int kStagedLoads = 0;
   static constexpr int kRowsPerWave = 256 / WAVES;
   static constexpr int kPer = kRowsPerWave / 8;
   const char* base;
@@ -646,75 +523,27 @@ struct KMajorLoader {
 #pragma unroll
     for (int q = 0; q < kPer; ++q) issue_one(r, stage, q);
   }
-  __device__ __forceinline__ void commit(lds_char*) const {}
-};
-
-// RegLoader: the same addressing as DirectLoader, through registers (global ->
-// VGPR with buffer loads in issue(), VGPR -> swizzled LDS in commit()).
-template <int ROWS, int WAVES>
-struct RegLoader {
-  static constexpr int kRowsPerWave = ROWS / WAVES;
-  static constexpr int kPer = kRowsPerWave / 8;
-  static constexpr int kStagedLoads = kPer;
-  const char* base;
-  int64_t kt_stride, valid_bytes, kt_shrink;
-  uint32_t voff[kPer];
-  uint32_t lds_row0;
-  uint4 reg[kPer];
-
-  __device__ __forceinline__ void init(const void* base_, int64_t row_stride, int64_t kt_stride_,
-                                       int64_t valid_bytes_, int64_t kt_shrink_) {
-    base = static_cast<const char*>(base_);
-    kt_stride = kt_stride_;
-    valid_bytes = valid_bytes_;
-    kt_shrink = kt_shrink_;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    lds_row0 = (uint32_t)(wave * kRowsPerWave);
-    const int rr = lane >> 3;
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int row = (int)lds_row0 + 8 * q + rr;
-      voff[q] = (uint32_t)(row * row_stride + (lane & 7) * 16);
-    }
-  }
-  __device__ __forceinline__ void issue(int64_t kt, lds_char*) {
-    const rsrc_t r = make_rsrc(base + kt * kt_stride, valid_bytes - kt * kt_shrink);
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) reg[q] = buf_load16(r, voff[q]);
-  }
-  __device__ __forceinline__ void commit(lds_char* stage) const {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int q = 0; q < kPer; ++q)
-      lds_store<u32x4_t>(stage + lds_offset((int)lds_row0 + 8 * q + (lane >> 3), lane & 7),
-                         as_u32x4(reg[q]));
-  }
 };
 
 // ---------------------------------------------------------------- mainloop
 // Runs k-tiles [0, nk) through a two-stage LDS pipeline.  Entering k-tile kt
 // (after a barrier), stage kt&1 holds k-tile kt and the other stage is free:
-// direct loaders start k-tile kt+1 into it (bf16 with kSpread: spread over
-// kt's MFMAs; otherwise at once, in one group); staged loaders write the
-// registers they fetched one k-tile earlier halfway through kt's MFMAs and
-// then fetch k-tile kt+2.  Before the closing barrier every wave waits for
-// its own direct reads of k-tile kt+1 (the staged fetches, issued later, may
-// stay in flight).  after_ktile(kt) runs once every wave has finished k-tile
-// kt and no direct read is in flight (it may use registers and global memory,
-// not LDS).
+// the loaders start k-tile kt+1 into it (bf16 with kSpread: spread over kt's
+// MFMAs; otherwise at once, in one group).  Before the closing barrier every
+// wave waits for its own reads of k-tile kt+1.  after_ktile(kt) runs once
+// every wave has finished k-tile kt and no read is in flight (it may use
+// registers and global memory, not LDS).
 // kTrA (bf16 only): the A tile is k-major (see read_a_tr) and its fragments
 // are read with transposed loads.
 template <typename T, class S, bool kSpread = true, bool kTrA = false, bool kTrB = false,
           class LA, class LB, class Hook>
 __device__ __forceinline__ void mainloop(Accum<S>& acc, LA& la, LB& lb, int64_t nk, lds_char* smem,
                                          const LanePos& p, Hook&& after_ktile) {
-  constexpr int kStaged = LA::kStagedLoads + LB::kStagedLoads;
-  static_assert(sizeof(T) == 4 || !(kTrA || kTrB) || (kSpread && kStaged == 0),
-                "bf16 k-major fragments: direct loaders, spread issue");
+  static_assert(sizeof(T) == 4 || !(kTrA || kTrB) || kSpread,
+                "bf16 k-major fragments: spread issue");
   if (nk <= 0) return;
-  if constexpr (kSpread && sizeof(T) == 2 && kStaged == 0) {
-    // bf16, direct loaders: k-tile kt+1's load instructions are spread over
+  if constexpr (kSpread && sizeof(T) == 2) {
+    // bf16: k-tile kt+1's load instructions are spread over
     // k-tile kt's MFMAs, one every kEvery MFMAs from the first (every second
     // when they then still end in the first half of the k-tile).  After the
     // last k-tile they read an empty range into the idle stage; the closing
@@ -748,59 +577,8 @@ __device__ __forceinline__ void mainloop(Accum<S>& acc, LA& la, LB& lb, int64_t 
     }
     return;
   }
-  lds_char* const stage0 = smem;
-  la.issue(0, stage0);
-  lb.issue(0, stage0 + S::BM * kRowBytes);
-  la.commit(stage0);
-  lb.commit(stage0 + S::BM * kRowBytes);
-  if (nk > 1) {
-    if constexpr (LA::kStagedLoads > 0) la.issue(1, nullptr);
-    if constexpr (LB::kStagedLoads > 0) lb.issue(1, nullptr);
-    wait_vmcnt<kStaged>();
-  } else {
-    wait_vmcnt<0>();
-  }
-  __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const lds_char* cur = smem + (kt & 1) * S::kStageBytes;
-    lds_char* nxt = smem + ((kt + 1) & 1) * S::kStageBytes;
-    if (kt + 1 < nk) {
-      if constexpr (LA::kStagedLoads == 0) la.issue(kt + 1, nxt);
-      if constexpr (LB::kStagedLoads == 0) lb.issue(kt + 1, nxt + S::BM * kRowBytes);
-    }
-    MmaSel<T, S, kTrA, kTrB>::type::ktile(acc, cur, cur + S::BM * kRowBytes, p, [&] {
-      if constexpr (kStaged > 0) {
-        if (kt + 1 < nk) {
-          la.commit(nxt);
-          lb.commit(nxt + S::BM * kRowBytes);
-        }
-        if (kt + 2 < nk) {
-          if constexpr (LA::kStagedLoads > 0) la.issue(kt + 2, nullptr);
-          if constexpr (LB::kStagedLoads > 0) lb.issue(kt + 2, nullptr);
-        }
-      }
-    });
-    if (kt + 2 < nk)
-      wait_vmcnt<kStaged>();
-    else
-      wait_vmcnt<0>();
-    __syncthreads();
-    after_ktile(kt);
-  }
-}
-
-// The bf16 mainloop of the 16 x 16 x 32 policy (direct loaders, k-tile kt+1's
-// loads spread over k-tile kt's MFMAs, as in mainloop's bf16 path).
-template <class S, bool kTrA = false, bool kTrB = false, class LA, class LB, class Hook>
-__device__ __forceinline__ void mainloop16(Accum16<S>& acc, LA& la, LB& lb, int64_t nk,
-                                           lds_char* smem, const LanePos& p, Hook&& after_ktile) {
-  static_assert(LA::kStagedLoads == 0 && LB::kStagedLoads == 0, "direct loaders");
-  using M = Mma16x16<S, kTrA, kTrB>;
-  constexpr int kLoads = LA::kPer + LB::kPer;
-  constexpr int kMfmas = M::kSteps * M::MB * M::NB;
-  constexpr int kEvery = 2 * kLoads <= kMfmas / 2 ? 2 : 1;
-  static_assert(kLoads <= kMfmas, "one load instruction per MFMA at most");
-  if (nk <= 0) return;
+  // fp32, or bf16 without kSpread: k-tile kt+1's loads in one group at the
+  // start of k-tile kt
   la.issue(0, smem);
   lb.issue(0, smem + S::BM * kRowBytes);
   wait_vmcnt<0>();
@@ -808,17 +586,11 @@ __device__ __forceinline__ void mainloop16(Accum16<S>& acc, LA& la, LB& lb, int6
   for (int64_t kt = 0; kt < nk; ++kt) {
     const lds_char* cur = smem + (kt & 1) * S::kStageBytes;
     lds_char* nxt = smem + ((kt + 1) & 1) * S::kStageBytes;
-    const bool more = kt + 1 < nk;
-    const rsrc_t ra = la.rsrc(kt + 1, more), rb = lb.rsrc(kt + 1, more);
-    M::ktile_spread(acc, cur, cur + S::BM * kRowBytes, p, [&](int idx) {
-      if (idx % kEvery == 0 && idx / kEvery < kLoads) {
-        const int q = idx / kEvery;
-        if (q < LA::kPer)
-          la.issue_one(ra, nxt, q);
-        else
-          lb.issue_one(rb, nxt + S::BM * kRowBytes, q - LA::kPer);
-      }
-    });
+    if (kt + 1 < nk) {
+      la.issue(kt + 1, nxt);
+      lb.issue(kt + 1, nxt + S::BM * kRowBytes);
+    }
+    MmaSel<T, S, kTrA, kTrB>::type::ktile(acc, cur, cur + S::BM * kRowBytes, p, [] {});
     wait_vmcnt<0>();
     __syncthreads();
     after_ktile(kt);
@@ -855,7 +627,6 @@ template <typename T, class S, int kStores, class LA, class LB, class Hook>
 __device__ __forceinline__ void mainloop_with_stores(Accum<S>& acc, LA& la, LB& lb, int64_t nk,
                                                      lds_char* smem, const LanePos& p,
                                                      Hook&& before_ktile) {
-  static_assert(LA::kStagedLoads == 0 && LB::kStagedLoads == 0, "direct loaders");
   constexpr int kLeave = kStores < 63 ? kStores : 63;
   if (nk <= 0) return;
   la.issue(0, smem);
