@@ -79,24 +79,6 @@ __global__ __launch_bounds__(256) void to_kblocked_kernel(const T* __restrict__ 
   }
 }
 
-// Z = SiLU(A_g) * A_u from the fp32 pre-activations (row t of A_g and A_u at
-// t * ld), in the activation type (the same SiLU as the forward's epilogue).
-// 4 values per item.
-template <typename T>
-__global__ void swiglu_rows_kernel(const float* __restrict__ Ag, const float* __restrict__ Au,
-                                   int64_t ld, T* __restrict__ Z, int64_t f, int64_t n4) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < n4; it += stride) {
-    const int64_t t = it * 4 / f, c = it * 4 - t * f;
-    const float4 g = *reinterpret_cast<const float4*>(Ag + t * ld + c);
-    const float4 u = *reinterpret_cast<const float4*>(Au + t * ld + c);
-    const float gg[4] = {g.x, g.y, g.z, g.w}, uu[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      Elem<T>::store(Z + it * 4 + e, gg[e] * __builtin_amdgcn_rcpf(1.0f + __expf(-gg[e])) * uu[e]);
-  }
-}
-
 // SwiGLU derivative.  With Z = SiLU(A_g) * A_u and s = sigmoid(A_g):
 //   dA_g = dZ * A_u * s * (1 + A_g (1 - s)),  dA_u = dZ * A_g * s.
 // Row t of the output holds [dA_g[t][0..f) | dA_u[t][0..f)] (the A operand
@@ -326,19 +308,6 @@ hipError_t launch_to_kblocked(const void* src, void* dst, const Dims& dm, int64_
     hipLaunchKernelGGL(to_kblocked_kernel<float>, grid, dim3(256), 0, s,
                        static_cast<const float*>(src), static_cast<float*>(dst), dm, R,
                        reverse ? 1 : 0);
-  return hipGetLastError();
-}
-
-hipError_t launch_swiglu_rows(const float* Ag, const float* Au, int64_t ld, void* Z,
-                              const Dims& dm, hipStream_t s) {
-  const int64_t n4 = dm.B * dm.T * dm.f / 4;
-  const dim3 g(grid_cap(n4, 256, 65536));
-  if (dm.dt == Dtype::BF16)
-    hipLaunchKernelGGL(swiglu_rows_kernel<uint16_t>, g, dim3(256), 0, s, Ag, Au, ld,
-                       static_cast<uint16_t*>(Z), dm.f, n4);
-  else
-    hipLaunchKernelGGL(swiglu_rows_kernel<float>, g, dim3(256), 0, s, Ag, Au, ld,
-                       static_cast<float*>(Z), dm.f, n4);
   return hipGetLastError();
 }
 

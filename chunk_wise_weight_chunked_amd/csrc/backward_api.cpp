@@ -232,13 +232,15 @@ ttt_status_t ttt_mlp_backward_batched(
   if (e != hipSuccess) return hip_fail(e, "backward");
 
   // 2. The plain GEMMs (the library's batched MFMA GEMM, fp32 accumulation):
-  //    first the fp32 pre-activations [A_g | A_u] = H [W_gate; W_up]ᵀ in one
-  //    GEMM (row t holds both, 2f wide) and V^ = U W_target.
+  //    first the fp32 pre-activations [A_g | A_u] = H [W_gate; W_up]ᵀ (row t
+  //    holds both, 2f wide) with Z = SiLU(A_g) A_u from the same launch, and
+  //    V^ = U W_target.
   Gemm gemm{dm.dt, s};
   const bool f32 = true, act_f32 = dm.dt == ttt::Dtype::F32;  // output types
   const int64_t B = dm.B, T = dm.T, C = dm.C, N = dm.N, sl = (int64_t)(B * d * f);
   const int64_t Di = (int64_t)d, Fi = (int64_t)f, BTi = (int64_t)BT;
-  gemm(kRowK, kRowK, BTi, 2 * Fi, Di, 1.f, H, Di, 0, Wgu, Di, 0, false, Ag, 2 * Fi, 0, 1, f32);
+  e = ttt::launch_preact_swiglu(dm.dt, H, WgU, BTi, Di, Fi, Ag, Z, s);
+  if (e != hipSuccess) return hip_fail(e, "backward");
   if (dm.proj)
     gemm(kRowK, kRowK, BTi, Di, Di, 1.f, U, Di, 0, WtT, Di, 0, false, V, Di, 0, 1, act_f32);
   if (gemm.err != hipSuccess) return hip_fail(gemm.err, "backward gemm");
@@ -253,14 +255,13 @@ ttt_status_t ttt_mlp_backward_batched(
   if (e == hipSuccess && dm.proj) e = ttt::launch_to_kblocked(U, Uk, dm, dm.d, false, s);
   if (e != hipSuccess) return hip_fail(e, "backward");
 
-  // 3. Z from them, in row-major and in the scans' k-blocked layout (chunks in
-  //    order and reversed); dOᵀ k-blocked with the chunks reversed.  Then, in
+  // 3. Z in the scans' k-blocked layout (chunks in order and reversed); dOᵀ
+  //    k-blocked with the chunks reversed.  Then, in
   //    one launch, the forward's scan (slot j = W^(j-1), written transposed)
   //    and the same scan over dOᵀ and Z in reverse chunk order from dW_final
   //    (slot j = S_j; its final state is the gradient of the starting
   //    weight).
-  e = ttt::launch_swiglu_rows(Ag, Au, 2 * Fi, Z, dm, s);
-  if (e == hipSuccess) e = ttt::launch_to_kblocked(Z, Zt, dm, dm.f, false, s);
+  e = ttt::launch_to_kblocked(Z, Zt, dm, dm.f, false, s);
   if (e == hipSuccess) e = ttt::launch_to_kblocked(Z, Ztr, dm, dm.f, true, s);
   if (e == hipSuccess) e = ttt::launch_to_kblocked(dO, dOtr, dm, dm.d, true, s);
   if (e == hipSuccess)

@@ -182,6 +182,69 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         g.alpha, false);
 }
 
+// [A_g | A_u] = H [W_gate; W_up]ᵀ in fp32 and Z = SiLU(A_g) * A_u in one
+// launch.  B is the interleaved weight WgU ([f/32][2][32][d]: 32 gate rows,
+// then the 32 up rows of the same features), so each 64-column pass of a
+// tile holds the gate and up sums of 32 features.  Row t of Ag holds A_g at
+// [0, f) and A_u at [f, 2f); Z is [BT][f] in the activation type, computed
+// from the same fp32 values as SiLU(g) * u (the forward's arithmetic).
+template <typename T>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void preact_kernel(
+    const T* __restrict__ H, const T* __restrict__ WgU, int64_t BT, int64_t d, int64_t f,
+    float* __restrict__ Ag, T* __restrict__ Z) {
+  using S = GTile;
+  __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
+  lds_char* smem = (lds_char*)smem_raw;
+  constexpr int TB = kRowBytes / (int)sizeof(T);
+  const int tiles_m = (int)((BT + S::BM - 1) / S::BM);
+  const int tiles_n = (int)((2 * f + S::BN - 1) / S::BN);
+  const TileCoord tc = grouped_tile(xcd_remap(blockIdx.x, (int)gridDim.x), tiles_m, tiles_n, 8);
+  const int64_t m0 = (int64_t)tc.m * S::BM, n0 = (int64_t)tc.n * S::BN;
+  Accum<S> acc;
+  acc.zero();
+  const LanePos p = lane_pos<S>();
+  auto la = make_loader<T, kRowK, S::BM>(reinterpret_cast<const char*>(H), d, 0, 0, m0, BT, d);
+  auto lb = make_loader<T, kRowK, S::BN>(reinterpret_cast<const char*>(WgU), d, 0, 0, n0, 2 * f, d);
+  mainloop<T, S>(acc, la, lb, (d + TB - 1) / TB, smem, p, [](int64_t) {});
+
+  for (int q = 0; q < S::BN / kEpiCols; ++q) {
+    __syncthreads();  // the mainloop's (or the previous pass's) reads of LDS are done
+#pragma unroll
+    for (int j = 0; j < S::NB; ++j) {
+      const int col = p.wave_n0 + 32 * j;
+      if (col < kEpiCols * q || col >= kEpiCols * q + kEpiCols) continue;
+      const int c = col - kEpiCols * q + (p.lane & 31);
+#pragma unroll
+      for (int i = 0; i < S::MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          lds_store<float>(smem + ((uint32_t)p.row(i, r) * kEpiStride + c) * 4, acc.v[i][j][r]);
+    }
+    __syncthreads();
+    const int64_t pair = (n0 + kEpiCols * q) / 64;  // gate/up block pair: features 32 pair ..
+    if (64 * pair >= 2 * f) continue;
+    const int64_t feat = 32 * pair;
+    for (int it = threadIdx.x; it < S::BM * 4; it += S::kThreads) {
+      const int t = it / 4, c = (it % 4) * 8;
+      if (m0 + t >= BT) continue;
+      const uint32_t row = (uint32_t)t * kEpiStride;
+      const floatx4_t g0 = lds_load<floatx4_t>(smem + (row + c) * 4);
+      const floatx4_t g1 = lds_load<floatx4_t>(smem + (row + c + 4) * 4);
+      const floatx4_t u0 = lds_load<floatx4_t>(smem + (row + 32 + c) * 4);
+      const floatx4_t u1 = lds_load<floatx4_t>(smem + (row + 32 + c + 4) * 4);
+      const float g[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+      const float u[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+      float* ag = Ag + (m0 + t) * 2 * f + feat + c;
+      store8<float>(ag, g, false);
+      store8<float>(ag + f, u, false);
+      float z[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[e] = g[e] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[e])) * u[e];
+      store8<T>(Z + (m0 + t) * f + feat + c, z, false);
+    }
+  }
+}
+
 template <typename T>
 hipError_t launch_gemm_t(const GemmArgs& g, const GemmArgs* g2, hipStream_t s) {
   const int64_t tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
@@ -275,6 +338,21 @@ hipError_t launch_gemm2(const GemmArgs& g, const GemmArgs& g2, hipStream_t s) {
     return hipErrorInvalidValue;
   if (g.dt == Dtype::BF16) return launch_gemm_t<uint16_t>(g, &g2, s);
   return launch_gemm_t<float>(g, &g2, s);
+}
+
+hipError_t launch_preact_swiglu(Dtype dt, const void* H, const void* WgU, int64_t BT, int64_t d,
+                                int64_t f, float* Ag, void* Z, hipStream_t s) {
+  if (BT <= 0) return hipSuccess;
+  if (d % 64 != 0 || f % 64 != 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(((BT + 255) / 256) * ((2 * f + 255) / 256)));
+  if (dt == Dtype::BF16)
+    hipLaunchKernelGGL(preact_kernel<uint16_t>, grid, dim3(512), 0, s,
+                       static_cast<const uint16_t*>(H), static_cast<const uint16_t*>(WgU), BT, d,
+                       f, Ag, static_cast<uint16_t*>(Z));
+  else
+    hipLaunchKernelGGL(preact_kernel<float>, grid, dim3(512), 0, s, static_cast<const float*>(H),
+                       static_cast<const float*>(WgU), BT, d, f, Ag, static_cast<float*>(Z));
+  return hipGetLastError();
 }
 
 hipError_t launch_transpose(const void* src, void* dst, int64_t rows, int64_t cols, Dtype dt,

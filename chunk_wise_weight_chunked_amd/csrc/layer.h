@@ -168,6 +168,12 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
 // runs first on the same accumulators and C is written once.  Only the pair
 // (kRowK, kRowK) + (kRowK, kTiledKMajor) is built.
 hipError_t launch_gemm2(const GemmArgs& g, const GemmArgs& g2, hipStream_t s);
+// The backward's pre-activations and gated activations in one launch:
+// Ag [BT][2f] fp32 (A_g at columns [0, f), A_u at [f, 2f)) = H WgUᵀ with the
+// interleaved gate/up weight WgU of launch_weight_prep, and Z [BT][f] =
+// SiLU(A_g) * A_u in type dt.  d and f multiples of 64.
+hipError_t launch_preact_swiglu(Dtype dt, const void* H, const void* WgU, int64_t BT, int64_t d,
+                                int64_t f, float* Ag, void* Z, hipStream_t s);
 // dst [cols][rows] = srcᵀ for src [rows][cols] of element type dt.
 hipError_t launch_transpose(const void* src, void* dst, int64_t rows, int64_t cols, Dtype dt,
                             hipStream_t s);
@@ -179,10 +185,6 @@ constexpr int kDotPartials = 1024;        // partial sums of the learning rate's
 // reversed if `reverse`), zeros in the padding columns.
 hipError_t launch_to_kblocked(const void* src, void* dst, const Dims& dm, int64_t R, bool reverse,
                               hipStream_t s);
-// Z [B*T][f] = SiLU(A_g) * A_u (activation type) from fp32 pre-activations
-// (row t of A_g and A_u at t * ld).
-hipError_t launch_swiglu_rows(const float* Ag, const float* Au, int64_t ld, void* Z,
-                              const Dims& dm, hipStream_t s);
 // The scans of two independent problems (same shapes) in one launch: the
 // first writes its slots transposed ([N][B][f][d], slots1t), the second in
 // tiles of TB x TB (slots2: [N][B][d/TB][f/TB][TB][TB], TB = 128 bytes of the
