@@ -375,6 +375,25 @@ def test_full_workload_prefix_and_final_weight(name):
     assert e_w <= tol_for(w.dtype) and e_dw <= tol_for(w.dtype)
 
 
+@pytest.mark.parametrize("name", ["qwen3_4b_32k", "small_4x128k"])
+def test_full_size_sequential_mode_bitwise(name):
+    """Sequential mode at full size (one launch per chunk's read-modify-write of
+    the fp32 state, the single-chunk update tiles, a group's outputs batched)
+    against the default chunk-parallel groups: the fp32 state sums run in the
+    same order, so outputs and final weights are the same bits."""
+    w = synth.WORKLOADS[name]
+    dev = to_device(synth.workload_inputs(w))
+    runs = []
+    for mode in ("auto", "sequential"):
+        O, W = tm.forward_batched(dev["H"], dev["X0"], dev["W_gate"], dev["W_up"],
+                                  dev["W_down0"], dev["taps"], dev["W_target"], w.eta, w.chunk,
+                                  mode=mode)
+        torch.cuda.synchronize()
+        runs.append((O, W))
+        print(f"[full] {name} {mode}: done", flush=True)
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
+
+
 # ------------------------------------------------- coherent-accumulation stress
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 def test_repeated_block_stress(dtype):
