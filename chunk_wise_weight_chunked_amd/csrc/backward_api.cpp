@@ -66,58 +66,51 @@ BackwardPlan plan_backward(const ttt::Dims& dm) {
   return p;
 }
 
-// C = alpha A' B'ᵀ (+ C when accumulate) on the library's batched GEMM, with
-// each operand's layout (ttt::GemmLayout, see layer.h); the first failure is
-// kept.
+// The arguments of one product C = alpha A' B'ᵀ (+ C when accumulate) of the
+// library's batched GEMM, with each operand's layout (ttt::GemmLayout, see
+// layer.h).
+ttt::GemmArgs product(ttt::Dtype dt, int32_t la, int32_t lb, int64_t M, int64_t N, int64_t K,
+                      float alpha, const void* A, int64_t lda, int64_t sa, const void* B,
+                      int64_t ldb, int64_t sb, bool accumulate, void* C, int64_t ldc, int64_t sc,
+                      int64_t batch, bool c_f32, int64_t K_last = -1) {
+  ttt::GemmArgs g{};
+  g.dt = dt;
+  g.A = A;
+  g.lda = lda;
+  g.sa = sa;
+  g.a_layout = la;
+  g.B = B;
+  g.ldb = ldb;
+  g.sb = sb;
+  g.b_layout = lb;
+  g.C = C;
+  g.ldc = ldc;
+  g.sc = sc;
+  g.c_f32 = c_f32 ? 1 : 0;
+  g.accumulate = accumulate ? 1 : 0;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.K_last = K_last < 0 ? K : K_last;
+  g.batch = batch;
+  g.alpha = alpha;
+  return g;
+}
+
+// Launches products on one stream, keeping the first failure.
 struct Gemm {
   ttt::Dtype dt;
   hipStream_t s;
   hipError_t err = hipSuccess;
-  void operator()(int32_t la, int32_t lb, int64_t M, int64_t N, int64_t K, float alpha,
-                  const void* A, int64_t lda, int64_t sa, const void* B, int64_t ldb, int64_t sb,
-                  bool accumulate, void* C, int64_t ldc, int64_t sc, int64_t batch, bool c_f32,
-                  int64_t K_last = -1) {
-    if (err != hipSuccess || M == 0 || N == 0) {
-      hold = pending = false;
-      return;
-    }
-    ttt::GemmArgs g{};
-    g.dt = dt;
-    g.A = A;
-    g.lda = lda;
-    g.sa = sa;
-    g.a_layout = la;
-    g.B = B;
-    g.ldb = ldb;
-    g.sb = sb;
-    g.b_layout = lb;
-    g.C = C;
-    g.ldc = ldc;
-    g.sc = sc;
-    g.c_f32 = c_f32 ? 1 : 0;
-    g.accumulate = accumulate ? 1 : 0;
-    g.M = M;
-    g.N = N;
-    g.K = K;
-    g.K_last = K_last < 0 ? K : K_last;
-    g.batch = batch;
-    g.alpha = alpha;
-    if (pending) {
-      err = ttt::launch_gemm2(g, first, s);
-      pending = false;
-    } else if (hold) {
-      first = g;
-      pending = true;
-      hold = false;
-    } else {
-      err = ttt::launch_gemm(g, s);
-    }
+  template <class... A>
+  void operator()(A... a) {
+    if (err == hipSuccess) err = ttt::launch_gemm(product(dt, a...), s);
   }
-  // The next call's product is held and added into the one after it (one
-  // launch, C written once; its C and accumulate are ignored).
-  void fuse_next() { hold = true; }
-  ttt::GemmArgs first{};
-  bool hold = false, pending = false;
+  // g.C = g.alpha (g.A g.Bᵀ + g2.alpha g2.A g2.Bᵀ) in one launch (g2's C
+  // unused).
+  void pair(const ttt::GemmArgs& g, const ttt::GemmArgs& g2) {
+    if (err == hipSuccess) err = ttt::launch_gemm2(g, g2, s);
+  }
 };
 
 using ttt::kKBlocked;
@@ -287,11 +280,12 @@ ttt_status_t ttt_mlp_backward_batched(
     const int64_t r = b0 * T + j * C;  // first row
     const char* WjT = Wslots + (size_t)(j * sl + b0 * Di * Fi) * es;
     const char* Sj = Sslots + (size_t)(j * sl + b0 * Di * Fi) * es;
-    gemm.fuse_next();
-    gemm(kRowK, kTiledKMajor, rows, Fi, Di, dm.eta, Vc + r * d * es, Di, row_stride * Di, Sj,
-         Fi, slot_stride, false, nullptr, Fi, row_stride * Fi, count, f32);
-    gemm(kRowK, kRowK, rows, Fi, Di, 1.f, dOc + r * d * es, Di, row_stride * Di, WjT, Di,
-         slot_stride, false, dZ + r * f, Fi, row_stride * Fi, count, f32);
+    gemm.pair(product(dm.dt, kRowK, kRowK, rows, Fi, Di, 1.f, dOc + r * d * es, Di,
+                      row_stride * Di, WjT, Di, slot_stride, false, dZ + r * f, Fi,
+                      row_stride * Fi, count, f32),
+              product(dm.dt, kRowK, kTiledKMajor, rows, Fi, Di, dm.eta, Vc + r * d * es, Di,
+                      row_stride * Di, Sj, Fi, slot_stride, false, nullptr, Fi, row_stride * Fi,
+                      count, f32));
     gemm(kRowK, kTiledRowK, rows, Di, Fi, 1.f, Zc + r * f * es, Fi, row_stride * Fi, Sj, Fi,
          slot_stride, false, Gf + r * d, Di, row_stride * Di, count, f32);
   };
