@@ -60,6 +60,14 @@ using OutTile = TileShape<256, 256, 4, 2>;
 static_assert(OutTile::kThreads == Tile::kThreads && OutTile::kLdsBytes == Tile::kLdsBytes,
               "output and scan tiles share a launch");
 using OneChunkTile = TileShape<128, 128, 2, 2>;  // single-chunk updates
+// LDS for the staged slot rows: 4 KB per wave of the 256 x 256 scan tile.
+constexpr int kSlotStageBytes = 8 * 4096;
+// bf16 slots are staged through LDS when chunks are short (a slot every 8
+// k-tiles or fewer): there the stores, not the k-loop, hold the scan tiles.
+template <typename T>
+bool staged_slots(const Dims& dm) {
+  return sizeof(T) == 2 && dm.Cp / (kRowBytes / (int64_t)sizeof(T)) <= 8;
+}
 #define TTT_GEMM_KERNEL                                  \
   __global__ __launch_bounds__(TTT_GEMM_THREADS)          \
   __attribute__((amdgpu_waves_per_eu(TTT_GEMM_WPE, TTT_GEMM_WPE)))
@@ -526,7 +534,12 @@ __global__ __launch_bounds__(256) void rows_to_vt_kernel(Dims dm, const T* __res
 // (m, n) of a slot at ((m / TB) (f / TB) + n / TB) TB^2 + (m % TB) TB + n % TB
 // with TB = 128 bytes of T -- every k-tile of a product that contracts over d
 // (k-major) or over f (rows of 128 bytes) is then whole 128-row blocks of
-// TB rows each, contiguous in memory.
+// TB rows each, contiguous in memory; bit 3 (instead of bit 0, bf16 and the
+// 256 x 256 tile only): the `slots` layout of bit 0, each wave's block rows
+// staged through a 4 KB region of LDS past the k-tile stages (the caller's
+// `smem` holds S::kLdsBytes + kSlotStageBytes) and stored as whole 128-byte
+// row segments, 16 bytes per lane: a quarter of the store instructions, for
+// short chunks, whose slots come every few k-tiles.
 template <typename T, class S, int kSlots = 1>
 __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __restrict__ Vt,
                                                    const T* __restrict__ Zt,
@@ -592,10 +605,13 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
                               p.wave_n0 + ((p.lane & 31) & ~1)) * 2u;
   // store instructions per lane of one slot: row-major pairs (bf16) or
   // values (fp32); transposed, 4 consecutive rows of a column in one store
-  static_assert((kSlots & 5) != 5, "one layout in `slots`");
+  constexpr bool kStaged = (kSlots & 8) != 0;
+  static_assert(__builtin_popcount(kSlots & 13) <= 1, "one layout in `slots`");
+  static_assert(!kStaged || (sizeof(T) == 2 && S::WM == 128 && S::WN == 64),
+                "staged slots: bf16, waves of 128 x 64");
   constexpr int kSlotStores =
       ((kSlots & 5) ? S::MB * 4 * S::NB * (sizeof(T) == 2 ? 2 : 4) : 0) +
-      ((kSlots & 2) ? S::MB * 4 * S::NB : 0);
+      ((kSlots & 2) ? S::MB * 4 * S::NB : 0) + (kStaged ? S::MB * 4 : 0);
   const uint32_t lane_t = (uint32_t)(((p.wave_n0 + (p.lane & 31)) * d + p.wave_m0 +
                                       4 * (p.lane >> 5)) * (int64_t)sizeof(T));
   const uint32_t du = (uint32_t)d;
@@ -680,10 +696,54 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
         __builtin_amdgcn_sched_barrier(0);
       }
   };
+  // Staged slots: block row i of the wave (32 rows x 64 columns, bf16) goes
+  // to the wave's LDS region as column pairs (row r at r * 128 bytes, its
+  // 16-byte chunk c at c ^ (r & 7)), then back as 16-byte chunks, lane l
+  // taking chunk l & 7 of row 8 s + l / 8, and out as whole row segments.
+  // A wave's LDS accesses run in order, so each block row's reads come
+  // before the next one's writes.
+  lds_char* const stage_slot = smem + S::kLdsBytes + (threadIdx.x >> 6) * 4096;
+  const uint32_t lane_row = (uint32_t)((p.lane >> 3) * f + 8 * (p.lane & 7)) * 2u;
+  const uint32_t wave_off = (uint32_t)(p.wave_m0 * f + p.wave_n0) * 2u;
+  auto write_slot_staged = [&](int64_t js) {
+    const rsrc_t sr = make_rsrc(slots + js * slot_stride + b * d * f + corner,
+                                span * (int64_t)sizeof(T));
+#pragma unroll
+    for (int i = 0; i < S::MB; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < S::NB; ++j) {
+          float z[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[e] = acc.v[i][j][4 * q + e];
+          uint32_t w[2];
+          pair_pack(z, odd, w);
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const int row = 8 * q + 4 * (p.lane >> 5) + (odd ? 2 : 0) + r;
+            const int col = 32 * j + ((p.lane & 31) & ~1);
+            lds_store<uint32_t>(stage_slot + row * kRowBytes + ((((col >> 3) ^ (row & 7))) << 4) +
+                                    (col & 7) * 2,
+                                w[r]);
+          }
+        }
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int row = 8 * s4 + (p.lane >> 3);
+        const u32x4_t v =
+            lds_load<u32x4_t>(stage_slot + row * kRowBytes + ((((p.lane & 7) ^ (row & 7))) << 4));
+        __builtin_amdgcn_raw_buffer_store_b128(
+            v, sr, lane_row, wave_off + (uint32_t)((32 * i + 8 * s4) * f) * 2u, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   auto write_slot = [&](int64_t jj) {
     const int64_t js = dm.reverse_slots ? gc - 1 - jj : jj;
     if constexpr ((kSlots & 2) != 0) write_slot_t(js);
     if constexpr ((kSlots & 4) != 0) write_slot_tiled(js);
+    if constexpr (kStaged) write_slot_staged(js);
     if constexpr ((kSlots & 1) == 0) return;
     const rsrc_t sr = make_rsrc(slots + js * slot_stride + b * d * f + corner,
                                 span * (int64_t)sizeof(T));
@@ -719,7 +779,7 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
   };
 
   // none: the increments' sum only
-  const bool with_slots = (kSlots & 5) ? slots != nullptr : slots_t != nullptr;
+  const bool with_slots = (kSlots & 13) ? slots != nullptr : slots_t != nullptr;
   if (with_slots) write_slot(0);
   const int64_t kt_per_chunk = dm.Cp / TB;
   // a streaming call leaves the sequence's last chunk out of the state (its
@@ -855,7 +915,7 @@ TTT_GEMM_KERNEL void down_proj_kernel(Dims dm, const T* __restrict__ Z,
 // k-loop is the group's tokens, the outputs' is f): workgroups [0, n1) run
 // it, [n1, pad) exit at once (pad rounds n1 up to a multiple of 8, so the
 // second kind starts on XCD 0), the rest run the other kind.
-template <typename T>
+template <typename T, int kScanSlots = 1>
 TTT_GEMM_KERNEL void scan_apply_kernel(Dims dm, const T* __restrict__ Vt, const T* __restrict__ Zt,
                                        float* __restrict__ W_state, T* __restrict__ scan_slots,
                                        int64_t g0, int64_t gc, int n1, int pad, int outputs_first,
@@ -863,15 +923,16 @@ TTT_GEMM_KERNEL void scan_apply_kernel(Dims dm, const T* __restrict__ Vt, const 
                                        T* __restrict__ O, int64_t a0, int64_t ac) {
   static_assert(Tile::kThreads == PrefixTile::kThreads && Tile::kLdsBytes == PrefixTile::kLdsBytes,
                 "both parts share the launch shape");
-  __shared__ __attribute__((aligned(16))) char smem_raw[Tile::kLdsBytes];
+  __shared__ __attribute__((aligned(16)))
+  char smem_raw[Tile::kLdsBytes + ((kScanSlots & 8) ? kSlotStageBytes : 0)];
   const int b = blockIdx.x;
   const int n2 = (int)gridDim.x - pad;
   const bool first = b < pad;
   if (first && b >= n1) return;
   const int blk = first ? b : b - pad, nblk = first ? n1 : n2;
   if (first != (outputs_first != 0))
-    prefix_update_tile<T, PrefixTile>(dm, Vt, Zt, W_state, scan_slots, g0, gc, blk, nblk,
-                                      (lds_char*)smem_raw);
+    prefix_update_tile<T, PrefixTile, kScanSlots>(dm, Vt, Zt, W_state, scan_slots, g0, gc, blk,
+                                                  nblk, (lds_char*)smem_raw);
   else
     down_proj_tile<T>(dm, Z, apply_slots, O, a0, ac, blk, nblk, (lds_char*)smem_raw);
 }
@@ -883,21 +944,21 @@ TTT_GEMM_KERNEL void scan_apply_kernel(Dims dm, const T* __restrict__ Vt, const 
 // projection tiles fill the rest.  The scan reads the target columns of
 // chunks g0 .. g0 + gc - 1, the projection writes those of chunks from t_lo
 // on: disjoint 64-token blocks.
-template <typename T>
+template <typename T, int kScanSlots = 1>
 TTT_GEMM_KERNEL void scan_target_kernel(Dims dm, const T* __restrict__ Vt,
                                         const T* __restrict__ Zt, float* __restrict__ W_state,
                                         T* __restrict__ scan_slots, int64_t g0, int64_t gc,
                                         int scan_blocks, int scan_pad, const T* __restrict__ rows,
                                         const T* __restrict__ WtT, T* __restrict__ Vt_out,
                                         int64_t t_lo) {
-  constexpr int kLds = TargetLds<T>::kBytes > PrefixTile::kLdsBytes ? TargetLds<T>::kBytes
-                                                                    : PrefixTile::kLdsBytes;
+  constexpr int kScanLds = PrefixTile::kLdsBytes + ((kScanSlots & 8) ? kSlotStageBytes : 0);
+  constexpr int kLds = TargetLds<T>::kBytes > kScanLds ? TargetLds<T>::kBytes : kScanLds;
   __shared__ __attribute__((aligned(16))) char smem_raw[kLds];
   const int b = blockIdx.x;
   if (b < scan_pad) {
     if (b < scan_blocks)
-      prefix_update_tile<T, PrefixTile>(dm, Vt, Zt, W_state, scan_slots, g0, gc, b, scan_blocks,
-                                        (lds_char*)smem_raw);
+      prefix_update_tile<T, PrefixTile, kScanSlots>(dm, Vt, Zt, W_state, scan_slots, g0, gc, b,
+                                                    scan_blocks, (lds_char*)smem_raw);
     return;
   }
   target_tile<T>(dm, rows, WtT, Vt_out, t_lo, dm.T, b - scan_pad, (int)gridDim.x - scan_pad,
@@ -1210,9 +1271,17 @@ static void launch_scan_target_t(const Dims& dm, const T* Vt, const T* Zt, float
   const int64_t pad = (scan + 7) / 8 * 8;
   const int64_t tiles =
       ((dm.T - t_lo + Tile::BM - 1) / Tile::BM) * dm.B * ((dm.d + Tile::BN - 1) / Tile::BN);
-  hipLaunchKernelGGL(scan_target_kernel<T>, dim3((unsigned)(pad + tiles)), dim3(Tile::kThreads), 0,
-                     s, dm, Vt, Zt, W_state, scan_slots, (int64_t)0, gc, (int)scan, (int)pad, rows,
-                     WtT, const_cast<T*>(Vt), t_lo);
+  if constexpr (sizeof(T) == 2) {
+    if (staged_slots<T>(dm)) {
+      hipLaunchKernelGGL((scan_target_kernel<T, 8>), dim3((unsigned)(pad + tiles)),
+                         dim3(Tile::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, (int64_t)0,
+                         gc, (int)scan, (int)pad, rows, WtT, const_cast<T*>(Vt), t_lo);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((scan_target_kernel<T, 1>), dim3((unsigned)(pad + tiles)),
+                     dim3(Tile::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, (int64_t)0, gc,
+                     (int)scan, (int)pad, rows, WtT, const_cast<T*>(Vt), t_lo);
 }
 
 bool scan_target_fits(const Dims& dm) {
@@ -1263,9 +1332,17 @@ static void launch_scan_apply_t(const Dims& dm, const T* Vt, const T* Zt, float*
     const bool outputs_first = down_tiles > 0 && scan > 0 && gc * dm.Cp < dm.f;
     const int64_t n1 = outputs_first ? down_tiles : scan, n2 = outputs_first ? scan : down_tiles;
     const int64_t pad = (n1 + 7) / 8 * 8;
-    hipLaunchKernelGGL(scan_apply_kernel<T>, dim3((unsigned)(pad + n2)), dim3(Tile::kThreads), 0,
-                       s, dm, Vt, Zt, W_state, scan_slots, g0, gc, (int)n1, (int)pad,
-                       outputs_first ? 1 : 0, Z, apply_slots, O, a0, ac);
+    if constexpr (sizeof(T) == 2) {
+      if (staged_slots<T>(dm)) {
+        hipLaunchKernelGGL((scan_apply_kernel<T, 8>), dim3((unsigned)(pad + n2)),
+                           dim3(Tile::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, g0, gc,
+                           (int)n1, (int)pad, outputs_first ? 1 : 0, Z, apply_slots, O, a0, ac);
+        return;
+      }
+    }
+    hipLaunchKernelGGL((scan_apply_kernel<T, 1>), dim3((unsigned)(pad + n2)),
+                       dim3(Tile::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, g0, gc,
+                       (int)n1, (int)pad, outputs_first ? 1 : 0, Z, apply_slots, O, a0, ac);
     return;
   }
   // 64 x 64 scan tiles when 256 does not divide the weight (d and f are

@@ -228,8 +228,11 @@ def test_scan_kernels_leave_only_stores_in_flight(tmp_path):
     # (tile shapes, slot layouts, data types)
     prefix = [n for n in funcs if "prefix_update_kernel" in n]
     assert len(prefix) >= 4, prefix
-    for key in SCAN_KERNELS + prefix:
-        body = _body(funcs, key)
+    # every instantiation of each scan kernel (slot layouts, data types)
+    names = sorted({n for key in SCAN_KERNELS for n in funcs if key in n}) + prefix
+    assert len(names) >= len(SCAN_KERNELS) + len(prefix), names
+    for key in names:
+        body = funcs[key]
         waits = _barrier_waits(body)
         leaves_stores = 0
         for at, states in waits.items():
