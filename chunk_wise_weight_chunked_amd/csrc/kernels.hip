@@ -62,11 +62,11 @@ static_assert(OutTile::kThreads == Tile::kThreads && OutTile::kLdsBytes == Tile:
 using OneChunkTile = TileShape<128, 128, 2, 2>;  // single-chunk updates
 // LDS for the staged slot rows: 4 KB per wave of the 256 x 256 scan tile.
 constexpr int kSlotStageBytes = 8 * 4096;
-// bf16 slots are staged through LDS when chunks are short (a slot every 8
-// k-tiles or fewer): there the stores, not the k-loop, hold the scan tiles.
+// bf16 slots are staged through LDS (a quarter of the store instructions);
+// fp32 slots keep the direct stores.
 template <typename T>
-bool staged_slots(const Dims& dm) {
-  return sizeof(T) == 2 && dm.Cp / (kRowBytes / (int64_t)sizeof(T)) <= 8;
+bool staged_slots(const Dims&) {
+  return sizeof(T) == 2;
 }
 #define TTT_GEMM_KERNEL                                  \
   __global__ __launch_bounds__(TTT_GEMM_THREADS)          \
@@ -527,19 +527,19 @@ __global__ __launch_bounds__(256) void rows_to_vt_kernel(Dims dm, const T* __res
 // result does not depend on how the chunks are grouped.  The tile shape S
 // divides d and f exactly (the host picks it), so every tile is full.
 // Tile `blk` of `nblk` (workgroups [0, nblk) of the launch are these tiles).
-// kSlots: which slot layouts are written -- bit 0: `slots` [G][B][d][f] (what
-// the outputs read); bit 1: `slots_t` [G][B][f][d], the weights transposed
-// (the backward's products that contract over d read them with K
-// contiguous); bit 2 (instead of bit 0): `slots` in TB x TB tiles, element
-// (m, n) of a slot at ((m / TB) (f / TB) + n / TB) TB^2 + (m % TB) TB + n % TB
-// with TB = 128 bytes of T -- every k-tile of a product that contracts over d
-// (k-major) or over f (rows of 128 bytes) is then whole 128-row blocks of
-// TB rows each, contiguous in memory; bit 3 (instead of bit 0, bf16 and the
-// 256 x 256 tile only): the `slots` layout of bit 0, each wave's block rows
-// staged through a 4 KB region of LDS past the k-tile stages (the caller's
-// `smem` holds S::kLdsBytes + kSlotStageBytes) and stored as whole 128-byte
-// row segments, 16 bytes per lane: a quarter of the store instructions, for
-// short chunks, whose slots come every few k-tiles.
+// kSlots: the slot layout, one of bits 0-2 -- 1: `slots` [G][B][d][f] (what
+// the outputs read); 2: `slots_t` [G][B][f][d], the weights transposed (the
+// backward's products that contract over d read them with K contiguous); 4:
+// `slots` in TB x TB tiles, element (m, n) of a slot at
+// ((m / TB) (f / TB) + n / TB) TB^2 + (m % TB) TB + n % TB with TB = 128
+// bytes of T -- every k-tile of a product that contracts over d (k-major) or
+// over f (rows of 128 bytes) is then whole 128-row blocks of TB rows each,
+// contiguous in memory.  Bit 3 (bf16 and waves of 128 x 64 only): the same
+// layout, each wave's 32-row block rows staged through a 4 KB region of LDS
+// past the k-tile stages (the caller's `smem` holds S::kLdsBytes +
+// kSlotStageBytes) and stored 16 bytes per lane as whole row segments (128
+// bytes of a row, 64 of a transposed row, 4 KB runs of a tile): 16 store
+// instructions per lane and slot instead of 64 (32 transposed).
 template <typename T, class S, int kSlots = 1>
 __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __restrict__ Vt,
                                                    const T* __restrict__ Zt,
@@ -605,13 +605,14 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
                               p.wave_n0 + ((p.lane & 31) & ~1)) * 2u;
   // store instructions per lane of one slot: row-major pairs (bf16) or
   // values (fp32); transposed, 4 consecutive rows of a column in one store
+  constexpr int kLayout = kSlots & 7;
   constexpr bool kStaged = (kSlots & 8) != 0;
-  static_assert(__builtin_popcount(kSlots & 13) <= 1, "one layout in `slots`");
+  static_assert(kLayout == 1 || kLayout == 2 || kLayout == 4, "one slot layout");
   static_assert(!kStaged || (sizeof(T) == 2 && S::WM == 128 && S::WN == 64),
                 "staged slots: bf16, waves of 128 x 64");
-  constexpr int kSlotStores =
-      ((kSlots & 5) ? S::MB * 4 * S::NB * (sizeof(T) == 2 ? 2 : 4) : 0) +
-      ((kSlots & 2) ? S::MB * 4 * S::NB : 0) + (kStaged ? S::MB * 4 : 0);
+  constexpr int kSlotStores = kStaged        ? S::MB * 4
+                              : kLayout == 2 ? S::MB * 4 * S::NB
+                                             : S::MB * 4 * S::NB * (sizeof(T) == 2 ? 2 : 4);
   const uint32_t lane_t = (uint32_t)(((p.wave_n0 + (p.lane & 31)) * d + p.wave_m0 +
                                       4 * (p.lane >> 5)) * (int64_t)sizeof(T));
   const uint32_t du = (uint32_t)d;
@@ -697,17 +698,44 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
       }
   };
   // Staged slots: block row i of the wave (32 rows x 64 columns, bf16) goes
-  // to the wave's LDS region as column pairs (row r at r * 128 bytes, its
-  // 16-byte chunk c at c ^ (r & 7)), then back as 16-byte chunks, lane l
-  // taking chunk l & 7 of row 8 s + l / 8, and out as whole row segments.
-  // A wave's LDS accesses run in order, so each block row's reads come
-  // before the next one's writes.
+  // to the wave's LDS region and back as 16-byte chunks, one row segment per
+  // 2-8 lanes, then out with one 16-byte store per chunk.  Rows and tiles:
+  // the LDS image is row-major (row r at r * 128 bytes, its 16-byte chunk c
+  // at c ^ (r & 7)), written as column pairs; lane l reads chunk l & 7 of
+  // row 8 s + l / 8.  Transposed: the image is column-major (column n at
+  // n * 64 bytes, chunk c -- rows 8 c .. 8 c + 7 -- at c ^ ((n / 4) & 3)),
+  // written as the lane's 4 consecutive rows of a column; lane l reads chunk
+  // l & 3 of column 16 s + l / 4.  Both swizzles keep the writes at two
+  // passes and the reads conflict-free.  A wave's LDS accesses run in order,
+  // so each block row's reads come before the next one's writes.
   lds_char* const stage_slot = smem + S::kLdsBytes + (threadIdx.x >> 6) * 4096;
-  const uint32_t lane_row = (uint32_t)((p.lane >> 3) * f + 8 * (p.lane & 7)) * 2u;
-  const uint32_t wave_off = (uint32_t)(p.wave_m0 * f + p.wave_n0) * 2u;
+  uint32_t lane_st = 0, wave_st = 0;  // per-lane and per-wave byte offsets of the stores
+  int64_t base_st = 0, span_st = 0;   // first element and extent from it
+  if constexpr (kLayout == 1) {
+    lane_st = (uint32_t)((p.lane >> 3) * f + 8 * (p.lane & 7)) * 2u;
+    wave_st = (uint32_t)(p.wave_m0 * f + p.wave_n0) * 2u;
+    base_st = b * d * f + corner;
+    span_st = span;
+  } else if constexpr (kLayout == 2) {
+    lane_st = (uint32_t)((p.lane >> 2) * d + 8 * (p.lane & 3)) * 2u;
+    wave_st = (uint32_t)(p.wave_n0 * d + p.wave_m0) * 2u;
+    base_st = b * d * f + n0 * d + m0;
+    span_st = (f - n0) * d - m0;
+  } else {
+    lane_st = (uint32_t)(8 * p.lane) * 2u;  // 8 rows of TB values: 1 KB in a row of lanes
+    wave_st = (uint32_t)((p.wave_m0 / TB) * fT * TB * TB + (p.wave_n0 / TB) * TB * TB) * 2u;
+    base_st = b * d * f + corner_t;
+    span_st = d * f - corner_t;
+  }
+  auto staged_uniform = [&](int i, int s4) -> uint32_t {
+    if constexpr (kLayout == 1) return (uint32_t)((32 * i + 8 * s4) * f) * 2u;
+    if constexpr (kLayout == 2) return (uint32_t)(16 * s4 * d + 32 * i) * 2u;
+    const int r = 32 * i + 8 * s4;  // rows of the wave; TB = 64 divides 32 * 2
+    return (uint32_t)((r / TB) * fT * TB * TB + (r % TB) * TB) * 2u;
+  };
   auto write_slot_staged = [&](int64_t js) {
-    const rsrc_t sr = make_rsrc(slots + js * slot_stride + b * d * f + corner,
-                                span * (int64_t)sizeof(T));
+    T* const dst = kLayout == 2 ? slots_t : slots;
+    const rsrc_t sr = make_rsrc(dst + js * slot_stride + base_st, span_st * (int64_t)sizeof(T));
 #pragma unroll
     for (int i = 0; i < S::MB; ++i) {
 #pragma unroll
@@ -717,34 +745,48 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
           float z[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) z[e] = acc.v[i][j][4 * q + e];
-          uint32_t w[2];
-          pair_pack(z, odd, w);
+          if constexpr (kLayout == 2) {
+            const int n = 32 * j + (p.lane & 31);
+            lds_store<u32x2_t>(stage_slot + n * 64 + ((q ^ ((n >> 2) & 3)) << 4) +
+                                   (p.lane >> 5) * 8,
+                               u32x2_t{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])});
+          } else {
+            uint32_t w[2];
+            pair_pack(z, odd, w);
 #pragma unroll
-          for (int r = 0; r < 2; ++r) {
-            const int row = 8 * q + 4 * (p.lane >> 5) + (odd ? 2 : 0) + r;
-            const int col = 32 * j + ((p.lane & 31) & ~1);
-            lds_store<uint32_t>(stage_slot + row * kRowBytes + ((((col >> 3) ^ (row & 7))) << 4) +
-                                    (col & 7) * 2,
-                                w[r]);
+            for (int r = 0; r < 2; ++r) {
+              const int row = 8 * q + 4 * (p.lane >> 5) + (odd ? 2 : 0) + r;
+              const int col = 32 * j + ((p.lane & 31) & ~1);
+              lds_store<uint32_t>(stage_slot + row * kRowBytes +
+                                      ((((col >> 3) ^ (row & 7))) << 4) + (col & 7) * 2,
+                                  w[r]);
+            }
           }
         }
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        const int row = 8 * s4 + (p.lane >> 3);
-        const u32x4_t v =
-            lds_load<u32x4_t>(stage_slot + row * kRowBytes + ((((p.lane & 7) ^ (row & 7))) << 4));
-        __builtin_amdgcn_raw_buffer_store_b128(
-            v, sr, lane_row, wave_off + (uint32_t)((32 * i + 8 * s4) * f) * 2u, 0);
+        u32x4_t v;
+        if constexpr (kLayout == 2) {
+          const int n = 16 * s4 + (p.lane >> 2);
+          v = lds_load<u32x4_t>(stage_slot + n * 64 + (((p.lane & 3) ^ ((n >> 2) & 3)) << 4));
+        } else {
+          const int row = 8 * s4 + (p.lane >> 3);
+          v = lds_load<u32x4_t>(stage_slot + row * kRowBytes + ((((p.lane & 7) ^ (row & 7))) << 4));
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(v, sr, lane_st, wave_st + staged_uniform(i, s4), 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto write_slot = [&](int64_t jj) {
     const int64_t js = dm.reverse_slots ? gc - 1 - jj : jj;
-    if constexpr ((kSlots & 2) != 0) write_slot_t(js);
-    if constexpr ((kSlots & 4) != 0) write_slot_tiled(js);
-    if constexpr (kStaged) write_slot_staged(js);
-    if constexpr ((kSlots & 1) == 0) return;
+    if constexpr (kStaged) {
+      write_slot_staged(js);
+      return;
+    }
+    if constexpr (kLayout == 2) write_slot_t(js);
+    if constexpr (kLayout == 4) write_slot_tiled(js);
+    if constexpr (kLayout != 1) return;
     const rsrc_t sr = make_rsrc(slots + js * slot_stride + b * d * f + corner,
                                 span * (int64_t)sizeof(T));
 #pragma unroll
@@ -779,7 +821,7 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
   };
 
   // none: the increments' sum only
-  const bool with_slots = (kSlots & 13) ? slots != nullptr : slots_t != nullptr;
+  const bool with_slots = kLayout == 2 ? slots_t != nullptr : slots != nullptr;
   if (with_slots) write_slot(0);
   const int64_t kt_per_chunk = dm.Cp / TB;
   // a streaming call leaves the sequence's last chunk out of the state (its
@@ -976,15 +1018,17 @@ TTT_GEMM_KERNEL void dual_scan_kernel(Dims d1, const T* __restrict__ Vt1, const 
                                       const T* __restrict__ Vt2, const T* __restrict__ Zt2,
                                       float* __restrict__ W2, T* __restrict__ slots2, int blocks,
                                       int pad) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[Tile::kLdsBytes];
+  constexpr int kStage = sizeof(T) == 2 ? 8 : 0;  // bf16 slots staged through LDS
+  __shared__ __attribute__((aligned(16)))
+  char smem_raw[Tile::kLdsBytes + (kStage ? kSlotStageBytes : 0)];
   const int b = blockIdx.x;
   if (b < pad) {
     if (b < blocks)
-      prefix_update_tile<T, PrefixTile, 2>(d1, Vt1, Zt1, W1, nullptr, 0, d1.N, b, blocks,
-                                           (lds_char*)smem_raw, slots1t);
+      prefix_update_tile<T, PrefixTile, 2 | kStage>(d1, Vt1, Zt1, W1, nullptr, 0, d1.N, b, blocks,
+                                                    (lds_char*)smem_raw, slots1t);
   } else if (b - pad < blocks) {
-    prefix_update_tile<T, PrefixTile, 4>(d2, Vt2, Zt2, W2, slots2, 0, d2.N, b - pad, blocks,
-                                         (lds_char*)smem_raw);
+    prefix_update_tile<T, PrefixTile, 4 | kStage>(d2, Vt2, Zt2, W2, slots2, 0, d2.N, b - pad,
+                                                  blocks, (lds_char*)smem_raw);
   }
 }
 
@@ -1273,7 +1317,7 @@ static void launch_scan_target_t(const Dims& dm, const T* Vt, const T* Zt, float
       ((dm.T - t_lo + Tile::BM - 1) / Tile::BM) * dm.B * ((dm.d + Tile::BN - 1) / Tile::BN);
   if constexpr (sizeof(T) == 2) {
     if (staged_slots<T>(dm)) {
-      hipLaunchKernelGGL((scan_target_kernel<T, 8>), dim3((unsigned)(pad + tiles)),
+      hipLaunchKernelGGL((scan_target_kernel<T, 9>), dim3((unsigned)(pad + tiles)),
                          dim3(Tile::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, (int64_t)0,
                          gc, (int)scan, (int)pad, rows, WtT, const_cast<T*>(Vt), t_lo);
       return;
@@ -1334,7 +1378,7 @@ static void launch_scan_apply_t(const Dims& dm, const T* Vt, const T* Zt, float*
     const int64_t pad = (n1 + 7) / 8 * 8;
     if constexpr (sizeof(T) == 2) {
       if (staged_slots<T>(dm)) {
-        hipLaunchKernelGGL((scan_apply_kernel<T, 8>), dim3((unsigned)(pad + n2)),
+        hipLaunchKernelGGL((scan_apply_kernel<T, 9>), dim3((unsigned)(pad + n2)),
                            dim3(Tile::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, g0, gc,
                            (int)n1, (int)pad, outputs_first ? 1 : 0, Z, apply_slots, O, a0, ac);
         return;
