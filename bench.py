@@ -34,7 +34,8 @@ def log(*a):
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for rel in ("chunk_wise_weight_chunked_amd/csrc/kernels.hip",
-                "chunk_wise_weight_chunked_amd/csrc/gemm_core.h"):
+                "chunk_wise_weight_chunked_amd/csrc/gemm_core.h",
+                "chunk_wise_weight_chunked_amd/csrc/epilogue.h"):
         with open(os.path.join(ROOT, rel), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -253,9 +253,9 @@ ttt_status_t run_activations(const ttt::Dims& dm, const ttt::WorkspacePlan& wp, 
     return ttt::launch_weight_prep(dm, Wg, Wu, Wt, taps, WgU, WtT, tapsT, s);
   });
   if (e != hipSuccess) return hip_fail(e, "weight_prep");
-  const bool padded = dm.Cp != dm.C || dm.T % dm.C != 0;
+  const bool padded = !ttt::chunk_map_is_identity(dm);
   if (padded) {
-    e = staged(kPad, s, [&] { return ttt::launch_pad_fill(Zt, Vt, dm, s); });
+    e = staged(kPad, s, [&] { return ttt::launch_pad_fill(Zt, dm.f, Vt, dm.d, dm, s); });
     if (e != hipSuccess) return hip_fail(e, "pad_fill");
   }
   e = staged(kTarget, s, [&] {

@@ -20,7 +20,7 @@ namespace {
 // own regions, 256-byte aligned.
 struct BackwardPlan {
   ttt::WorkspacePlan fwd;
-  size_t wst, u, v, agu, ztr, dotr, sslots, dz, da, wgu, g, gf, du, tpart, dpart, wtpart, dak,
+  size_t wst, u, v, agu, ztr, dotr, sslots, da, wgu, g, gf, du, tpart, dpart, wtpart, dak,
       hk, uk, gk, wgut, total;
   int64_t wt_slices;  // token slices of the dW_target product (split over K = B*T)
 };
@@ -43,7 +43,6 @@ BackwardPlan plan_backward(const ttt::Dims& dm) {
   p.ztr = take(f * (size_t)dm.P * es);                    // Zt, chunks reversed
   p.dotr = take(d * (size_t)dm.P * es);                   // dOᵀ k-blocked, chunks reversed
   p.sslots = take((size_t)dm.N * dm.B * d * f * es);      // S_j, reversed chunk order
-  p.dz = take(BT * f * 4);                                // dZ (fp32)
   p.da = take(BT * 2 * f * es);                           // [dA_g | dA_u]
   p.wgu = take(2 * f * d * es);                           // [W_gate; W_up]
   p.gf = take(BT * d * 4);                                // G = Z_j S_jᵀ (dV^ = eta G), fp32
@@ -105,11 +104,6 @@ struct Gemm {
   template <class... A>
   void operator()(A... a) {
     if (err == hipSuccess) err = ttt::launch_gemm(product(dt, a...), s);
-  }
-  // g.C = g.alpha (g.A g.Bᵀ + g2.alpha g2.A g2.Bᵀ) in one launch (g2's C
-  // unused).
-  void pair(const ttt::GemmArgs& g, const ttt::GemmArgs& g2) {
-    if (err == hipSuccess) err = ttt::launch_gemm2(g, g2, s);
   }
 };
 
@@ -200,12 +194,10 @@ ttt_status_t ttt_mlp_backward_batched(
   float* Wst = reinterpret_cast<float*>(base + bp.wst);
   void* U = dm.conv ? static_cast<void*>(base + bp.u) : const_cast<void*>(X0);
   void* V = dm.proj ? static_cast<void*>(base + bp.v) : U;
-  float* Ag = reinterpret_cast<float*>(base + bp.agu);  // row t at t * 2f
-  float* Au = Ag + f;
+  float* Ag = reinterpret_cast<float*>(base + bp.agu);  // row t: [A_g | A_u], 2f wide
   void* Ztr = base + bp.ztr;
   void* dOtr = base + bp.dotr;
   char* Sslots = base + bp.sslots;
-  float* dZ = reinterpret_cast<float*>(base + bp.dz);
   char* dA = base + bp.da;
   char* Wgu = base + bp.wgu;
   float* Gf = reinterpret_cast<float*>(base + bp.gf);
@@ -218,7 +210,8 @@ ttt_status_t ttt_mlp_backward_batched(
   hipError_t e = init ? ttt::launch_state_reset(Wst, W_down0, dm.dt, dm.B, dm.d, dm.f, s)
                       : hipMemcpyAsync(Wst, W_start, state, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess) e = ttt::launch_weight_prep(dm, W_gate, W_up, W_target, conv_taps, WgU, WtT, tapsT, s);
-  if (e == hipSuccess && (dm.Cp != dm.C || dm.T % dm.C != 0)) e = ttt::launch_pad_fill(Zt, Vt, dm, s);
+  if (e == hipSuccess && !ttt::chunk_map_is_identity(dm))
+    e = ttt::launch_pad_fill(Zt, dm.f, Vt, dm.d, dm, s);
   if (e == hipSuccess) e = ttt::launch_target(dm, X0, tapsT, WtT, dm.conv ? U : Z, Vt, s);
   if (e == hipSuccess) e = hipMemcpyAsync(Wgu, W_gate, f * d * es, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(Wgu + f * d * es, W_up, f * d * es, hipMemcpyDeviceToDevice, s);
@@ -238,7 +231,6 @@ ttt_status_t ttt_mlp_backward_batched(
     gemm(kRowK, kRowK, BTi, Di, Di, 1.f, U, Di, 0, WtT, Di, 0, false, V, Di, 0, 1, act_f32);
   if (gemm.err != hipSuccess) return hip_fail(gemm.err, "backward gemm");
   // operands of the later products in the layouts they are read in
-  void* dAk = base + bp.dak;
   void* Hk = base + bp.hk;
   void* Uk = base + bp.uk;
   void* Gk = base + bp.gk;
@@ -267,11 +259,17 @@ ttt_status_t ttt_mlp_backward_batched(
   if (e != hipSuccess) return hip_fail(e, "backward");
 
   // per chunk j: dZ_j = dO_j W^(j-1) + eta V^_j S_j (one launch: both
-  // products on the same accumulators) and G_j = Z_j S_jᵀ, with W^(j-1)
-  // (transposed: K = d contiguous) and S_j (in TB x TB tiles: k-major tiles
-  // for dZ, K-contiguous tiles for G) in slot j.  The full chunks of a sequence are one batch
-  // (rows C apart, slots B*d*f apart); a ragged last chunk is one batch over
-  // the sequences.
+  // products on the same accumulators) with the SwiGLU derivative in its
+  // epilogue, which writes dA = [dA_g | dA_u] row-major and k-blocked; and
+  // G_j = Z_j S_jᵀ.  W^(j-1) (transposed: K = d contiguous) and S_j (in
+  // TB x TB tiles: k-major tiles for dZ, K-contiguous tiles for G) are in
+  // slot j.  The full chunks of a sequence are one batch (rows C apart, slots
+  // B*d*f apart); a ragged last chunk is one batch over the sequences.
+  void* dAk = base + bp.dak;
+  if (!ttt::chunk_map_is_identity(dm)) {
+    e = ttt::launch_pad_fill(dAk, 2 * Fi, nullptr, 0, dm, s);  // padding token columns of dAk
+    if (e != hipSuccess) return hip_fail(e, "backward");
+  }
   const char* Zc = static_cast<const char*>(Z);
   const char* dOc = static_cast<const char*>(dO);
   const char* Vc = static_cast<const char*>(V);
@@ -280,12 +278,13 @@ ttt_status_t ttt_mlp_backward_batched(
     const int64_t r = b0 * T + j * C;  // first row
     const char* WjT = Wslots + (size_t)(j * sl + b0 * Di * Fi) * es;
     const char* Sj = Sslots + (size_t)(j * sl + b0 * Di * Fi) * es;
-    gemm.pair(product(dm.dt, kRowK, kRowK, rows, Fi, Di, 1.f, dOc + r * d * es, Di,
-                      row_stride * Di, WjT, Di, slot_stride, false, dZ + r * f, Fi,
-                      row_stride * Fi, count, f32),
-              product(dm.dt, kRowK, kTiledKMajor, rows, Fi, Di, dm.eta, Vc + r * d * es, Di,
-                      row_stride * Di, Sj, Fi, slot_stride, false, nullptr, Fi, row_stride * Fi,
-                      count, f32));
+    if (gemm.err == hipSuccess)
+      gemm.err = ttt::launch_dz_swiglu(
+          product(dm.dt, kRowK, kRowK, rows, Fi, Di, 1.f, dOc + r * d * es, Di, row_stride * Di,
+                  WjT, Di, slot_stride, false, nullptr, Fi, 0, count, f32),
+          product(dm.dt, kRowK, kTiledKMajor, rows, Fi, Di, dm.eta, Vc + r * d * es, Di,
+                  row_stride * Di, Sj, Fi, slot_stride, false, nullptr, Fi, 0, count, f32),
+          dm, r, row_stride, Ag, dA, dAk, s);
     gemm(kRowK, kTiledRowK, rows, Di, Fi, 1.f, Zc + r * f * es, Fi, row_stride * Fi, Sj, Fi,
          slot_stride, false, Gf + r * d, Di, row_stride * Di, count, f32);
   };
@@ -294,13 +293,10 @@ ttt_status_t ttt_mlp_backward_batched(
     for (int64_t b = 0; b < B; ++b) chunk_gemms(0, C, b, full, C, sl);
   if (full < N) chunk_gemms(full, T - full * C, 0, B, T, Di * Fi);
   if (gemm.err != hipSuccess) return hip_fail(gemm.err, "backward gemm");
-  // 4. eta's gradient sum_t <V^[t], G[t]>; the SwiGLU derivative; dH and the
-  //    gated MLP's weight gradients
+  // 4. eta's gradient sum_t <V^[t], G[t]>; dH and the gated MLP's weight
+  //    gradients
   e = ttt::launch_dot(V, Gf, BTi * Di, dm.dt, 1.0f, dpart, d_eta, s);
-  if (e == hipSuccess) e = ttt::launch_swiglu_backward(dZ, Ag, Au, 2 * Fi, dA, dm, s);
   if (e == hipSuccess && dm.proj) e = ttt::launch_from_f32(Gf, G, BTi * Di, dm.dt, s);
-  if (e != hipSuccess) return hip_fail(e, "backward");
-  e = ttt::launch_to_kblocked(dA, dAk, dm, 2 * dm.f, false, s);
   if (e == hipSuccess && dm.proj) e = ttt::launch_to_kblocked(G, Gk, dm, dm.d, false, s);
   if (e != hipSuccess) return hip_fail(e, "backward");
   const int64_t tb = 128 / (int64_t)es, P = dm.P;  // tokens per 128-byte block row

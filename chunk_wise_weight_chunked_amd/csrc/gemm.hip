@@ -16,6 +16,7 @@
 
 #include <algorithm>
 
+#include "epilogue.h"
 #include "gemm_core.h"
 #include "layer.h"
 
@@ -130,34 +131,39 @@ __device__ __forceinline__ auto make_loader(const char* X, int64_t ld, int64_t s
 
 constexpr bool is_kmajor(int l) { return l == kKMajor || l == kTiledKMajor; }
 
-// kLA2 >= 0: the second product (g2's A, B, K and alpha; g's M, N and batch)
-// runs first on the same accumulators, which are then scaled by g2.alpha.
-template <typename T, int kLA, int kLB, int kLA2 = -1, int kLB2 = -1>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(
-    GemmArgs g, GemmArgs g2) {
-  using S = GTile;
-  static_assert(S::kLdsBytes >= S::BM * kEpiStride * 4, "epilogue stage fits the pipeline's LDS");
-  __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
-  lds_char* smem = (lds_char*)smem_raw;
-  constexpr int64_t es = sizeof(T);
-  constexpr int TB = kRowBytes / (int)sizeof(T);
+// The tile's position: batch b and the first row and column of the tile.
+struct GemmTilePos {
+  int64_t b, m0, n0;
+};
+
+template <class S>
+__device__ __forceinline__ GemmTilePos gemm_tile_pos(const GemmArgs& g) {
   const int tiles_m = (int)((g.M + S::BM - 1) / S::BM);
   const int tiles_n = (int)((g.N + S::BN - 1) / S::BN);
   const int per_batch = tiles_m * tiles_n;
   const int L = xcd_remap(blockIdx.x, (int)gridDim.x);
   const int64_t b = L / per_batch;
   const TileCoord tc = grouped_tile(L - (int)b * per_batch, tiles_m, tiles_n, 8);
-  const int64_t m0 = (int64_t)tc.m * S::BM, n0 = (int64_t)tc.n * S::BN;
+  return GemmTilePos{b, (int64_t)tc.m * S::BM, (int64_t)tc.n * S::BN};
+}
 
-  Accum<S> acc;
+// acc = A[b] B[b]ᵀ of g for the tile at t; with kLA2 >= 0, the second
+// product (g2's A, B, K and alpha; g's M, N and batch) runs first on the
+// same accumulators, which are then scaled by g2.alpha.
+template <typename T, int kLA, int kLB, int kLA2, int kLB2, class S>
+__device__ __forceinline__ void gemm_accumulate(const GemmArgs& g, const GemmArgs& g2,
+                                                const GemmTilePos& t, Accum<S>& acc,
+                                                lds_char* smem, const LanePos& p) {
+  constexpr int64_t es = sizeof(T);
+  constexpr int TB = kRowBytes / (int)sizeof(T);
+  const int64_t b = t.b;
   acc.zero();
-  const LanePos p = lane_pos<S>();
   if constexpr (kLA2 >= 0) {
     const int64_t K2 = b + 1 == g2.batch ? g2.K_last : g2.K;
     auto la = make_loader<T, kLA2, S::BM>(static_cast<const char*>(g2.A) + b * g2.sa * es, g2.lda,
-                                          g2.sa, b, m0, g.M, K2);
+                                          g2.sa, b, t.m0, g.M, K2);
     auto lb = make_loader<T, kLB2, S::BN>(static_cast<const char*>(g2.B) + b * g2.sb * es, g2.ldb,
-                                          g2.sb, b, n0, g.N, K2);
+                                          g2.sb, b, t.n0, g.N, K2);
     mainloop<T, S, true, is_kmajor(kLA2), is_kmajor(kLB2)>(acc, la, lb, (K2 + TB - 1) / TB, smem,
                                                            p, [](int64_t) {});
 #pragma unroll
@@ -169,17 +175,128 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   const int64_t K = b + 1 == g.batch ? g.K_last : g.K;
   auto la = make_loader<T, kLA, S::BM>(static_cast<const char*>(g.A) + b * g.sa * es, g.lda, g.sa,
-                                       b, m0, g.M, K);
+                                       b, t.m0, g.M, K);
   auto lb = make_loader<T, kLB, S::BN>(static_cast<const char*>(g.B) + b * g.sb * es, g.ldb, g.sb,
-                                       b, n0, g.N, K);
+                                       b, t.n0, g.N, K);
   mainloop<T, S, true, is_kmajor(kLA), is_kmajor(kLB)>(acc, la, lb, (K + TB - 1) / TB, smem, p,
                                                        [](int64_t) {});
+}
+
+template <typename T, int kLA, int kLB>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(
+    GemmArgs g) {
+  using S = GTile;
+  static_assert(S::kLdsBytes >= S::BM * kEpiStride * 4, "epilogue stage fits the pipeline's LDS");
+  __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
+  lds_char* smem = (lds_char*)smem_raw;
+  const GemmTilePos t = gemm_tile_pos<S>(g);
+  Accum<S> acc;
+  const LanePos p = lane_pos<S>();
+  gemm_accumulate<T, kLA, kLB, -1, -1>(g, g, t, acc, smem, p);
   if (g.c_f32)
-    gemm_epilogue<S, float>(acc, p, smem, static_cast<float*>(g.C) + b * g.sc, g.ldc, m0, n0, g.M,
-                            g.N, g.alpha, g.accumulate != 0);
+    gemm_epilogue<S, float>(acc, p, smem, static_cast<float*>(g.C) + t.b * g.sc, g.ldc, t.m0, t.n0,
+                            g.M, g.N, g.alpha, g.accumulate != 0);
   else
-    gemm_epilogue<S, T>(acc, p, smem, static_cast<T*>(g.C) + b * g.sc, g.ldc, m0, n0, g.M, g.N,
-                        g.alpha, false);
+    gemm_epilogue<S, T>(acc, p, smem, static_cast<T*>(g.C) + t.b * g.sc, g.ldc, t.m0, t.n0, g.M,
+                        g.N, g.alpha, false);
+}
+
+// dZ = dO_j W^(j-1) + eta V^_j S_j in the accumulators (g: dO_j and the
+// transposed weight slot, both K-contiguous; g2: V^_j and S_j read as k-major
+// tiles), then the SwiGLU derivative per element: dZ never leaves the tile.
+// Epilogue per pass of kPass columns: dZ staged in fp32; each thread takes
+// two token rows x 8 columns, reads A_g and A_u (fp32) for them, writes the
+// row-major dA runs and puts the values into two token-major stages (dA_g,
+// dA_u), which then leave as k-blocked block rows.  The derivative is the
+// plain formula in fp32 (sigmoid as 1 / (1 + exp(-A_g))).
+template <typename T>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void dz_swiglu_kernel(
+    GemmArgs g, GemmArgs g2, Dims dm, int64_t row0, int64_t row_stride,
+    const float* __restrict__ Ag, T* __restrict__ dA, T* __restrict__ dAk) {
+  using S = GTile;
+  constexpr int kPass = sizeof(T) == 2 ? 64 : 32;  // columns per epilogue pass
+  constexpr int kStride = kPass + 8;               // floats per staged dZ row
+  using St = Stage<T, S::kThreads, kPass>;
+  constexpr int kDzBytes = S::BM * kStride * 4;
+  constexpr int kEpiBytes = kDzBytes + 2 * St::kBytes;
+  constexpr int kLds = S::kLdsBytes > kEpiBytes ? S::kLdsBytes : kEpiBytes;
+  static_assert(St::kToks == S::BM && S::BN % kPass == 0 && kPass % 32 == 0,
+                "passes cover whole 32-column blocks of the tile's rows");
+  __shared__ __attribute__((aligned(16))) char smem_raw[kLds];
+  lds_char* smem = (lds_char*)smem_raw;
+  const GemmTilePos t = gemm_tile_pos<S>(g);
+  Accum<S> acc;
+  const LanePos p = lane_pos<S>();
+  gemm_accumulate<T, kRowK, kRowK, kRowK, kTiledKMajor>(g, g2, t, acc, smem, p);
+
+  const int64_t f = dm.f, f2 = 2 * dm.f;
+  const int64_t grow0 = row0 + t.b * row_stride + t.m0;  // token row of tile row 0
+  const int rows_valid = (int)min<int64_t>(S::BM, g.M - t.m0);
+  const ChunkMap cm = chunk_map(dm);
+  lds_char* const dz = smem;
+  lds_char* const stage_g = smem + kDzBytes;
+  lds_char* const stage_u = stage_g + St::kBytes;
+  constexpr int kGroups = kPass / 8;
+  for (int q = 0; q < S::BN / kPass; ++q) {
+    __syncthreads();  // the mainloop's (or the previous pass's) reads of LDS are done
+#pragma unroll
+    for (int j = 0; j < S::NB; ++j) {
+      const int col = p.wave_n0 + 32 * j;
+      if (col < kPass * q || col >= kPass * q + kPass) continue;
+      const int c = col - kPass * q + (p.lane & 31);
+#pragma unroll
+      for (int i = 0; i < S::MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          lds_store<float>(dz + ((uint32_t)p.row(i, r) * kStride + c) * 4, g.alpha * acc.v[i][j][r]);
+    }
+    __syncthreads();
+    const int64_t cb = t.n0 + kPass * q;
+    const int ncols = (int)max<int64_t>(0, min<int64_t>(kPass, g.N - cb));
+    for (int it = threadIdx.x; it < (S::BM / 2) * kGroups; it += S::kThreads) {
+      const int t0 = 2 * (it / kGroups), c = (it % kGroups) * 8;
+      if (t0 >= rows_valid || c >= ncols) continue;
+      float dag[2][8], dau[2][8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int tr = t0 + h;
+        if (tr >= rows_valid) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dag[h][e] = dau[h][e] = 0.0f;
+          continue;
+        }
+        const uint32_t srow = (uint32_t)tr * kStride + c;
+        const floatx4_t z0 = lds_load<floatx4_t>(dz + srow * 4);
+        const floatx4_t z1 = lds_load<floatx4_t>(dz + (srow + 4) * 4);
+        const float* a = Ag + (grow0 + tr) * f2 + cb + c;
+        const float4 g0 = *reinterpret_cast<const float4*>(a);
+        const float4 g1 = *reinterpret_cast<const float4*>(a + 4);
+        const float4 u0 = *reinterpret_cast<const float4*>(a + f);
+        const float4 u1 = *reinterpret_cast<const float4*>(a + f + 4);
+        const float zz[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
+        const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float sg = 1.0f / (1.0f + __expf(-gg[e]));
+          dag[h][e] = zz[e] * uu[e] * sg * (1.0f + gg[e] * (1.0f - sg));
+          dau[h][e] = zz[e] * gg[e] * sg;
+        }
+        T* const out = dA + (grow0 + tr) * f2 + cb + c;
+        store8<T>(out, dag[h], false);
+        store8<T>(out + f, dau[h], false);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        St::put2(stage_g, c + e, t0, dag[0][e], dag[1][e]);
+        St::put2(stage_u, c + e, t0, dau[0][e], dau[1][e]);
+      }
+    }
+    __syncthreads();
+    const int32_t r0 = (int32_t)grow0, r1 = (int32_t)(grow0 + rows_valid);
+    St::flush_tokens(stage_g, dAk, f2, cb, ncols, r0, r1, cm);
+    St::flush_tokens(stage_u, dAk, f2, f + cb, ncols, r0, r1, cm);
+  }
 }
 
 // [A_g | A_u] = H [W_gate; W_up]ᵀ in fp32 and Z = SiLU(A_g) * A_u in one
@@ -246,39 +363,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 template <typename T>
-hipError_t launch_gemm_t(const GemmArgs& g, const GemmArgs* g2, hipStream_t s) {
+hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s) {
   const int64_t tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
   const dim3 grid((unsigned)tiles), block(512);
   const int32_t combo = g.a_layout * 8 + g.b_layout;
-  if (g2) {
-    // the fused pair the backward uses: dO W (K contiguous) + eta V^ S (tiles)
-    if (combo != kRowK * 8 + kRowK || g2->a_layout != kRowK || g2->b_layout != kTiledKMajor)
-      return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_kernel<T, kRowK, kRowK, kRowK, kTiledKMajor>), grid, block, 0, s, g,
-                       *g2);
-    return hipGetLastError();
-  }
   switch (combo) {
     case kRowK * 8 + kRowK:
-      hipLaunchKernelGGL((gemm_kernel<T, kRowK, kRowK>), grid, block, 0, s, g, g);
+      hipLaunchKernelGGL((gemm_kernel<T, kRowK, kRowK>), grid, block, 0, s, g);
       break;
     case kRowK * 8 + kKMajor:
-      hipLaunchKernelGGL((gemm_kernel<T, kRowK, kKMajor>), grid, block, 0, s, g, g);
+      hipLaunchKernelGGL((gemm_kernel<T, kRowK, kKMajor>), grid, block, 0, s, g);
       break;
     case kRowK * 8 + kTiledRowK:
-      hipLaunchKernelGGL((gemm_kernel<T, kRowK, kTiledRowK>), grid, block, 0, s, g, g);
+      hipLaunchKernelGGL((gemm_kernel<T, kRowK, kTiledRowK>), grid, block, 0, s, g);
       break;
     case kRowK * 8 + kTiledKMajor:
-      hipLaunchKernelGGL((gemm_kernel<T, kRowK, kTiledKMajor>), grid, block, 0, s, g, g);
+      hipLaunchKernelGGL((gemm_kernel<T, kRowK, kTiledKMajor>), grid, block, 0, s, g);
       break;
     case kKMajor * 8 + kRowK:
-      hipLaunchKernelGGL((gemm_kernel<T, kKMajor, kRowK>), grid, block, 0, s, g, g);
+      hipLaunchKernelGGL((gemm_kernel<T, kKMajor, kRowK>), grid, block, 0, s, g);
       break;
     case kKMajor * 8 + kKMajor:
-      hipLaunchKernelGGL((gemm_kernel<T, kKMajor, kKMajor>), grid, block, 0, s, g, g);
+      hipLaunchKernelGGL((gemm_kernel<T, kKMajor, kKMajor>), grid, block, 0, s, g);
       break;
     case kKBlocked * 8 + kKBlocked:
-      hipLaunchKernelGGL((gemm_kernel<T, kKBlocked, kKBlocked>), grid, block, 0, s, g, g);
+      hipLaunchKernelGGL((gemm_kernel<T, kKBlocked, kKBlocked>), grid, block, 0, s, g);
       break;
     default:
       return hipErrorInvalidValue;
@@ -327,17 +436,27 @@ __global__ __launch_bounds__(256) void transpose_rect_kernel(T* __restrict__ dst
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
   if (!gemm_args_ok(g)) return hipErrorInvalidValue;
-  if (g.dt == Dtype::BF16) return launch_gemm_t<uint16_t>(g, nullptr, s);
-  return launch_gemm_t<float>(g, nullptr, s);
+  if (g.dt == Dtype::BF16) return launch_gemm_t<uint16_t>(g, s);
+  return launch_gemm_t<float>(g, s);
 }
 
-hipError_t launch_gemm2(const GemmArgs& g, const GemmArgs& g2, hipStream_t s) {
+hipError_t launch_dz_swiglu(const GemmArgs& g, const GemmArgs& g2, const Dims& dm, int64_t row0,
+                            int64_t row_stride, const float* Ag, void* dA, void* dAk,
+                            hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
-  if (!gemm_args_ok(g) || !gemm_args_ok(g2) || g2.dt != g.dt || g2.M != g.M || g2.N != g.N ||
-      g2.batch != g.batch || g.accumulate)
+  if (!gemm_args_ok(g) || !gemm_args_ok(g2) || g2.dt != g.dt || g.dt != dm.dt || g2.M != g.M ||
+      g2.N != g.N || g2.batch != g.batch || g.N != dm.f || g.a_layout != kRowK ||
+      g.b_layout != kRowK || g2.a_layout != kRowK || g2.b_layout != kTiledKMajor ||
+      row0 < 0 || row0 + (g.batch - 1) * row_stride + g.M > dm.B * dm.T)
     return hipErrorInvalidValue;
-  if (g.dt == Dtype::BF16) return launch_gemm_t<uint16_t>(g, &g2, s);
-  return launch_gemm_t<float>(g, &g2, s);
+  const dim3 grid((unsigned)(((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch)), block(512);
+  if (g.dt == Dtype::BF16)
+    hipLaunchKernelGGL(dz_swiglu_kernel<uint16_t>, grid, block, 0, s, g, g2, dm, row0, row_stride,
+                       Ag, static_cast<uint16_t*>(dA), static_cast<uint16_t*>(dAk));
+  else
+    hipLaunchKernelGGL(dz_swiglu_kernel<float>, grid, block, 0, s, g, g2, dm, row0, row_stride, Ag,
+                       static_cast<float*>(dA), static_cast<float*>(dAk));
+  return hipGetLastError();
 }
 
 hipError_t launch_preact_swiglu(Dtype dt, const void* H, const void* WgU, int64_t BT, int64_t d,

@@ -40,6 +40,12 @@ struct Dims {
   int64_t out_T = 0;           // ... and output row t goes to O row b * out_T + t - out_skip
 };
 
+// Token row t's column in the chunk-padded token-major layouts is t itself:
+// whole chunks (T a multiple of C) and no padding (Cp = C).
+__host__ __device__ inline bool chunk_map_is_identity(const Dims& dm) {
+  return dm.Cp == dm.C && dm.N * dm.C == dm.T;
+}
+
 // Workspace regions (byte offsets from the workspace base, 256-byte aligned).
 // The slots are one set of G per group, two sets when there are several
 // groups: the scan of group g+1 writes one set while the outputs of group g
@@ -63,7 +69,10 @@ hipError_t launch_state_reset(float* W_state, const void* W0, Dtype w0_dt, int64
 // W_gate/W_up interleaved into WgU, W_target transposed into WtT, taps to fp32 tapsT.
 hipError_t launch_weight_prep(const Dims& dm, const void* Wg, const void* Wu, const void* Wt,
                               const void* taps, void* WgU, void* WtT, float* tapsT, hipStream_t s);
-hipError_t launch_pad_fill(void* zt, void* vt, const Dims& dm, hipStream_t s);
+// Zeros at the padding token columns (j >= chunk length) of two k-blocked
+// token-major matrices: a with Ra rows, b with Rb rows (Rb = 0: a only).
+hipError_t launch_pad_fill(void* a, int64_t Ra, void* b, int64_t Rb, const Dims& dm,
+                           hipStream_t s);
 hipError_t launch_swiglu(const Dims& dm, const void* H, const void* WgU, void* Z, void* Zt,
                          hipStream_t s);
 // eta * V^ into Vt: the conv of X0 into U (scratch of B*T x d elements) if
@@ -163,11 +172,19 @@ struct GemmArgs {
   float alpha;
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
-// C[b] = g.alpha (A[b] B[b]ᵀ + g2.alpha A2[b] B2[b]ᵀ) from g's and g2's
-// operands, g's output, M, N and batch (g2's must agree); the second product
-// runs first on the same accumulators and C is written once.  Only the pair
-// (kRowK, kRowK) + (kRowK, kTiledKMajor) is built.
-hipError_t launch_gemm2(const GemmArgs& g, const GemmArgs& g2, hipStream_t s);
+// The backward's dZ and SwiGLU derivative in one launch.  Per batch b,
+// dZ[b] = g.alpha (A[b] B[b]ᵀ + g2.alpha A2[b] B2[b]ᵀ) (g's operands (kRowK,
+// kRowK), g2's (kRowK, kTiledKMajor); g's M, N = f and batch; the second
+// product runs first on the same accumulators) stays in the tile; with
+// s = sigmoid(A_g), the epilogue writes dA_g = dZ A_u s (1 + A_g (1 - s)) and
+// dA_u = dZ A_g s for the tile's tokens, row t of batch b being token row
+// row0 + b * row_stride + t of the whole batch of sequences: row-major into
+// dA [BT][2f] (dA_g at [0, f), dA_u at [f, 2f)) and k-blocked token-major into
+// dAk ([P/TB][2f][TB], the chunk-padded token columns of dm; padding columns
+// are not written).  Ag [BT][2f] fp32 holds A_g and A_u the same way.
+hipError_t launch_dz_swiglu(const GemmArgs& g, const GemmArgs& g2, const Dims& dm, int64_t row0,
+                            int64_t row_stride, const float* Ag, void* dA, void* dAk,
+                            hipStream_t s);
 // The backward's pre-activations and gated activations in one launch:
 // Ag [BT][2f] fp32 (A_g at columns [0, f), A_u at [f, 2f)) = H WgUᵀ with the
 // interleaved gate/up weight WgU of launch_weight_prep, and Z [BT][f] =
@@ -192,10 +209,6 @@ hipError_t launch_to_kblocked(const void* src, void* dst, const Dims& dm, int64_
 hipError_t launch_dual_scan(const Dims& d1, const void* Vt1, const void* Zt1, float* W1,
                             void* slots1t, const Dims& d2, const void* Vt2, const void* Zt2,
                             float* W2, void* slots2, hipStream_t s);
-// dA [B*T][2f] = [dA_g | dA_u] from dZ (fp32 [B*T][f]) and A_g, A_u (fp32,
-// row t at t * ld).
-hipError_t launch_swiglu_backward(const float* dZ, const float* Ag, const float* Au, int64_t ld,
-                                  void* dA, const Dims& dm, hipStream_t s);
 // dX0 and dtaps from dU = scale * src (fp32 [B*T][d]); `part` holds
 // target_backward_ranges(dm) * 8 * d floats.
 int64_t target_backward_ranges(const Dims& dm);
