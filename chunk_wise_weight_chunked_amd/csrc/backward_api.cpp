@@ -20,7 +20,7 @@ namespace {
 // own regions, 256-byte aligned.
 struct BackwardPlan {
   ttt::WorkspacePlan fwd;
-  size_t wst, u, v, agu, ztr, dotr, sslots, da, wgu, g, gf, du, tpart, dpart, wtpart, dak,
+  size_t wst, u, v, agu, ztr, dotr, sslots, da, g, gf, du, tpart, dpart, wtpart, dak,
       hk, uk, gk, wgut, total;
   int64_t wt_slices;  // token slices of the dW_target product (split over K = B*T)
 };
@@ -44,7 +44,6 @@ BackwardPlan plan_backward(const ttt::Dims& dm) {
   p.dotr = take(d * (size_t)dm.P * es);                   // dOᵀ k-blocked, chunks reversed
   p.sslots = take((size_t)dm.N * dm.B * d * f * es);      // S_j, reversed chunk order
   p.da = take(BT * 2 * f * es);                           // [dA_g | dA_u]
-  p.wgu = take(2 * f * d * es);                           // [W_gate; W_up]
   p.gf = take(BT * d * 4);                                // G = Z_j S_jᵀ (dV^ = eta G), fp32
   p.g = take(dm.proj ? BT * d * es : 0);                  // G rounded: the GEMMs' operand
   p.du = take(dm.proj ? BT * d * 4 : 0);                  // dU (fp32)
@@ -199,7 +198,6 @@ ttt_status_t ttt_mlp_backward_batched(
   void* dOtr = base + bp.dotr;
   char* Sslots = base + bp.sslots;
   char* dA = base + bp.da;
-  char* Wgu = base + bp.wgu;
   float* Gf = reinterpret_cast<float*>(base + bp.gf);
   void* G = base + bp.g;
   float* dU = reinterpret_cast<float*>(base + bp.du);
@@ -212,31 +210,30 @@ ttt_status_t ttt_mlp_backward_batched(
   if (e == hipSuccess) e = ttt::launch_weight_prep(dm, W_gate, W_up, W_target, conv_taps, WgU, WtT, tapsT, s);
   if (e == hipSuccess && !ttt::chunk_map_is_identity(dm))
     e = ttt::launch_pad_fill(Zt, dm.f, Vt, dm.d, dm, s);
-  if (e == hipSuccess) e = ttt::launch_target(dm, X0, tapsT, WtT, dm.conv ? U : Z, Vt, s);
-  if (e == hipSuccess) e = hipMemcpyAsync(Wgu, W_gate, f * d * es, hipMemcpyDeviceToDevice, s);
-  if (e == hipSuccess) e = hipMemcpyAsync(Wgu + f * d * es, W_up, f * d * es, hipMemcpyDeviceToDevice, s);
+  // eta V^ token-major into Vt and, with a projection, V^ row-major into V
+  if (e == hipSuccess)
+    e = ttt::launch_target(dm, X0, tapsT, WtT, dm.conv ? U : Z, Vt, s, -1, dm.proj ? V : nullptr);
   if (e != hipSuccess) return hip_fail(e, "backward");
 
   // 2. The plain GEMMs (the library's batched MFMA GEMM, fp32 accumulation):
   //    first the fp32 pre-activations [A_g | A_u] = H [W_gate; W_up]ᵀ (row t
-  //    holds both, 2f wide) with Z = SiLU(A_g) A_u from the same launch, and
-  //    V^ = U W_target.
+  //    holds both, 2f wide) with Z = SiLU(A_g) A_u from the same launch.
   Gemm gemm{dm.dt, s};
   const bool f32 = true, act_f32 = dm.dt == ttt::Dtype::F32;  // output types
   const int64_t B = dm.B, T = dm.T, C = dm.C, N = dm.N, sl = (int64_t)(B * d * f);
   const int64_t Di = (int64_t)d, Fi = (int64_t)f, BTi = (int64_t)BT;
   e = ttt::launch_preact_swiglu(dm.dt, H, WgU, BTi, Di, Fi, Ag, Z, s);
   if (e != hipSuccess) return hip_fail(e, "backward");
-  if (dm.proj)
-    gemm(kRowK, kRowK, BTi, Di, Di, 1.f, U, Di, 0, WtT, Di, 0, false, V, Di, 0, 1, act_f32);
-  if (gemm.err != hipSuccess) return hip_fail(gemm.err, "backward gemm");
   // operands of the later products in the layouts they are read in
   void* Hk = base + bp.hk;
   void* Uk = base + bp.uk;
   void* Gk = base + bp.gk;
   void* WguT = base + bp.wgut;
   e = ttt::launch_to_kblocked(H, Hk, dm, dm.d, false, s);
-  if (e == hipSuccess) e = ttt::launch_transpose(Wgu, WguT, 2 * Fi, Di, dm.dt, s);
+  // [W_gate; W_up]ᵀ: row c holds W_gate[:, c] then W_up[:, c]
+  if (e == hipSuccess) e = ttt::launch_transpose(W_gate, WguT, Fi, Di, dm.dt, s, 2 * Fi);
+  if (e == hipSuccess)
+    e = ttt::launch_transpose(W_up, static_cast<char*>(WguT) + f * es, Fi, Di, dm.dt, s, 2 * Fi);
   if (e == hipSuccess && dm.proj) e = ttt::launch_to_kblocked(U, Uk, dm, dm.d, false, s);
   if (e != hipSuccess) return hip_fail(e, "backward");
 

@@ -416,7 +416,8 @@ bool gemm_args_ok(const GemmArgs& g) {
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_rect_kernel(T* __restrict__ dst,
                                                              const T* __restrict__ src,
-                                                             int64_t rows, int64_t cols) {
+                                                             int64_t rows, int64_t cols,
+                                                             int64_t ld_dst) {
   __shared__ T tile[64][65];
   const int64_t i0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -427,7 +428,7 @@ __global__ __launch_bounds__(256) void transpose_rect_kernel(T* __restrict__ dst
   __syncthreads();
   for (int r = ty; r < 64; r += 4) {
     const int64_t j = j0 + r, i = i0 + tx;
-    if (i < rows && j < cols) dst[j * rows + i] = tile[tx][r];
+    if (i < rows && j < cols) dst[j * ld_dst + i] = tile[tx][r];
   }
 }
 
@@ -475,14 +476,18 @@ hipError_t launch_preact_swiglu(Dtype dt, const void* H, const void* WgU, int64_
 }
 
 hipError_t launch_transpose(const void* src, void* dst, int64_t rows, int64_t cols, Dtype dt,
-                            hipStream_t s) {
+                            hipStream_t s, int64_t ld_dst) {
+  if (ld_dst < 0) ld_dst = rows;
+  if (ld_dst < rows) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
   if (dt == Dtype::BF16)
     hipLaunchKernelGGL(transpose_rect_kernel<uint16_t>, grid, dim3(256), 0, s,
-                       static_cast<uint16_t*>(dst), static_cast<const uint16_t*>(src), rows, cols);
+                       static_cast<uint16_t*>(dst), static_cast<const uint16_t*>(src), rows, cols,
+                       ld_dst);
   else
     hipLaunchKernelGGL(transpose_rect_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<float*>(dst), static_cast<const float*>(src), rows, cols);
+                       static_cast<float*>(dst), static_cast<const float*>(src), rows, cols,
+                       ld_dst);
   return hipGetLastError();
 }
 

@@ -309,12 +309,13 @@ struct TargetLds {
 };
 
 // Tile `blk` of `nblk` of the projection of token rows [t_lo, t_hi) of every
-// sequence (tiles do not straddle sequences).
-template <typename T>
+// sequence (tiles do not straddle sequences): eta V^ into Vt and, with kV,
+// V^ itself (unscaled, row-major [B*T][d]) into V.
+template <typename T, bool kV = false>
 __device__ __forceinline__ void target_tile(const Dims& dm, const T* __restrict__ U,
                                             const T* __restrict__ WtT, T* __restrict__ Vt,
                                             int64_t t_lo, int64_t t_hi, int blk, int nblk,
-                                            lds_char* smem) {
+                                            lds_char* smem, T* __restrict__ V = nullptr) {
   using S = Tile;
   constexpr int kPass = TargetLds<T>::kPass;
   using St = typename TargetLds<T>::St;
@@ -350,16 +351,23 @@ __device__ __forceinline__ void target_tile(const Dims& dm, const T* __restrict_
     stage_cols<T, S, kPass>(smem, acc, p, q, [&](float x) { return eta * x; });
     __syncthreads();
     const int64_t cb = col0 + kPass * q;
-    St::flush_tokens(smem, Vt, d, cb, (int)max<int64_t>(0, min<int64_t>(kPass, d - cb)), row0,
-                     row_end, cm);
+    const int ncols = (int)max<int64_t>(0, min<int64_t>(kPass, d - cb));
+    St::flush_tokens(smem, Vt, d, cb, ncols, row0, row_end, cm);
+    if constexpr (kV) {
+      __syncthreads();
+      stage_cols<T, S, kPass>(smem, acc, p, q, [](float x) { return x; });
+      __syncthreads();
+      St::flush_rows(smem, V, row0, d, cb, ncols, 0, min(S::BM, row_end - row0));
+    }
   }
 }
 
-template <typename T>
+template <typename T, bool kV = false>
 TTT_GEMM_KERNEL void target_kernel(Dims dm, const T* __restrict__ U, const T* __restrict__ WtT,
-                                   T* __restrict__ Vt, int64_t t_lo, int64_t t_hi) {
+                                   T* __restrict__ Vt, int64_t t_lo, int64_t t_hi,
+                                   T* __restrict__ V) {
   __shared__ __attribute__((aligned(16))) char smem_raw[TargetLds<T>::kBytes];
-  target_tile<T>(dm, U, WtT, Vt, t_lo, t_hi, blockIdx.x, gridDim.x, (lds_char*)smem_raw);
+  target_tile<T, kV>(dm, U, WtT, Vt, t_lo, t_hi, blockIdx.x, gridDim.x, (lds_char*)smem_raw, V);
 }
 
 // eta * R (R [B*T][d] row-major: X0 or U) into Vt, for the targets without a
@@ -1146,7 +1154,7 @@ hipError_t launch_swiglu(const Dims& dm, const void* H, const void* WgU, void* Z
 
 template <typename T>
 static void launch_target_t(const Dims& dm, const T* X0, const float* tapsT, const T* WtT, T* U,
-                            T* Vt, int64_t t_hi, hipStream_t s) {
+                            T* Vt, int64_t t_hi, T* V, hipStream_t s) {
   const int64_t BT = dm.B * dm.T;
   const T* rows = X0;  // the rows the projection (or the copy into Vt) reads
   if (dm.conv) {
@@ -1161,8 +1169,12 @@ static void launch_target_t(const Dims& dm, const T* X0, const float* tapsT, con
   if (dm.proj) {
     if (t_hi <= 0) return;
     const int64_t tiles = ((t_hi + Tile::BM - 1) / Tile::BM) * dm.B * ((dm.d + Tile::BN - 1) / Tile::BN);
-    hipLaunchKernelGGL(target_kernel<T>, dim3((unsigned)tiles), dim3(Tile::kThreads), 0, s, dm,
-                       rows, WtT, Vt, (int64_t)0, t_hi);
+    if (V != nullptr)
+      hipLaunchKernelGGL((target_kernel<T, true>), dim3((unsigned)tiles), dim3(Tile::kThreads), 0,
+                         s, dm, rows, WtT, Vt, (int64_t)0, t_hi, V);
+    else
+      hipLaunchKernelGGL((target_kernel<T, false>), dim3((unsigned)tiles), dim3(Tile::kThreads), 0,
+                         s, dm, rows, WtT, Vt, (int64_t)0, t_hi, V);
   } else {
     hipLaunchKernelGGL(rows_to_vt_kernel<T>, dim3((unsigned)((BT + 255) / 256), (unsigned)((dm.d + 63) / 64)),
                        dim3(256), 0, s, dm, rows, Vt);
@@ -1170,16 +1182,18 @@ static void launch_target_t(const Dims& dm, const T* X0, const float* tapsT, con
 }
 
 hipError_t launch_target(const Dims& dm, const void* X0, const void* tapsT, const void* WtT,
-                         void* U, void* Vt, hipStream_t s, int64_t t_hi) {
+                         void* U, void* Vt, hipStream_t s, int64_t t_hi, void* V) {
   if (t_hi < 0) t_hi = dm.T;
+  if (V != nullptr && (!dm.proj || t_hi != dm.T)) return hipErrorInvalidValue;
   if (dm.dt == Dtype::BF16)
     launch_target_t<uint16_t>(dm, static_cast<const uint16_t*>(X0),
                               static_cast<const float*>(tapsT), static_cast<const uint16_t*>(WtT),
-                              static_cast<uint16_t*>(U), static_cast<uint16_t*>(Vt), t_hi, s);
+                              static_cast<uint16_t*>(U), static_cast<uint16_t*>(Vt), t_hi,
+                              static_cast<uint16_t*>(V), s);
   else
     launch_target_t<float>(dm, static_cast<const float*>(X0), static_cast<const float*>(tapsT),
                            static_cast<const float*>(WtT), static_cast<float*>(U),
-                           static_cast<float*>(Vt), t_hi, s);
+                           static_cast<float*>(Vt), t_hi, static_cast<float*>(V), s);
   return hipGetLastError();
 }
 

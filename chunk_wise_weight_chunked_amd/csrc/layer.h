@@ -78,9 +78,11 @@ hipError_t launch_swiglu(const Dims& dm, const void* H, const void* WgU, void* Z
 // eta * V^ into Vt: the conv of X0 into U (scratch of B*T x d elements) if
 // dm.conv, then the projection by W_target if dm.proj (each part left out is
 // the identity).  With a projection, t_hi >= 0 projects only token rows
-// [0, t_hi) of each sequence (the conv always covers all rows).
+// [0, t_hi) of each sequence (the conv always covers all rows); V (not null:
+// a projection of all rows only) also receives V^ unscaled, row-major
+// [B*T][d].
 hipError_t launch_target(const Dims& dm, const void* X0, const void* taps, const void* WtT,
-                         void* U, void* Vt, hipStream_t s, int64_t t_hi = -1);
+                         void* U, void* Vt, hipStream_t s, int64_t t_hi = -1, void* V = nullptr);
 // Whether launch_scan_target serves these dims (a projection, and the scan
 // tiles divide the weight).
 bool scan_target_fits(const Dims& dm);
@@ -191,9 +193,10 @@ hipError_t launch_dz_swiglu(const GemmArgs& g, const GemmArgs& g2, const Dims& d
 // SiLU(A_g) * A_u in type dt.  d and f multiples of 64.
 hipError_t launch_preact_swiglu(Dtype dt, const void* H, const void* WgU, int64_t BT, int64_t d,
                                 int64_t f, float* Ag, void* Z, hipStream_t s);
-// dst [cols][rows] = srcᵀ for src [rows][cols] of element type dt.
+// dst [cols][ld_dst] = srcᵀ (columns [0, rows) of each dst row) for src
+// [rows][cols] of element type dt; ld_dst < 0: rows.
 hipError_t launch_transpose(const void* src, void* dst, int64_t rows, int64_t cols, Dtype dt,
-                            hipStream_t s);
+                            hipStream_t s, int64_t ld_dst = -1);
 
 // Backward-pass kernels (backward.hip).
 constexpr int kTargetBackwardRows = 256;  // token rows per partial sum of the taps' gradient
