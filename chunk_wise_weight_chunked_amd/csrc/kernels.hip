@@ -25,7 +25,8 @@
 //   WtT        [d][d]              W_target transposed ([j_out][c_in])
 //   tapsT      [8][d] fp32         taps transposed, zero for k >= K
 //   W_state    [B][d][f] fp32      fast weight
-//   slots      [G][B][d][f]        weight used by each chunk of the group
+//   slots      [G][B][d/TB][f/TB][TB][TB]  weight used by each chunk of the group,
+//                                  in TB x TB tiles (TB = 128 bytes of T)
 // Token t of sequence b has token column p = (b N + i) Cp + j (i = t / C,
 // j = t % C, Cp = C rounded up to 64); columns with j >= chunk length hold
 // zeros.  In the k-blocked layouts one k-tile of a GEMM (TB tokens of R rows)
@@ -61,6 +62,12 @@ using OutTile = TileShape<256, 256, 4, 2>;
 static_assert(OutTile::kThreads == Tile::kThreads && OutTile::kLdsBytes == Tile::kLdsBytes,
               "output and scan tiles share a launch");
 using OneChunkTile = TileShape<128, 128, 2, 2>;  // single-chunk updates
+// The forward's weight slots are stored in TB x TB tiles (layout 4 of
+// prefix_update_tile): an output tile reads each k-tile of its slot rows as
+// four contiguous 8 KB tiles, and a scan tile writes its slot as 4 KB runs
+// (against 128-byte row segments one slot row apart in the row-major layout,
+// which measured 0.7-0.8% slower per step).
+constexpr int kFwdSlots = 4;
 // LDS for the staged slot rows: 4 KB per wave of the 256 x 256 scan tile.
 constexpr int kSlotStageBytes = 8 * 4096;
 // bf16 slots are staged through LDS (a quarter of the store instructions);
@@ -780,8 +787,13 @@ __device__ __forceinline__ void down_proj_tile(const Dims& dm, const T* __restri
   const int64_t row0 = b * T_seq + c_begin + m0;  // first token row of the tile
   const T* slot = slots + (jj * dm.B + b) * d * f;
 
+  // the slot in TB x TB tiles: k-tile kt of slot rows n0.. is tile column kt
+  // of each TB-row block (block rows f * 128 bytes apart)
+  static_assert(kFwdSlots == 4, "tiled forward slots");
+  constexpr int TB = kRowBytes / (int)sizeof(T);
   DirectLoader<S::BN, S::kWaves> lb;
-  lb.init(reinterpret_cast<const char*>(slot) + n0 * ld, ld, kRowBytes, (d - n0) * ld, kRowBytes);
+  lb.init_blocked(reinterpret_cast<const char*>(slot) + (n0 / TB) * f * kRowBytes, TB,
+                  f * kRowBytes, TB * kRowBytes, ((d - n0) / TB) * f * kRowBytes, TB * kRowBytes);
 
   Accum<S> acc;
   acc.zero();
@@ -1207,13 +1219,13 @@ static void launch_scan_target_t(const Dims& dm, const T* Vt, const T* Zt, float
       ((dm.T - t_lo + Tile::BM - 1) / Tile::BM) * dm.B * ((dm.d + Tile::BN - 1) / Tile::BN);
   if constexpr (sizeof(T) == 2) {
     if (staged_slots<T>(dm)) {
-      hipLaunchKernelGGL((scan_target_kernel<T, 9>), dim3((unsigned)(pad + tiles)),
+      hipLaunchKernelGGL((scan_target_kernel<T, kFwdSlots | 8>), dim3((unsigned)(pad + tiles)),
                          dim3(Tile::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, (int64_t)0,
                          gc, (int)scan, (int)pad, rows, WtT, const_cast<T*>(Vt), t_lo);
       return;
     }
   }
-  hipLaunchKernelGGL((scan_target_kernel<T, 1>), dim3((unsigned)(pad + tiles)),
+  hipLaunchKernelGGL((scan_target_kernel<T, kFwdSlots>), dim3((unsigned)(pad + tiles)),
                      dim3(Tile::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, (int64_t)0, gc,
                      (int)scan, (int)pad, rows, WtT, const_cast<T*>(Vt), t_lo);
 }
@@ -1252,7 +1264,7 @@ static void launch_scan_apply_t(const Dims& dm, const T* Vt, const T* Zt, float*
     // one chunk's update alone (sequential mode): 128 x 128 tiles, two
     // workgroups per CU, so that one's state load and store overlap the
     // other's MFMAs, and four times the tiles to spread over the CUs
-    hipLaunchKernelGGL((prefix_update_kernel<T, OneChunkTile, 1, 2>),
+    hipLaunchKernelGGL((prefix_update_kernel<T, OneChunkTile, kFwdSlots, 2>),
                        dim3((unsigned)((dm.d / OneChunkTile::BM) * (dm.f / OneChunkTile::BN) * dm.B)),
                        dim3(OneChunkTile::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, g0, gc,
                        static_cast<T*>(nullptr));
@@ -1268,13 +1280,13 @@ static void launch_scan_apply_t(const Dims& dm, const T* Vt, const T* Zt, float*
     const int64_t pad = (n1 + 7) / 8 * 8;
     if constexpr (sizeof(T) == 2) {
       if (staged_slots<T>(dm)) {
-        hipLaunchKernelGGL((scan_apply_kernel<T, 9>), dim3((unsigned)(pad + n2)),
+        hipLaunchKernelGGL((scan_apply_kernel<T, kFwdSlots | 8>), dim3((unsigned)(pad + n2)),
                            dim3(Tile::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, g0, gc,
                            (int)n1, (int)pad, outputs_first ? 1 : 0, Z, apply_slots, O, a0, ac);
         return;
       }
     }
-    hipLaunchKernelGGL((scan_apply_kernel<T, 1>), dim3((unsigned)(pad + n2)),
+    hipLaunchKernelGGL((scan_apply_kernel<T, kFwdSlots>), dim3((unsigned)(pad + n2)),
                        dim3(Tile::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, g0, gc,
                        (int)n1, (int)pad, outputs_first ? 1 : 0, Z, apply_slots, O, a0, ac);
     return;
@@ -1283,7 +1295,7 @@ static void launch_scan_apply_t(const Dims& dm, const T* Vt, const T* Zt, float*
   // multiples of 64): two launches in the same order.
   using Small = TileShape<64, 64, 2, 2>;
   if (gc > 0)
-    hipLaunchKernelGGL((prefix_update_kernel<T, Small>),
+    hipLaunchKernelGGL((prefix_update_kernel<T, Small, kFwdSlots>),
                        dim3((unsigned)((dm.d / Small::BM) * (dm.f / Small::BN) * dm.B)),
                        dim3(Small::kThreads), 0, s, dm, Vt, Zt, W_state, scan_slots, g0, gc,
                        static_cast<T*>(nullptr));
