@@ -301,8 +301,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // [A_g | A_u] = H [W_gate; W_up]ᵀ in fp32 and Z = SiLU(A_g) * A_u in one
 // launch.  B is the interleaved weight WgU ([f/32][2][32][d]: 32 gate rows,
-// then the 32 up rows of the same features), so each 64-column pass of a
-// tile holds the gate and up sums of 32 features.  Row t of Ag holds A_g at
+// then the 32 up rows of the same features; in TB x TB tiles when
+// wgu_tiled(d, es)), so each 64-column pass of a tile holds the gate and up
+// sums of 32 features.  Row t of Ag holds A_g at
 // [0, f) and A_u at [f, 2f); Z is [BT][f] in the activation type, computed
 // from the same fp32 values as SiLU(g) * u (the forward's arithmetic).
 template <typename T>
@@ -321,7 +322,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   acc.zero();
   const LanePos p = lane_pos<S>();
   auto la = make_loader<T, kRowK, S::BM>(reinterpret_cast<const char*>(H), d, 0, 0, m0, BT, d);
-  auto lb = make_loader<T, kRowK, S::BN>(reinterpret_cast<const char*>(WgU), d, 0, 0, n0, 2 * f, d);
+  const char* const wgu = reinterpret_cast<const char*>(WgU);
+  auto lb = wgu_tiled(d, (int64_t)sizeof(T)) ? make_loader<T, kTiledRowK, S::BN>(wgu, d, 0, 0, n0, 2 * f, d)
+                                             : make_loader<T, kRowK, S::BN>(wgu, d, 0, 0, n0, 2 * f, d);
   mainloop<T, S>(acc, la, lb, (d + TB - 1) / TB, smem, p, [](int64_t) {});
 
   for (int q = 0; q < S::BN / kEpiCols; ++q) {

@@ -22,6 +22,7 @@
 //   Zt         [P/TB][f][TB]       Z token-major, k-blocked (S4's B operand)
 //   Vt         [P/TB][d][TB]       eta * V^ token-major, k-blocked (S4's A operand)
 //   WgU        [f/32][2][32][d]    W_gate / W_up rows interleaved in blocks of 32
+//                                  (in TB x TB tiles when wgu_tiled(d, es))
 //   WtT        [d][d]              W_target transposed ([j_out][c_in])
 //   tapsT      [8][d] fp32         taps transposed, zero for k >= K
 //   W_state    [B][d][f] fp32      fast weight
@@ -148,8 +149,15 @@ TTT_GEMM_KERNEL void swiglu_kernel(Dims dm, const T* __restrict__ H, const T* __
   la.init(reinterpret_cast<const char*>(H) + row0 * ld, ld, kRowBytes, (BT - row0) * ld,
           kRowBytes);
   DirectLoader<S::BN, S::kWaves> lb;
-  lb.init(reinterpret_cast<const char*>(WgU) + 2 * feat0 * ld, ld, kRowBytes,
-          (2 * f - 2 * feat0) * ld, kRowBytes);
+  if (wgu_tiled(d, (int64_t)sizeof(T))) {
+    constexpr int TB = kRowBytes / (int)sizeof(T);
+    lb.init_blocked(reinterpret_cast<const char*>(WgU) + (2 * feat0 / TB) * d * kRowBytes, TB,
+                    d * kRowBytes, TB * kRowBytes, ((2 * f - 2 * feat0) / TB) * d * kRowBytes,
+                    TB * kRowBytes);
+  } else {
+    lb.init(reinterpret_cast<const char*>(WgU) + 2 * feat0 * ld, ld, kRowBytes,
+            (2 * f - 2 * feat0) * ld, kRowBytes);
+  }
 
   Accum<S> acc;
   acc.zero();
@@ -954,16 +962,20 @@ __global__ void transpose_kernel(T* __restrict__ dst, const T* __restrict__ src,
 }
 
 // WgU[(n/32)*64 + (n%32)] = W_gate[n], WgU[(n/32)*64 + 32 + (n%32)] = W_up[n]
-// (rows of d elements), 16 bytes per thread.
+// (rows of d elements), 16 bytes per thread; tb > 0: in tb x tb tiles.
 __global__ void interleave_kernel(uint4* __restrict__ dst, const uint4* __restrict__ wg,
-                                  const uint4* __restrict__ wu, int64_t f, int64_t row_vecs) {
+                                  const uint4* __restrict__ wu, int64_t f, int64_t row_vecs,
+                                  int32_t tb) {
   const int64_t total = 2 * f * row_vecs;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
     const int64_t r = e / row_vecs, v = e - r * row_vecs;
     const int64_t blk = r / 64, w = r % 64;
     const int64_t n = blk * 32 + (w & 31);
-    dst[e] = (w < 32 ? wg : wu)[n * row_vecs + v];
+    // tb > 0: row r, vector v in TB x TB tiles (8 vectors of 16 bytes per tile row)
+    const int64_t at = tb > 0 ? ((r / tb) * (row_vecs / 8) + v / 8) * (tb * 8) + (r % tb) * 8 + v % 8
+                              : e;
+    dst[at] = (w < 32 ? wg : wu)[n * row_vecs + v];
   }
 }
 
@@ -1114,7 +1126,10 @@ hipError_t launch_weight_prep(const Dims& dm, const void* Wg, const void* Wu, co
   const int64_t row_vecs = dm.d * (int64_t)dtype_bytes(dm.dt) / 16;
   hipLaunchKernelGGL(interleave_kernel, dim3(grid_for(2 * dm.f * row_vecs, 256, 16384)), dim3(256),
                      0, s, static_cast<uint4*>(WgU), static_cast<const uint4*>(Wg),
-                     static_cast<const uint4*>(Wu), dm.f, row_vecs);
+                     static_cast<const uint4*>(Wu), dm.f, row_vecs,
+                     wgu_tiled(dm.d, (int64_t)dtype_bytes(dm.dt))
+                         ? (int32_t)(kRowBytes / dtype_bytes(dm.dt))
+                         : 0);
   const dim3 tgrid((unsigned)((dm.d + 63) / 64), (unsigned)((dm.d + 63) / 64));
   const unsigned tblocks = (unsigned)((dm.d + 255) / 256);
   if (dm.dt == Dtype::BF16) {

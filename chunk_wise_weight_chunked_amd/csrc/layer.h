@@ -46,6 +46,13 @@ __host__ __device__ inline bool chunk_map_is_identity(const Dims& dm) {
   return dm.Cp == dm.C && dm.N * dm.C == dm.T;
 }
 
+// WgU (the interleaved gate/up weight, d elements of es bytes per row) is
+// stored in TB x TB tiles of 128-byte rows when a row is longer than 4 KB: a
+// k-tile of 256 WgU rows is then four contiguous 8 KB tiles instead of 256
+// segments a row apart.  Shorter rows stay row-major (a 256-row block is
+// contiguous there already, and tiles measured slower).
+__host__ __device__ inline bool wgu_tiled(int64_t d, int64_t es) { return d * es > 4096; }
+
 // Workspace regions (byte offsets from the workspace base, 256-byte aligned).
 // The slots are one set of G per group, two sets when there are several
 // groups: the scan of group g+1 writes one set while the outputs of group g
