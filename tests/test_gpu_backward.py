@@ -37,6 +37,9 @@ CASES = [
     (1, 1, 64, 64, 1, 1, torch.bfloat16, "conv_proj", "next", False, True),     # T = 1
     (2, 70, 64, 128, 4, 1, torch.float32, "conv_proj", "next", False, True),    # C = 1
     (1, 130, 128, 64, 1, 65, torch.bfloat16, "conv_proj", "self", False, True),  # K = 1, C odd
+    # gate/up weight rows longer than 4 KB (stored in tiles)
+    (1, 150, 2112, 128, 4, 64, torch.bfloat16, "conv_proj", "next", False, True),
+    (1, 150, 1088, 128, 4, 64, torch.float32, "conv_proj", "next", False, True),
 ]
 
 

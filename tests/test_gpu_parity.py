@@ -89,6 +89,9 @@ SMALL = [
     (1, 1, 64, 64, 4, 16, torch.float32, 1e-1),         # a single token
     (2, 513, 320, 384, 5, 256, torch.float32, 1e-2),    # fp32, several tiles
     (1, 600, 320, 128, 4, 128, torch.bfloat16, 1e-2),   # d > f: conv output wider than Z
+    # gate/up weight rows longer than 4 KB (stored in tiles), 64 x 64 scan tiles
+    (1, 300, 2112, 128, 4, 128, torch.bfloat16, 1e-2),
+    (1, 200, 1088, 192, 4, 64, torch.float32, 1e-2),
 ]
 
 
