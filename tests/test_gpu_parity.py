@@ -378,7 +378,7 @@ def test_full_workload_prefix_and_final_weight(name):
     assert e_w <= tol_for(w.dtype) and e_dw <= tol_for(w.dtype)
 
 
-@pytest.mark.parametrize("name", ["qwen3_4b_32k", "small_4x128k"])
+@pytest.mark.parametrize("name", ["qwen3_4b_32k", "small_4x128k", "qwen3_4b_128k"])
 def test_full_size_sequential_mode_bitwise(name):
     """Sequential mode at full size (one launch per chunk's read-modify-write of
     the fp32 state, the single-chunk update tiles, a group's outputs batched)
@@ -395,6 +395,19 @@ def test_full_size_sequential_mode_bitwise(name):
         runs.append((O, W))
         print(f"[full] {name} {mode}: done", flush=True)
     assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
+
+
+@pytest.mark.parametrize("dtype,C,T", [(torch.bfloat16, 1024, 2500), (torch.float32, 512, 1100)],
+                         ids=["bf16", "f32"])
+def test_sequential_update_many_tiles_bitwise(dtype, C, T):
+    """Sequential mode with chunks of 16 k-tiles, more single-chunk update
+    tiles than the GPU holds at once (four sequences of a 1024 x 4096 weight)
+    and a ragged last chunk, against the chunk-parallel groups: the same
+    bits."""
+    dev = to_device(synth.make_inputs(4, T, 1024, 4096, 4, dtype, seed=31))
+    ref = run_gpu(dev, 1e-2, C, mode="chunk_parallel")
+    got = run_gpu(dev, 1e-2, C, mode="sequential")
+    assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1])
 
 
 # ------------------------------------------------- coherent-accumulation stress
