@@ -230,10 +230,10 @@ ttt_status_t ttt_mlp_backward_batched(
   void* Gk = base + bp.gk;
   void* WguT = base + bp.wgut;
   e = ttt::launch_to_kblocked(H, Hk, dm, dm.d, false, s);
-  // [W_gate; W_up]ᵀ: row c holds W_gate[:, c] then W_up[:, c]
-  if (e == hipSuccess) e = ttt::launch_transpose(W_gate, WguT, Fi, Di, dm.dt, s, 2 * Fi);
-  if (e == hipSuccess)
-    e = ttt::launch_transpose(W_up, static_cast<char*>(WguT) + f * es, Fi, Di, dm.dt, s, 2 * Fi);
+  // [W_gate; W_up]ᵀ in TB x TB tiles (dH's B operand): row c holds
+  // W_gate[:, c] then W_up[:, c]
+  if (e == hipSuccess) e = ttt::launch_transpose(W_gate, WguT, Fi, Di, dm.dt, s, 2 * Fi, 0, true);
+  if (e == hipSuccess) e = ttt::launch_transpose(W_up, WguT, Fi, Di, dm.dt, s, 2 * Fi, Fi, true);
   if (e == hipSuccess && dm.proj) e = ttt::launch_to_kblocked(U, Uk, dm, dm.d, false, s);
   if (e != hipSuccess) return hip_fail(e, "backward");
 
@@ -297,7 +297,7 @@ ttt_status_t ttt_mlp_backward_batched(
   if (e == hipSuccess && dm.proj) e = ttt::launch_to_kblocked(G, Gk, dm, dm.d, false, s);
   if (e != hipSuccess) return hip_fail(e, "backward");
   const int64_t tb = 128 / (int64_t)es, P = dm.P;  // tokens per 128-byte block row
-  gemm(kRowK, kRowK, BTi, Di, 2 * Fi, 1.f, dA, 2 * Fi, 0, WguT, 2 * Fi, 0, false, dH, Di, 0, 1,
+  gemm(kRowK, kTiledRowK, BTi, Di, 2 * Fi, 1.f, dA, 2 * Fi, 0, WguT, 2 * Fi, 0, false, dH, Di, 0, 1,
        act_f32);
   // dW_gate and dW_up (dA_gᵀ H, dA_uᵀ H over every token column) as one
   // launch of two products: the second's A starts f rows into each block and

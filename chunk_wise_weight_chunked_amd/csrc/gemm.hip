@@ -414,13 +414,16 @@ bool gemm_args_ok(const GemmArgs& g) {
   return true;
 }
 
-// dst[j][i] = src[i][j], through a 64 x 64 LDS tile (padded against bank
-// conflicts); 256 threads, 4 rows per pass.
+// dst[j][col0 + i] = src[i][j], through a 64 x 64 LDS tile (padded against
+// bank conflicts); 256 threads, 4 rows per pass.  dst has ld_dst columns,
+// row-major, or (tb > 0) in tb x tb tiles: element (r, c) at
+// ((r / tb) (ld_dst / tb) + c / tb) tb^2 + (r % tb) tb + c % tb.
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_rect_kernel(T* __restrict__ dst,
                                                              const T* __restrict__ src,
                                                              int64_t rows, int64_t cols,
-                                                             int64_t ld_dst) {
+                                                             int64_t ld_dst, int64_t col0,
+                                                             int32_t tb) {
   __shared__ T tile[64][65];
   const int64_t i0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -431,7 +434,11 @@ __global__ __launch_bounds__(256) void transpose_rect_kernel(T* __restrict__ dst
   __syncthreads();
   for (int r = ty; r < 64; r += 4) {
     const int64_t j = j0 + r, i = i0 + tx;
-    if (i < rows && j < cols) dst[j * ld_dst + i] = tile[tx][r];
+    if (i >= rows || j >= cols) continue;
+    const int64_t c = col0 + i;
+    const int64_t at = tb > 0 ? ((j / tb) * (ld_dst / tb) + c / tb) * tb * tb + (j % tb) * tb + c % tb
+                              : j * ld_dst + c;
+    dst[at] = tile[tx][r];
   }
 }
 
@@ -479,18 +486,20 @@ hipError_t launch_preact_swiglu(Dtype dt, const void* H, const void* WgU, int64_
 }
 
 hipError_t launch_transpose(const void* src, void* dst, int64_t rows, int64_t cols, Dtype dt,
-                            hipStream_t s, int64_t ld_dst) {
+                            hipStream_t s, int64_t ld_dst, int64_t col0, bool tiled) {
   if (ld_dst < 0) ld_dst = rows;
-  if (ld_dst < rows) return hipErrorInvalidValue;
+  const int32_t tb = tiled ? (int32_t)(kRowBytes / dtype_bytes(dt)) : 0;
+  if (col0 < 0 || col0 + rows > ld_dst) return hipErrorInvalidValue;
+  if (tiled && (ld_dst % tb != 0 || cols % tb != 0)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
   if (dt == Dtype::BF16)
     hipLaunchKernelGGL(transpose_rect_kernel<uint16_t>, grid, dim3(256), 0, s,
                        static_cast<uint16_t*>(dst), static_cast<const uint16_t*>(src), rows, cols,
-                       ld_dst);
+                       ld_dst, col0, tb);
   else
     hipLaunchKernelGGL(transpose_rect_kernel<float>, grid, dim3(256), 0, s,
                        static_cast<float*>(dst), static_cast<const float*>(src), rows, cols,
-                       ld_dst);
+                       ld_dst, col0, tb);
   return hipGetLastError();
 }
 

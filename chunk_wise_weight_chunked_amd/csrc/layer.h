@@ -200,10 +200,12 @@ hipError_t launch_dz_swiglu(const GemmArgs& g, const GemmArgs& g2, const Dims& d
 // SiLU(A_g) * A_u in type dt.  d and f multiples of 64.
 hipError_t launch_preact_swiglu(Dtype dt, const void* H, const void* WgU, int64_t BT, int64_t d,
                                 int64_t f, float* Ag, void* Z, hipStream_t s);
-// dst [cols][ld_dst] = srcᵀ (columns [0, rows) of each dst row) for src
-// [rows][cols] of element type dt; ld_dst < 0: rows.
+// dst [cols][ld_dst] = srcᵀ into columns [col0, col0 + rows) of each dst row,
+// for src [rows][cols] of element type dt; ld_dst < 0: rows.  tiled: dst in
+// TB x TB tiles of 128-byte rows (ld_dst and cols multiples of TB).
 hipError_t launch_transpose(const void* src, void* dst, int64_t rows, int64_t cols, Dtype dt,
-                            hipStream_t s, int64_t ld_dst = -1);
+                            hipStream_t s, int64_t ld_dst = -1, int64_t col0 = 0,
+                            bool tiled = false);
 
 // Backward-pass kernels (backward.hip).
 constexpr int kTargetBackwardRows = 256;  // token rows per partial sum of the taps' gradient
