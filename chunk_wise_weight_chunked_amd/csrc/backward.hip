@@ -5,9 +5,9 @@
 // section 3.2 chunk order).  Its chunk-structured part, the sums
 // S_j = dW_final + sum_{m > j} dO_mᵀ Z_m, is the forward's streamed prefix
 // run over the chunks in reverse order; the kernels here lay the operands out
-// for that (chunk-reversed, k-blocked token-major), and do the elementwise and
-// reduction steps: the SwiGLU derivative, the conv's transpose and its taps'
-// gradient, and the learning rate's gradient.
+// for the products (k-blocked token-major), and do the elementwise and
+// reduction steps: the conv's transpose and its taps' gradient, and the
+// learning rate's gradient.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,14 +34,13 @@ unsigned grid_cap(int64_t n, int64_t per_block, int64_t cap) {
 }
 
 // dst = the rows of src ([B][T][R] row-major) in the k-blocked token-major
-// layout [P/TB][R][TB] (TB = 128 bytes of tokens: 64 bf16, 32 fp32), with the
-// chunks of every sequence in reverse order if `reverse`, and zeros in the
-// padding columns.  One TB-token x 64-row tile per workgroup, through LDS;
+// layout [P/TB][R][TB] (TB = 128 bytes of tokens: 64 bf16, 32 fp32), with
+// zeros in the padding columns.  One TB-token x 64-row tile per workgroup, through LDS;
 // global reads and writes are 16 bytes per lane.
 template <typename T>
 __global__ __launch_bounds__(256) void to_kblocked_kernel(const T* __restrict__ src,
-                                                          T* __restrict__ dst, Dims dm, int64_t R,
-                                                          int32_t reverse) {
+                                                          T* __restrict__ dst, Dims dm,
+                                                          int64_t R) {
   constexpr int TB = kRowBytes / (int)sizeof(T);
   constexpr int EPC = 16 / (int)sizeof(T);   // values per 16-byte chunk
   constexpr int IN_CHUNKS = 64 / EPC;         // chunks of a token's 64 rows
@@ -50,9 +49,8 @@ __global__ __launch_bounds__(256) void to_kblocked_kernel(const T* __restrict__ 
   const int64_t q = blockIdx.x;                 // TB-token block of the layout
   const int64_t r0 = (int64_t)blockIdx.y * 64;  // first row of the tile
   const int64_t tiles_per_chunk = dm.Cp / TB;
-  const int64_t chunk_rev = q / tiles_per_chunk, jb = q - chunk_rev * tiles_per_chunk;
-  const int64_t b = chunk_rev / dm.N, i_dst = chunk_rev - b * dm.N;
-  const int64_t i = reverse ? dm.N - 1 - i_dst : i_dst;
+  const int64_t chunk = q / tiles_per_chunk, jb = q - chunk * tiles_per_chunk;
+  const int64_t b = chunk / dm.N, i = chunk - b * dm.N;
   const int64_t len = std::min<int64_t>(dm.C, dm.T - i * dm.C);  // tokens of chunk i
   for (int it = threadIdx.x; it < TB * IN_CHUNKS; it += 256) {
     const int e = it / IN_CHUNKS, cc = it % IN_CHUNKS;  // token e, chunk cc of its rows
@@ -271,18 +269,16 @@ __global__ void fill_f32_kernel(float* __restrict__ out, int64_t n, float v) {
 
 }  // namespace
 
-hipError_t launch_to_kblocked(const void* src, void* dst, const Dims& dm, int64_t R, bool reverse,
+hipError_t launch_to_kblocked(const void* src, void* dst, const Dims& dm, int64_t R,
                               hipStream_t s) {
   const int64_t tb = kRowBytes / (int64_t)dtype_bytes(dm.dt);
   const dim3 grid((unsigned)(dm.P / tb), (unsigned)((R + 63) / 64));
   if (dm.dt == Dtype::BF16)
     hipLaunchKernelGGL(to_kblocked_kernel<uint16_t>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), dm, R,
-                       reverse ? 1 : 0);
+                       static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), dm, R);
   else
     hipLaunchKernelGGL(to_kblocked_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(src), static_cast<float*>(dst), dm, R,
-                       reverse ? 1 : 0);
+                       static_cast<const float*>(src), static_cast<float*>(dst), dm, R);
   return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@ namespace {
 // own regions, 256-byte aligned.
 struct BackwardPlan {
   ttt::WorkspacePlan fwd;
-  size_t wst, u, v, agu, ztr, dotr, sslots, da, g, gf, du, tpart, dpart, wtpart, dak,
+  size_t wst, u, v, agu, dot, sslots, da, g, gf, du, tpart, dpart, wtpart, dak,
       hk, uk, gk, wgut, total;
   int64_t wt_slices;  // token slices of the dW_target product (split over K = B*T)
 };
@@ -40,9 +40,8 @@ BackwardPlan plan_backward(const ttt::Dims& dm) {
   p.u = take(dm.conv ? BT * d * es : 0);                  // conv output U
   p.v = take(dm.proj ? BT * d * es : 0);                  // V^ = U W_target, row-major
   p.agu = take(BT * 2 * f * 4);                           // [A_g | A_u] per row (fp32)
-  p.ztr = take(f * (size_t)dm.P * es);                    // Zt, chunks reversed
-  p.dotr = take(d * (size_t)dm.P * es);                   // dOᵀ k-blocked, chunks reversed
-  p.sslots = take((size_t)dm.N * dm.B * d * f * es);      // S_j, reversed chunk order
+  p.dot = take(d * (size_t)dm.P * es);                    // dOᵀ k-blocked
+  p.sslots = take((size_t)dm.N * dm.B * d * f * es);      // S_j in slot j
   p.da = take(BT * 2 * f * es);                           // [dA_g | dA_u]
   p.gf = take(BT * d * 4);                                // G = Z_j S_jᵀ (dV^ = eta G), fp32
   p.g = take(dm.proj ? BT * d * es : 0);                  // G rounded: the GEMMs' operand
@@ -194,8 +193,7 @@ ttt_status_t ttt_mlp_backward_batched(
   void* U = dm.conv ? static_cast<void*>(base + bp.u) : const_cast<void*>(X0);
   void* V = dm.proj ? static_cast<void*>(base + bp.v) : U;
   float* Ag = reinterpret_cast<float*>(base + bp.agu);  // row t: [A_g | A_u], 2f wide
-  void* Ztr = base + bp.ztr;
-  void* dOtr = base + bp.dotr;
+  void* dOt = base + bp.dot;
   char* Sslots = base + bp.sslots;
   char* dA = base + bp.da;
   float* Gf = reinterpret_cast<float*>(base + bp.gf);
@@ -229,30 +227,28 @@ ttt_status_t ttt_mlp_backward_batched(
   void* Uk = base + bp.uk;
   void* Gk = base + bp.gk;
   void* WguT = base + bp.wgut;
-  e = ttt::launch_to_kblocked(H, Hk, dm, dm.d, false, s);
+  e = ttt::launch_to_kblocked(H, Hk, dm, dm.d, s);
   // [W_gate; W_up]ᵀ in TB x TB tiles (dH's B operand): row c holds
   // W_gate[:, c] then W_up[:, c]
   if (e == hipSuccess) e = ttt::launch_transpose(W_gate, WguT, Fi, Di, dm.dt, s, 2 * Fi, 0, true);
   if (e == hipSuccess) e = ttt::launch_transpose(W_up, WguT, Fi, Di, dm.dt, s, 2 * Fi, Fi, true);
-  if (e == hipSuccess && dm.proj) e = ttt::launch_to_kblocked(U, Uk, dm, dm.d, false, s);
+  if (e == hipSuccess && dm.proj) e = ttt::launch_to_kblocked(U, Uk, dm, dm.d, s);
   if (e != hipSuccess) return hip_fail(e, "backward");
 
-  // 3. Z in the scans' k-blocked layout (chunks in order and reversed); dOᵀ
-  //    k-blocked with the chunks reversed.  Then, in
-  //    one launch, the forward's scan (slot j = W^(j-1), written transposed)
-  //    and the same scan over dOᵀ and Z in reverse chunk order from dW_final
+  // 3. Z and dOᵀ in the scans' k-blocked layout.  Then, in one launch, the
+  //    forward's scan (slot j = W^(j-1), written transposed) and the same
+  //    scan over dOᵀ and Z walking the chunks last to first from dW_final
   //    (slot j = S_j; its final state is the gradient of the starting
   //    weight).
-  e = ttt::launch_to_kblocked(Z, Zt, dm, dm.f, false, s);
-  if (e == hipSuccess) e = ttt::launch_to_kblocked(Z, Ztr, dm, dm.f, true, s);
-  if (e == hipSuccess) e = ttt::launch_to_kblocked(dO, dOtr, dm, dm.d, true, s);
+  e = ttt::launch_to_kblocked(Z, Zt, dm, dm.f, s);
+  if (e == hipSuccess) e = ttt::launch_to_kblocked(dO, dOt, dm, dm.d, s);
   if (e == hipSuccess)
     e = dW_final ? hipMemcpyAsync(dW_start, dW_final, state, hipMemcpyDeviceToDevice, s)
                  : ttt::launch_fill_f32(dW_start, (int64_t)(state / 4), 0.0f, s);
   ttt::Dims dr = dm;
   dr.reverse_slots = true;  // S_j lands in slot j
   if (e == hipSuccess)
-    e = ttt::launch_dual_scan(dm, Vt, Zt, Wst, Wslots, dr, dOtr, Ztr, dW_start, Sslots, s);
+    e = ttt::launch_dual_scan(dm, Vt, Zt, Wst, Wslots, dr, dOt, Zt, dW_start, Sslots, s);
   if (e != hipSuccess) return hip_fail(e, "backward");
 
   // per chunk j: dZ_j = dO_j W^(j-1) + eta V^_j S_j (one launch: both
@@ -294,7 +290,7 @@ ttt_status_t ttt_mlp_backward_batched(
   //    gradients
   e = ttt::launch_dot(V, Gf, BTi * Di, dm.dt, 1.0f, dpart, d_eta, s);
   if (e == hipSuccess && dm.proj) e = ttt::launch_from_f32(Gf, G, BTi * Di, dm.dt, s);
-  if (e == hipSuccess && dm.proj) e = ttt::launch_to_kblocked(G, Gk, dm, dm.d, false, s);
+  if (e == hipSuccess && dm.proj) e = ttt::launch_to_kblocked(G, Gk, dm, dm.d, s);
   if (e != hipSuccess) return hip_fail(e, "backward");
   const int64_t tb = 128 / (int64_t)es, P = dm.P;  // tokens per 128-byte block row
   gemm(kRowK, kTiledRowK, BTi, Di, 2 * Fi, 1.f, dA, 2 * Fi, 0, WguT, 2 * Fi, 0, false, dH, Di, 0, 1,

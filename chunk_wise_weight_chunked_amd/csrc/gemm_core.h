@@ -623,22 +623,24 @@ __device__ __forceinline__ void lds_barrier() {
 // the loads they wait behind are only those of the following k-tile.  kStores
 // must not exceed the stores actually issued, or loads would stay in flight
 // past the barrier (the compiled scan kernels are checked for this).
-template <typename T, class S, int kStores, class LA, class LB, class Hook>
+// kmap(kt) is the loaders' k-tile for step kt (the identity, or another
+// order of the same k-tiles).
+template <typename T, class S, int kStores, class LA, class LB, class Hook, class KMap>
 __device__ __forceinline__ void mainloop_with_stores(Accum<S>& acc, LA& la, LB& lb, int64_t nk,
                                                      lds_char* smem, const LanePos& p,
-                                                     Hook&& before_ktile) {
+                                                     Hook&& before_ktile, KMap&& kmap) {
   constexpr int kLeave = kStores < 63 ? kStores : 63;
   if (nk <= 0) return;
-  la.issue(0, smem);
-  lb.issue(0, smem + S::BM * kRowBytes);
+  la.issue(kmap(0), smem);
+  lb.issue(kmap(0), smem + S::BM * kRowBytes);
   wait_vmcnt<0>();
   __syncthreads();
   for (int64_t kt = 0; kt < nk; ++kt) {
     const lds_char* cur = smem + (kt & 1) * S::kStageBytes;
     lds_char* nxt = smem + ((kt + 1) & 1) * S::kStageBytes;
     if (kt + 1 < nk) {
-      la.issue(kt + 1, nxt);
-      lb.issue(kt + 1, nxt + S::BM * kRowBytes);
+      la.issue(kmap(kt + 1), nxt);
+      lb.issue(kmap(kt + 1), nxt + S::BM * kRowBytes);
     }
     const bool stored = before_ktile(kt);
     Mma<T, S>::ktile(acc, cur, cur + S::BM * kRowBytes, p, [] {});

@@ -436,7 +436,7 @@ __global__ __launch_bounds__(256) void rows_to_vt_kernel(Dims dm, const T* __res
 // kSlotStageBytes) and stored 16 bytes per lane as whole row segments (128
 // bytes of a row, 64 of a transposed row, 4 KB runs of a tile): 16 store
 // instructions per lane and slot instead of 64 (32 transposed).
-template <typename T, class S, int kSlots = 1>
+template <typename T, class S, int kSlots = 1, bool kRevChunks = false>
 __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __restrict__ Vt,
                                                    const T* __restrict__ Zt,
                                                    float* __restrict__ W_state,
@@ -730,13 +730,25 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
   // one group: both operands are token-major k-blocks, each instruction one
   // contiguous KB, and spreading them measured slower here.)
   int64_t next_slot = 1, next_slot_kt = kt_per_chunk;  // counters, not a division per k-tile
-  mainloop_with_stores<T, S, kSlotStores>(acc, la, lb, nk, smem, p, [&](int64_t kt) {
-    if (kt != next_slot_kt || !with_slots) return false;
-    write_slot(next_slot);
-    ++next_slot;
-    next_slot_kt += kt_per_chunk;
-    return true;
-  });
+  // kRevChunks: the group's chunks in reverse order (each chunk's k-tiles in
+  // order) from operands stored in forward order
+  mainloop_with_stores<T, S, kSlotStores>(
+      acc, la, lb, nk, smem, p,
+      [&](int64_t kt) {
+        if (kt != next_slot_kt || !with_slots) return false;
+        write_slot(next_slot);
+        ++next_slot;
+        next_slot_kt += kt_per_chunk;
+        return true;
+      },
+      [&](int64_t kt) -> int64_t {
+        if constexpr (kRevChunks) {
+          const int64_t c = kt / kt_per_chunk;
+          return (gc - 1 - 2 * c) * kt_per_chunk + kt;
+        } else {
+          return kt;
+        }
+      });
   if (skip && gc > 1 && with_slots) write_slot(gc - 1);
 
 #pragma unroll
@@ -755,14 +767,14 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
 }
 
 // kOcc: workgroups meant to share a CU (the register budget follows).
-template <typename T, class S, int kSlots = 1, int kOcc = 1>
+template <typename T, class S, int kSlots = 1, int kOcc = 1, bool kRevChunks = false>
 __global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(
     kOcc * S::kWaves / 4, kOcc * S::kWaves / 4))) void prefix_update_kernel(
     Dims dm, const T* __restrict__ Vt, const T* __restrict__ Zt, float* __restrict__ W_state,
     T* __restrict__ slots, int64_t g0, int64_t gc, T* __restrict__ slots_t) {
   __shared__ __attribute__((aligned(16))) char smem_raw[S::kLdsBytes];
-  prefix_update_tile<T, S, kSlots>(dm, Vt, Zt, W_state, slots, g0, gc, blockIdx.x, gridDim.x,
-                                   (lds_char*)smem_raw, slots_t);
+  prefix_update_tile<T, S, kSlots, kRevChunks>(dm, Vt, Zt, W_state, slots, g0, gc, blockIdx.x,
+                                               gridDim.x, (lds_char*)smem_raw, slots_t);
 }
 
 // ===================================================================== S3
@@ -928,8 +940,8 @@ TTT_GEMM_KERNEL void dual_scan_kernel(Dims d1, const T* __restrict__ Vt1, const 
       prefix_update_tile<T, PrefixTile, 2 | kStage>(d1, Vt1, Zt1, W1, nullptr, 0, d1.N, b, blocks,
                                                     (lds_char*)smem_raw, slots1t);
   } else if (b - pad < blocks) {
-    prefix_update_tile<T, PrefixTile, 4 | kStage>(d2, Vt2, Zt2, W2, slots2, 0, d2.N, b - pad,
-                                                  blocks, (lds_char*)smem_raw);
+    prefix_update_tile<T, PrefixTile, 4 | kStage, true>(d2, Vt2, Zt2, W2, slots2, 0, d2.N,
+                                                        b - pad, blocks, (lds_char*)smem_raw);
   }
 }
 
@@ -1348,8 +1360,8 @@ static void launch_dual_scan_t(const Dims& d1, const T* Vt1, const T* Zt1, float
     const dim3 grid((unsigned)((d1.d / Small::BM) * (d1.f / Small::BN) * d1.B));
     hipLaunchKernelGGL((prefix_update_kernel<T, Small, 2>), grid, dim3(Small::kThreads), 0, s, d1,
                        Vt1, Zt1, W1, static_cast<T*>(nullptr), (int64_t)0, d1.N, slots1t);
-    hipLaunchKernelGGL((prefix_update_kernel<T, Small, 4>), grid, dim3(Small::kThreads), 0, s, d2,
-                       Vt2, Zt2, W2, slots2, (int64_t)0, d2.N, static_cast<T*>(nullptr));
+    hipLaunchKernelGGL((prefix_update_kernel<T, Small, 4, 1, true>), grid, dim3(Small::kThreads),
+                       0, s, d2, Vt2, Zt2, W2, slots2, (int64_t)0, d2.N, static_cast<T*>(nullptr));
     return;
   }
   const int blocks = (int)((d1.d / PrefixTile::BM) * (d1.f / PrefixTile::BN) * d1.B);

@@ -210,14 +210,14 @@ hipError_t launch_transpose(const void* src, void* dst, int64_t rows, int64_t co
 // Backward-pass kernels (backward.hip).
 constexpr int kTargetBackwardRows = 256;  // token rows per partial sum of the taps' gradient
 constexpr int kDotPartials = 1024;        // partial sums of the learning rate's gradient
-// dst = rows of src [B][T][R] in the k-blocked token-major layout (chunks
-// reversed if `reverse`), zeros in the padding columns.
-hipError_t launch_to_kblocked(const void* src, void* dst, const Dims& dm, int64_t R, bool reverse,
+// dst = rows of src [B][T][R] in the k-blocked token-major layout, zeros in
+// the padding columns.
+hipError_t launch_to_kblocked(const void* src, void* dst, const Dims& dm, int64_t R,
                               hipStream_t s);
 // The scans of two independent problems (same shapes) in one launch: the
 // first writes its slots transposed ([N][B][f][d], slots1t), the second in
 // tiles of TB x TB (slots2: [N][B][d/TB][f/TB][TB][TB], TB = 128 bytes of the
-// type).
+// type) and walks its chunks last to first (operands in forward order).
 hipError_t launch_dual_scan(const Dims& d1, const void* Vt1, const void* Zt1, float* W1,
                             void* slots1t, const Dims& d2, const void* Vt2, const void* Zt2,
                             float* W2, void* slots2, hipStream_t s);
