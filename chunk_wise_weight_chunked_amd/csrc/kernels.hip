@@ -669,7 +669,9 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
           const int row = 8 * s4 + (p.lane >> 3);
           v = lds_load<u32x4_t>(stage_slot + row * kRowBytes + ((((p.lane & 7) ^ (row & 7))) << 4));
         }
-        __builtin_amdgcn_raw_buffer_store_b128(v, sr, lane_st, wave_st + staged_uniform(i, s4), 0);
+        // non-temporal (cache policy nt): the slot is read back by the next
+        // launch's output tiles, long after it has left this XCD's L2
+        __builtin_amdgcn_raw_buffer_store_b128(v, sr, lane_st, wave_st + staged_uniform(i, s4), 2);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
