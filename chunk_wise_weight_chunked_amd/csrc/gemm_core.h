@@ -610,26 +610,20 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// The one-group-issue mainloop for a tile that stores part of its
-// accumulator to global memory between k-tiles.  before_ktile(kt) runs once
-// k-tile kt+1's loads are issued and before kt's MFMAs, while the accumulator
-// holds the sum over k-tiles [0, kt); it returns whether it issued kStores
-// store instructions.  One counter (vmcnt) covers vector loads, direct-to-LDS
-// loads and stores, and they retire in issue order -- the model gfx950's
-// compiler itself uses: for a direct-to-LDS load, three stores and a barrier
-// before the LDS is read it emits vmcnt(3).  So after such a k-tile the
-// closing wait leaves the last min(kStores, 63) operations -- the stores -- in
-// flight: they drain during the MFMAs instead of holding up the barrier, and
-// the loads they wait behind are only those of the following k-tile.  kStores
-// must not exceed the stores actually issued, or loads would stay in flight
-// past the barrier (the compiled scan kernels are checked for this).
-// kmap(kt) is the loaders' k-tile for step kt (the identity, or another
-// order of the same k-tiles).
-template <typename T, class S, int kStores, class LA, class LB, class Hook, class KMap>
+// The mainloop of a tile that stores part of its accumulator to global memory
+// between k-tiles (the prefix scan's weight slots).  before_ktile(kt) runs
+// before k-tile kt's MFMAs, while the accumulator holds the sum over k-tiles
+// [0, kt), and issues the stores when kt starts a chunk.  bf16: k-tile kt+1's
+// loads are then spread over kt's MFMAs (one every kEvery MFMAs, as in
+// mainloop); fp32: issued in one group before the stores.  Every k-tile ends
+// with vmcnt(0): the stores drain within the k-tile that issues them and no
+// vector-memory operation is in flight at the barrier.  kmap(kt) is the
+// loaders' k-tile for step kt (the identity, or another order of the same
+// k-tiles).
+template <typename T, class S, class LA, class LB, class Hook, class KMap>
 __device__ __forceinline__ void mainloop_with_stores(Accum<S>& acc, LA& la, LB& lb, int64_t nk,
                                                      lds_char* smem, const LanePos& p,
                                                      Hook&& before_ktile, KMap&& kmap) {
-  constexpr int kLeave = kStores < 63 ? kStores : 63;
   if (nk <= 0) return;
   la.issue(kmap(0), smem);
   lb.issue(kmap(0), smem + S::BM * kRowBytes);
@@ -638,16 +632,33 @@ __device__ __forceinline__ void mainloop_with_stores(Accum<S>& acc, LA& la, LB& 
   for (int64_t kt = 0; kt < nk; ++kt) {
     const lds_char* cur = smem + (kt & 1) * S::kStageBytes;
     lds_char* nxt = smem + ((kt + 1) & 1) * S::kStageBytes;
-    if (kt + 1 < nk) {
-      la.issue(kmap(kt + 1), nxt);
-      lb.issue(kmap(kt + 1), nxt + S::BM * kRowBytes);
+    const bool more = kt + 1 < nk;
+    if constexpr (sizeof(T) == 2) {
+      using M = Mma16<S, false, false>;
+      constexpr int kLoads = LA::kPer + LB::kPer;
+      constexpr int kMfmas = M::kSteps * S::MB * S::NB;
+      constexpr int kEvery = 2 * kLoads <= kMfmas / 2 ? 2 : 1;
+      static_assert(kLoads <= kMfmas, "one load instruction per MFMA at most");
+      before_ktile(kt);
+      const rsrc_t ra = la.rsrc(kmap(kt + 1), more), rb = lb.rsrc(kmap(kt + 1), more);
+      M::ktile_spread(acc, cur, cur + S::BM * kRowBytes, p, [&](int idx) {
+        if (idx % kEvery == 0 && idx / kEvery < kLoads) {
+          const int q = idx / kEvery;
+          if (q < LA::kPer)
+            la.issue_one(ra, nxt, q);
+          else
+            lb.issue_one(rb, nxt + S::BM * kRowBytes, q - LA::kPer);
+        }
+      });
+    } else {
+      if (more) {
+        la.issue(kmap(kt + 1), nxt);
+        lb.issue(kmap(kt + 1), nxt + S::BM * kRowBytes);
+      }
+      before_ktile(kt);
+      Mma<T, S>::ktile(acc, cur, cur + S::BM * kRowBytes, p, [] {});
     }
-    const bool stored = before_ktile(kt);
-    Mma<T, S>::ktile(acc, cur, cur + S::BM * kRowBytes, p, [] {});
-    if (stored)
-      wait_vmcnt<kLeave>();
-    else
-      wait_vmcnt<0>();
+    wait_vmcnt<0>();
     lds_barrier();
   }
 }

@@ -492,7 +492,7 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
 
   const int64_t slot_stride = dm.B * d * f;
   // bf16 slots leave as 32-bit column pairs (pair_pack): half the store
-  // instructions, so that all of them fit the wait counter's range
+  // instructions of 16-bit stores
   const bool odd = p.lane & 1;
   uint32_t lane_pair[2];
 #pragma unroll
@@ -506,9 +506,6 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
   static_assert(kLayout == 1 || kLayout == 2 || kLayout == 4, "one slot layout");
   static_assert(!kStaged || (sizeof(T) == 2 && S::WM == 128 && S::WN == 64),
                 "staged slots: bf16, waves of 128 x 64");
-  constexpr int kSlotStores = kStaged        ? S::MB * 4
-                              : kLayout == 2 ? S::MB * 4 * S::NB
-                                             : S::MB * 4 * S::NB * (sizeof(T) == 2 ? 2 : 4);
   const uint32_t lane_t = (uint32_t)(((p.wave_n0 + (p.lane & 31)) * d + p.wave_m0 +
                                       4 * (p.lane >> 5)) * (int64_t)sizeof(T));
   const uint32_t du = (uint32_t)d;
@@ -728,20 +725,18 @@ __device__ __forceinline__ void prefix_update_tile(const Dims& dm, const T* __re
   const bool skip = dm.skip_last && g0 + gc == dm.N;
   const int64_t nk = (skip ? gc - 1 : gc) * kt_per_chunk;
   // Slot jj (the weight after jj chunks) is stored before the MFMAs of the
-  // chunk's first k-tile and drains while they run.  (The loads are issued in
-  // one group: both operands are token-major k-blocks, each instruction one
-  // contiguous KB, and spreading them measured slower here.)
+  // chunk's first k-tile and drains while they run, ahead of the next
+  // k-tile's loads (spread over the MFMAs for bf16).
   int64_t next_slot = 1, next_slot_kt = kt_per_chunk;  // counters, not a division per k-tile
   // kRevChunks: the group's chunks in reverse order (each chunk's k-tiles in
   // order) from operands stored in forward order
-  mainloop_with_stores<T, S, kSlotStores>(
+  mainloop_with_stores<T, S>(
       acc, la, lb, nk, smem, p,
       [&](int64_t kt) {
-        if (kt != next_slot_kt || !with_slots) return false;
+        if (kt != next_slot_kt || !with_slots) return;
         write_slot(next_slot);
         ++next_slot;
         next_slot_kt += kt_per_chunk;
-        return true;
       },
       [&](int64_t kt) -> int64_t {
         if constexpr (kRevChunks) {

@@ -1,22 +1,20 @@
-"""The vector-memory wait model the scan kernels rely on, checked on the CPU
-against gfx950 code that hipcc generates.
+"""The vector-memory waits of the scan kernels, checked on the CPU against
+gfx950 code that hipcc generates.
 
-The prefix scan stores a weight slot between issuing the next k-tile's
-direct-to-LDS loads and that k-tile's barrier, and then waits with
-vmcnt(N) for N >= 1, leaving the last N vector-memory operations (the slot
-stores) in flight.  That is correct only if one counter covers loads and
-stores and they retire in issue order, so that vmcnt(N) implies that
-everything issued before the last N operations has completed.
+The prefix scan stores a weight slot at the start of each chunk's first
+k-tile, before that k-tile's MFMAs, and ends every k-tile with vmcnt(0) and
+a barrier: no vector-memory operation is in flight when another wave reads
+the LDS stage the direct-to-LDS loads filled.  (An earlier form left the slot
+stores in flight with vmcnt(N), which is correct only if one counter retires
+loads and stores in issue order; the code no longer relies on that.)
 
-1. The compiler's own wait insertion for gfx950 assumes exactly that: for a
-   direct-to-LDS load, three stores and a workgroup barrier before the LDS is
-   read, it emits vmcnt(3), not vmcnt(0); for a global load followed by three
-   stores and a use of the loaded value, likewise vmcnt(3).
-2. In the compiled scan kernels, every vmcnt(N > 0) that guards a barrier has
-   at least N stores, and no load, among the last N vector-memory
-   instructions before it (in program text: the store block sits between the
-   loads and the wait), so the loads it must cover are not among those left
-   in flight.
+1. The counter model of the compiler's own wait insertion for gfx950, kept as
+   the record of what vmcnt(N) means there: for a direct-to-LDS load, three
+   stores and a workgroup barrier before the LDS is read, it emits vmcnt(3),
+   not vmcnt(0); for a global load followed by three stores and a use of the
+   loaded value, likewise vmcnt(3).
+2. In the compiled scan kernels, no wait that guards a barrier leaves a load
+   in flight on any path (a dataflow pass over the basic blocks).
 
 No GPU is needed: both checks read the AMD assembly of code built here.
 """
@@ -221,36 +219,28 @@ def _barrier_waits(body):
     return found
 
 
-def test_scan_kernels_leave_only_stores_in_flight(tmp_path):
+def test_scan_kernels_leave_no_load_in_flight(tmp_path):
     src = os.path.join(hipbuild.CSRC, "kernels.hip")
     funcs = _functions(_compile(src, str(tmp_path / "kernels.s")))
     # the scan launches, and every instantiation of the scan-only kernel
     # (tile shapes, slot layouts, data types)
     prefix = [n for n in funcs if "prefix_update_kernel" in n]
     assert len(prefix) >= 4, prefix
-    # every instantiation of each scan kernel (slot layouts, data types)
     names = sorted({n for key in SCAN_KERNELS for n in funcs if key in n}) + prefix
     assert len(names) >= len(SCAN_KERNELS) + len(prefix), names
     for key in names:
         body = funcs[key]
-        waits = _barrier_waits(body)
-        leaves_stores = 0
-        for at, states in waits.items():
+        assert any("s_barrier" in l for l in body), key  # the k-loop's barrier is there
+        for at, states in _barrier_waits(body).items():
             n = int(WAIT_VM.match(body[at]).group(1))
-            # what the wait leaves in flight is stores only, on every path of
-            # the control flow; or, where the pass cannot tell two tests of
-            # one condition apart (stores issued under `if (stored)`, the
-            # wait chosen by the same test further on), the n vector-memory
-            # instructions right before it in the text are all stores
+            # on every path of the control flow, what the wait leaves in
+            # flight is stores only; or, where the pass cannot tell two tests
+            # of one condition apart, the n vector-memory instructions right
+            # before it in the text are all stores
             if any("L" in st for st in states):
                 prev = [l for l in body[:at] if VMEM.match(l)][-n:]
                 assert len(prev) == n and all(VMEM.match(l).group(2) == "store" for l in prev), (
                     key, at, n, [l.strip() for l in prev if VMEM.match(l).group(2) != "store"][:4])
-                leaves_stores += 1
-            elif any("S" in st for st in states):
-                leaves_stores += 1
-        # and the scan's own wait, which leaves slot stores in flight, is there
-        assert leaves_stores > 0, key
 
 
 def test_dataflow_sees_a_load_left_in_flight():
