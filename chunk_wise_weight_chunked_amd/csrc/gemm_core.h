@@ -534,9 +534,11 @@ struct KMajorLoader {
 // every wave has finished k-tile kt and no read is in flight (it may use
 // registers and global memory, not LDS).
 // kTrA (bf16 only): the A tile is k-major (see read_a_tr) and its fragments
-// are read with transposed loads.
+// are read with transposed loads.  kEveryWant (bf16 spread issue): one load
+// every kEveryWant MFMAs; 0 takes every second MFMA when the loads then still
+// end in the first half of the k-tile, else every MFMA.
 template <typename T, class S, bool kSpread = true, bool kTrA = false, bool kTrB = false,
-          class LA, class LB, class Hook>
+          int kEveryWant = 0, class LA, class LB, class Hook>
 __device__ __forceinline__ void mainloop(Accum<S>& acc, LA& la, LB& lb, int64_t nk, lds_char* smem,
                                          const LanePos& p, Hook&& after_ktile) {
   static_assert(sizeof(T) == 4 || !(kTrA || kTrB) || kSpread,
@@ -544,15 +546,14 @@ __device__ __forceinline__ void mainloop(Accum<S>& acc, LA& la, LB& lb, int64_t 
   if (nk <= 0) return;
   if constexpr (kSpread && sizeof(T) == 2) {
     // bf16: k-tile kt+1's load instructions are spread over
-    // k-tile kt's MFMAs, one every kEvery MFMAs from the first (every second
-    // when they then still end in the first half of the k-tile).  After the
+    // k-tile kt's MFMAs, one every kEvery MFMAs from the first.  After the
     // last k-tile they read an empty range into the idle stage; the closing
     // wait drains them before the caller touches LDS.
     using M = Mma16<S, kTrA, kTrB>;
     constexpr int kLoads = LA::kPer + LB::kPer;
     constexpr int kMfmas = M::kSteps * S::MB * S::NB;
-    constexpr int kEvery = 2 * kLoads <= kMfmas / 2 ? 2 : 1;
-    static_assert(kLoads <= kMfmas, "one load instruction per MFMA at most");
+    constexpr int kEvery = kEveryWant > 0 ? kEveryWant : (2 * kLoads <= kMfmas / 2 ? 2 : 1);
+    static_assert(kLoads * kEvery <= kMfmas, "the loads fit the k-tile's MFMAs");
     la.issue(0, smem);
     lb.issue(0, smem + S::BM * kRowBytes);
     wait_vmcnt<0>();

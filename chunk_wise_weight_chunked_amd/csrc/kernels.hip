@@ -825,7 +825,9 @@ __device__ __forceinline__ void down_proj_tile(const Dims& dm, const T* __restri
     KMajorLoader<T, S::kWaves> la;
     la.init(reinterpret_cast<const char*>(Zs) + (col0 / kTokenAlign) * block_bytes, block_bytes,
             kRowBytes, kTokenAlign * kRowBytes, (dm.P - col0) / kTokenAlign * block_bytes);
-    mainloop<T, S, true, true>(acc, la, lb, ld / kRowBytes, smem, p, [](int64_t) {});
+    // one load per MFMA: the output tiles' operands come from HBM (slots of the
+    // previous launch, Z of the previous group), so they are issued early
+    mainloop<T, S, true, true, false, 1>(acc, la, lb, ld / kRowBytes, smem, p, [](int64_t) {});
   } else {
     DirectLoader<S::BM, S::kWaves> la;
     la.init(reinterpret_cast<const char*>(Zs) + row0 * ld, ld, kRowBytes, (c_len - m0) * ld,
