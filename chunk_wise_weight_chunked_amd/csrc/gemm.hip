@@ -131,6 +131,12 @@ __device__ __forceinline__ auto make_loader(const char* X, int64_t ld, int64_t s
 
 constexpr bool is_kmajor(int l) { return l == kKMajor || l == kTiledKMajor; }
 
+// The batched products issue one next-k-tile load per MFMA: their operands
+// (per-chunk weights and gradient sums, k-blocked copies) mostly stream from
+// HBM, and issuing the loads early measured faster (the 32K backward 22.41 ->
+// 21.86 ms) than one every second MFMA.
+constexpr int kGemmEvery = 1;
+
 // The tile's position: batch b and the first row and column of the tile.
 struct GemmTilePos {
   int64_t b, m0, n0;
@@ -164,7 +170,7 @@ __device__ __forceinline__ void gemm_accumulate(const GemmArgs& g, const GemmArg
                                           g2.sa, b, t.m0, g.M, K2);
     auto lb = make_loader<T, kLB2, S::BN>(static_cast<const char*>(g2.B) + b * g2.sb * es, g2.ldb,
                                           g2.sb, b, t.n0, g.N, K2);
-    mainloop<T, S, true, is_kmajor(kLA2), is_kmajor(kLB2)>(acc, la, lb, (K2 + TB - 1) / TB, smem,
+    mainloop<T, S, true, is_kmajor(kLA2), is_kmajor(kLB2), kGemmEvery>(acc, la, lb, (K2 + TB - 1) / TB, smem,
                                                            p, [](int64_t) {});
 #pragma unroll
     for (int i = 0; i < S::MB; ++i)
@@ -178,7 +184,7 @@ __device__ __forceinline__ void gemm_accumulate(const GemmArgs& g, const GemmArg
                                        b, t.m0, g.M, K);
   auto lb = make_loader<T, kLB, S::BN>(static_cast<const char*>(g.B) + b * g.sb * es, g.ldb, g.sb,
                                        b, t.n0, g.N, K);
-  mainloop<T, S, true, is_kmajor(kLA), is_kmajor(kLB)>(acc, la, lb, (K + TB - 1) / TB, smem, p,
+  mainloop<T, S, true, is_kmajor(kLA), is_kmajor(kLB), kGemmEvery>(acc, la, lb, (K + TB - 1) / TB, smem, p,
                                                        [](int64_t) {});
 }
 
